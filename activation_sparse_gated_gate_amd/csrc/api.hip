@@ -1,0 +1,266 @@
+// api.hip -- the C ABI of libsffn: descriptor validation, workspace layout and
+// dispatch to the gfx950 kernels.  Every entry point validates its arguments
+// before any launch and reports problems through the status code.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <stdio.h>
+#include <string.h>
+
+#include "sffn_internal.h"
+
+namespace sffn {
+
+static thread_local char g_hip_err[256] = "";
+
+static sffn_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return SFFN_OK;
+    snprintf(g_hip_err, sizeof g_hip_err, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return SFFN_ERR_HIP;
+}
+
+PersistentLayout persistent_layout(const sffn_layer_desc &D)
+{
+    PersistentLayout P{};
+    const int d = D.d_model, f = D.d_ff, wt = D.wtype;
+    const size_t mat = row_bytes(wt, d) * (size_t)f;
+    const size_t scl_f = wt == SFFN_W_INT4_G128 ? (size_t)f * (d / 128) * 2 : 0;  // [f][d/128]
+    const size_t scl_d = wt == SFFN_W_INT4_G128 ? (size_t)d * (f / 128) * 2 : 0;  // [d][f/128] or transposed
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    const bool dec = D.layouts & SFFN_LAYOUT_DECODE;
+    const bool pre = D.layouts & SFFN_LAYOUT_PREFILL;
+    P.wg = dec ? take(mat) : 0;
+    P.sg = dec ? take(scl_f) : 0;
+    P.wu = dec ? take(mat) : 0;
+    P.su = dec ? take(scl_f) : 0;
+    P.wdt = dec ? take(mat) : 0;
+    P.sdt = dec ? take(scl_d) : 0;
+    P.wdn = dec ? take((size_t)f * 8) : 0;
+    P.wd = take(mat);
+    P.sd = take(scl_d);
+    P.wgu = pre ? take(2 * mat) : 0;
+    P.wdp = P.wd;
+    P.total = o;
+    return P;
+}
+
+ScratchLayout scratch_layout(const sffn_layer_desc &D)
+{
+    ScratchLayout S{};
+    const int d = D.d_model, f = D.d_ff;
+    const size_t B = (size_t)D.max_rows;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    if (D.layouts & SFFN_LAYOUT_DECODE) {
+        S.xhat = take(B * d * 4);
+        S.G = take(B * f * 4);
+        S.U = take(B * f * 4);
+        S.keys = take(B * f * 8);
+        S.bits = take(B * (f / 32) * 4);
+        S.list_cnt = take((size_t)f * 4);
+        S.list_idx = take(((size_t)f + 64) * 4);
+        S.partial = take((size_t)kGatherWGs * B * d * 4);
+    }
+    if (D.layouts & SFFN_LAYOUT_PREFILL) {
+        S.tscore = take(B * 4 * 2);   // scores and their sorted copy
+        S.tflag = take(B * 4);
+        S.pH = take(B * f * 2);       // H (bf16) for up to L gathered rows
+    }
+    S.total = o;
+    return S;
+}
+
+static bool desc_ok(const sffn_layer_desc *D, sffn_status *why)
+{
+    *why = SFFN_ERR_INVALID_ARG;
+    if (!D) return false;
+    if (D->d_model < 256 || D->d_model > 16384 || D->d_model % 256) return false;
+    if (D->d_ff < 128 || D->d_ff > 65536 || D->d_ff % 128) return false;
+    if (D->wtype < SFFN_W_F32 || D->wtype > SFFN_W_INT4_G128) return false;
+    if (D->act != SFFN_ACT_RELU && D->act != SFFN_ACT_SILU) return false;
+    if ((D->rmsnorm != 0 && D->rmsnorm != 1) || (D->residual != 0 && D->residual != 1)) return false;
+    if (D->layouts <= 0 || (D->layouts & ~(SFFN_LAYOUT_DECODE | SFFN_LAYOUT_PREFILL))) return false;
+    if (D->rmsnorm && !(D->eps >= 0.0f)) return false;
+    if (D->max_rows < 1) return false;
+    if (D->layouts & SFFN_LAYOUT_DECODE) {
+        if (D->max_rows > kMaxDecodeRows) return false;
+        if (D->wtype == SFFN_W_INT4_G128 && D->max_rows > kMaxInt4Rows) { *why = SFFN_ERR_UNSUPPORTED; return false; }
+    }
+    if (D->layouts & SFFN_LAYOUT_PREFILL) {
+        if (D->max_rows > kMaxPrefillRows) return false;
+        if (D->wtype != SFFN_W_BF16 || D->act != SFFN_ACT_SILU || D->rmsnorm || D->residual) {
+            *why = SFFN_ERR_UNSUPPORTED;
+            return false;
+        }
+    }
+    return true;
+}
+
+}  // namespace sffn
+
+using namespace sffn;
+
+struct sffn_layer {
+    Layer L;
+};
+
+extern "C" {
+
+const char *sffn_status_string(sffn_status s)
+{
+    switch (s) {
+    case SFFN_OK: return "ok";
+    case SFFN_ERR_INVALID_ARG: return "invalid argument";
+    case SFFN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SFFN_ERR_WORKSPACE: return "workspace too small";
+    case SFFN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *sffn_last_hip_error(void) { return g_hip_err; }
+
+sffn_status sffn_workspace_size(const sffn_layer_desc *desc, size_t *persistent_bytes, size_t *scratch_bytes)
+{
+    sffn_status why;
+    if (!desc_ok(desc, &why)) return why;
+    if (!persistent_bytes || !scratch_bytes) return SFFN_ERR_INVALID_ARG;
+    *persistent_bytes = persistent_layout(*desc).total;
+    *scratch_bytes = scratch_layout(*desc).total;
+    return SFFN_OK;
+}
+
+sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const void *w_up, const void *w_down,
+                        const void *s_gate, const void *s_up, const void *s_down, void *persistent,
+                        size_t persistent_bytes, void *stream, sffn_t *out)
+{
+    sffn_status why;
+    if (!desc_ok(desc, &why)) return why;
+    if (!out || !w_gate || !w_up || !w_down || !persistent) return SFFN_ERR_INVALID_ARG;
+    const bool i4 = desc->wtype == SFFN_W_INT4_G128;
+    if (i4 != (s_gate != nullptr) || i4 != (s_up != nullptr) || i4 != (s_down != nullptr)) return SFFN_ERR_INVALID_ARG;
+    if ((uintptr_t)persistent & 255) return SFFN_ERR_INVALID_ARG;
+    if (((uintptr_t)w_gate | (uintptr_t)w_up | (uintptr_t)w_down) & 15) return SFFN_ERR_INVALID_ARG;
+    const PersistentLayout P = persistent_layout(*desc);
+    if (persistent_bytes < P.total) return SFFN_ERR_WORKSPACE;
+
+    sffn_layer *h = new (std::nothrow) sffn_layer;
+    if (!h) return SFFN_ERR_INVALID_ARG;
+    Layer &L = h->L;
+    L.desc = *desc;
+    uint8_t *base = (uint8_t *)persistent;
+    const bool dec = desc->layouts & SFFN_LAYOUT_DECODE;
+    if (dec) {
+        L.wg = base + P.wg;
+        L.wu = base + P.wu;
+        L.wdt = base + P.wdt;
+        L.wdn = (const double *)(base + P.wdn);
+        if (i4) {
+            L.sg = (const uint16_t *)(base + P.sg);
+            L.su = (const uint16_t *)(base + P.su);
+            L.sdt = (const uint16_t *)(base + P.sdt);
+        }
+    }
+    L.wd = base + P.wd;
+    if (i4) L.sd = (const uint16_t *)(base + P.sd);
+    if (desc->layouts & SFFN_LAYOUT_PREFILL) {
+        L.wgu = (const uint16_t *)(base + P.wgu);
+        L.wdp = (const uint16_t *)(base + P.wdp);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_relayout(L, w_gate, w_up, w_down, s_gate, s_up, s_down, base, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_status(e);
+    }
+    *out = h;
+    return SFFN_OK;
+}
+
+void sffn_destroy(sffn_t layer) { delete layer; }
+
+static bool decode_mode(int m)
+{
+    return m == SFFN_MODE_ALL || m == SFFN_MODE_EXACT || m == SFFN_MODE_THRESH || m == SFFN_MODE_TOPK;
+}
+
+static sffn_status policy_ok(const sffn_layer *h, const sffn_policy *p)
+{
+    if (!h || !p) return SFFN_ERR_INVALID_ARG;
+    const sffn_layer_desc &D = h->L.desc;
+    if (p->mode == SFFN_MODE_TOKENS) {
+        if (!(D.layouts & SFFN_LAYOUT_PREFILL)) return SFFN_ERR_INVALID_ARG;
+        if (!(p->mass_thresh >= 0.0) || p->recent_n < 0 || p->min_keep < 0) return SFFN_ERR_INVALID_ARG;
+        return SFFN_OK;
+    }
+    if (!decode_mode(p->mode) && p->mode != SFFN_MODE_DENSE) return SFFN_ERR_INVALID_ARG;
+    if (!(D.layouts & SFFN_LAYOUT_DECODE)) return SFFN_ERR_INVALID_ARG;
+    if (p->mode == SFFN_MODE_TOPK && (p->topk_k < 1 || p->topk_k > D.d_ff)) return SFFN_ERR_INVALID_ARG;
+    if (p->use_union != 0 && p->use_union != 1) return SFFN_ERR_INVALID_ARG;
+    if (p->mode == SFFN_MODE_TOPK && D.act != SFFN_ACT_SILU) return SFFN_ERR_UNSUPPORTED;
+    return SFFN_OK;
+}
+
+sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows, int32_t *idx_out,
+                        int32_t *count_out, void *scratch, size_t scratch_bytes, void *stream)
+{
+    sffn_status s = policy_ok(layer, policy);
+    if (s != SFFN_OK) return s;
+    if (policy->mode == SFFN_MODE_DENSE) return SFFN_ERR_INVALID_ARG;
+    const sffn_layer_desc &D = layer->L.desc;
+    if (!in || !idx_out || !count_out || !scratch) return SFFN_ERR_INVALID_ARG;
+    if (rows < 1 || rows > D.max_rows) return SFFN_ERR_INVALID_ARG;
+    if ((uintptr_t)scratch & 255) return SFFN_ERR_INVALID_ARG;
+    if (scratch_bytes < scratch_layout(D).total) return SFFN_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (policy->mode == SFFN_MODE_TOKENS) {
+        if ((uintptr_t)in & 15) return SFFN_ERR_INVALID_ARG;
+        PrefillSelectCall c{&layer->L, (const uint16_t *)in, rows, policy->mass_thresh, policy->recent_n,
+                            policy->min_keep, idx_out, count_out, (uint8_t *)scratch, st};
+        return hip_status(launch_prefill_select(c));
+    }
+    if ((uintptr_t)in & 15) return SFFN_ERR_INVALID_ARG;
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->gate_bias, policy->theta,
+                 rows, (const float *)in, nullptr, idx_out, count_out, (uint8_t *)scratch, st};
+    return hip_status(launch_decode(c, false));
+}
+
+sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows, void *out,
+                         const int32_t *idx_in, const int32_t *count_in, int32_t *idx_out, int32_t *count_out,
+                         void *scratch, size_t scratch_bytes, void *stream)
+{
+    sffn_status s = policy_ok(layer, policy);
+    if (s != SFFN_OK) return s;
+    const sffn_layer_desc &D = layer->L.desc;
+    if (!in || !out || !scratch) return SFFN_ERR_INVALID_ARG;
+    if (rows < 1 || rows > D.max_rows) return SFFN_ERR_INVALID_ARG;
+    if ((uintptr_t)scratch & 255) return SFFN_ERR_INVALID_ARG;
+    if (((uintptr_t)in | (uintptr_t)out) & 15) return SFFN_ERR_INVALID_ARG;
+    if (scratch_bytes < scratch_layout(D).total) return SFFN_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (policy->mode == SFFN_MODE_TOKENS) {
+        if (!idx_in || !count_in || idx_out || count_out) return SFFN_ERR_INVALID_ARG;
+        PrefillForwardCall c{&layer->L, (const uint16_t *)in, (uint16_t *)out, rows, idx_in, count_in,
+                             (uint8_t *)scratch, st};
+        return hip_status(launch_prefill_forward(c));
+    }
+    if (idx_in || count_in) return SFFN_ERR_INVALID_ARG;
+    if (in == out) return SFFN_ERR_INVALID_ARG;
+    if (policy->mode == SFFN_MODE_DENSE && (idx_out || count_out)) return SFFN_ERR_INVALID_ARG;
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->gate_bias, policy->theta,
+                 rows, (const float *)in, (float *)out, idx_out, count_out, (uint8_t *)scratch, st};
+    return hip_status(launch_decode(c, true));
+}
+
+}  // extern "C"

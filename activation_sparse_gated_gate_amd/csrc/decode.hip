@@ -1,0 +1,817 @@
+// decode.hip -- gfx950 kernels of the decode path (batch of 1..16 tokens).
+//
+// Path (one layer, all launches on the caller's stream, no host sync):
+//   [rmsnorm]  x_hat = x / sqrt(mean(x^2) + eps) in the fixed fp32 order
+//   gate       g'_j = fl(W_gate[j,:] . x_hat + b) for every neuron j, in the fixed
+//              fp32 order (64 lane accumulators, chunk c -> lane c mod 64, halving
+//              tree), fused with the selection predicate and a per-workgroup
+//              compaction (wave ballot + mbcnt) into ascending active lists.
+//              Exact ReLU gating and the gate threshold follow denseflux
+//              (sections 3, 4.1, 5.1-5.3): the gate is read in full, W_up rows and
+//              W_down columns only for active neurons.
+//   topk       (weight-aware top-k, WiSparse notes, sections 2.3 / 3.2) the gate
+//              kernel also produces u in the fixed order; one workgroup per token
+//              ranks score = |silu(g') u| * ||W_down[:, j]||_2 (fp64) with an exact
+//              radix select, ties to the lower index; the union over the batch is
+//              compacted into the same ascending lists.
+//   gather     the active list is cut into equal shares; each workgroup reads
+//              only its neurons' W_up rows (u, then h = act(g') u) and W_down^T
+//              rows, accumulating a partial y with coalesced 16-byte loads.
+//   reduce     y = sum of the partials in a fixed order (+ x for the residual).
+// The dense baseline (mode DENSE) is two plain GEMV launches: gate+up fused
+// (h for every neuron), then W_down rows dotted with h.
+#include <hip/hip_runtime.h>
+
+#include "dev_common.h"
+
+namespace sffn {
+
+enum { OUT_GATE = 0, OUT_GATE_UP = 1, OUT_DENSE_GU = 2, OUT_DENSE_DOWN = 3 };
+
+// ---------------------------------------------------------------------------
+// launch configuration per weight type and batch bucket
+// ---------------------------------------------------------------------------
+template <int WT, int BT> struct Cfg {
+    static constexpr int E = Chunk<WT>::E;
+    // chunk-columns staged per slice: keeps x in LDS at <= 32 KB (64 KB int4 x 8)
+    static constexpr int KMAX =
+        WT == SFFN_W_F32 ? (BT == 1 ? 4 : BT == 4 ? 2 : 1)
+        : WT == SFFN_W_BF16 ? (BT == 1 ? 8 : BT == 4 ? 2 : 1)
+                            : (BT == 1 ? 2 : 1);
+    static constexpr int RPW = BT == 1 ? 4 : 2;      // rows per wave
+    static constexpr int NW = BT >= 8 ? 8 : 4;       // waves per workgroup
+    static constexpr int CPT = (WT == SFFN_W_BF16 && BT == 1) ? 16 : (WT == SFFN_W_F32 ? 4 : 8);
+    static constexpr int UNR = BT >= 8 ? 2 : 4;      // down rows in flight per thread
+};
+
+// ---------------------------------------------------------------------------
+// RMSNorm prologue (one wave per token)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_rmsnorm(const float *__restrict__ x, float *__restrict__ xhat,
+                                                int d, float eps)
+{
+    const int t = blockIdx.x, lane = threadIdx.x;
+    const float *xt = x + (size_t)t * d;
+    float acc = 0.0f;
+    for (int c = lane; c < d / 4; c += 64) {
+        const float4 v = *(const float4 *)(xt + 4 * c);
+        acc = __builtin_fmaf(v.x, v.x, acc);
+        acc = __builtin_fmaf(v.y, v.y, acc);
+        acc = __builtin_fmaf(v.z, v.z, acc);
+        acc = __builtin_fmaf(v.w, v.w, acc);
+    }
+    const float ss = wave_tree_sum(acc);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int i = lane; i < d; i += 64) xhat[(size_t)t * d + i] = xt[i] * r;
+}
+
+// ---------------------------------------------------------------------------
+// row dot products in the fixed order: gate (+up), dense gate-up, dense down
+// ---------------------------------------------------------------------------
+struct RowDotArgs {
+    const uint8_t *w0;
+    const uint16_t *s0;
+    const uint8_t *w1;
+    const uint16_t *s1;
+    int rows, cols, B;
+    const float *x;      // [B][cols]
+    float *o0;           // G / H / out, [B][rows]
+    float *o1;           // U, [B][rows]
+    const float *resid;  // [B][rows] or null
+    int mode, act;
+    float bias, theta;
+    int *list_cnt, *list_idx;
+};
+
+template <int WT, int BT, int OUT>
+__global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotArgs a)
+{
+    using C = Cfg<WT, BT>;
+    constexpr int E = C::E, KMAX = C::KMAX, NW = C::NW;
+    constexpr bool TWO = (OUT == OUT_GATE_UP || OUT == OUT_DENSE_GU);
+    constexpr int RPW = TWO ? (C::RPW > 1 ? C::RPW / 2 : 1) : C::RPW;
+    constexpr int R = NW * RPW;
+    constexpr int SL = KMAX * 64 * E;  // floats per token per slice
+    __shared__ __align__(16) float xs[BT * SL];
+    __shared__ int flags[R];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row_base = blockIdx.x * R;
+    const int rowA = row_base + wave * RPW;
+    const int nch = a.cols / E;
+    const int K = (nch + 63) >> 6;
+    const size_t rb = (WT == SFFN_W_F32) ? (size_t)a.cols * 4 : (WT == SFFN_W_BF16) ? (size_t)a.cols * 2 : (size_t)a.cols / 2;
+    const int sst = a.cols / 128;
+    const int B = a.B;
+
+    float ag[BT][RPW], au[BT][RPW];
+#pragma unroll
+    for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) ag[t][r] = au[t][r] = 0.0f;
+
+    for (int k0 = 0; k0 < K; k0 += KMAX) {
+        const int e0 = k0 * 64 * E;
+        const int ne = min(SL, a.cols - e0);
+        const int n4 = ne >> 2;
+        __syncthreads();
+        for (int i = threadIdx.x; i < B * n4; i += NW * 64) {
+            const int t = i / n4, c4 = i - t * n4;
+            *(float4 *)&xs[t * SL + 4 * c4] = *(const float4 *)&a.x[(size_t)t * a.cols + e0 + 4 * c4];
+        }
+        __syncthreads();
+
+        uint4 w0v[KMAX][RPW], w1v[TWO ? KMAX : 1][TWO ? RPW : 1];
+        float s0v[KMAX][RPW], s1v[TWO ? KMAX : 1][TWO ? RPW : 1];
+#pragma unroll
+        for (int kk = 0; kk < KMAX; ++kk) {
+            const int c = (k0 + kk) * 64 + lane;
+            const bool ok = (k0 + kk < K) && (c < nch);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int row = rowA + r;
+                w0v[kk][r] = make_uint4(0, 0, 0, 0);
+                s0v[kk][r] = 0.0f;
+                if constexpr (TWO) { w1v[kk][r] = make_uint4(0, 0, 0, 0); s1v[kk][r] = 0.0f; }
+                if (ok && row < a.rows) {
+                    w0v[kk][r] = ld16(a.w0 + (size_t)row * rb + (size_t)c * 16);
+                    if constexpr (WT == SFFN_W_INT4_G128) s0v[kk][r] = half_bits_to_float(a.s0[(size_t)row * sst + (c >> 2)]);
+                    if constexpr (TWO) {
+                        w1v[kk][r] = ld16(a.w1 + (size_t)row * rb + (size_t)c * 16);
+                        if constexpr (WT == SFFN_W_INT4_G128) s1v[kk][r] = half_bits_to_float(a.s1[(size_t)row * sst + (c >> 2)]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < KMAX; ++kk) {
+            const int c = (k0 + kk) * 64 + lane;
+            if ((k0 + kk < K) && (c < nch)) {
+#pragma unroll
+                for (int t = 0; t < BT; ++t) {
+                    if (t < B) {
+                        float xv[E];
+                        const float4 *xp = (const float4 *)&xs[t * SL + kk * 64 * E + lane * E];
+#pragma unroll
+                        for (int e4 = 0; e4 < E / 4; ++e4) {
+                            const float4 v = xp[e4];
+                            xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
+                            xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
+                        }
+#pragma unroll
+                        for (int r = 0; r < RPW; ++r) {
+                            ag[t][r] = chunk_dot<WT>(w0v[kk][r], s0v[kk][r], xv, ag[t][r]);
+                            if constexpr (TWO) au[t][r] = chunk_dot<WT>(w1v[kk][r], s1v[kk][r], xv, au[t][r]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        if (t < B) {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                ag[t][r] = wave_tree_sum(ag[t][r]);
+                if constexpr (TWO) au[t][r] = wave_tree_sum(au[t][r]);
+            }
+        }
+    }
+
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int row = rowA + r;
+            int on = 0;
+            if (row < a.rows) {
+#pragma unroll
+                for (int t = 0; t < BT; ++t) {
+                    if (t < B) {
+                        const size_t o = (size_t)t * a.rows + row;
+                        if constexpr (OUT == OUT_GATE || OUT == OUT_GATE_UP) {
+                            const float gp = ag[t][r] + a.bias;
+                            a.o0[o] = gp;
+                            if constexpr (OUT == OUT_GATE_UP) a.o1[o] = au[t][r];
+                            on |= gate_pred(a.mode, gp, a.theta) ? 1 : 0;
+                        } else if constexpr (OUT == OUT_DENSE_GU) {
+                            a.o0[o] = act_f32(a.act, ag[t][r] + a.bias) * au[t][r];
+                        } else {
+                            a.o0[o] = a.resid ? ag[t][r] + a.resid[o] : ag[t][r];
+                        }
+                    }
+                }
+            }
+            if constexpr (OUT == OUT_GATE) flags[wave * RPW + r] = on;
+        }
+    }
+    if constexpr (OUT == OUT_GATE) {
+        // ascending compaction of this workgroup's rows: ballot + mbcnt, no atomics
+        __syncthreads();
+        if (wave == 0 && a.list_cnt) {
+            const int on = lane < R ? flags[lane] : 0;
+            const uint64_t m = __ballot(on);
+            if (on) a.list_idx[(size_t)blockIdx.x * R + mbcnt64(m)] = row_base + lane;
+            if (lane == 0) a.list_cnt[blockIdx.x] = __popcll(m);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// weight-aware top-k (one workgroup per token)
+// ---------------------------------------------------------------------------
+
+// fp64 exp: Cody-Waite reduction by ln2 (head/tail split) and a degree-13 Taylor
+// polynomial in Horner form with fused multiply-adds, scaled by 2^n
+// (W. J. Cody and W. Waite, Software Manual for the Elementary Functions).
+// Written so that every step is one IEEE operation; the CPU reference
+// implements the same published method independently.
+__device__ double exp64(double z)
+{
+    if (z > 709.0) return __builtin_huge_val();
+    if (z < -745.0) return 0.0;
+    const double log2e = 0x1.71547652b82fep+0;
+    const double ln2_hi = 0x1.62e42feep-1;
+    const double ln2_lo = 0x1.a39ef35793c76p-33;
+    const double c[14] = {0x1.0000000000000p+0,  0x1.0000000000000p+0,  0x1.0000000000000p-1,
+                          0x1.5555555555555p-3,  0x1.5555555555555p-5,  0x1.1111111111111p-7,
+                          0x1.6c16c16c16c17p-10, 0x1.a01a01a01a01ap-13, 0x1.a01a01a01a01ap-16,
+                          0x1.71de3a556c734p-19, 0x1.27e4fb7789f5cp-22, 0x1.ae64567f544e4p-26,
+                          0x1.1eed8eff8d898p-29, 0x1.6124613a86d09p-33};
+    const double n = rint(z * log2e);
+    double r = fma(-n, ln2_hi, z);
+    r = fma(-n, ln2_lo, r);
+    double p = c[13];
+#pragma unroll
+    for (int k = 12; k >= 0; --k) p = fma(p, r, c[k]);
+    return ldexp(p, (int)n);
+}
+
+__device__ __forceinline__ uint64_t topk_key(float g, float u, double n)
+{
+    const double gd = (double)g;
+    const double silu = gd / (1.0 + exp64(-gd));
+    const double s = fabs(silu * (double)u) * n;  // >= 0: the bits order like the values
+    return (uint64_t)__double_as_longlong(s);
+}
+
+struct TopkArgs {
+    const float *G, *U;
+    const double *wdn;
+    int f, k, nw32;
+    uint64_t *keys;
+    uint32_t *bits;
+};
+
+__global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
+{
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float *g = a.G + (size_t)t * a.f;
+    const float *u = a.U + (size_t)t * a.f;
+    uint64_t *key = a.keys + (size_t)t * a.f;
+    __shared__ int hist[256];
+    __shared__ uint64_t s_prefix;
+    __shared__ int s_kk;
+    __shared__ int tmp[17];
+
+    for (int j = tid; j < a.f; j += 1024) key[j] = topk_key(g[j], u[j], a.wdn[j]);
+    __syncthreads();
+
+    // exact radix select of the k-th largest key, most significant byte first
+    uint64_t prefix = 0, pmask = 0;
+    int kk = a.k;
+    for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < a.f; j += 1024) {
+            const uint64_t v = key[j];
+            if ((v & pmask) == prefix) atomicAdd(&hist[(int)((v >> shift) & 255)], 1);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int cum = 0, D = 0;
+            for (int dd = 255; dd >= 0; --dd) {
+                const int h = hist[dd];
+                if (cum + h >= kk) { D = dd; break; }
+                cum += h;
+            }
+            s_kk = kk - cum;
+            s_prefix = prefix | ((uint64_t)D << shift);
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        kk = s_kk;
+        pmask |= (uint64_t)255 << shift;
+    }
+    // every key above T is kept; of the keys equal to T the kk lowest indices
+    const uint64_t T = prefix;
+    const int wpt = (a.nw32 + 1023) / 1024;
+    const int w0 = tid * wpt, w1 = min(a.nw32, w0 + wpt);
+    int eq = 0;
+    for (int w = w0; w < w1; ++w)
+        for (int b = 0; b < 32; ++b) {
+            const int j = w * 32 + b;
+            if (j < a.f && key[j] == T) ++eq;
+        }
+    int tot;
+    int rank = block_exclusive_scan(eq, tmp, &tot);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bitsw = 0;
+        for (int b = 0; b < 32; ++b) {
+            const int j = w * 32 + b;
+            if (j >= a.f) break;
+            const uint64_t v = key[j];
+            bool on = v > T;
+            if (v == T) { on = rank < kk; ++rank; }
+            if (on) bitsw |= 1u << b;
+        }
+        a.bits[(size_t)t * a.nw32 + w] = bitsw;
+    }
+}
+
+// union of the per-token top-k bits, compacted per 64 neurons (one wave each)
+__global__ __launch_bounds__(256) void k_mask_lists(const uint32_t *__restrict__ bits, int nw32, int B,
+                                                    int f, int *__restrict__ list_cnt,
+                                                    int *__restrict__ list_idx)
+{
+    const int lane = threadIdx.x & 63;
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk * 64 >= f) return;
+    const int j = blk * 64 + lane;
+    int on = 0;
+    if (j < f)
+        for (int t = 0; t < B; ++t) on |= (bits[(size_t)t * nw32 + (j >> 5)] >> (j & 31)) & 1;
+    const uint64_t m = __ballot(on);
+    if (on) list_idx[(size_t)blk * 64 + mbcnt64(m)] = j;
+    if (lane == 0) list_cnt[blk] = __popcll(m);
+}
+
+// ---------------------------------------------------------------------------
+// gather: the active list in equal shares -> partial y
+// ---------------------------------------------------------------------------
+struct GatherArgs {
+    const int *list_cnt, *list_idx;
+    int nL, R;
+    const float *G, *U;
+    const uint32_t *bits;
+    int nw32;
+    const float *x;
+    int B, d, f;
+    const uint8_t *wu;
+    const uint16_t *su;
+    const uint8_t *wdt;
+    const uint16_t *sdt;
+    int mode, act, use_union;
+    float theta;
+    float *partial;  // [P][B][d]
+    int32_t *idx_out, *count_out;
+    int maxs;        // capacity of the share arrays
+    int stage_x;     // 1: the up projection runs here (x slices in LDS)
+};
+
+// Share of the concatenated per-block lists for this workgroup: writes the
+// neuron indices to jl[0..ns) (and to idx_out), returns ns.  pref needs nL+1 ints.
+__device__ int share_of_lists(const int *cnt, const int *idx, int nL, int R, int *pref, int *jl,
+                              int32_t *idx_out, int32_t *count_out, int *tmp)
+{
+    const int NT = blockDim.x, tid = threadIdx.x;
+    const int per = (nL + NT - 1) / NT;
+    const int i0 = min(nL, tid * per), i1 = min(nL, i0 + per);
+    int s = 0;
+    for (int i = i0; i < i1; ++i) s += cnt[i];
+    int total;
+    int run = block_exclusive_scan(s, tmp, &total);
+    for (int i = i0; i < i1; ++i) {
+        pref[i] = run;
+        run += cnt[i];
+    }
+    if (tid == 0) pref[nL] = total;
+    __syncthreads();
+    const int P = gridDim.x, q = blockIdx.x;
+    const int lo = (int)((int64_t)q * total / P), hi = (int)((int64_t)(q + 1) * total / P);
+    for (int p = lo + tid; p < hi; p += NT) {
+        int a = 0, b = nL - 1;
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (pref[mid] <= p) a = mid; else b = mid - 1;
+        }
+        const int j = idx[(size_t)a * R + (p - pref[a])];
+        jl[p - lo] = j;
+        if (idx_out) idx_out[p] = j;
+    }
+    if (q == 0 && tid == 0 && count_out) *count_out = total;
+    __syncthreads();
+    return hi - lo;
+}
+
+__global__ __launch_bounds__(256) void k_emit_list(const int *cnt, const int *idx, int nL, int R,
+                                                   int32_t *idx_out, int32_t *count_out, int maxs)
+{
+    extern __shared__ __align__(16) int lds_e[];
+    __shared__ int tmp[17];
+    int *jl = lds_e, *pref = lds_e + maxs;
+    share_of_lists(cnt, idx, nL, R, pref, jl, idx_out, count_out, tmp);
+}
+
+template <int WT, int BT>
+__global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherArgs a)
+{
+    using C = Cfg<WT, BT>;
+    constexpr int E = C::E, KMAX = C::KMAX, NW = C::NW, RPW = C::RPW, CPT = C::CPT, UNR = C::UNR;
+    constexpr int NT = NW * 64;
+    constexpr int R2 = NW * RPW;
+    constexpr int SL = KMAX * 64 * E;
+    extern __shared__ __align__(16) unsigned char lds[];
+    float *xs = (float *)lds;
+    float *hs = xs + (a.stage_x ? BT * SL : 0);
+    int *jl = (int *)(hs + (size_t)a.maxs * BT);
+    int *pref = jl + a.maxs;
+    __shared__ int tmp[17];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int B = a.B, d = a.d, f = a.f;
+    const int ns = share_of_lists(a.list_cnt, a.list_idx, a.nL, a.R, pref, jl, a.idx_out, a.count_out, tmp);
+
+    // ---- phase A: h_tj for the share ----
+    if (a.mode == SFFN_MODE_TOPK) {
+        for (int i = tid; i < ns * B; i += NT) {
+            const int jj = i / B, t = i - jj * B, j = jl[jj];
+            const float gp = a.G[(size_t)t * f + j];
+            const bool on = a.use_union || ((a.bits[(size_t)t * a.nw32 + (j >> 5)] >> (j & 31)) & 1);
+            hs[jj * BT + t] = on ? act_f32(a.act, gp) * a.U[(size_t)t * f + j] : 0.0f;
+        }
+    } else {
+        const int nch = d / E, K = (nch + 63) >> 6;
+        const size_t rb = (WT == SFFN_W_F32) ? (size_t)d * 4 : (WT == SFFN_W_BF16) ? (size_t)d * 2 : (size_t)d / 2;
+        const int sst = d / 128;
+        const int ngroups = (ns + R2 - 1) / R2;
+        const bool single = K <= KMAX;
+        for (int gi = 0; gi < ngroups; ++gi) {
+            float au[BT][RPW];
+#pragma unroll
+            for (int t = 0; t < BT; ++t)
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) au[t][r] = 0.0f;
+            int jrow[RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int jj = gi * R2 + wave * RPW + r;
+                jrow[r] = jj < ns ? jl[jj] : -1;
+            }
+            for (int k0 = 0; k0 < K; k0 += KMAX) {
+                if (!single || gi == 0) {
+                    const int e0 = k0 * 64 * E;
+                    const int n4 = min(SL, d - e0) >> 2;
+                    __syncthreads();
+                    for (int i = tid; i < B * n4; i += NT) {
+                        const int t = i / n4, c4 = i - t * n4;
+                        *(float4 *)&xs[t * SL + 4 * c4] = *(const float4 *)&a.x[(size_t)t * d + e0 + 4 * c4];
+                    }
+                    __syncthreads();
+                }
+                uint4 wv[KMAX][RPW];
+                float sv[KMAX][RPW];
+#pragma unroll
+                for (int kk = 0; kk < KMAX; ++kk) {
+                    const int c = (k0 + kk) * 64 + lane;
+                    const bool ok = (k0 + kk < K) && (c < nch);
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) {
+                        wv[kk][r] = make_uint4(0, 0, 0, 0);
+                        sv[kk][r] = 0.0f;
+                        if (ok && jrow[r] >= 0) {
+                            wv[kk][r] = ld16(a.wu + (size_t)jrow[r] * rb + (size_t)c * 16);
+                            if constexpr (WT == SFFN_W_INT4_G128) sv[kk][r] = half_bits_to_float(a.su[(size_t)jrow[r] * sst + (c >> 2)]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < KMAX; ++kk) {
+                    const int c = (k0 + kk) * 64 + lane;
+                    if ((k0 + kk < K) && (c < nch)) {
+#pragma unroll
+                        for (int t = 0; t < BT; ++t) {
+                            if (t < B) {
+                                float xv[E];
+                                const float4 *xp = (const float4 *)&xs[t * SL + kk * 64 * E + lane * E];
+#pragma unroll
+                                for (int e4 = 0; e4 < E / 4; ++e4) {
+                                    const float4 v = xp[e4];
+                                    xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
+                                    xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
+                                }
+#pragma unroll
+                                for (int r = 0; r < RPW; ++r) au[t][r] = chunk_dot<WT>(wv[kk][r], sv[kk][r], xv, au[t][r]);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < BT; ++t)
+                if (t < B)
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) au[t][r] = wave_tree_sum(au[t][r]);
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    if (jrow[r] < 0) continue;
+                    const int jj = gi * R2 + wave * RPW + r;
+#pragma unroll
+                    for (int t = 0; t < BT; ++t) {
+                        if (t < B) {
+                            const float gp = a.G[(size_t)t * f + jrow[r]];
+                            const bool on = a.use_union || gate_pred(a.mode, gp, a.theta);
+                            hs[jj * BT + t] = on ? act_f32(a.act, gp) * au[t][r] : 0.0f;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase B: partial y over the share's W_down^T rows ----
+    float *part = a.partial + (size_t)blockIdx.x * B * d;
+    for (int c0 = 0; c0 < d; c0 += NT * CPT) {
+        const int col = c0 + tid * CPT;
+        const bool okc = col < d;
+        float acc[BT][CPT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[t][c] = 0.0f;
+
+        if constexpr (WT == SFFN_W_INT4_G128) {
+            // y_i += s[g][i] * sum_{j in g} h_j q_ji: integer weights summed per
+            // 128-neuron group, then scaled once per group
+            float T[BT][CPT];
+#pragma unroll
+            for (int t = 0; t < BT; ++t)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) T[t][c] = 0.0f;
+            int cur = -1;
+            const size_t rbd = (size_t)d / 2;
+            for (int jj0 = 0; jj0 < ns; jj0 += UNR) {
+                uint32_t qv[UNR][CPT / 8];
+                int jv[UNR];
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    jv[u] = (jj0 + u < ns) ? jl[jj0 + u] : -1;
+#pragma unroll
+                    for (int w = 0; w < CPT / 8; ++w)
+                        qv[u][w] = (okc && jv[u] >= 0) ? *(const uint32_t *)(a.wdt + (size_t)jv[u] * rbd + col / 2 + 4 * w) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    if (jv[u] < 0) break;
+                    const int g = jv[u] >> 7;
+                    if (g != cur) {
+                        if (cur >= 0 && okc) {
+#pragma unroll
+                            for (int c = 0; c < CPT; ++c) {
+                                const float s = half_bits_to_float(a.sdt[(size_t)cur * d + col + c]);
+#pragma unroll
+                                for (int t = 0; t < BT; ++t) {
+                                    acc[t][c] = __builtin_fmaf(s, T[t][c], acc[t][c]);
+                                    T[t][c] = 0.0f;
+                                }
+                            }
+                        }
+                        cur = g;
+                    }
+#pragma unroll
+                    for (int t = 0; t < BT; ++t) {
+                        if (t < B) {
+                            const float h = hs[(jj0 + u) * BT + t];
+#pragma unroll
+                            for (int c = 0; c < CPT; ++c)
+                                T[t][c] = __builtin_fmaf(h, (float)nib(qv[u][c >> 3], c & 7), T[t][c]);
+                        }
+                    }
+                }
+            }
+            if (cur >= 0 && okc) {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    const float s = half_bits_to_float(a.sdt[(size_t)cur * d + col + c]);
+#pragma unroll
+                    for (int t = 0; t < BT; ++t) acc[t][c] = __builtin_fmaf(s, T[t][c], acc[t][c]);
+                }
+            }
+        } else {
+            constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
+            constexpr int NV = CPT * EB / 16;  // 16-byte loads per row per thread
+            const size_t rbd = (size_t)d * EB;
+            for (int jj0 = 0; jj0 < ns; jj0 += UNR) {
+                uint4 wv[UNR][NV];
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    const int jj = jj0 + u;
+                    const bool ok = okc && jj < ns;
+                    const int j = ok ? jl[jj] : 0;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        wv[u][v] = ok ? ld16(a.wdt + (size_t)j * rbd + (size_t)col * EB + 16 * v) : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    if (jj0 + u >= ns) break;
+                    float w[CPT];
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) unpack<WT>(wv[u][v], w + v * (16 / EB));
+#pragma unroll
+                    for (int t = 0; t < BT; ++t) {
+                        if (t < B) {
+                            const float h = hs[(jj0 + u) * BT + t];
+#pragma unroll
+                            for (int c = 0; c < CPT; ++c) acc[t][c] = __builtin_fmaf(h, w[c], acc[t][c]);
+                        }
+                    }
+                }
+            }
+        }
+        if (okc) {
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                if (t < B) {
+                    float *dst = part + (size_t)t * d + col;
+#pragma unroll
+                    for (int c = 0; c < CPT; c += 4)
+                        *(float4 *)(dst + c) = make_float4(acc[t][c], acc[t][c + 1], acc[t][c + 2], acc[t][c + 3]);
+                }
+            }
+        }
+    }
+}
+
+// y = sum over the partials in a fixed order (+ residual)
+__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ partial, int P, int BD,
+                                                const float *__restrict__ resid, float *__restrict__ out)
+{
+    __shared__ float red[4][64];
+    const int l = threadIdx.x & 63, qg = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + l;
+    float s = 0.0f;
+    if (col < BD)
+        for (int q = qg; q < P; q += 4) s += partial[(size_t)q * BD + col];
+    red[qg][l] = s;
+    __syncthreads();
+    if (qg == 0 && col < BD) {
+        float y = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+        if (resid) y += resid[col];
+        out[col] = y;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <int WT, int BT, int OUT>
+static hipError_t run_rowdot(const RowDotArgs &a, hipStream_t st)
+{
+    using C = Cfg<WT, BT>;
+    constexpr bool TWO = (OUT == OUT_GATE_UP || OUT == OUT_DENSE_GU);
+    constexpr int RPW = TWO ? (C::RPW > 1 ? C::RPW / 2 : 1) : C::RPW;
+    const int R = C::NW * RPW;
+    const int grid = (a.rows + R - 1) / R;
+    hipLaunchKernelGGL((k_rowdot<WT, BT, OUT>), dim3(grid), dim3(C::NW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int WT, int BT>
+static int gate_rows_per_block()
+{
+    return Cfg<WT, BT>::NW * Cfg<WT, BT>::RPW;
+}
+
+template <int WT, int BT>
+static hipError_t run_gather(const GatherArgs &a0, hipStream_t st)
+{
+    using C = Cfg<WT, BT>;
+    GatherArgs a = a0;
+    const int P = kGatherWGs;
+    a.maxs = (a.f + P - 1) / P + 1;
+    a.stage_x = a.mode != SFFN_MODE_TOPK;
+    const size_t lds = (a.stage_x ? (size_t)BT * C::KMAX * 64 * C::E * 4 : 0) + (size_t)a.maxs * BT * 4 +
+                       (size_t)a.maxs * 4 + (size_t)(a.nL + 1) * 4;
+    static bool attr_set = false;
+    if (lds > 65536 && !attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_gather<WT, BT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_gather<WT, BT>), dim3(P), dim3(C::NW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int WT, int BT>
+static hipError_t decode_typed(const DecodeCall &c, bool forward)
+{
+    const Layer &L = *c.L;
+    const sffn_layer_desc &D = L.desc;
+    const int d = D.d_model, f = D.d_ff, B = c.B;
+    const ScratchLayout S = scratch_layout(D);
+    uint8_t *sc = c.scratch;
+    hipStream_t st = c.stream;
+    hipError_t e;
+
+    const float *xin = c.x;
+    if (D.rmsnorm) {
+        float *xh = (float *)(sc + S.xhat);
+        hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(64), 0, st, c.x, xh, d, D.eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        xin = xh;
+    }
+    float *G = (float *)(sc + S.G);
+    float *U = (float *)(sc + S.U);
+    int *lcnt = (int *)(sc + S.list_cnt);
+    int *lidx = (int *)(sc + S.list_idx);
+
+    RowDotArgs r{};
+    r.B = B;
+    r.mode = c.mode;
+    r.act = D.act;
+    r.bias = c.bias;
+    r.theta = c.theta;
+
+    if (c.mode == SFFN_MODE_DENSE) {
+        r.w0 = L.wg; r.s0 = L.sg; r.w1 = L.wu; r.s1 = L.su;
+        r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
+        if ((e = run_rowdot<WT, BT, OUT_DENSE_GU>(r, st)) != hipSuccess) return e;
+        RowDotArgs q{};
+        q.w0 = L.wd; q.s0 = L.sd; q.rows = d; q.cols = f; q.B = B; q.x = G; q.o0 = c.out;
+        q.resid = D.residual ? c.x : nullptr;
+        return run_rowdot<WT, BT, OUT_DENSE_DOWN>(q, st);
+    }
+
+    int nL, R;
+    const int nw32 = f / 32;
+    uint32_t *bits = (uint32_t *)(sc + S.bits);
+    r.w0 = L.wg; r.s0 = L.sg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
+    if (c.mode == SFFN_MODE_TOPK) {
+        r.w1 = L.wu; r.s1 = L.su; r.o1 = U;
+        if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st)) != hipSuccess) return e;
+        TopkArgs t{G, U, L.wdn, f, c.topk_k, nw32, (uint64_t *)(sc + S.keys), bits};
+        hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), 0, st, t);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        nL = f / kListRowsTopk;
+        R = kListRowsTopk;
+        hipLaunchKernelGGL(k_mask_lists, dim3((nL + 3) / 4), dim3(256), 0, st, (const uint32_t *)bits, nw32, B, f,
+                           lcnt, lidx);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        r.list_cnt = lcnt;
+        r.list_idx = lidx;
+        if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st)) != hipSuccess) return e;
+        R = gate_rows_per_block<WT, BT>();
+        nL = (f + R - 1) / R;
+    }
+
+    if (!forward) {
+        const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
+        hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nL + 1) * 4, st,
+                           (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs);
+        return hipGetLastError();
+    }
+
+    GatherArgs g{};
+    g.list_cnt = lcnt; g.list_idx = lidx; g.nL = nL; g.R = R;
+    g.G = G; g.U = U; g.bits = bits; g.nw32 = nw32;
+    g.x = xin; g.B = B; g.d = d; g.f = f;
+    g.wu = L.wu; g.su = L.su; g.wdt = L.wdt; g.sdt = L.sdt;
+    g.mode = c.mode; g.act = D.act; g.use_union = c.use_union; g.theta = c.theta;
+    float *partial = (float *)(sc + S.partial);
+    g.partial = partial;
+    g.idx_out = c.idx_out; g.count_out = c.count_out;
+    if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
+
+    const int BD = B * d;
+    hipLaunchKernelGGL(k_reduce, dim3((BD + 63) / 64), dim3(256), 0, st, (const float *)partial, kGatherWGs, BD,
+                       D.residual ? c.x : nullptr, c.out);
+    return hipGetLastError();
+}
+
+template <int WT>
+static hipError_t decode_bt(const DecodeCall &c, bool forward)
+{
+    if (c.B <= 1) return decode_typed<WT, 1>(c, forward);
+    if (c.B <= 4) return decode_typed<WT, 4>(c, forward);
+    if (c.B <= 8) return decode_typed<WT, 8>(c, forward);
+    if constexpr (WT != SFFN_W_INT4_G128) return decode_typed<WT, 16>(c, forward);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeCall &c, bool forward)
+{
+    switch (c.L->desc.wtype) {
+    case SFFN_W_F32: return decode_bt<SFFN_W_F32>(c, forward);
+    case SFFN_W_BF16: return decode_bt<SFFN_W_BF16>(c, forward);
+    default: return decode_bt<SFFN_W_INT4_G128>(c, forward);
+    }
+}
+
+}  // namespace sffn

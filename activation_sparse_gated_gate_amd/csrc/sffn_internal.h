@@ -1,0 +1,107 @@
+// sffn_internal.h -- shared definitions of the gfx950 library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sffn.h"
+
+namespace sffn {
+
+// ---------------------------------------------------------------------------
+// limits and launch constants
+// ---------------------------------------------------------------------------
+constexpr int kMaxDecodeRows = 16;
+constexpr int kMaxInt4Rows = 8;
+constexpr int kMaxPrefillRows = 16384;
+constexpr int kGatherWGs = 256;      // partitions of the active list (partial sums)
+constexpr int kListRowsTopk = 64;    // neurons per compaction block after top-k
+constexpr int kMassBlock = 256;      // sorted scores per block of the fp64 mass prefix
+constexpr int kIlvRows = 32;         // prefill: W_gate / W_up interleave granularity
+
+// weight bytes per row of `cols` elements
+inline size_t row_bytes(int wtype, int cols)
+{
+    return wtype == SFFN_W_F32 ? (size_t)cols * 4 : wtype == SFFN_W_BF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// the handle
+// ---------------------------------------------------------------------------
+struct Layer {
+    sffn_layer_desc desc;
+    // decode layouts
+    const uint8_t *wg = nullptr, *wu = nullptr;   // [f][d]
+    const uint16_t *sg = nullptr, *su = nullptr;  // int4 scales [f][d/128]
+    const uint8_t *wdt = nullptr;                 // W_down^T [f][d]
+    const uint16_t *sdt = nullptr;                // int4 scales [f/128][d]
+    const uint8_t *wd = nullptr;                  // W_down natural [d][f] (dense baseline)
+    const uint16_t *sd = nullptr;                 // int4 scales [d][f/128]
+    const double *wdn = nullptr;                  // ||W_down[:, j]||_2, [f]
+    // prefill layouts (bf16)
+    const uint16_t *wgu = nullptr;                // [f/32][2][32][d]: gate rows then up rows
+    const uint16_t *wdp = nullptr;                // W_down natural [d][f]
+};
+
+// persistent-buffer layout, in creation order
+struct PersistentLayout {
+    size_t wg, sg, wu, su, wdt, sdt, wd, sd, wdn, wgu, wdp, total;
+};
+PersistentLayout persistent_layout(const sffn_layer_desc &d);
+
+// scratch layout for one call
+struct ScratchLayout {
+    size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
+    size_t tscore, tflag, pH;                                            // prefill
+    size_t total;
+    int n_lists_gate, rows_per_list_gate;
+};
+ScratchLayout scratch_layout(const sffn_layer_desc &d);
+
+// ---------------------------------------------------------------------------
+// kernel launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+struct DecodeCall {
+    const Layer *L;
+    int mode, use_union, topk_k;
+    float bias, theta;
+    int B;
+    const float *x;     // [B][d] caller input
+    float *out;         // [B][d] caller output (forward) or nullptr (select)
+    int32_t *idx_out, *count_out;
+    uint8_t *scratch;
+    hipStream_t stream;
+};
+hipError_t launch_decode(const DecodeCall &c, bool forward);
+
+struct PrefillSelectCall {
+    const Layer *L;
+    const uint16_t *A;
+    int rows;
+    double mass;
+    int recent_n, min_keep;
+    int32_t *idx_out, *count_out;
+    uint8_t *scratch;
+    hipStream_t stream;
+};
+hipError_t launch_prefill_select(const PrefillSelectCall &c);
+
+struct PrefillForwardCall {
+    const Layer *L;
+    const uint16_t *Y;
+    uint16_t *X;
+    int rows;
+    const int32_t *keep, *count;
+    uint8_t *scratch;
+    hipStream_t stream;
+};
+hipError_t launch_prefill_forward(const PrefillForwardCall &c);
+
+hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up, const void *w_down,
+                           const void *s_gate, const void *s_up, const void *s_down,
+                           uint8_t *persistent, hipStream_t stream);
+
+}  // namespace sffn

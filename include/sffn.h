@@ -1,0 +1,210 @@
+/*
+ * sffn.h -- C ABI of the activation-sparse gated FFN library (libsffn.so, gfx950).
+ *
+ * The library evaluates one gated FFN layer
+ *
+ *     y = W_down . ( m (.) act(W_gate x + b) (.) (W_up x) )
+ *
+ * where neuron j owns row j of W_gate, row j of W_up and column j of W_down
+ * (denseflux: skipping most of a dense FFN, section 1 "why the FFN"), and the
+ * mask m keeps only the neurons that matter for each token:
+ *
+ *   SFFN_MODE_ALL     every neuron, through the sparse kernels (100% active);
+ *   SFFN_MODE_EXACT   ReLU exact gating: neurons with fl32(g + b) > 0; the skipped
+ *                     neurons have an exactly zero activation, so the result
+ *                     equals the dense FFN (denseflux, sections 3 and 5.1-5.3);
+ *   SFFN_MODE_THRESH  a threshold on |SiLU(W_gate x)| (denseflux, section 4.1),
+ *                     given in the gate domain: neurons with fl32(g + b) > theta.
+ *                     For theta > 0 this equals |SiLU(g + b)| > SiLU(theta)
+ *                     whenever SiLU(theta) exceeds SiLU's minimum depth 0.2785;
+ *   SFFN_MODE_TOPK    weight-aware top-k: the topk_k neurons with the largest
+ *                     score |SiLU(g + b) * u| * ||W_down[:, j]||_2, ties to the
+ *                     lower index (WiSparse reproduction notes, sections 2.3 and
+ *                     3.2); with use_union a batch runs over the union of its
+ *                     tokens' sets (same notes, section 5, batch > 1);
+ *   SFFN_MODE_DENSE   the dense FFN through plain dense GEMV kernels (baseline);
+ *   SFFN_MODE_TOKENS  token-selective prefill (RedKnot article, Algorithm 1 and
+ *                     the section on the token-selective sparse FFN): token
+ *                     importance = L2 norm of the attention output row; keep the
+ *                     shortest prefix of the tokens in descending importance whose
+ *                     mass reaches mass_thresh of the total, plus the last
+ *                     recent_n tokens, plus top-ranked tokens up to min_keep;
+ *                     mass_thresh >= 1 or an all-zero score row keeps every
+ *                     token; X_next = Y + FFN(Y) on kept rows, Y elsewhere.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer named *device* is HIP device memory; descriptors and
+ *    policies are host memory read during the call only.
+ *  - The caller owns every buffer (weights, inputs, outputs, index lists,
+ *    workspaces).  The library allocates no device memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream); no call synchronises the host, except sffn_create, which waits
+ *    for its relayout kernels before returning.  Device-side counts stay on
+ *    the device; synchronise the stream before reading results.
+ *  - Argument validation happens before any launch and returns a status;
+ *    no exception or abort crosses the ABI.  After SFFN_ERR_HIP the outputs
+ *    are undefined and the handle stays valid.
+ *  - Non-finite inputs are undefined behaviour (not detected).
+ *  - Calls on one handle from different streams need distinct scratch buffers.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sffn_status {
+    SFFN_OK = 0,
+    SFFN_ERR_INVALID_ARG = 1,  /* NULL pointer, size out of range, bad enum */
+    SFFN_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    SFFN_ERR_WORKSPACE = 3,    /* workspace smaller than sffn_workspace_size says */
+    SFFN_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} sffn_status;
+
+/* weight storage formats */
+enum {
+    SFFN_W_F32 = 0,        /* fp32 */
+    SFFN_W_BF16 = 1,       /* bf16 bit patterns (uint16) */
+    SFFN_W_INT4_G128 = 2   /* int4, groups of 128 along the input dimension, fp16 scales */
+};
+
+enum { SFFN_ACT_RELU = 0, SFFN_ACT_SILU = 1 };
+
+enum {
+    SFFN_MODE_ALL = 0,
+    SFFN_MODE_EXACT = 1,
+    SFFN_MODE_THRESH = 2,
+    SFFN_MODE_TOPK = 3,
+    SFFN_MODE_TOKENS = 4,
+    SFFN_MODE_DENSE = 5
+};
+
+/* which internal layouts sffn_create builds */
+enum { SFFN_LAYOUT_DECODE = 1, SFFN_LAYOUT_PREFILL = 2 };
+
+/*
+ * Layer descriptor.
+ *  d_model   multiple of 256, 256..16384
+ *  d_ff      multiple of 128, 128..65536
+ *  max_rows  decode: tokens per call, 1..16; prefill: sequence length, 1..16384
+ *  wtype     SFFN_W_*; prefill requires SFFN_W_BF16
+ *  act       SFFN_ACT_RELU (ReGLU) or SFFN_ACT_SILU (SwiGLU); prefill requires SILU
+ *  rmsnorm   1: the FFN input is x * 1/sqrt(mean(x^2) + eps) (unit weight), decode only
+ *  residual  1: decode output is x + y instead of y
+ *  eps       RMSNorm epsilon
+ *  layouts   SFFN_LAYOUT_* bit set
+ */
+typedef struct sffn_layer_desc {
+    int32_t d_model;
+    int32_t d_ff;
+    int32_t max_rows;
+    int32_t wtype;
+    int32_t act;
+    int32_t rmsnorm;
+    int32_t residual;
+    float eps;
+    int32_t layouts;
+} sffn_layer_desc;
+
+/*
+ * Per-call policy.
+ *  mode         SFFN_MODE_*
+ *  gate_bias    b added to the gate pre-activation (fp32 add) before the
+ *               activation and every predicate
+ *  theta        THRESH: gate-domain threshold
+ *  topk_k       TOPK: neurons kept per token, 1..d_ff
+ *  use_union    decode batches: 1 = every token of the call is computed over
+ *               the union of the tokens' selected sets; 0 = each token over
+ *               its own set (the gathered rows are still the union)
+ *  mass_thresh  TOKENS: fraction of the total importance mass (fp64)
+ *  recent_n     TOKENS: trailing tokens always kept (>= 0)
+ *  min_keep     TOKENS: minimum kept tokens (>= 0)
+ */
+typedef struct sffn_policy {
+    int32_t mode;
+    float gate_bias;
+    float theta;
+    int32_t topk_k;
+    int32_t use_union;
+    int32_t recent_n;
+    int32_t min_keep;
+    int32_t reserved;
+    double mass_thresh;
+} sffn_policy;
+
+typedef struct sffn_layer *sffn_t;
+
+/*
+ * Bytes the caller must provide: `persistent` for sffn_create (relayouted
+ * weights, kept for the life of the handle) and `scratch` for every
+ * sffn_select / sffn_forward call (reused between calls, contents not
+ * preserved).  Both are device buffers aligned to 256 bytes.
+ */
+sffn_status sffn_workspace_size(const sffn_layer_desc *desc, size_t *persistent_bytes,
+                                size_t *scratch_bytes);
+
+/*
+ * Builds a layer handle.  Weights are device buffers in natural layout:
+ *   W_gate, W_up: [d_ff][d_model] row-major; W_down: [d_model][d_ff] row-major.
+ *   int4: packed bytes [rows][cols/2] (even column in the low nibble, two's
+ *   complement) with fp16 scales [rows][cols/128] in s_gate / s_up / s_down;
+ *   other formats pass NULL scales.
+ * The library copies what it needs into `persistent` (row-major W_gate and
+ * W_up, the transposed W_down^T [d_ff][d_model] for decode with its scales
+ * regrouped as [d_ff/128][d_model], the fp64 column norms ||W_down[:, j]||_2,
+ * and for prefill W_gate / W_up interleaved in blocks of 32 rows plus a copy of
+ * W_down), waits for the copies to finish and keeps no weight pointer.
+ * On success *out receives the handle (free with sffn_destroy).
+ */
+sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const void *w_up,
+                        const void *w_down, const void *s_gate, const void *s_up,
+                        const void *s_down, void *persistent, size_t persistent_bytes,
+                        void *stream, sffn_t *out);
+
+/*
+ * Selection only.
+ *  decode modes (ALL, EXACT, THRESH, TOPK): `in` = x, fp32 [rows][d_model];
+ *    idx_out (device, capacity d_ff) receives the ascending union of the
+ *    selected neuron indices and count_out (device, one int32) its length.
+ *  TOKENS: `in` = A, the attention output, bf16 [rows][d_model] (rows = L);
+ *    idx_out (device, capacity rows) receives the kept token indices in
+ *    ascending order and count_out their number.
+ */
+sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows,
+                        int32_t *idx_out, int32_t *count_out, void *scratch,
+                        size_t scratch_bytes, void *stream);
+
+/*
+ * Forward.
+ *  decode modes and DENSE: `in` = x fp32 [rows][d_model] (device); `out` =
+ *    fp32 [rows][d_model] (device), y, or x + y with residual; out must not
+ *    alias in.  idx_in / count_in must be NULL.  idx_out / count_out
+ *    (optional, device) receive the ascending union list as in sffn_select.
+ *  TOKENS: `in` = Y bf16 [rows][d_model]; `out` = X_next bf16 [rows][d_model];
+ *    idx_in / count_in (device, required) = the keep list from sffn_select.
+ *    X_next may alias Y: then only kept rows are written.  Otherwise un-kept
+ *    rows are copied bit for bit.  idx_out / count_out must be NULL.
+ */
+sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows,
+                         void *out, const int32_t *idx_in, const int32_t *count_in,
+                         int32_t *idx_out, int32_t *count_out, void *scratch,
+                         size_t scratch_bytes, void *stream);
+
+/* Frees the host-side handle (the persistent buffer stays the caller's). */
+void sffn_destroy(sffn_t layer);
+
+/* Static text for a status code. */
+const char *sffn_status_string(sffn_status status);
+
+/* Last HIP error text recorded by this thread, or "" (diagnostics only). */
+const char *sffn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

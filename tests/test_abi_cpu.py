@@ -1,0 +1,95 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every symbol include/sffn.h declares, and rejects
+bad descriptors / arguments before it would touch the GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sffn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sffn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
+              "sffn_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import activation_sparse_gated_gate_amd as sf
+    lib = C.CDLL(sf.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(sf.EXPORTS) >= set(_declared())
+
+
+def _desc(**kw):
+    import activation_sparse_gated_gate_amd as sf
+    base = dict(d_model=4096, d_ff=11008, max_rows=1, wtype=sf.W_BF16, act=sf.ACT_RELU, rmsnorm=0,
+                residual=0, eps=1e-6, layouts=sf.LAYOUT_DECODE)
+    base.update(kw)
+    return sf.LayerDesc(*[base[k] for k, _ in sf.LayerDesc._fields_])
+
+
+def test_workspace_sizes_cover_the_layouts():
+    import activation_sparse_gated_gate_amd as sf
+    st, pb, sb = sf.sffn_workspace_size(_desc())
+    assert st == sf.SFFN_OK
+    mat = 4096 * 11008 * 2
+    assert pb >= 4 * mat + 11008 * 8        # W_gate, W_up, W_down^T, W_down, norms
+    assert sb >= 256 * 4096 * 4             # partial sums
+    st, pb5, sb5 = sf.sffn_workspace_size(_desc(d_model=5120, d_ff=25600, max_rows=16384,
+                                                act=sf.ACT_SILU, layouts=sf.LAYOUT_PREFILL))
+    assert st == sf.SFFN_OK
+    assert pb5 >= 3 * 5120 * 25600 * 2
+    assert sb5 >= 16384 * 25600 * 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=4000), 1), (dict(d_ff=1000), 1), (dict(max_rows=0), 1), (dict(max_rows=17), 1),
+    (dict(wtype=3), 1), (dict(act=2), 1), (dict(layouts=0), 1), (dict(layouts=4), 1),
+    (dict(wtype=2, max_rows=16), 2), (dict(layouts=2, wtype=0, act=1), 2),
+    (dict(layouts=2, act=0), 2), (dict(layouts=2, max_rows=16385, act=1), 1),
+])
+def test_descriptor_validation(kw, status):
+    import activation_sparse_gated_gate_amd as sf
+    st, _, _ = sf.sffn_workspace_size(_desc(**kw))
+    assert st == status
+
+
+def test_create_rejects_bad_arguments_before_any_launch():
+    import activation_sparse_gated_gate_amd as sf
+    d = _desc()
+    st, pb, _ = sf.sffn_workspace_size(d)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    assert sf.sffn_create(d, None, fake, fake, None, None, None, fake, pb, None)[0] == sf.SFFN_ERR_INVALID_ARG
+    assert sf.sffn_create(d, fake, fake, fake, fake, None, None, fake, pb, None)[0] == sf.SFFN_ERR_INVALID_ARG
+    assert sf.sffn_create(d, fake, fake, fake, None, None, None, fake + 16, pb, None)[0] == sf.SFFN_ERR_INVALID_ARG
+    assert sf.sffn_create(d, fake, fake, fake, None, None, None, fake, pb - 1, None)[0] == sf.SFFN_ERR_WORKSPACE
+    d4 = _desc(wtype=sf.W_INT4_G128, act=sf.ACT_SILU, d_model=2048)
+    st, pb4, _ = sf.sffn_workspace_size(d4)
+    assert sf.sffn_create(d4, fake, fake, fake, None, None, None, fake, pb4, None)[0] == sf.SFFN_ERR_INVALID_ARG
+
+
+def test_select_forward_reject_null_handle():
+    import activation_sparse_gated_gate_amd as sf
+    p = sf.make_policy("exact")
+    assert sf.sffn_forward(None, p, 1 << 20, 1, 1 << 21, None, None, None, None, 1 << 22, 1, None) == 1
+    assert sf.sffn_select(None, p, 1 << 20, 1, 1 << 21, 1 << 21, 1 << 22, 1, None) == 1
+
+
+def test_status_strings():
+    import activation_sparse_gated_gate_amd as sf
+    assert sf.sffn_status_string(0) == "ok"
+    assert sf.sffn_status_string(3) == "workspace too small"
+    assert sf.sffn_status_string(99) == "unknown status"

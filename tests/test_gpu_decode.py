@@ -1,0 +1,241 @@
+"""GPU parity of the decode path against the CPU oracle (through the C ABI).
+
+Bars: selected index sets and the fixed-order gate values bit-exact; outputs
+within relative L2 1e-5 (fp32), 2e-3 (bf16), 5e-3 (int4, same dequantised
+weights); repeated runs bitwise identical.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from gpu_util import make_layer, rel_l2, run_decode, scratch_views
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.WT_F32: 1e-5, synth.WT_BF16: 2e-3, synth.WT_I4: 5e-3}
+
+
+def _sf():
+    import activation_sparse_gated_gate_amd as sf
+    return sf
+
+
+def _check(layer, w, x, mode, tol, **kw):
+    """Run one call on the GPU and the oracle; compare everything unique."""
+    sf = _sf()
+    pol = sf.make_policy(mode, gate_bias=kw.get("bias", 0.0), theta=kw.get("theta", 0.0),
+                         topk_k=kw.get("topk_k", 1), use_union=kw.get("union", False))
+    y, idx, n = run_decode(layer, pol, x)
+    ref = oracle.decode(w, x, mode=mode, bias=kw.get("bias", 0.0), theta=kw.get("theta", 0.0),
+                        topk_k=kw.get("topk_k", 1), union=kw.get("union", False),
+                        rmsnorm=layer.desc.rmsnorm, residual=layer.desc.residual)
+    B = x.shape[0]
+    xh, g, u = scratch_views(layer, B)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), ref["g"].view(np.uint32)), "gate values differ"
+    if layer.desc.rmsnorm:
+        assert np.array_equal(xh.cpu().numpy().view(np.uint32), ref["xhat"].view(np.uint32)), "x_hat differs"
+    if mode == "topk":
+        assert np.array_equal(u.cpu().numpy().view(np.uint32), ref["u"].view(np.uint32)), "up values differ"
+    assert n == ref["idx"].size and np.array_equal(idx, ref["idx"]), "selected sets differ"
+    err = rel_l2(y, ref["y"])
+    assert err <= tol, "relative L2 %.3g > %.3g" % (err, tol)
+    return y, ref, err
+
+
+# ---------------------------------------------------------------------------
+# config 1: fp32, 512 / 1408, exact ReLU gating at a = 0.2, 64 tokens
+# ---------------------------------------------------------------------------
+
+def test_cfg1_exact_gating_64_tokens_and_equals_dense():
+    sf = _sf()
+    w = synth.cfg1_weights()
+    x = synth.cfg1_tokens(64)
+    b = synth.gate_offset_for_active_fraction(synth.CFG1_ACTIVE)
+    layer = make_layer(w, 1)
+    worst = 0.0
+    active = []
+    for t in range(64):
+        y, ref, err = _check(layer, w, x[t:t + 1], "exact", 1e-5, bias=b)
+        worst = max(worst, err)
+        active.append(ref["idx"].size / 1408)
+        # the dense FFN (plain GEMV kernels) gives the same y
+        yd, _, _ = run_decode(layer, sf.make_policy("dense", gate_bias=b), x[t:t + 1], want_list=False)
+        assert rel_l2(yd, ref["y"]) <= 1e-5
+        assert rel_l2(y, yd) <= 2e-5
+    assert abs(np.mean(active) - 0.2) < 0.02
+    print("cfg1 worst relL2 %.3g, mean active %.4f" % (worst, np.mean(active)))
+
+
+def test_cfg1_repeat_is_bitwise_deterministic():
+    sf = _sf()
+    w = synth.cfg1_weights()
+    x = synth.cfg1_tokens(3)
+    b = synth.gate_offset_for_active_fraction(0.2)
+    layer = make_layer(w, 1)
+    pol = sf.make_policy("exact", gate_bias=b)
+    for t in range(3):
+        y1, i1, _ = run_decode(layer, pol, x[t:t + 1])
+        y2, i2, _ = run_decode(layer, pol, x[t:t + 1])
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+        assert np.array_equal(i1, i2)
+
+
+# ---------------------------------------------------------------------------
+# config 2: bf16 Llama-2-7B FFN shape, a in {1.0, 0.6, 0.3, 0.1}
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def cfg2():
+    w = synth.cfg2_weights()
+    x = synth.cfg2_tokens(6)
+    layer = make_layer(w, 1)
+    yield w, x, layer
+    layer.close()
+
+
+@pytest.mark.parametrize("a", [1.0, 0.6, 0.3, 0.1])
+def test_cfg2_full_shape(cfg2, a):
+    w, x, layer = cfg2
+    mode = "all" if a == 1.0 else "exact"
+    b = 0.0 if a == 1.0 else synth.gate_offset_for_active_fraction(a)
+    fr = []
+    for t in range(x.shape[0]):
+        y, ref, err = _check(layer, w, x[t:t + 1], mode, 2e-3, bias=b)
+        fr.append(ref["idx"].size / w.d_ff)
+    assert abs(np.mean(fr) - a) < 0.03, fr
+
+
+def test_cfg2_dense_mode_matches_oracle(cfg2):
+    sf = _sf()
+    w, x, layer = cfg2
+    y, _, _ = run_decode(layer, sf.make_policy("dense"), x[:1], want_list=False)
+    ref = oracle.decode(w, x[:1], mode="all")
+    assert rel_l2(y, ref["y"]) <= 2e-3
+
+
+def test_cfg2_select_entry_matches_forward_list(cfg2):
+    import torch
+    sf = _sf()
+    from gpu_util import tensor
+    w, x, layer = cfg2
+    b = synth.gate_offset_for_active_fraction(0.3)
+    pol = sf.make_policy("exact", gate_bias=b)
+    xt = tensor(x[:1])
+    idx = torch.full((w.d_ff,), -1, dtype=torch.int32, device=xt.device)
+    cnt = torch.zeros(1, dtype=torch.int32, device=xt.device)
+    layer.select(pol, xt, idx, cnt)
+    torch.cuda.synchronize()
+    n = int(cnt.item())
+    _, fidx, fn = run_decode(layer, pol, x[:1])
+    assert n == fn and np.array_equal(idx[:n].cpu().numpy(), fidx)
+
+
+# ---------------------------------------------------------------------------
+# batches, ragged sizes, modes, edge cases (reduced shapes)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wt", [synth.WT_F32, synth.WT_BF16])
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 11, 16])
+def test_batches_thresh_and_exact(wt, B):
+    d, f = 768, 1664   # d: 3 chunk-columns for fp32 / 1.5 for bf16 (ragged); f: 104 blocks of 16
+    act = synth.ACT_SILU
+    w = synth._make_weights(wt, d, f, act, (900 + B, 901 + B, 902 + B))
+    x = synth.normal_f32(950 + B, (B, d))
+    if wt == synth.WT_BF16:
+        x = synth.round_to_bf16(x)
+    layer = make_layer(w, 16)
+    th = synth.gate_threshold_for_active_fraction(0.13)
+    tol = TOL[wt]
+    _check(layer, w, x, "thresh", tol, theta=th, union=True)
+    _check(layer, w, x, "thresh", tol, theta=th, union=False)
+    _check(layer, w, x, "all", tol)
+    relu = synth._make_weights(wt, d, f, synth.ACT_RELU, (900 + B, 901 + B, 902 + B))
+    lr = make_layer(relu, 16)
+    _check(lr, relu, x, "exact", tol, bias=synth.gate_offset_for_active_fraction(0.3), union=False)
+
+
+def test_rmsnorm_residual_batch16():
+    w = synth._make_weights(synth.WT_BF16, 1024, 2048, synth.ACT_SILU, (961, 962, 963))
+    x = synth.normal_f32(964, (16, 1024)) * np.float32(2.5)
+    layer = make_layer(w, 16, rmsnorm=True, residual=True)
+    th = synth.gate_threshold_for_active_fraction(0.3)
+    _check(layer, w, x, "thresh", 2e-3, theta=th, union=True)
+    _check(layer, w, x[:7], "all", 2e-3)
+
+
+def test_no_active_neuron_gives_zero_output():
+    sf = _sf()
+    w = synth._make_weights(synth.WT_BF16, 512, 1408, synth.ACT_RELU, (971, 972, 973))
+    x = synth.round_to_bf16(synth.normal_f32(974, (2, 512)))
+    layer = make_layer(w, 2)
+    y, idx, n = run_decode(layer, sf.make_policy("exact", gate_bias=-40.0), x)
+    assert n == 0 and np.all(y == 0.0)
+    layer_r = make_layer(w, 2, residual=True)
+    y, idx, n = run_decode(layer_r, sf.make_policy("exact", gate_bias=-40.0), x)
+    assert n == 0 and np.array_equal(y, x)
+
+
+def test_all_neurons_active_exact_equals_all():
+    sf = _sf()
+    w = synth._make_weights(synth.WT_BF16, 512, 1408, synth.ACT_RELU, (981, 982, 983))
+    x = synth.round_to_bf16(synth.normal_f32(984, (1, 512)))
+    layer = make_layer(w, 1)
+    y1, i1, n1 = run_decode(layer, sf.make_policy("exact", gate_bias=40.0), x)
+    y2, i2, n2 = run_decode(layer, sf.make_policy("all", gate_bias=40.0), x)
+    assert n1 == n2 == 1408 and np.array_equal(i1, i2)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# config 3: int4 weight-aware top-k, batch 1 and 8 (union)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def cfg3():
+    w = synth.cfg3_weights()
+    x = synth.cfg3_tokens(16)
+    layer = make_layer(w, 8)
+    yield w, x, layer
+    layer.close()
+
+
+@pytest.mark.parametrize("pct", synth.CFG3_KEEP_PCT)
+def test_cfg3_topk_batch1(cfg3, pct):
+    w, x, layer = cfg3
+    k = synth.topk_count(w.d_ff, pct)
+    for t in range(3):
+        _check(layer, w, x[t:t + 1], "topk", 5e-3, topk_k=k)
+
+
+@pytest.mark.parametrize("pct", synth.CFG3_KEEP_PCT)
+def test_cfg3_topk_batch8_union(cfg3, pct):
+    w, x, layer = cfg3
+    k = synth.topk_count(w.d_ff, pct)
+    y, ref, err = _check(layer, w, x[8:16], "topk", 5e-3, topk_k=k, union=True)
+    dens = ref["idx"].size / w.d_ff
+    assert dens > oracle.group_active_probability(pct / 100, 8) - 0.15
+
+
+def test_topk_k_equals_f_and_k_one(cfg3):
+    w, x, layer = cfg3
+    _check(layer, w, x[:2], "topk", 5e-3, topk_k=w.d_ff, union=True)
+    _check(layer, w, x[:3], "topk", 5e-3, topk_k=1, union=False)
+
+
+def test_topk_ties_lower_index_first():
+    # duplicated neurons give bit-identical scores; k cuts through the tie
+    w = synth._make_weights(synth.WT_BF16, 512, 256, synth.ACT_SILU, (991, 992, 993))
+    for m in (w.w_gate, w.w_up):
+        m[200] = m[17]
+        m[90] = m[17]
+    w.w_down[:, 200] = w.w_down[:, 17]
+    w.w_down[:, 90] = w.w_down[:, 17]
+    x = synth.round_to_bf16(synth.normal_f32(994, (1, 512)))
+    full = oracle.decode(w, x, mode="topk", topk_k=256)
+    s = np.array([oracle.score(full["g"][0, j], full["u"][0, j], full["wdn"][j]) for j in range(256)])
+    ahead = int((s > s[17]).sum())
+    layer = make_layer(w, 1)
+    _, ref, _ = _check(layer, w, x, "topk", 2e-3, topk_k=ahead + 2)
+    assert 17 in ref["idx"] and 90 in ref["idx"] and 200 not in ref["idx"]
