@@ -28,7 +28,7 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
          "tokens": MODE_TOKENS, "dense": MODE_DENSE}
 
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
-           "sffn_status_string", "sffn_last_hip_error")
+           "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer")
 
 
 class LayerDesc(C.Structure):
@@ -75,6 +75,8 @@ def _load():
     lib.sffn_status_string.restype = C.c_char_p
     lib.sffn_last_hip_error.argtypes = []
     lib.sffn_last_hip_error.restype = C.c_char_p
+    lib.sffn_set_kernel_timer.argtypes = [P, P, P, I]
+    lib.sffn_set_kernel_timer.restype = I
     return lib
 
 
@@ -117,6 +119,11 @@ def sffn_forward(handle, policy, inp, rows, out, idx_in, count_in, idx_out, coun
 
 def sffn_destroy(handle) -> None:
     _lib.sffn_destroy(handle)
+
+
+def sffn_set_kernel_timer(handle, begin_events, end_events, n) -> int:
+    """begin_events / end_events: ctypes arrays of hipEvent_t handles (or None when n = 0)."""
+    return _lib.sffn_set_kernel_timer(handle, begin_events, end_events, int(n))
 
 
 # ---------------------------------------------------------------------------
@@ -183,6 +190,16 @@ class Layer:
                           self.scratch.data_ptr(), self.scratch_bytes, self._stream(stream))
         if st != SFFN_OK:
             raise SffnError(st, "sffn_forward")
+
+    def arm_kernel_timer(self, events):
+        """events: list of (begin, end) torch.cuda.Event(enable_timing=True) pairs;
+        the next len(events) forward calls time their main kernel into them."""
+        n = len(events)
+        self._timer_arrays = ((C.c_void_p * n)(*[b.cuda_event for b, _ in events]),
+                              (C.c_void_p * n)(*[e.cuda_event for _, e in events]))
+        st = sffn_set_kernel_timer(self.handle, self._timer_arrays[0], self._timer_arrays[1], n)
+        if st != SFFN_OK:
+            raise SffnError(st, "sffn_set_kernel_timer")
 
     def close(self):
         if getattr(self, "handle", None):

@@ -3,6 +3,7 @@
 // before any launch and reports problems through the status code.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <new>
 #include <stdio.h>
 #include <string.h>
@@ -69,7 +70,9 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         S.bits = take(B * (f / 32) * 4);
         S.list_cnt = take((size_t)f * 4);
         S.list_idx = take(((size_t)f + 64) * 4);
-        S.partial = take((size_t)kGatherWGs * B * d * 4);
+        // partial sums: kGatherWGs per token for the batched gather; the batch-1
+        // fused kernel uses ceil(f / RB) <= max(256, ceil(f / 48)) workgroups
+        S.partial = take(std::max((size_t)kGatherWGs * B, (size_t)(f + 47) / 48 + 256) * d * 4);
     }
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         S.tscore = take(B * 4 * 2);   // scores and their sorted copy
@@ -112,6 +115,7 @@ using namespace sffn;
 
 struct sffn_layer {
     Layer L;
+    KernelTimer timer;
 };
 
 extern "C" {
@@ -158,6 +162,7 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
     if (!h) return SFFN_ERR_INVALID_ARG;
     Layer &L = h->L;
     L.desc = *desc;
+    L.timer = &h->timer;
     uint8_t *base = (uint8_t *)persistent;
     const bool dec = desc->layouts & SFFN_LAYOUT_DECODE;
     if (dec) {
@@ -189,6 +194,16 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
 }
 
 void sffn_destroy(sffn_t layer) { delete layer; }
+
+sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events, int32_t n)
+{
+    if (!layer || n < 0 || (n > 0 && (!begin_events || !end_events))) return SFFN_ERR_INVALID_ARG;
+    layer->timer.begin = begin_events;
+    layer->timer.end = end_events;
+    layer->timer.n = n;
+    layer->timer.next = 0;
+    return SFFN_OK;
+}
 
 static bool decode_mode(int m)
 {

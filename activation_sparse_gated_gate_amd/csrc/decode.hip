@@ -22,6 +22,8 @@
 // (h for every neuron), then W_down rows dotted with h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 
 namespace sffn {
@@ -666,6 +668,325 @@ __global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ partia
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// batch-1 kernels.  One 1024-thread workgroup per compute unit, every weight
+// row load issued before x is staged into LDS, so each workgroup keeps its whole
+// share of rows in flight at once (up to 3 rows x 8 KB per wave).
+// ---------------------------------------------------------------------------
+constexpr int kB1NW = 16;                    // waves per workgroup
+constexpr int kB1NT = kB1NW * 64;
+constexpr int kB1RPW = 3;                    // rows per wave per phase
+constexpr int kFusedMaxRB = 48;              // neurons per workgroup of the fused kernel
+
+struct FusedArgs {
+    const uint8_t *wg, *wu, *wdt;
+    const float *x;
+    float *G;          // [f] g' (for inspection)
+    float *partial;    // [P][d]
+    int *list_cnt, *list_idx;  // per-workgroup ascending active lists (stride RB)
+    int f, RB;
+    int mode, act;
+    float bias, theta;
+};
+
+template <int WT, int KC>
+__device__ __forceinline__ void load_row(uint4 (&w)[KC], const uint8_t *base, size_t rb, int row, int lane)
+{
+#pragma unroll
+    for (int k = 0; k < KC; ++k) w[k] = ld16(base + (size_t)row * rb + (size_t)(k * 64 + lane) * 16);
+}
+
+// fixed-order dot of one row (chunks in registers) with x in LDS
+template <int WT, int KC>
+__device__ __forceinline__ float dot_row_lds(const uint4 (&w)[KC], const float *xs, int lane)
+{
+    constexpr int E = Chunk<WT>::E;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        float xv[E];
+        const float4 *xp = (const float4 *)(xs + (size_t)(k * 64 + lane) * E);
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) {
+            const float4 v = xp[e4];
+            xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
+            xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
+        }
+        acc = chunk_dot<WT>(w[k], 0.0f, xv, acc);
+    }
+    return wave_tree_sum(acc);
+}
+
+__device__ __forceinline__ void stage_vec(float *xs, const float *x, int n)
+{
+    for (int i = threadIdx.x; i < n / 4; i += blockDim.x) ((float4 *)xs)[i] = ((const float4 *)x)[i];
+}
+
+// Fused sparse layer for one token.  Each workgroup owns RB consecutive
+// neurons; wave w walks neurons w, w + 8, ... with the next gate row prefetched.
+// For an active neuron the wave loads its W_up row and W_down^T row together,
+// forms h = act(g') u and accumulates h * W_down^T[j] into a per-wave partial y
+// held in registers (lane p owns the columns of chunks p, p + 64, ...).  No
+// barrier separates gate, up and down, so the memory pipe keeps streaming
+// while some waves wait on dependent loads.  At the end the 8 wave partials are
+// summed in a fixed order through LDS into the workgroup's partial.
+constexpr int kFusedNW = 8;
+constexpr int kFusedNT = kFusedNW * 64;
+
+template <int WT, int KC>
+__global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
+{
+    constexpr int E = Chunk<WT>::E;
+    constexpr int NW = kFusedNW, NT = kFusedNT;
+    constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
+    constexpr int D = KC * 64 * E;
+    constexpr size_t RBYTES = (size_t)D * EB;
+    __shared__ __align__(16) float xs[D];
+    __shared__ __align__(16) float ysum[NW * D];
+    __shared__ int flags[kFusedMaxRB];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = blockIdx.x * a.RB;
+    const int nr = min(a.RB, a.f - r0);
+
+    uint4 ga[KC], gb[KC];
+    if (wave < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + wave, lane);
+    stage_vec(xs, a.x, D);
+    __syncthreads();
+
+    // this wave's partial y lives in its own LDS slice (lane p owns the columns
+    // of chunks p, p + 64, ...), so only the running rows occupy registers
+    float *yw = ysum + (size_t)wave * D;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        float4 *dst = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) dst[e4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+
+    // one neuron: gate value from `cur`, then (if active) up and down rows
+    auto neuron = [&](const uint4 (&cur)[KC], int i) {
+        const float g = dot_row_lds<WT, KC>(cur, xs, lane);
+        const float gp = g + a.bias;
+        const bool on = gate_pred(a.mode, gp, a.theta);
+        if (lane == 0) {
+            a.G[r0 + i] = gp;
+            flags[i] = on ? 1 : 0;
+        }
+        if (on) {
+            uint4 ua[KC], da[KC];
+            load_row<WT, KC>(ua, a.wu, RBYTES, r0 + i, lane);
+            load_row<WT, KC>(da, a.wdt, RBYTES, r0 + i, lane);
+            const float u = dot_row_lds<WT, KC>(ua, xs, lane);
+            const float h = act_f32(a.act, gp) * u;
+#pragma unroll
+            for (int k = 0; k < KC; ++k) {
+                float w[E];
+                unpack<WT>(da[k], w);
+                float4 *yv = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
+#pragma unroll
+                for (int e4 = 0; e4 < E / 4; ++e4) {
+                    float4 v = yv[e4];
+                    v.x = __builtin_fmaf(h, w[4 * e4 + 0], v.x);
+                    v.y = __builtin_fmaf(h, w[4 * e4 + 1], v.y);
+                    v.z = __builtin_fmaf(h, w[4 * e4 + 2], v.z);
+                    v.w = __builtin_fmaf(h, w[4 * e4 + 3], v.w);
+                    yv[e4] = v;
+                }
+            }
+        }
+    };
+    for (int i = wave; i < nr; i += 2 * NW) {
+        const int i2 = i + NW;
+        if (i2 < nr) load_row<WT, KC>(gb, a.wg, RBYTES, r0 + i2, lane);
+        neuron(ga, i);
+        if (i2 >= nr) break;
+        const int i3 = i2 + NW;
+        if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
+        neuron(gb, i2);
+    }
+
+    // fixed-order sum of the wave partials
+    __syncthreads();
+    for (int c = threadIdx.x; c < D / 4; c += NT) {
+        float4 acc = ((const float4 *)ysum)[c];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const float4 v = ((const float4 *)(ysum + (size_t)w * D))[c];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        ((float4 *)(a.partial + (size_t)blockIdx.x * D))[c] = acc;
+    }
+    // ascending list of this workgroup's active neurons (ballot + mbcnt)
+    if (wave == 0) {
+        const int on = lane < nr ? flags[lane] : 0;
+        const uint64_t m = __ballot(on);
+        if (on) a.list_idx[(size_t)blockIdx.x * a.RB + mbcnt64(m)] = r0 + lane;
+        if (lane == 0) a.list_cnt[blockIdx.x] = __popcll(m);
+    }
+}
+
+// Dense baseline, step 1: h_j = act(W_gate[j] . x + b) * (W_up[j] . x) for every
+// neuron, one row pair per wave.
+template <int WT, int KC>
+__global__ __launch_bounds__(kB1NT) void k_dense_gu_b1(const uint8_t *__restrict__ wg, const uint8_t *__restrict__ wu,
+                                                       const float *__restrict__ x, float *__restrict__ H, int f,
+                                                       int act, float bias)
+{
+    constexpr int E = Chunk<WT>::E;
+    constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
+    constexpr int D = KC * 64 * E;
+    constexpr size_t RBYTES = (size_t)D * EB;
+    __shared__ __align__(16) float xs[D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = blockIdx.x * kB1NW + wave;
+    uint4 w0[KC], w1[KC];
+    if (j < f) {
+        load_row<WT, KC>(w0, wg, RBYTES, j, lane);
+        load_row<WT, KC>(w1, wu, RBYTES, j, lane);
+    }
+    stage_vec(xs, x, D);
+    __syncthreads();
+    if (j < f) {
+        const float g = dot_row_lds<WT, KC>(w0, xs, lane);
+        const float u = dot_row_lds<WT, KC>(w1, xs, lane);
+        if (lane == 0) H[j] = act_f32(act, g + bias) * u;
+    }
+}
+
+// Dense baseline, step 2: y_i = W_down[i, :] . h (+ x_i), one row per wave,
+// chunk groups of 12 double-buffered; h staged in LDS (f <= 16384).
+template <int WT>
+__global__ __launch_bounds__(kB1NT) void k_dense_down_b1(const uint8_t *__restrict__ wd, const float *__restrict__ H,
+                                                         int d, int f, const float *__restrict__ resid,
+                                                         float *__restrict__ out)
+{
+    constexpr int E = Chunk<WT>::E;
+    constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
+    constexpr int KG = 12;
+    extern __shared__ __align__(16) float hs[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.x * kB1NW + wave;
+    const int nch = f / E;
+    const size_t rb = (size_t)f * EB;
+    uint4 wa[KG], wb[KG];
+    auto load = [&](uint4 (&w)[KG], int k0) {
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            const int c = (k0 + k) * 64 + lane;
+            w[k] = (i < d && c < nch) ? ld16(wd + (size_t)i * rb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto dot = [&](const uint4 (&w)[KG], int k0, float acc) {
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            const int c = (k0 + k) * 64 + lane;
+            if (c < nch) {
+                float xv[E];
+                const float4 *xp = (const float4 *)(hs + (size_t)c * E);
+#pragma unroll
+                for (int e4 = 0; e4 < E / 4; ++e4) {
+                    const float4 v = xp[e4];
+                    xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
+                    xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
+                }
+                acc = chunk_dot<WT>(w[k], 0.0f, xv, acc);
+            }
+        }
+        return acc;
+    };
+    const int K = (nch + 63) / 64;
+    load(wa, 0);
+    stage_vec(hs, H, f);
+    __syncthreads();
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += 2 * KG) {
+        if (k0 + KG < K) load(wb, k0 + KG);
+        acc = dot(wa, k0, acc);
+        if (k0 + KG >= K) break;
+        if (k0 + 2 * KG < K) load(wa, k0 + 2 * KG);
+        acc = dot(wb, k0 + KG, acc);
+    }
+    acc = wave_tree_sum(acc);
+    if (lane == 0 && i < d) out[i] = resid ? acc + resid[i] : acc;
+}
+
+// y = sum over the partials in a fixed order (+ residual): 16 columns per
+// workgroup; thread (column, group g) sums partials g, g + 64, g + 128, ...
+// with all of its loads issued before the first add, then the 64 groups are
+// combined in a fixed order through LDS.
+__global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ partial, int P, int BD,
+                                                   const float *__restrict__ resid, float *__restrict__ out)
+{
+    __shared__ float red[64][17];
+    __shared__ float red2[16][17];
+    const int l = threadIdx.x & 15, qg = threadIdx.x >> 4;
+    const int col = blockIdx.x * 16 + l;
+    float s = 0.0f;
+    if (col < BD) {
+        for (int q0 = qg; q0 < P; q0 += 64 * 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = q0 + 64 * u;
+                v[u] = q < P ? partial[(size_t)q * BD + col] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+    }
+    red[qg][l] = s;
+    __syncthreads();
+    if (qg < 16) {
+        float v = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) v += red[qg * 4 + g][l];
+        red2[qg][l] = v;
+    }
+    __syncthreads();
+    if (qg == 0 && col < BD) {
+        float y = 0.0f;
+        for (int g = 0; g < 16; ++g) y += red2[g][l];
+        if (resid) y += resid[col];
+        out[col] = y;
+    }
+}
+
+template <int WT>
+static hipError_t run_decode_b1(const FusedArgs &a, int KC, int P, hipStream_t st)
+{
+    switch (KC) {
+#define CASE_KC(k)                                                                                 \
+    case k:                                                                                        \
+        hipLaunchKernelGGL((k_decode_b1<WT, k>), dim3(P), dim3(kFusedNT), 0, st, a);               \
+        return hipGetLastError();
+        CASE_KC(1) CASE_KC(2) CASE_KC(3) CASE_KC(4) CASE_KC(5) CASE_KC(6) CASE_KC(7) CASE_KC(8)
+#undef CASE_KC
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int WT>
+static hipError_t run_dense_gu_b1(int KC, const uint8_t *wg, const uint8_t *wu, const float *x, float *H, int f,
+                                  int act, float bias, hipStream_t st)
+{
+    const int grid = (f + kB1NW - 1) / kB1NW;
+    switch (KC) {
+#define CASE_KC(k)                                                                                         \
+    case k:                                                                                                \
+        hipLaunchKernelGGL((k_dense_gu_b1<WT, k>), dim3(grid), dim3(kB1NT), 0, st, wg, wu, x, H, f, act, bias); \
+        return hipGetLastError();
+        CASE_KC(1) CASE_KC(2) CASE_KC(3) CASE_KC(4) CASE_KC(5) CASE_KC(6) CASE_KC(7) CASE_KC(8)
+#undef CASE_KC
+    }
+    return hipErrorInvalidValue;
+}
+
+// rows per workgroup of the fused batch-1 kernel: one workgroup per CU when
+// d_ff allows it, never more than 48 rows
+inline int fused_rows_per_wg(int f) { return std::min(kFusedMaxRB, std::max(1, (f + 255) / 256)); }
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -738,6 +1059,43 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     r.bias = c.bias;
     r.theta = c.theta;
 
+    if constexpr (BT == 1 && WT != SFFN_W_INT4_G128) {
+        constexpr int E = Chunk<WT>::E;
+        const int KC = d / (64 * E);
+        const bool fits = d % (64 * E) == 0 && KC >= 1 && KC <= 8;
+        if (c.mode == SFFN_MODE_DENSE && fits && f <= 16384) {
+            if ((e = run_dense_gu_b1<WT>(KC, L.wg, L.wu, xin, G, f, D.act, c.bias, st)) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_dense_down_b1<WT>, dim3((d + kB1NW - 1) / kB1NW), dim3(kB1NT), (size_t)f * 4, st,
+                               L.wd, (const float *)G, d, f, D.residual ? c.x : nullptr, c.out);
+            return hipGetLastError();
+        }
+        if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && fits) {
+            FusedArgs fa{};
+            fa.wg = L.wg; fa.wu = L.wu; fa.wdt = L.wdt;
+            fa.x = xin;
+            fa.G = G;
+            fa.partial = (float *)(sc + S.partial);
+            fa.list_cnt = lcnt; fa.list_idx = lidx;
+            fa.f = f;
+            fa.RB = fused_rows_per_wg(f);
+            fa.mode = c.mode; fa.act = D.act; fa.bias = c.bias; fa.theta = c.theta;
+            const int P = (f + fa.RB - 1) / fa.RB;
+            if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
+            if ((e = run_decode_b1<WT>(fa, KC, P, st)) != hipSuccess) return e;
+            if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+            if (c.idx_out || c.count_out) {
+                const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
+                hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + P + 1) * 4, st,
+                                   (const int *)lcnt, (const int *)lidx, P, fa.RB, c.idx_out, c.count_out, maxs);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            if (!forward) return hipSuccess;
+            hipLaunchKernelGGL(k_reduce16, dim3((d + 15) / 16), dim3(1024), 0, st, (const float *)(sc + S.partial), P, d,
+                               D.residual ? c.x : nullptr, c.out);
+            return hipGetLastError();
+        }
+    }
+
     if (c.mode == SFFN_MODE_DENSE) {
         r.w0 = L.wg; r.s0 = L.sg; r.w1 = L.wu; r.s1 = L.su;
         r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
@@ -754,7 +1112,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     r.w0 = L.wg; r.s0 = L.sg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
     if (c.mode == SFFN_MODE_TOPK) {
         r.w1 = L.wu; r.s1 = L.su; r.o1 = U;
+        if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
         if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st)) != hipSuccess) return e;
+        if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
         TopkArgs t{G, U, L.wdn, f, c.topk_k, nw32, (uint64_t *)(sc + S.keys), bits};
         hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), 0, st, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -766,7 +1126,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     } else {
         r.list_cnt = lcnt;
         r.list_idx = lidx;
+        if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
         if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st)) != hipSuccess) return e;
+        if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
         R = gate_rows_per_block<WT, BT>();
         nL = (f + R - 1) / R;
     }

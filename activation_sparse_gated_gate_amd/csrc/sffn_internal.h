@@ -31,6 +31,24 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 // the handle
 // ---------------------------------------------------------------------------
+// optional per-launch events around the main kernel (diagnostics)
+struct KernelTimer {
+    void *const *begin = nullptr;
+    void *const *end = nullptr;
+    int n = 0, next = 0;
+    hipError_t before(hipStream_t st)
+    {
+        return next < n ? hipEventRecord((hipEvent_t)begin[next], st) : hipSuccess;
+    }
+    hipError_t after(hipStream_t st)
+    {
+        if (next >= n) return hipSuccess;
+        hipError_t e = hipEventRecord((hipEvent_t)end[next], st);
+        ++next;
+        return e;
+    }
+};
+
 struct Layer {
     sffn_layer_desc desc;
     // decode layouts
@@ -44,6 +62,7 @@ struct Layer {
     // prefill layouts (bf16)
     const uint16_t *wgu = nullptr;                // [f/32][2][32][d]: gate rows then up rows
     const uint16_t *wdp = nullptr;                // W_down natural [d][f]
+    KernelTimer *timer = nullptr;                 // owned by the handle
 };
 
 // persistent-buffer layout, in creation order

@@ -203,6 +203,18 @@ const char *sffn_status_string(sffn_status status);
 /* Last HIP error text recorded by this thread, or "" (diagnostics only). */
 const char *sffn_last_hip_error(void);
 
+/*
+ * Diagnostics for benchmarks: arm per-launch timing of the path's main kernel
+ * (the decode gate/selection kernel, the prefill gate-up GEMM).  The next n
+ * sffn_forward calls on this handle record begin_events[i] / end_events[i]
+ * (hipEvent_t, created by the caller with timing enabled) on the call's stream
+ * immediately before and after that kernel; later calls record nothing.  The
+ * arrays are host memory and must stay valid until those n calls are made.
+ * n = 0 disarms.  Not thread-safe: do not arm a handle used by two threads.
+ */
+sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events,
+                                  int32_t n);
+
 #ifdef __cplusplus
 }
 #endif
