@@ -1,11 +1,442 @@
-// prefill.hip -- token-selective prefill (placeholder until the kernels land).
+// prefill.hip -- token-selective prefill FFN (gfx950).
+//
+// RedKnot article, Algorithm 1 (section on why the FFN is the hidden
+// bottleneck) and the section on the token-selective sparse FFN: the FFN runs
+// only on the important tokens S, Z[~S] = 0 and X_next = Y + Z.
+//   t1 k_token_norms   s_i = ||A_i||_2 (attention output row), sum of squares in
+//                      the fixed fp32 order (64 lane accumulators), IEEE sqrt.
+//   t2 k_token_select  one workgroup: sort the (score, index) keys descending,
+//                      fp64 cumulative mass in blocks of 256 sorted entries,
+//                      shortest prefix reaching mass * total, plus the last
+//                      recent_n tokens, plus top-ranked tokens up to min_keep;
+//                      mass >= 1 or total == 0 keeps every token.  Writes the
+//                      ascending keep list, its length and per-token flags, all
+//                      on the device (no host synchronisation).
+//   t3 k_gemm<GATE_UP> H = SiLU(Y_S W_gate^T) (.) (Y_S W_up^T), bf16 MFMA with
+//                      the A rows gathered through the keep list and the gate /
+//                      up columns of the same neurons in one tile (the weights
+//                      are interleaved in blocks of 32 rows at creation).
+//   t4 k_gemm<DOWN>    Z = H W_down^T; epilogue X_next[S_m] = bf16(Y[S_m] + Z_m),
+//                      a scatter through the keep list.
+//   k_copy_unkept      X_next[i] = Y[i] for i not kept (skipped when X_next == Y).
+// Tiles whose rows start past the device-side count exit at once, so the grid
+// is sized for the largest count without a host round trip.
 #include <hip/hip_runtime.h>
 
 #include "dev_common.h"
 
 namespace sffn {
 
-hipError_t launch_prefill_select(const PrefillSelectCall &) { return hipErrorNotSupported; }
-hipError_t launch_prefill_forward(const PrefillForwardCall &) { return hipErrorNotSupported; }
+// ---------------------------------------------------------------------------
+// t1: token norms
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict__ A, int L, int d,
+                                                     float *__restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= L) return;
+    const int nch = d / 8;
+    const uint8_t *rp = (const uint8_t *)(A + (size_t)row * d);
+    float acc = 0.0f;
+    constexpr int KB = 8;  // chunk-columns loaded per batch
+    for (int k0 = 0; k0 * 64 < nch; k0 += KB) {
+        uint4 v[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int c = (k0 + k) * 64 + lane;
+            v[k] = c < nch ? ld16(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int c = (k0 + k) * 64 + lane;
+            if (c < nch) {
+                float w[8];
+                unpack<SFFN_W_BF16>(v[k], w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(w[e], w[e], acc);
+            }
+        }
+    }
+    acc = wave_tree_sum(acc);
+    if (lane == 0) s[row] = sqrtf(acc);
+}
+
+// ---------------------------------------------------------------------------
+// t2: token selection (one workgroup of 1024 threads)
+// ---------------------------------------------------------------------------
+struct SelectArgs {
+    const float *s;
+    int L, recent_n, min_keep;
+    double mass;
+    int32_t *keep, *count;
+    int32_t *flags;  // [L] 1 = kept
+};
+
+__device__ __forceinline__ uint64_t rank_key(float s, int i)
+{
+    // descending key order = score descending, then index ascending
+    return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+__global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
+{
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    const int L = a.L, tid = threadIdx.x, NT = 1024;
+    int N = 1;
+    while (N < L) N <<= 1;
+    uint64_t *key = (uint64_t *)lds_raw;                      // [N]
+    unsigned char *in = lds_raw + (size_t)N * 8;              // [L] membership
+    __shared__ double blk_total[kMaxPrefillRows / kMassBlock + 1];
+    __shared__ double blk_base[kMaxPrefillRows / kMassBlock + 1];
+    __shared__ int s_m, s_all, s_cnt;
+    __shared__ int tmp[17];
+
+    for (int i = tid; i < N; i += NT) key[i] = i < L ? rank_key(a.s[i], i) : 0ull;
+    for (int i = tid; i < L; i += NT) in[i] = 0;
+    if (tid == 0) s_m = L;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < N; i += NT) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const uint64_t x = key[i], y = key[p];
+                    const bool desc = (i & k) == 0;
+                    if (desc ? (x < y) : (x > y)) {
+                        key[i] = y;
+                        key[p] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // fp64 cumulative mass in blocks of kMassBlock sorted entries
+    const int nb = (L + kMassBlock - 1) / kMassBlock;
+    if (tid < nb) {
+        double run = 0.0;
+        const int b1 = min(L, (tid + 1) * kMassBlock);
+        for (int k = tid * kMassBlock; k < b1; ++k) run = run + (double)__uint_as_float((uint32_t)(key[k] >> 32));
+        blk_total[tid] = run;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double base = 0.0;
+        for (int b = 0; b < nb; ++b) {
+            blk_base[b] = base;
+            base = base + blk_total[b];
+        }
+        const double total = base;  // equals the last cumulative value
+        s_all = (a.mass >= 1.0 || total == 0.0) ? 1 : 0;
+        blk_base[nb] = total;
+    }
+    __syncthreads();
+    const bool all = s_all != 0;
+    if (!all && a.mass > 0.0) {
+        const double thr = a.mass * blk_base[nb];
+        if (tid < nb) {
+            double run = 0.0;
+            const int b1 = min(L, (tid + 1) * kMassBlock);
+            for (int k = tid * kMassBlock; k < b1; ++k) {
+                run = run + (double)__uint_as_float((uint32_t)(key[k] >> 32));
+                if (blk_base[tid] + run >= thr) {
+                    atomicMin(&s_m, k);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        // the shortest prefix: ranks 0..m
+        for (int r = tid; r <= s_m; r += NT) in[0xFFFFFFFFu - (uint32_t)key[r]] = 1;
+    }
+    __syncthreads();
+    if (all) {
+        for (int i = tid; i < L; i += NT) in[i] = 1;
+    } else {
+        for (int i = max(0, L - a.recent_n) + tid; i < L; i += NT) in[i] = 1;
+    }
+    __syncthreads();
+    // min_keep: add the highest-ranked tokens not yet kept.  Threads own
+    // contiguous runs of ranks; a scan of their not-yet-kept counts tells each
+    // thread how many of its tokens are among the first `need` ones.
+    {
+        int c = 0;
+        for (int i = tid; i < L; i += NT) c += in[i];
+        int tot;
+        block_exclusive_scan(c, tmp, &tot);
+        const int need = a.min_keep - tot;
+        if (need > 0) {
+            const int per = (L + NT - 1) / NT;
+            const int r0 = min(L, tid * per), r1 = min(L, r0 + per);
+            int free = 0;
+            for (int r = r0; r < r1; ++r) free += in[0xFFFFFFFFu - (uint32_t)key[r]] ? 0 : 1;
+            int ftot;
+            int before = block_exclusive_scan(free, tmp, &ftot);
+            for (int r = r0; r < r1 && before < need; ++r) {
+                const int i = (int)(0xFFFFFFFFu - (uint32_t)key[r]);
+                if (!in[i]) {
+                    in[i] = 1;
+                    ++before;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // ascending keep list: contiguous token runs per thread, block scan of counts
+    const int per = (L + NT - 1) / NT;
+    const int i0 = min(L, tid * per), i1 = min(L, i0 + per);
+    int c = 0;
+    for (int i = i0; i < i1; ++i) c += in[i] ? 1 : 0;
+    int tot;
+    int pos = block_exclusive_scan(c, tmp, &tot);
+    for (int i = i0; i < i1; ++i) {
+        const int on = in[i] ? 1 : 0;
+        a.flags[i] = on;
+        if (on) a.keep[pos++] = i;
+    }
+    if (tid == 0) *a.count = tot;
+}
+
+// ---------------------------------------------------------------------------
+// t3 / t4: gathered bf16 MFMA GEMM,  C[m][n] = sum_k A[m][k] B[n][k]
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+enum { EPI_GATE_UP = 0, EPI_DOWN = 1 };
+
+constexpr int GBM = 128, GBN = 128, GBK = 64;
+constexpr int GLDA = GBK + 8;  // LDS row pitch in bf16 (16-byte pad)
+
+struct GemmArgs {
+    const uint16_t *A;      // GATE_UP: Y [L][K] gathered through keep; DOWN: H [Mmax][K]
+    const uint16_t *B;      // [N][K]
+    int K, N;
+    const int32_t *keep;    // kept token indices
+    const int32_t *count;   // device count M
+    uint16_t *H;            // GATE_UP output [Mmax][N/2]
+    const uint16_t *Y;      // DOWN: residual rows
+    uint16_t *X;            // DOWN: output rows (scatter)
+    int ldo;                // row length of H (GATE_UP) or X/Y (DOWN)
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
+{
+    __shared__ __align__(16) uint16_t As[GBM * GLDA];
+    __shared__ __align__(16) uint16_t Bs[GBN * GLDA];
+    __shared__ int rowsrc[GBM];
+
+    const int M = *a.count;
+    const int mt = (M + GBM - 1) / GBM;
+    const int nt = a.N / GBN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, 64 x 64 each
+    const int KT = a.K / GBK;
+
+    for (int tile = blockIdx.x; tile < mt * nt; tile += gridDim.x) {
+        const int tm = tile % mt, tn = tile / mt;
+        const int m0 = tm * GBM, n0 = tn * GBN;
+        __syncthreads();
+        if (tid < GBM) {
+            const int m = m0 + tid;
+            rowsrc[tid] = m < M ? (EPI == EPI_GATE_UP ? a.keep[m] : m) : -1;
+        }
+        __syncthreads();
+
+        // each thread moves 4 A chunks and 4 B chunks of 16 bytes per k-tile
+        uint4 ra[4], rb[4];
+        auto gload = [&](int kt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + q * 256;        // 0..1023
+                const int r = c >> 3, kc = c & 7;   // row, 8-element chunk
+                const int src = rowsrc[r];
+                ra[q] = src >= 0 ? ld16(a.A + (size_t)src * a.K + (size_t)kt * GBK + kc * 8) : make_uint4(0, 0, 0, 0);
+                rb[q] = ld16(a.B + (size_t)(n0 + r) * a.K + (size_t)kt * GBK + kc * 8);
+            }
+        };
+        auto sstore = [&]() {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + q * 256;
+                const int r = c >> 3, kc = c & 7;
+                *(uint4 *)&As[r * GLDA + kc * 8] = ra[q];
+                *(uint4 *)&Bs[r * GLDA + kc * 8] = rb[q];
+            }
+        };
+
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+        gload(0);
+        sstore();
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+            for (int ks = 0; ks < GBK / 16; ++ks) {
+                bf16x8 fa[2], fb[2];
+                const int kk = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    fa[i] = *(const bf16x8 *)&As[(wm * 64 + i * 32 + (lane & 31)) * GLDA + kk];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    fb[j] = *(const bf16x8 *)&Bs[(wn * 64 + j * 32 + (lane & 31)) * GLDA + kk];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+            __syncthreads();
+            if (kt + 1 < KT) {
+                sstore();
+                __syncthreads();
+            }
+        }
+
+        // epilogue.  Output element (row, col) of a 32x32 tile: lane holds
+        // col = lane & 31 and rows 8*g + 4*(lane >> 5) + e for acc index 4*g + e.
+        const int ccol = lane & 31;
+        if constexpr (EPI == EPI_GATE_UP) {
+            // wave columns: [gate of neurons j0..j0+31 | up of the same neurons]
+            const int j = (n0 + wn * 64) / 2 + ccol;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rl = wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                        const int m = m0 + rl;
+                        if (m < M) {
+                            const float gv = acc[i][0][4 * g + e], uv = acc[i][1][4 * g + e];
+                            const float h = gv / (1.0f + expf(-gv)) * uv;
+                            a.H[(size_t)m * a.ldo + j] = f32_to_bf16_rne(h);
+                        }
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int rl = wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                            const int m = m0 + rl;
+                            if (m < M) {
+                                const int tok = a.keep[m];
+                                const int n = n0 + wn * 64 + j * 32 + ccol;
+                                const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
+                                a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
+                            }
+                        }
+        }
+    }
+}
+
+// flags[i] = 1 iff i is in the ascending keep list (binary search per token)
+__global__ __launch_bounds__(256) void k_fill_flags(int32_t *__restrict__ flags, int L, const int32_t *__restrict__ keep,
+                                                    const int32_t *__restrict__ count)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= L) return;
+    int lo = 0, hi = *count;  // search [lo, hi)
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (keep[mid] < i) lo = mid + 1; else hi = mid;
+    }
+    flags[i] = (lo < *count && keep[lo] == i) ? 1 : 0;
+}
+
+// X_next rows of tokens that are not kept: a copy of Y
+__global__ __launch_bounds__(256) void k_copy_unkept(const uint16_t *__restrict__ Y, uint16_t *__restrict__ X,
+                                                     const int32_t *__restrict__ flags, int d)
+{
+    const int row = blockIdx.x;
+    if (flags[row]) return;
+    const uint4 *src = (const uint4 *)(Y + (size_t)row * d);
+    uint4 *dst = (uint4 *)(X + (size_t)row * d);
+    for (int i = threadIdx.x; i < d / 8; i += 256) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_prefill_select(const PrefillSelectCall &c)
+{
+    const Layer &L = *c.L;
+    const int d = L.desc.d_model, rows = c.rows;
+    const ScratchLayout S = scratch_layout(L.desc);
+    float *sc_s = (float *)(c.scratch + S.tscore);
+    int32_t *flags = (int32_t *)(c.scratch + S.tflag);
+    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, c.stream, c.A, rows, d, sc_s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int N = 1;
+    while (N < rows) N <<= 1;
+    const size_t lds = (size_t)N * 8 + (size_t)rows;
+    static bool attr = false;
+    if (!attr) {
+        e = hipFuncSetAttribute((const void *)k_token_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)((size_t)kMaxPrefillRows * 8 + kMaxPrefillRows));
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    SelectArgs a{sc_s, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out, flags};
+    hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_forward(const PrefillForwardCall &c)
+{
+    const Layer &L = *c.L;
+    const int d = L.desc.d_model, f = L.desc.d_ff, rows = c.rows;
+    const ScratchLayout S = scratch_layout(L.desc);
+    uint16_t *H = (uint16_t *)(c.scratch + S.pH);
+    int32_t *flags = (int32_t *)(c.scratch + S.tflag);
+    hipError_t e;
+    if (c.X != c.Y) {
+        // flags come from the keep list: rebuild them here so that forward does
+        // not depend on a previous select call on the same scratch
+        hipLaunchKernelGGL(k_fill_flags, dim3((rows + 255) / 256), dim3(256), 0, c.stream, flags, rows, c.keep,
+                           c.count);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_copy_unkept, dim3(rows), dim3(256), 0, c.stream, c.Y, c.X, (const int32_t *)flags, d);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int mt_max = (rows + GBM - 1) / GBM;
+    GemmArgs g{};
+    g.A = c.Y; g.B = L.wgu; g.K = d; g.N = 2 * f; g.keep = c.keep; g.count = c.count; g.H = H; g.ldo = f;
+    const int tiles1 = mt_max * (2 * f / GBN);
+    if ((e = L.timer->before(c.stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gemm<EPI_GATE_UP>, dim3(std::min(tiles1, 2048)), dim3(256), 0, c.stream, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = L.timer->after(c.stream)) != hipSuccess) return e;
+    GemmArgs g2{};
+    g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
+    g2.ldo = d;
+    const int tiles2 = mt_max * (d / GBN);
+    hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(std::min(tiles2, 2048)), dim3(256), 0, c.stream, g2);
+    return hipGetLastError();
+}
 
 }  // namespace sffn
