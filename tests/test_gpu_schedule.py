@@ -1,0 +1,69 @@
+"""GPU parity of the 28-layer decode schedule (config 4) against the oracle.
+
+Layers 0-7 keep every neuron, layers 8-19 use the gate threshold for a ~ 0.3
+and layers 20-27 the one for a ~ 0.13; a batch of 16 tokens runs over the union
+of its selected sets; each layer is RMSNorm -> FFN -> residual.
+
+Per layer (teacher-forced: the oracle gets the GPU's input x_l): x_hat and the
+gate values bit-exact, the selected union bit-exact, x_{l+1} within relative L2
+2e-3.  Over the whole stack: the GPU's x_28 against a free oracle rollout within
+relative L2 2e-3.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from gpu_util import make_layer, rel_l2, run_decode, scratch_views
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_stack(n_layers, d, f, B, seed_shift=0):
+    import activation_sparse_gated_gate_amd as sf
+    x_gpu = synth.cfg4_input(B, d)
+    x_free = x_gpu.copy()
+    worst = 0.0
+    dens = []
+    for l in range(n_layers):
+        w = synth.cfg4_layer_weights(l + seed_shift, d, f)
+        mode, a = synth.cfg4_schedule(l)
+        th = synth.gate_threshold_for_active_fraction(a) if mode == "thresh" else 0.0
+        layer = make_layer(w, B, rmsnorm=True, residual=True)
+        pol = sf.make_policy(mode, theta=th, use_union=True)
+        y, idx, n = run_decode(layer, pol, x_gpu)
+        ref = oracle.decode(w, x_gpu, mode=mode, theta=th, union=True, rmsnorm=True, residual=True)
+        xh, g, _ = scratch_views(layer, B)
+        assert np.array_equal(xh.cpu().numpy().view(np.uint32), ref["xhat"].view(np.uint32)), l
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), ref["g"].view(np.uint32)), l
+        assert np.array_equal(idx, ref["idx"]), "layer %d selected union differs" % l
+        err = rel_l2(y, ref["y"])
+        assert err <= 2e-3, (l, err)
+        worst = max(worst, err)
+        dens.append(n / f)
+        free = oracle.decode(w, x_free, mode=mode, theta=th, union=True, rmsnorm=True, residual=True)
+        x_free = free["y"].astype(np.float32)
+        x_gpu = y
+        layer.close()
+    return x_gpu, x_free, worst, dens
+
+
+def test_schedule_reduced_width_28_layers():
+    # the full schedule at reduced width (d 512, f 2688, batch 16)
+    x_gpu, x_free, worst, dens = _run_stack(28, 512, 2688, 16)
+    assert rel_l2(x_gpu, x_free) <= 2e-3
+    assert all(v == 1.0 for v in dens[:8])
+    assert np.all(np.isfinite(x_gpu))
+
+
+def test_schedule_full_shape_28_layers():
+    # config 4 as stated: 28 layers, d_model 3584, d_ff 18944, batch 16
+    x_gpu, x_free, worst, dens = _run_stack(28, synth.CFG4_D, synth.CFG4_F, synth.CFG4_B)
+    err = rel_l2(x_gpu, x_free)
+    print("x_28 relL2 vs free rollout %.3g; worst layer %.3g; union density %s" %
+          (err, worst, [round(v, 3) for v in dens]))
+    assert err <= 2e-3
+    # union of 16 tokens: 1 - (1 - a)^16 (denseflux, section 4.2 law)
+    assert abs(np.mean(dens[8:20]) - oracle.group_active_probability(0.3, 16)) < 0.01
+    assert abs(np.mean(dens[20:]) - oracle.group_active_probability(0.13, 16)) < 0.02
