@@ -73,6 +73,8 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         // partial sums: kGatherWGs per token for the batched gather; the batch-1
         // fused kernel uses ceil(f / RB) <= max(256, ceil(f / 48)) workgroups
         S.partial = take(std::max((size_t)kGatherWGs * B, (size_t)(f + 47) / 48 + 256) * d * 4);
+        S.xsplit = take((size_t)2 * 16 * d * 2);   // x_hat as bf16 hi / lo, 16 token slots
+        S.hsplit = take((size_t)2 * 16 * f * 2);   // h as bf16 hi / lo, 16 token slots
     }
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         S.tscore = take(B * 4 * 2);   // scores and their sorted copy
@@ -224,6 +226,7 @@ static sffn_status policy_ok(const sffn_layer *h, const sffn_policy *p)
     if (p->mode == SFFN_MODE_TOPK && (p->topk_k < 1 || p->topk_k > D.d_ff)) return SFFN_ERR_INVALID_ARG;
     if (p->use_union != 0 && p->use_union != 1) return SFFN_ERR_INVALID_ARG;
     if (p->mode == SFFN_MODE_TOPK && D.act != SFFN_ACT_SILU) return SFFN_ERR_UNSUPPORTED;
+    if (p->mode == SFFN_MODE_TOPK && D.d_ff > kMaxTopkNeurons) return SFFN_ERR_UNSUPPORTED;
     return SFFN_OK;
 }
 

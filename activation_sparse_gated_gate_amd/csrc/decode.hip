@@ -54,17 +54,33 @@ __global__ __launch_bounds__(64) void k_rmsnorm(const float *__restrict__ x, flo
 {
     const int t = blockIdx.x, lane = threadIdx.x;
     const float *xt = x + (size_t)t * d;
+    const int nch = d / 4;
     float acc = 0.0f;
-    for (int c = lane; c < d / 4; c += 64) {
-        const float4 v = *(const float4 *)(xt + 4 * c);
-        acc = __builtin_fmaf(v.x, v.x, acc);
-        acc = __builtin_fmaf(v.y, v.y, acc);
-        acc = __builtin_fmaf(v.z, v.z, acc);
-        acc = __builtin_fmaf(v.w, v.w, acc);
+    // lane p folds chunks p, p + 64, ... in increasing order; 16 loads in flight
+    for (int k0 = 0; k0 * 64 < nch; k0 += 16) {
+        float4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int c = (k0 + u) * 64 + lane;
+            v[u] = c < nch ? *(const float4 *)(xt + 4 * c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if ((k0 + u) * 64 + lane < nch) {
+                acc = __builtin_fmaf(v[u].x, v[u].x, acc);
+                acc = __builtin_fmaf(v[u].y, v[u].y, acc);
+                acc = __builtin_fmaf(v[u].z, v[u].z, acc);
+                acc = __builtin_fmaf(v[u].w, v[u].w, acc);
+            }
+        }
     }
     const float ss = wave_tree_sum(acc);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int i = lane; i < d; i += 64) xhat[(size_t)t * d + i] = xt[i] * r;
+    for (int c = lane; c < nch; c += 64) {
+        float4 v = *(const float4 *)(xt + 4 * c);
+        v.x *= r; v.y *= r; v.z *= r; v.w *= r;
+        *(float4 *)(xhat + (size_t)t * d + 4 * c) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -266,56 +282,58 @@ struct TopkArgs {
     uint32_t *bits;
 };
 
+// One workgroup per token: score every neuron (fp64 key = the bits of the
+// non-negative score, so the integer order is the value order), then an exact
+// radix select of the k-th largest key T over the keys held in LDS, one byte
+// per pass from the top, each wave counting into its own histogram.  Keep
+// every neuron above T and, of those equal to T, the lowest indices (an
+// index-order scan).
 __global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
 {
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const float *g = a.G + (size_t)t * a.f;
-    const float *u = a.U + (size_t)t * a.f;
-    uint64_t *key = a.keys + (size_t)t * a.f;
-    __shared__ int hist[256];
+    extern __shared__ __align__(16) uint64_t skey[];  // [f]
+    __shared__ int hist[16][256];
     __shared__ uint64_t s_prefix;
     __shared__ int s_kk;
     __shared__ int tmp[17];
-
-    for (int j = tid; j < a.f; j += 1024) key[j] = topk_key(g[j], u[j], a.wdn[j]);
-    __syncthreads();
-
-    // exact radix select of the k-th largest key, most significant byte first
+    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+    const float *g = a.G + (size_t)t * a.f;
+    const float *u = a.U + (size_t)t * a.f;
+    for (int j = tid; j < a.f; j += 1024) skey[j] = topk_key(g[j], u[j], a.wdn[j]);
     uint64_t prefix = 0, pmask = 0;
     int kk = a.k;
     for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
-        if (tid < 256) hist[tid] = 0;
+        for (int i = tid; i < 16 * 256; i += 1024) (&hist[0][0])[i] = 0;
         __syncthreads();
         for (int j = tid; j < a.f; j += 1024) {
-            const uint64_t v = key[j];
-            if ((v & pmask) == prefix) atomicAdd(&hist[(int)((v >> shift) & 255)], 1);
+            const uint64_t v = skey[j];
+            if ((v & pmask) == prefix) atomicAdd(&hist[wave][(int)((v >> shift) & 255)], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            int cum = 0, D = 0;
-            for (int dd = 255; dd >= 0; --dd) {
-                const int h = hist[dd];
-                if (cum + h >= kk) { D = dd; break; }
-                cum += h;
-            }
-            s_kk = kk - cum;
-            s_prefix = prefix | ((uint64_t)D << shift);
+        // fold the wave histograms; thread i < 256 takes digit 255 - i, so an
+        // exclusive scan over threads counts the keys with a larger digit
+        int c = 0;
+        if (tid < 256)
+            for (int w = 0; w < 16; ++w) c += hist[w][255 - tid];
+        int tot;
+        const int above = block_exclusive_scan(c, tmp, &tot);
+        if (tid < 256 && above < kk && kk <= above + c) {
+            s_kk = kk - above;
+            s_prefix = prefix | ((uint64_t)(255 - tid) << shift);
         }
         __syncthreads();
         prefix = s_prefix;
         kk = s_kk;
         pmask |= (uint64_t)255 << shift;
     }
-    // every key above T is kept; of the keys equal to T the kk lowest indices
-    const uint64_t T = prefix;
+    const uint64_t T = prefix;  // kk = how many keys equal to T are kept
     const int wpt = (a.nw32 + 1023) / 1024;
-    const int w0 = tid * wpt, w1 = min(a.nw32, w0 + wpt);
+    const int w0 = min(a.nw32, tid * wpt), w1 = min(a.nw32, w0 + wpt);
     int eq = 0;
     for (int w = w0; w < w1; ++w)
         for (int b = 0; b < 32; ++b) {
             const int j = w * 32 + b;
-            if (j < a.f && key[j] == T) ++eq;
+            if (j < a.f && skey[j] == T) ++eq;
         }
     int tot;
     int rank = block_exclusive_scan(eq, tmp, &tot);
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
         for (int b = 0; b < 32; ++b) {
             const int j = w * 32 + b;
             if (j >= a.f) break;
-            const uint64_t v = key[j];
+            const uint64_t v = skey[j];
             bool on = v > T;
             if (v == T) { on = rank < kk; ++rank; }
             if (on) bitsw |= 1u << b;
@@ -649,25 +667,179 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
     }
 }
 
-// y = sum over the partials in a fixed order (+ residual)
-__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ partial, int P, int BD,
-                                                const float *__restrict__ resid, float *__restrict__ out)
+
+// ---------------------------------------------------------------------------
+// batched decode (5..16 tokens, bf16 weights): up and down on MFMA.
+// The gate GEMV stays in the fixed fp32 order (it decides the selection); the
+// up projection and the down projection only produce values, so they run on
+// v_mfma_f32_16x16x32_bf16 with their fp32 operand split into bf16 hi + lo
+// (x = hi + lo to about 2^-17 relative), two MFMAs per step, fp32 accumulate.
+//   k_split_x   x_hat [B][d] -> X_hi, X_lo [16][d] bf16 (tokens >= B are 0)
+//   k_up_mfma   one wave per gate block of 16 neurons: u for its active rows
+//               (gathered W_up rows are the A operand), h = m act(g') u ->
+//               H_hi, H_lo [16][f] (0 outside the selection)
+//   k_down_mfma one workgroup per 16 output columns: y = H W_down^T over all
+//               d_ff with h = 0 outside the union (W_down rows are read in full,
+//               the union-masked dense form), 16 waves split d_ff and are summed
+//               in a fixed order; epilogue adds the residual.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float v)
 {
-    __shared__ float red[4][64];
-    const int l = threadIdx.x & 63, qg = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + l;
-    float s = 0.0f;
-    if (col < BD)
-        for (int q = qg; q < P; q += 4) s += partial[(size_t)q * BD + col];
-    red[qg][l] = s;
-    __syncthreads();
-    if (qg == 0 && col < BD) {
-        float y = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
-        if (resid) y += resid[col];
-        out[col] = y;
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ x, int B, int d, uint16_t *__restrict__ xh,
+                                                 uint16_t *__restrict__ xl)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= 16 * d) return;
+    const int t = i / d;
+    const float v = t < B ? x[i] : 0.0f;
+    const uint16_t h = bf16_rne_bits(v);
+    xh[i] = h;
+    xl[i] = bf16_rne_bits(v - bf16_lo(h));
+}
+
+struct UpMfmaArgs {
+    const uint16_t *wu;        // [f][d] bf16
+    const uint16_t *xh, *xl;   // [16][d]
+    const float *G;            // [B][f]
+    const int *list_cnt, *list_idx;  // per gate block of 16 neurons
+    int nblk, d, f, B, mode, act, use_union;
+    float theta;
+    uint16_t *hh, *hl;         // [16][f]
+};
+
+__global__ __launch_bounds__(256) void k_up_mfma(const UpMfmaArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= a.nblk) return;
+    const int n = a.list_cnt[blk];
+    const int r = lane & 15;           // A row = neuron slot, B col = token
+    const int kq = (lane >> 4) * 8;    // k offset of this lane within a 32-step
+    const int j = r < n ? a.list_idx[blk * 16 + r] : -1;
+    const uint16_t *wrow = a.wu + (size_t)(j < 0 ? 0 : j) * a.d;
+    const uint16_t *xhr = a.xh + (size_t)r * a.d;
+    const uint16_t *xlr = a.xl + (size_t)r * a.d;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int KS = a.d / 32;
+    constexpr int U = 8;
+    for (int k0 = 0; k0 < KS; k0 += U) {
+        bf16x8_t av[U], bh[U], bl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (k0 + u) * 32 + kq;
+            const bool ok = k0 + u < KS;
+            uint4 w = (ok && j >= 0) ? *(const uint4 *)(wrow + k) : make_uint4(0, 0, 0, 0);
+            uint4 xh = ok ? *(const uint4 *)(xhr + k) : make_uint4(0, 0, 0, 0);
+            uint4 xl = ok ? *(const uint4 *)(xlr + k) : make_uint4(0, 0, 0, 0);
+            __builtin_memcpy(&av[u], &w, 16);
+            __builtin_memcpy(&bh[u], &xh, 16);
+            __builtin_memcpy(&bl[u], &xl, 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bh[u], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[u], acc, 0, 0, 0);
+        }
+    }
+    // C[neuron slot][token]: lane holds token = lane & 15, slots 4 * (lane >> 4) + e
+    const int t = lane & 15;
+    // write H rows: every neuron of the block gets a value (0 when inactive)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int slot = 4 * (lane >> 4) + e;
+        float h = 0.0f;
+        int js = -1;
+        if (slot < n) {
+            js = a.list_idx[blk * 16 + slot];
+            if (t < a.B) {
+                const float gp = a.G[(size_t)t * a.f + js];
+                const bool on = a.use_union || gate_pred(a.mode, gp, a.theta);
+                h = on ? act_f32(a.act, gp) * acc[e] : 0.0f;
+            }
+        }
+        if (js >= 0) {
+            const uint16_t hb = bf16_rne_bits(h);
+            a.hh[(size_t)t * a.f + js] = hb;
+            a.hl[(size_t)t * a.f + js] = bf16_rne_bits(h - bf16_lo(hb));
+        }
+    }
+    // neurons of the block that are not selected: h = 0
+    for (int q = lane; q < 16 * 16; q += 64) {
+        const int tt = q >> 4, rr = q & 15;
+        const int jn = blk * 16 + rr;
+        if (jn >= a.f) continue;
+        bool active = false;
+        for (int s2 = 0; s2 < n; ++s2) active |= a.list_idx[blk * 16 + s2] == jn;
+        if (!active) {
+            a.hh[(size_t)tt * a.f + jn] = 0;
+            a.hl[(size_t)tt * a.f + jn] = 0;
+        }
     }
 }
 
+struct DownMfmaArgs {
+    const uint16_t *wd;        // W_down [d][f] bf16
+    const uint16_t *hh, *hl;   // [16][f]
+    int d, f, B;
+    const float *resid;        // [B][d] or null
+    float *out;                // [B][d]
+};
+
+__global__ __launch_bounds__(1024) void k_down_mfma(const DownMfmaArgs a)
+{
+    __shared__ float red[16][16][17];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i0 = blockIdx.x * 16;
+    const int r = lane & 15, kq = (lane >> 4) * 8;
+    const int KS = a.f / 32;
+    const int per = (KS + 15) / 16;
+    const int ks0 = wave * per, ks1 = min(KS, ks0 + per);
+    const uint16_t *wrow = a.wd + (size_t)(i0 + r) * a.f;
+    const uint16_t *hhr = a.hh + (size_t)r * a.f;
+    const uint16_t *hlr = a.hl + (size_t)r * a.f;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int U = 8;
+    for (int k0 = ks0; k0 < ks1; k0 += U) {
+        bf16x8_t av[U], bh[U], bl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (k0 + u) * 32 + kq;
+            const bool ok = k0 + u < ks1;
+            uint4 w = ok ? *(const uint4 *)(wrow + k) : make_uint4(0, 0, 0, 0);
+            uint4 xh = ok ? *(const uint4 *)(hhr + k) : make_uint4(0, 0, 0, 0);
+            uint4 xl = ok ? *(const uint4 *)(hlr + k) : make_uint4(0, 0, 0, 0);
+            __builtin_memcpy(&av[u], &w, 16);
+            __builtin_memcpy(&bh[u], &xh, 16);
+            __builtin_memcpy(&bl[u], &xl, 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bh[u], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[u], acc, 0, 0, 0);
+        }
+    }
+    // C[output column i0 + row][token]: lane holds token = lane & 15, rows 4*(lane>>4)+e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][4 * (lane >> 4) + e][lane & 15] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int row = threadIdx.x >> 4, t = threadIdx.x & 15;
+        float y = 0.0f;
+        for (int w = 0; w < 16; ++w) y += red[w][row][t];
+        if (t < a.B) {
+            const size_t o = (size_t)t * a.d + i0 + row;
+            a.out[o] = a.resid ? y + a.resid[o] : y;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // batch-1 kernels.  One 1024-thread workgroup per compute unit, every weight
@@ -1106,6 +1278,37 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         return run_rowdot<WT, BT, OUT_DENSE_DOWN>(q, st);
     }
 
+    if constexpr (WT == SFFN_W_BF16 && BT >= 8) {
+        if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE) {
+            // fixed-order gate with per-block lists, then MFMA up and down
+            r.w0 = L.wg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
+            r.list_cnt = lcnt; r.list_idx = lidx;
+            if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
+            if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st)) != hipSuccess) return e;
+            if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+            const int R = gate_rows_per_block<WT, BT>();  // 16
+            const int nblk = (f + R - 1) / R;
+            if (c.idx_out || c.count_out) {
+                const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
+                hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nblk + 1) * 4, st,
+                                   (const int *)lcnt, (const int *)lidx, nblk, R, c.idx_out, c.count_out, maxs);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            if (!forward) return hipSuccess;
+            uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
+            uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
+            hipLaunchKernelGGL(k_split_x, dim3((16 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            UpMfmaArgs ua{(const uint16_t *)L.wu, xh, xl, G, lcnt, lidx, nblk, d, f, B, c.mode, D.act, c.use_union,
+                          c.theta, hh, hl};
+            hipLaunchKernelGGL(k_up_mfma, dim3((nblk + 3) / 4), dim3(256), 0, st, ua);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            DownMfmaArgs da{(const uint16_t *)L.wd, hh, hl, d, f, B, D.residual ? c.x : nullptr, c.out};
+            hipLaunchKernelGGL(k_down_mfma, dim3(d / 16), dim3(1024), 0, st, da);
+            return hipGetLastError();
+        }
+    }
+
     int nL, R;
     const int nw32 = f / 32;
     uint32_t *bits = (uint32_t *)(sc + S.bits);
@@ -1116,7 +1319,14 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st)) != hipSuccess) return e;
         if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
         TopkArgs t{G, U, L.wdn, f, c.topk_k, nw32, (uint64_t *)(sc + S.keys), bits};
-        hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), 0, st, t);
+        static bool attr_topk = false;
+        if (!attr_topk) {
+            if ((e = hipFuncSetAttribute((const void *)k_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         kMaxTopkNeurons * 8)) != hipSuccess)
+                return e;
+            attr_topk = true;
+        }
+        hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), (size_t)f * 8, st, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         nL = f / kListRowsTopk;
         R = kListRowsTopk;
@@ -1152,7 +1362,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
 
     const int BD = B * d;
-    hipLaunchKernelGGL(k_reduce, dim3((BD + 63) / 64), dim3(256), 0, st, (const float *)partial, kGatherWGs, BD,
+    hipLaunchKernelGGL(k_reduce16, dim3((BD + 15) / 16), dim3(1024), 0, st, (const float *)partial, kGatherWGs, BD,
                        D.residual ? c.x : nullptr, c.out);
     return hipGetLastError();
 }

@@ -96,23 +96,7 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     for (int i = tid; i < L; i += NT) in[i] = 0;
     if (tid == 0) s_m = L;
     __syncthreads();
-    // bitonic sort, descending
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N; i += NT) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const uint64_t x = key[i], y = key[p];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (x < y) : (x > y)) {
-                        key[i] = y;
-                        key[p] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    bitonic_sort_desc(key, N);
     // fp64 cumulative mass in blocks of kMassBlock sorted entries
     const int nb = (L + kMassBlock - 1) / kMassBlock;
     if (tid < nb) {

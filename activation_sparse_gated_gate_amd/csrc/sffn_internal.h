@@ -15,6 +15,7 @@ namespace sffn {
 constexpr int kMaxDecodeRows = 16;
 constexpr int kMaxInt4Rows = 8;
 constexpr int kMaxPrefillRows = 16384;
+constexpr int kMaxTopkNeurons = 16384;  // d_ff limit of the top-k mode (sort in LDS)
 constexpr int kGatherWGs = 256;      // partitions of the active list (partial sums)
 constexpr int kListRowsTopk = 64;    // neurons per compaction block after top-k
 constexpr int kMassBlock = 256;      // sorted scores per block of the fp64 mass prefix
@@ -74,6 +75,7 @@ PersistentLayout persistent_layout(const sffn_layer_desc &d);
 // scratch layout for one call
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
+    size_t xsplit, hsplit;                                               // decode, MFMA batches
     size_t tscore, tflag, pH;                                            // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;

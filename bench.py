@@ -1,28 +1,30 @@
-"""Benchmark of the activation-sparse gated FFN decode layer on one MI355X.
+"""Benchmarks of the activation-sparse gated FFN on one MI355X.
 
-Workload: the Llama-2-7B FFN layer shape (d_model 4096, d_ff 11008), bf16
-weights N(0, 1/d_in), batch 1, ReLU exact gating with the active fraction a
-set by the gate offset, 1024 seeded synthetic tokens resident in HBM.  A step
-is one layer forward for one token (gate GEMV with fused selection, gather of
-the active W_up / W_down^T rows, reduction).  Weight copies rotate so that the
-256 MB Infinity Cache cannot hold the working set (4 copies = 1.08 GB of
-sparse-path weights).
+Default workload (the headline): one decode FFN layer at the Llama-2-7B shape
+(d_model 4096, d_ff 11008), bf16 weights N(0, 1/d_in), batch 1, ReLU exact
+gating with the active fraction a set by the gate offset, 1024 seeded
+synthetic tokens resident in HBM.  A step is one layer forward for one token.
+Four weight copies rotate so that the 256 MB Infinity Cache cannot hold the
+working set.  Reported: microseconds per layer and effective HBM GB/s on the
+algorithmic bytes (W_gate in full, 16 KiB per active neuron, the token and
+output vectors) for a in {1.0, 0.6, 0.3, 0.1}, the dense baseline, the speed-up
+and its ideal 3 / (1 + 2a), the breakeven a (linear fit of sparse time against
+a, solved against dense), the roofline of the main kernel (HIP events around
+each of its launches) and the CPU oracle timed on the host cores.  `value` is
+the effective GB/s at a = 0.1.
 
-Reported: microseconds per layer and effective HBM GB/s on the algorithmic
-bytes (W_gate in full plus 16 KiB per active neuron plus the token and output
-vectors) for a in {1.0, 0.6, 0.3, 0.1}, the dense baseline, the speed-up, the
-breakeven a (linear fit of sparse time against a, solved against dense), the
-roofline of the main kernel (HIP events around each of its launches) and the
-CPU oracle timed on a bounded sample.  The headline `value` is the effective
-GB/s at a = 0.1.
+Other workloads (same JSON contract, one line each):
+  --workload topk      int4 Qwen2.5-3B FFN shape, weight-aware top-k, batch 1 and 8
+  --workload schedule  28 layers of 3584 / 18944 bf16 SwiGLU, batch 16, dense /
+                       a ~ 0.3 / a ~ 0.13 thresholds, RMSNorm and residual
+  --workload prefill   token-selective prefill, d_model 5120, d_ff 25600, L 16384
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -31,7 +33,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_FP32_PEAK_TFLOPS = 78.6   # non-packed fp32 FMA: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; breakeven a"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def parse():
@@ -39,6 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
+    p.add_argument("--workload", default="decode", choices=["decode", "topk", "schedule", "prefill"])
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--tokens", type=int, default=1024)
     p.add_argument("--graph-steps", type=int, default=64, help="steps captured per HIP graph")
@@ -48,37 +57,122 @@ def parse():
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# shared timing helpers
+# ---------------------------------------------------------------------------
+
+def graph_time_us(run, n_steps, graph_steps, n_graph_variants):
+    """Mean microseconds per step: run(s0, n) launches steps s0..s0+n-1; they are
+    captured into HIP graphs of graph_steps steps and replayed."""
+    import torch
+    G = graph_steps
+    n_graphs = max(1, n_steps // G)
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for gi in range(min(n_graphs, max(1, n_graph_variants))):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                run(gi * G, G)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for g in graphs[:2]:
+        g.replay()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for i in range(n_graphs):
+        graphs[i % len(graphs)].replay()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) * 1e3 / (n_graphs * G)
+
+
+def eager_time_us(run, n_steps):
+    import torch
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    run(0, n_steps)
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) * 1e3 / n_steps
+
+
+def main_kernel_us(layers, run, nk):
+    """Average duration of the library's main kernel over nk launches, from HIP
+    events recorded on the launch stream around each launch."""
+    import numpy as np
+    import torch
+    per = [[] for _ in layers]
+    ev = []
+    for s in range(nk):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()  # torch creates the HIP event on first record
+        e.record()
+        ev.append((b, e))
+        per[s % len(layers)].append((b, e))
+    torch.cuda.synchronize()
+    for i, L in enumerate(layers):
+        L.arm_kernel_timer(per[i])
+    run(0, nk)
+    torch.cuda.synchronize()
+    for L in layers:
+        L.arm_kernel_timer([])
+    return float(np.mean([b.elapsed_time(e) * 1e3 for b, e in ev]))
+
+
+def line(metric, value, unit, steps, warmup, ms_per_step, dtype, config, roofline, cpu, higher=True):
+    return {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": higher, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded)", "config": config, "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
+def dev_tensor(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def weights_dev(w):
+    out = {"w_gate": dev_tensor(w.w_gate), "w_up": dev_tensor(w.w_up), "w_down": dev_tensor(w.w_down)}
+    if w.s_gate is not None:
+        out.update(s_gate=dev_tensor(w.s_gate), s_up=dev_tensor(w.s_up), s_down=dev_tensor(w.s_down))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# decode, Llama-2-7B FFN shape, batch 1 (the headline)
+# ---------------------------------------------------------------------------
+
+def bench_decode(args):
     import numpy as np
     import torch
 
     import activation_sparse_gated_gate_amd as sf
     import synth
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     d, f = 4096, 11008
-    log = lambda *a: print(*a, file=sys.stderr, flush=True)
-
     t0 = time.time()
     w = synth.cfg2_weights(d, f)
     X = synth.cfg2_tokens(args.tokens, d)
     log("generated inputs in %.1fs" % (time.time() - t0))
-    wt = {"w_gate": torch.from_numpy(w.w_gate.view(np.int16)).to(dev),
-          "w_up": torch.from_numpy(w.w_up.view(np.int16)).to(dev),
-          "w_down": torch.from_numpy(w.w_down.view(np.int16)).to(dev)}
+    wt = weights_dev(w)
     layers = [sf.Layer(d, f, 1, sf.W_BF16, sf.ACT_RELU, wt) for _ in range(args.copies)]
     del wt
-    Xd = torch.from_numpy(X).to(dev)
+    Xd = dev_tensor(X)
     Yd = torch.empty_like(Xd)
     T = args.tokens
     xs = [Xd[i:i + 1] for i in range(T)]
     ys = [Yd[i:i + 1] for i in range(T)]
+    idx_buf = torch.empty(f, dtype=torch.int32, device="cuda:0")
     torch.cuda.synchronize()
 
     def policy(a):
@@ -86,67 +180,38 @@ def main():
             return sf.make_policy("all")
         return sf.make_policy("exact", gate_bias=synth.gate_offset_for_active_fraction(a))
 
-    def run_steps(pol, s0, n, counts=None):
-        for s in range(s0, s0 + n):
-            L = layers[s % args.copies]
-            if counts is None:
-                L.forward(pol, xs[s % T], ys[s % T])
-            else:
-                L.forward(pol, xs[s % T], ys[s % T], idx_out=idx_buf, count_out=counts[s - s0:s - s0 + 1])
+    def runner(pol, counts=None):
+        def run(s0, n):
+            for s in range(s0, s0 + n):
+                L = layers[s % len(layers)]
+                if counts is None:
+                    L.forward(pol, xs[s % T], ys[s % T])
+                else:
+                    L.forward(pol, xs[s % T], ys[s % T], idx_out=idx_buf, count_out=counts[s - s0:s - s0 + 1])
+        return run
 
-    idx_buf = torch.empty(f, dtype=torch.int32, device=dev)
-
-    def time_policy(pol, steps, warmup):
-        """Mean microseconds per layer over `steps` forwards (graph replay unless --no-graph)."""
-        run_steps(pol, 0, warmup)
+    def time_policy(pol):
+        run = runner(pol)
+        run(0, args.warmup)
         torch.cuda.synchronize()
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if args.no_graph:
-            st.record()
-            run_steps(pol, warmup, steps)
-            en.record()
-            torch.cuda.synchronize()
-            return st.elapsed_time(en) * 1e3 / steps
-        G = args.graph_steps
-        n_graphs = max(1, steps // G)
-        graphs = []
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for gi in range(min(n_graphs, max(1, T // G))):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=s):
-                    run_steps(pol, gi * G, G)
-                graphs.append(g)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        for g in graphs[:2]:
-            g.replay()
-        torch.cuda.synchronize()
-        st.record()
-        for i in range(n_graphs):
-            graphs[i % len(graphs)].replay()
-        en.record()
-        torch.cuda.synchronize()
-        return st.elapsed_time(en) * 1e3 / (n_graphs * G)
+            return eager_time_us(run, args.steps)
+        return graph_time_us(run, args.steps, args.graph_steps, T // args.graph_steps)
 
     def realized_active(pol, n):
-        cnt = torch.zeros(n, dtype=torch.int32, device=dev)
-        run_steps(pol, 0, n, counts=cnt)
+        cnt = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+        runner(pol, cnt)(0, n)
         torch.cuda.synchronize()
         return float(cnt.double().mean().item())
 
     def bytes_alg(n_active):
-        # W_gate in full + (W_up row + W_down^T row) per active neuron + index/value
-        # per active neuron + x in and y out (fp32)
+        # W_gate in full + (W_up row + W_down^T row + index/value) per active
+        # neuron + x in and y out (fp32)
         return f * d * 2 + n_active * (2 * d * 2 + 8) + 2 * d * 4
 
-    # ---- dense baseline ----
-    dense_us = time_policy(sf.make_policy("dense"), args.steps, args.warmup)
+    dense_us = time_policy(sf.make_policy("dense"))
     log("dense: %.2f us/layer (%.0f GB/s on %.1f MB)" % (dense_us, 3 * f * d * 2 / dense_us / 1e3,
                                                           3 * f * d * 2 / 1e6))
-
-    # ---- sparse sweep ----
     a_list = [1.0, 0.6, 0.3, 0.1]
     if args.sweep:
         a_list += [round(0.5 + 0.05 * i, 2) for i in range(10)]
@@ -154,61 +219,36 @@ def main():
     for a in a_list:
         pol = policy(a)
         n_act = realized_active(pol, min(T, 256))
-        us = time_policy(pol, args.steps, args.warmup)
+        us = time_policy(pol)
         B = bytes_alg(n_act)
-        rows[a] = dict(a=a, a_realized=round(n_act / f, 4), n_active=round(n_act, 1),
-                       us_per_layer=round(us, 3), bytes_alg=int(B), GBps=round(B / us / 1e3, 1),
-                       pct_peak=round(B / us / 1e3 / HBM_PEAK_GBS * 100, 1),
-                       speedup_vs_dense=round(dense_us / us, 3),
-                       ideal=round(3.0 / (1.0 + 2.0 * n_act / f), 3))
-        rows[a]["frac_of_ideal"] = round(rows[a]["speedup_vs_dense"] / rows[a]["ideal"], 3)
+        r = dict(a=a, a_realized=round(n_act / f, 4), n_active=round(n_act, 1), us_per_layer=round(us, 3),
+                 bytes_alg=int(B), GBps=round(B / us / 1e3, 1), pct_peak=round(B / us / 1e3 / HBM_PEAK_GBS * 100, 1),
+                 speedup_vs_dense=round(dense_us / us, 3), ideal=round(3.0 / (1.0 + 2.0 * n_act / f), 3))
+        r["frac_of_ideal"] = round(r["speedup_vs_dense"] / r["ideal"], 3)
+        rows[a] = r
         log("a=%.2f  n_active=%.0f  %.2f us/layer  %.0f GB/s (%.1f%% of peak)  speedup %.2fx (ideal %.2fx)"
-            % (a, n_act, us, rows[a]["GBps"], rows[a]["pct_peak"], rows[a]["speedup_vs_dense"],
-               rows[a]["ideal"]))
+            % (a, n_act, us, r["GBps"], r["pct_peak"], r["speedup_vs_dense"], r["ideal"]))
 
-    # breakeven: t(a) = t0 + c a fitted on the four headline points, solved against dense
     pts = [(rows[a]["a_realized"], rows[a]["us_per_layer"]) for a in (1.0, 0.6, 0.3, 0.1)]
-    xa = np.array([p[0] for p in pts])
-    ya = np.array([p[1] for p in pts])
-    c, t0f = np.polyfit(xa, ya, 1)
+    c, t0f = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
     breakeven = float((dense_us - t0f) / c) if c > 0 else float("inf")
 
-    # ---- roofline of the main kernel (gate GEMV + selection), a = 0.1 ----
     pol = policy(0.1)
-    run_steps(pol, 0, args.warmup)
+    run = runner(pol)
+    run(0, args.warmup)
     torch.cuda.synchronize()
-    nk = min(args.steps, 1024)
-    per_layer = [[] for _ in range(args.copies)]
-    ev = []
-    for s in range(nk):
-        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b.record()  # torch creates the HIP event on first record
-        e.record()
-        ev.append((b, e))
-        per_layer[s % args.copies].append((b, e))
-    torch.cuda.synchronize()
-    for i, L in enumerate(layers):
-        L.arm_kernel_timer(per_layer[i])
-    run_steps(pol, 0, nk)
-    torch.cuda.synchronize()
-    kus = float(np.mean([b.elapsed_time(e) * 1e3 for b, e in ev]))
-    for L in layers:
-        L.arm_kernel_timer([])
-    # the fused kernel reads W_gate in full and the W_up / W_down^T rows of the
-    # active neurons: the layer's algorithmic bytes at the realised a = 0.1
+    kus = main_kernel_us(layers, run, min(args.steps, 1024))
     k_bytes = bytes_alg(rows[0.1]["n_active"])
     achieved = k_bytes / kus / 1e3
-    log("main kernel (fused gate/selection/up/down): %.2f us avg over %d launches, %.0f GB/s"
-        % (kus, nk, achieved))
+    log("main kernel (fused gate/selection/up/down): %.2f us avg, %.0f GB/s" % (kus, achieved))
 
-    # ---- CPU oracle baseline on a bounded sample ----
     cpu = None
     if args.cpu_tokens > 0:
         import oracle
         threads = oracle.default_threads()
         b = synth.gate_offset_for_active_fraction(0.1)
-        n = args.cpu_tokens
-        oracle.decode(w, X[:1], mode="exact", bias=b, threads=threads)  # warm (page-in)
+        n = min(args.cpu_tokens, X.shape[0])
+        oracle.decode(w, X[:1], mode="exact", bias=b, threads=threads)
         t1 = time.time()
         r = oracle.decode(w, X[:n], mode="exact", bias=b, threads=threads)
         dt = time.time() - t1
@@ -216,43 +256,310 @@ def main():
         us_cpu = dt * 1e6 / n
         cpu = {"value": round(bytes_alg(n_act_cpu) / us_cpu / 1e3, 3), "unit": "GB/s",
                "us_per_layer": round(us_cpu, 1), "cores": threads, "kind": "oracle",
-               "sample": "%d tokens of the same workload at a = 0.1, one oracle call over all of them "
-                         "(OpenMP over tokens); %.1f s wall" % (n, dt)}
+               "sample": "%d tokens of the same workload at a = 0.1 in one oracle call (OpenMP over tokens), "
+                         "%.1f s wall" % (n, dt)}
         log("cpu oracle: %.0f us/layer with %d threads" % (us_cpu, threads))
 
     head = rows[0.1]
-    out = {
-        "metric": METRIC,
-        "value": head["GBps"],
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(head["us_per_layer"] / 1e3, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1/d_in) weights, N(0,1) tokens)",
-        "config": {
-            "workload": "decode gated-FFN layer, d_model 4096, d_ff 11008, bf16 weights, fp32 accumulate, "
-                        "batch 1, ReLU exact gating, a = 0.1 headline",
-            "tokens": T, "weight_copies": args.copies,
-            "timing": "HIP graph replay of %d-step captures" % args.graph_steps if not args.no_graph else "eager",
-            "dense_us_per_layer": round(dense_us, 3),
-            "sweep": [rows[a] for a in a_list],
-            "breakeven_a": round(breakeven, 3),
-            "breakeven_fit": {"t0_us": round(float(t0f), 3), "slope_us": round(float(c), 3)},
-        },
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_decode_b1<bf16,8> (gate GEMV + selection + compaction + up + down partial)",
-                     "kernel_us": round(kus, 3), "bytes_per_launch": int(k_bytes)},
-        "cpu_baseline": cpu,
-    }
+    cfg = {"workload": "decode gated-FFN layer, d_model 4096, d_ff 11008, bf16 weights, fp32 accumulate, "
+                       "batch 1, ReLU exact gating, a = 0.1 headline",
+           "tokens": T, "weight_copies": len(layers),
+           "timing": "eager" if args.no_graph else "HIP graph replay of %d-step captures" % args.graph_steps,
+           "dense_us_per_layer": round(dense_us, 3), "sweep": [rows[a] for a in a_list],
+           "breakeven_a": round(breakeven, 3),
+           "breakeven_fit": {"t0_us": round(float(t0f), 3), "slope_us": round(float(c), 3)}}
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_decode_b1<1,8> (gate GEMV + selection + compaction + up + down partial)",
+            "kernel_us": round(kus, 3), "bytes_per_launch": int(k_bytes)}
+    out = line(METRIC, head["GBps"], "GB/s", args.steps, args.warmup, round(head["us_per_layer"] / 1e3, 6),
+               "bf16", cfg, roof, cpu)
     print(json.dumps(out), flush=True)
     for L in layers:
         L.close()
+
+
+# ---------------------------------------------------------------------------
+# weight-aware top-k, int4 Qwen2.5-3B FFN shape, batch 1 and 8
+# ---------------------------------------------------------------------------
+
+def bench_topk(args):
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    d, f = 2048, 11008
+    w = synth.cfg3_weights(d, f)
+    X = synth.cfg3_tokens(args.tokens, d)
+    wt = weights_dev(w)
+    copies = 16  # 16 x 35 MB rotate past the Infinity Cache
+    layers = [sf.Layer(d, f, 8, sf.W_INT4_G128, sf.ACT_SILU, wt) for _ in range(copies)]
+    del wt
+    Xd = dev_tensor(X)
+    Yd = torch.empty_like(Xd)
+    T = args.tokens
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    idx = torch.empty(f, dtype=torch.int32, device="cuda:0")
+    steps = min(args.steps, 512)
+    gate_up_bytes = 2 * (f * d // 2 + f * (d // 128) * 2)
+
+    def bytes_alg(n_union, touched_groups):
+        # gate and up read in full (the score needs u), W_down^T rows of the
+        # union, the scale rows of touched 128-neuron groups, the column norms
+        return gate_up_bytes + n_union * (d // 2) + touched_groups * d * 2 + f * 8
+
+    rows = []
+    for B in (1, 8):
+        for pct in synth.CFG3_KEEP_PCT:
+            k = synth.topk_count(f, pct)
+            pol = sf.make_policy("topk", topk_k=k, use_union=B > 1)
+            xs = [Xd[i * B:(i + 1) * B] for i in range(T // B)]
+            ys = [Yd[i * B:(i + 1) * B] for i in range(T // B)]
+            nb = len(xs)
+
+            def run(s0, n, xs=xs, ys=ys, pol=pol, nb=nb):
+                for s in range(s0, s0 + n):
+                    layers[s % copies].forward(pol, xs[s % nb], ys[s % nb])
+            nu, tg = [], []
+            for i in range(min(nb, 32)):  # union size and touched groups (not timed)
+                layers[0].forward(pol, xs[i], ys[i], idx_out=idx, count_out=cnt)
+                torch.cuda.synchronize()
+                n = int(cnt.item())
+                sel = idx[:n].cpu().numpy()
+                nu.append(n)
+                tg.append(len(np.unique(sel // 128)))
+            run(0, args.warmup)
+            torch.cuda.synchronize()
+            us = eager_time_us(run, steps) if args.no_graph else graph_time_us(run, steps, 32, max(1, nb // 32))
+            Bb = bytes_alg(np.mean(nu), np.mean(tg))
+            r = dict(batch=B, keep_pct=pct, k=k, union=round(float(np.mean(nu)), 1),
+                     union_frac=round(float(np.mean(nu)) / f, 4), us_per_step=round(us, 3),
+                     us_per_token=round(us / B, 3), bytes_alg=int(Bb), GBps=round(Bb / us / 1e3, 1))
+            rows.append(r)
+            log("topk B=%d keep %d%%: union %.0f, %.2f us/step, %.0f GB/s" % (B, pct, r["union"], us, r["GBps"]))
+    pol = sf.make_policy("topk", topk_k=synth.topk_count(f, 17))
+    xs1 = [Xd[i:i + 1] for i in range(T)]
+
+    def run1(s0, n):
+        for s in range(s0, s0 + n):
+            layers[s % copies].forward(pol, xs1[s % T], Yd[:1])
+    run1(0, 64)
+    torch.cuda.synchronize()
+    kus = main_kernel_us(layers, run1, 256)
+    achieved = gate_up_bytes / kus / 1e3
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        threads = oracle.default_threads()
+        n = min(64, args.cpu_tokens)
+        t1 = time.time()
+        oracle.decode(w, X[:n], mode="topk", topk_k=synth.topk_count(f, 17), threads=threads)
+        dt = time.time() - t1
+        cpu = {"value": round(dt * 1e6 / n, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+               "sample": "%d tokens at batch 1, keep 17%%, one oracle call; %.1f s wall" % (n, dt)}
+    head = rows[0]
+    cfg = {"workload": "weight-aware top-k decode layer, int4-g128 fp16 scales, d_model 2048, d_ff 11008, "
+                       "SwiGLU, batch 1 and 8 (union), keep 17/30/50%", "weight_copies": copies, "results": rows}
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_rowdot<int4,1,gate_up> (gate and up in the fixed order, batch 1)",
+            "kernel_us": round(kus, 3), "bytes_per_launch": gate_up_bytes}
+    out = line("µs/step & effective HBM GB/s, weight-aware top-k", head["GBps"], "GB/s", steps, args.warmup,
+               round(head["us_per_step"] / 1e3, 6), "int4", cfg, roof, cpu)
+    print(json.dumps(out), flush=True)
+    for L in layers:
+        L.close()
+
+
+# ---------------------------------------------------------------------------
+# 28-layer schedule, batch 16
+# ---------------------------------------------------------------------------
+
+def bench_schedule(args):
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    d, f, B, NL = synth.CFG4_D, synth.CFG4_F, synth.CFG4_B, synth.CFG4_LAYERS
+    layers, pols = [], []
+    t0 = time.time()
+    for l in range(NL):
+        w = synth.cfg4_layer_weights(l, d, f)
+        wt = weights_dev(w)
+        layers.append(sf.Layer(d, f, B, sf.W_BF16, sf.ACT_SILU, wt, rmsnorm=True, residual=True))
+        del wt, w
+        mode, a = synth.cfg4_schedule(l)
+        th = synth.gate_threshold_for_active_fraction(a) if mode == "thresh" else 0.0
+        pols.append(sf.make_policy(mode, theta=th, use_union=True))
+    log("built 28 layers in %.1fs" % (time.time() - t0))
+    xs = [dev_tensor(synth.cfg4_input(B, d))] + [torch.empty(B, d, dtype=torch.float32, device="cuda:0")
+                                                for _ in range(NL)]
+
+    def step(s0, n):
+        for _ in range(n):
+            for l in range(NL):
+                layers[l].forward(pols[l], xs[l], xs[l + 1])
+    steps = min(args.steps, 64)
+    step(0, 2)
+    torch.cuda.synchronize()
+    us_step = eager_time_us(step, steps) if args.no_graph else graph_time_us(step, steps, 4, 1)
+    seg = {}
+    for name, l in (("all_0_7", 0), ("a0.3_8_19", 8), ("a0.13_20_27", 20)):
+        def one(s0, n, l=l):
+            for _ in range(n):
+                layers[l].forward(pols[l], xs[l], xs[l + 1])
+        seg[name] = round(graph_time_us(one, 64, 16, 1), 3)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    idx = torch.empty(f, dtype=torch.int32, device="cuda:0")
+    dens = []
+    for l in range(NL):
+        layers[l].forward(pols[l], xs[l], xs[l + 1], idx_out=idx, count_out=cnt)
+        torch.cuda.synchronize()
+        dens.append(int(cnt.item()) / f)
+    mat = f * d * 2
+    bytes_step = sum(mat + dn * f * 2 * d * 2 + 3 * B * d * 4 for dn in dens)
+    gbps = bytes_step / us_step / 1e3
+
+    def gl(s0, n):
+        for _ in range(n):
+            layers[8].forward(pols[8], xs[8], xs[9])
+    kus = main_kernel_us([layers[8]], gl, 64)
+    flops_gate = 2.0 * B * f * d
+    achieved = flops_gate / kus / 1e6
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        threads = oracle.default_threads()
+        w8 = synth.cfg4_layer_weights(8, d, f)
+        x8 = xs[8].cpu().numpy()
+        t1 = time.time()
+        oracle.decode(w8, x8, mode="thresh", theta=synth.gate_threshold_for_active_fraction(0.3), union=True,
+                      rmsnorm=True, residual=True, threads=threads)
+        dt = time.time() - t1
+        cpu = {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+               "sample": "one threshold layer (a ~ 0.3, batch 16), %.1f s wall" % dt}
+    cfg = {"workload": "28-layer decode schedule, d_model 3584, d_ff 18944, bf16 SwiGLU, batch 16, "
+                       "RMSNorm + residual, layers 0-7 all, 8-19 a~0.3, 20-27 a~0.13, union per step",
+           "us_per_layer_by_segment": seg, "union_density": [round(v, 4) for v in dens],
+           "bytes_per_step": int(bytes_step)}
+    roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "k_rowdot<bf16,16,gate> (fixed-order gate GEMV, 16 tokens, fp32 FMA)",
+            "kernel_us": round(kus, 3), "flops_per_launch": flops_gate}
+    out = line("µs per 28-layer step & effective HBM GB/s", round(gbps, 1), "GB/s", steps, 2,
+               round(us_step / 1e3, 4), "bf16", cfg, roof, cpu)
+    print(json.dumps(out), flush=True)
+    for L in layers:
+        L.close()
+
+
+# ---------------------------------------------------------------------------
+# token-selective prefill, d_model 5120, d_ff 25600, L 16384
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    d, f, L = synth.CFG5_D, synth.CFG5_F, synth.CFG5_L
+    w = synth.cfg5_weights(d, f)
+    Y, A = synth.cfg5_activations(L, d)
+    wt = weights_dev(w)
+    layer = sf.Layer(d, f, L, sf.W_BF16, sf.ACT_SILU, wt, layouts=sf.LAYOUT_PREFILL)
+    del wt
+    Yd, Ad = dev_tensor(Y), dev_tensor(A)
+    Xd = Yd.clone()
+    keep = torch.empty(L, dtype=torch.int32, device="cuda:0")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    fwd = sf.make_policy("tokens")
+    reps = 5
+    rows = []
+    for mass in synth.CFG5_MASS:
+        pol = sf.make_policy("tokens", mass_thresh=mass, recent_n=synth.CFG5_RECENT, min_keep=synth.CFG5_MIN_KEEP)
+        layer.select(pol, Ad, keep, cnt)
+        torch.cuda.synchronize()
+        M = int(cnt.item())
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        t_sel, t_ffn, t_oop = [], [], []
+        for _ in range(reps):
+            ev[0].record()
+            layer.select(pol, Ad, keep, cnt)
+            ev[1].record()
+            layer.forward(fwd, Xd, Xd, idx_in=keep, count_in=cnt)   # in place: t3 + t4
+            ev[2].record()
+            layer.forward(fwd, Yd, Xd, idx_in=keep, count_in=cnt)   # out of place: + copy of un-kept rows
+            ev[3].record()
+            torch.cuda.synchronize()
+            t_sel.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            t_ffn.append(ev[1].elapsed_time(ev[2]) * 1e3)
+            t_oop.append(ev[2].elapsed_time(ev[3]) * 1e3)
+        flops = 6.0 * M * d * f
+        us_ffn = float(np.median(t_ffn))
+        r = dict(mass=mass, kept=M, kept_frac=round(M / L, 4), select_us=round(float(np.median(t_sel)), 2),
+                 ffn_ms=round(us_ffn / 1e3, 4), ffn_out_of_place_ms=round(float(np.median(t_oop)) / 1e3, 4),
+                 tflops=round(flops / us_ffn / 1e6, 1),
+                 mfma_frac=round(flops / us_ffn / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
+        rows.append(r)
+        log("mass %.1f: kept %d, select %.1f us, FFN %.3f ms (%.0f TFLOP/s)"
+            % (mass, M, r["select_us"], r["ffn_ms"], r["tflops"]))
+    dense_ms = rows[-1]["ffn_ms"]
+    for r in rows:
+        r["speedup_vs_mass1"] = round(dense_ms / r["ffn_ms"], 3)
+    pol = sf.make_policy("tokens", mass_thresh=0.5, recent_n=synth.CFG5_RECENT, min_keep=1)
+    layer.select(pol, Ad, keep, cnt)
+    torch.cuda.synchronize()
+    M = int(cnt.item())
+
+    def run(s0, n):
+        for _ in range(n):
+            layer.forward(fwd, Xd, Xd, idx_in=keep, count_in=cnt)
+    kus = main_kernel_us([layer], run, 5)
+    fl = 2.0 * M * d * 2 * f
+    achieved = fl / kus / 1e6
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        threads = oracle.default_threads()
+        t1 = time.time()
+        s = oracle.token_norms(A, threads=threads)
+        k_ref, _, _ = oracle.token_select(s, 0.5, synth.CFG5_RECENT, 1)
+        t_sel = time.time() - t1
+        n = 16
+        t2 = time.time()
+        oracle.prefill_rows(w, Y, k_ref[:n], threads=threads)
+        dt = time.time() - t2
+        cpu = {"value": round((t_sel + dt / n * k_ref.size) * 1e3, 1), "unit": "ms per layer at mass 0.5",
+               "cores": threads, "kind": "oracle",
+               "sample": "selection over all %d tokens (%.2f s) + FFN on %d of the %d kept rows (%.1f s), "
+                         "scaled to all kept rows" % (L, t_sel, n, k_ref.size, dt)}
+    mid = rows[1]
+    cfg = {"workload": "token-selective prefill FFN, d_model 5120, d_ff 25600, L 16384, bf16 SwiGLU, "
+                       "top-P mass with recent_n 128, min_keep 1; value at mass 0.5", "results": rows}
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "k_gemm<gate_up> (gathered rows x interleaved W_gate/W_up, SwiGLU epilogue)",
+            "kernel_us": round(kus, 3), "flops_per_launch": fl}
+    out = line("ms per prefill FFN layer & TFLOP/s vs mass", mid["tflops"], "TFLOP/s", reps, 1, mid["ffn_ms"],
+               "bf16", cfg, roof, cpu)
+    print(json.dumps(out), flush=True)
+    layer.close()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
+     "prefill": bench_prefill}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -116,7 +116,8 @@ typedef struct sffn_layer_desc {
  *  gate_bias    b added to the gate pre-activation (fp32 add) before the
  *               activation and every predicate
  *  theta        THRESH: gate-domain threshold
- *  topk_k       TOPK: neurons kept per token, 1..d_ff
+ *  topk_k       TOPK: neurons kept per token, 1..d_ff (TOPK needs d_ff <= 16384
+ *               and act = SFFN_ACT_SILU, else SFFN_ERR_UNSUPPORTED)
  *  use_union    decode batches: 1 = every token of the call is computed over
  *               the union of the tokens' selected sets; 0 = each token over
  *               its own set (the gathered rows are still the union)
