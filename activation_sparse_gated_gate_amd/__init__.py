@@ -191,16 +191,6 @@ class Layer:
         if st != SFFN_OK:
             raise SffnError(st, "sffn_forward")
 
-    def arm_kernel_timer(self, events):
-        """events: list of (begin, end) torch.cuda.Event(enable_timing=True) pairs;
-        the next len(events) forward calls time their main kernel into them."""
-        n = len(events)
-        self._timer_arrays = ((C.c_void_p * n)(*[b.cuda_event for b, _ in events]),
-                              (C.c_void_p * n)(*[e.cuda_event for _, e in events]))
-        st = sffn_set_kernel_timer(self.handle, self._timer_arrays[0], self._timer_arrays[1], n)
-        if st != SFFN_OK:
-            raise SffnError(st, "sffn_set_kernel_timer")
-
     def close(self):
         if getattr(self, "handle", None):
             sffn_destroy(self.handle)

@@ -937,7 +937,31 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
         for (int e4 = 0; e4 < E / 4; ++e4) dst[e4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 
-    // one neuron: gate value from `cur`, then (if active) up and down rows
+    // Software pipeline per wave: while the W_up / W_down^T rows of the last
+    // active neuron are in flight, the wave computes the next gate row (whose
+    // load was issued one row earlier); the pending neuron is finished after.
+    uint4 ua[KC], da[KC];
+    int pend = -1;       // neuron whose up / down rows are in flight
+    float pend_g = 0.0f;
+    auto finish = [&]() {
+        const float u = dot_row_lds<WT, KC>(ua, xs, lane);
+        const float h = act_f32(a.act, pend_g) * u;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            float w[E];
+            unpack<WT>(da[k], w);
+            float4 *yv = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
+#pragma unroll
+            for (int e4 = 0; e4 < E / 4; ++e4) {
+                float4 v = yv[e4];
+                v.x = __builtin_fmaf(h, w[4 * e4 + 0], v.x);
+                v.y = __builtin_fmaf(h, w[4 * e4 + 1], v.y);
+                v.z = __builtin_fmaf(h, w[4 * e4 + 2], v.z);
+                v.w = __builtin_fmaf(h, w[4 * e4 + 3], v.w);
+                yv[e4] = v;
+            }
+        }
+    };
     auto neuron = [&](const uint4 (&cur)[KC], int i) {
         const float g = dot_row_lds<WT, KC>(cur, xs, lane);
         const float gp = g + a.bias;
@@ -946,27 +970,13 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
             a.G[r0 + i] = gp;
             flags[i] = on ? 1 : 0;
         }
+        if (pend >= 0) finish();
+        pend = -1;
         if (on) {
-            uint4 ua[KC], da[KC];
             load_row<WT, KC>(ua, a.wu, RBYTES, r0 + i, lane);
             load_row<WT, KC>(da, a.wdt, RBYTES, r0 + i, lane);
-            const float u = dot_row_lds<WT, KC>(ua, xs, lane);
-            const float h = act_f32(a.act, gp) * u;
-#pragma unroll
-            for (int k = 0; k < KC; ++k) {
-                float w[E];
-                unpack<WT>(da[k], w);
-                float4 *yv = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
-#pragma unroll
-                for (int e4 = 0; e4 < E / 4; ++e4) {
-                    float4 v = yv[e4];
-                    v.x = __builtin_fmaf(h, w[4 * e4 + 0], v.x);
-                    v.y = __builtin_fmaf(h, w[4 * e4 + 1], v.y);
-                    v.z = __builtin_fmaf(h, w[4 * e4 + 2], v.z);
-                    v.w = __builtin_fmaf(h, w[4 * e4 + 3], v.w);
-                    yv[e4] = v;
-                }
-            }
+            pend = i;
+            pend_g = gp;
         }
     };
     for (int i = wave; i < nr; i += 2 * NW) {
@@ -978,6 +988,7 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
         if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
         neuron(gb, i2);
     }
+    if (pend >= 0) finish();
 
     // fixed-order sum of the wave partials
     __syncthreads();
@@ -1126,12 +1137,12 @@ __global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ par
 }
 
 template <int WT>
-static hipError_t run_decode_b1(const FusedArgs &a, int KC, int P, hipStream_t st)
+static hipError_t run_decode_b1(const FusedArgs &a, int KC, int P, hipStream_t st, hipEvent_t evb, hipEvent_t eve)
 {
     switch (KC) {
 #define CASE_KC(k)                                                                                 \
     case k:                                                                                        \
-        hipLaunchKernelGGL((k_decode_b1<WT, k>), dim3(P), dim3(kFusedNT), 0, st, a);               \
+        SFFN_LAUNCH((k_decode_b1<WT, k>), dim3(P), dim3(kFusedNT), 0, st, evb, eve, a);            \
         return hipGetLastError();
         CASE_KC(1) CASE_KC(2) CASE_KC(3) CASE_KC(4) CASE_KC(5) CASE_KC(6) CASE_KC(7) CASE_KC(8)
 #undef CASE_KC
@@ -1163,14 +1174,14 @@ inline int fused_rows_per_wg(int f) { return std::min(kFusedMaxRB, std::max(1, (
 // host launchers
 // ---------------------------------------------------------------------------
 template <int WT, int BT, int OUT>
-static hipError_t run_rowdot(const RowDotArgs &a, hipStream_t st)
+static hipError_t run_rowdot(const RowDotArgs &a, hipStream_t st, hipEvent_t evb = nullptr, hipEvent_t eve = nullptr)
 {
     using C = Cfg<WT, BT>;
     constexpr bool TWO = (OUT == OUT_GATE_UP || OUT == OUT_DENSE_GU);
     constexpr int RPW = TWO ? (C::RPW > 1 ? C::RPW / 2 : 1) : C::RPW;
     const int R = C::NW * RPW;
     const int grid = (a.rows + R - 1) / R;
-    hipLaunchKernelGGL((k_rowdot<WT, BT, OUT>), dim3(grid), dim3(C::NW * 64), 0, st, a);
+    SFFN_LAUNCH((k_rowdot<WT, BT, OUT>), dim3(grid), dim3(C::NW * 64), 0, st, evb, eve, a);
     return hipGetLastError();
 }
 
@@ -1252,9 +1263,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             fa.RB = fused_rows_per_wg(f);
             fa.mode = c.mode; fa.act = D.act; fa.bias = c.bias; fa.theta = c.theta;
             const int P = (f + fa.RB - 1) / fa.RB;
-            if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
-            if ((e = run_decode_b1<WT>(fa, KC, P, st)) != hipSuccess) return e;
-            if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+            hipEvent_t evb = nullptr, eve = nullptr;
+            if (forward) L.timer->take(&evb, &eve);
+            if ((e = run_decode_b1<WT>(fa, KC, P, st, evb, eve)) != hipSuccess) return e;
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
                 hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + P + 1) * 4, st,
@@ -1283,9 +1294,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             // fixed-order gate with per-block lists, then MFMA up and down
             r.w0 = L.wg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
             r.list_cnt = lcnt; r.list_idx = lidx;
-            if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
-            if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st)) != hipSuccess) return e;
-            if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+            hipEvent_t evb = nullptr, eve = nullptr;
+            if (forward) L.timer->take(&evb, &eve);
+            if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st, evb, eve)) != hipSuccess) return e;
             const int R = gate_rows_per_block<WT, BT>();  // 16
             const int nblk = (f + R - 1) / R;
             if (c.idx_out || c.count_out) {
@@ -1315,9 +1326,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     r.w0 = L.wg; r.s0 = L.sg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
     if (c.mode == SFFN_MODE_TOPK) {
         r.w1 = L.wu; r.s1 = L.su; r.o1 = U;
-        if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
-        if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st)) != hipSuccess) return e;
-        if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+        hipEvent_t evb = nullptr, eve = nullptr;
+        if (forward) L.timer->take(&evb, &eve);
+        if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st, evb, eve)) != hipSuccess) return e;
         TopkArgs t{G, U, L.wdn, f, c.topk_k, nw32, (uint64_t *)(sc + S.keys), bits};
         static bool attr_topk = false;
         if (!attr_topk) {
@@ -1336,9 +1347,9 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     } else {
         r.list_cnt = lcnt;
         r.list_idx = lidx;
-        if (forward && (e = L.timer->before(st)) != hipSuccess) return e;
-        if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st)) != hipSuccess) return e;
-        if (forward && (e = L.timer->after(st)) != hipSuccess) return e;
+        hipEvent_t evb = nullptr, eve = nullptr;
+        if (forward) L.timer->take(&evb, &eve);
+        if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st, evb, eve)) != hipSuccess) return e;
         R = gate_rows_per_block<WT, BT>();
         nL = (f + R - 1) / R;
     }

@@ -411,10 +411,10 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     GemmArgs g{};
     g.A = c.Y; g.B = L.wgu; g.K = d; g.N = 2 * f; g.keep = c.keep; g.count = c.count; g.H = H; g.ldo = f;
     const int tiles1 = mt_max * (2 * f / GBN);
-    if ((e = L.timer->before(c.stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm<EPI_GATE_UP>, dim3(std::min(tiles1, 2048)), dim3(256), 0, c.stream, g);
+    hipEvent_t evb = nullptr, eve = nullptr;
+    L.timer->take(&evb, &eve);
+    SFFN_LAUNCH(k_gemm<EPI_GATE_UP>, dim3(std::min(tiles1, 2048)), dim3(256), 0, c.stream, evb, eve, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = L.timer->after(c.stream)) != hipSuccess) return e;
     GemmArgs g2{};
     g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
     g2.ldo = d;

@@ -1,6 +1,7 @@
 // sffn_internal.h -- shared definitions of the gfx950 library (not part of the ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -32,23 +33,35 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 // the handle
 // ---------------------------------------------------------------------------
-// optional per-launch events around the main kernel (diagnostics)
+// optional per-launch timing of the main kernel (diagnostics): the next n
+// launches of the path's main kernel take their start / stop events from this
+// list; the events are recorded by the kernel dispatch itself
+// (hipExtLaunchKernel), so they bracket the kernel and nothing else.
 struct KernelTimer {
     void *const *begin = nullptr;
     void *const *end = nullptr;
     int n = 0, next = 0;
-    hipError_t before(hipStream_t st)
+    void take(hipEvent_t *b, hipEvent_t *e)
     {
-        return next < n ? hipEventRecord((hipEvent_t)begin[next], st) : hipSuccess;
-    }
-    hipError_t after(hipStream_t st)
-    {
-        if (next >= n) return hipSuccess;
-        hipError_t e = hipEventRecord((hipEvent_t)end[next], st);
-        ++next;
-        return e;
+        if (next < n) {
+            *b = (hipEvent_t)begin[next];
+            *e = (hipEvent_t)end[next];
+            ++next;
+        } else {
+            *b = nullptr;
+            *e = nullptr;
+        }
     }
 };
+
+// launch with dispatch-recorded events when given, a plain launch otherwise
+#define SFFN_LAUNCH(kernel, grid, block, shmem, stream, evb, eve, ...)                                   \
+    do {                                                                                                \
+        if (evb)                                                                                        \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, evb, eve, 0, __VA_ARGS__);         \
+        else                                                                                            \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                        \
+    } while (0)
 
 struct Layer {
     sffn_layer_desc desc;

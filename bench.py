@@ -47,7 +47,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
-    p.add_argument("--workload", default="decode", choices=["decode", "topk", "schedule", "prefill"])
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "topk", "schedule", "prefill", "copy"])
+    p.add_argument("--a", type=float, nargs="*", default=None,
+                   help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
+    p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--tokens", type=int, default=1024)
     p.add_argument("--graph-steps", type=int, default=64, help="steps captured per HIP graph")
@@ -100,27 +104,61 @@ def eager_time_us(run, n_steps):
     return st.elapsed_time(en) * 1e3 / n_steps
 
 
-def main_kernel_us(layers, run, nk):
-    """Average duration of the library's main kernel over nk launches, from HIP
-    events recorded on the launch stream around each launch."""
+def _hip():
+    """The HIP runtime torch has loaded (same soname), for raw event handles."""
+    import ctypes as C
+    hip = C.CDLL("libamdhip64.so.7")
+    hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+    hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    hip.hipEventDestroy.argtypes = [C.c_void_p]
+    return hip
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def main_kernel_us(layers, run, nk, hold_ms=100.0):
+    """Average duration of the library's main kernel over nk launches, from the
+    start / stop events its own dispatch records (sffn_set_kernel_timer, which
+    launches it through hipExtLaunchKernel).  The events skip the system-scope
+    fence, so they bracket the kernel only.  A spin kernel of hold_ms runs
+    first so that the launches queue back to back."""
+    import ctypes as C
+
     import numpy as np
     import torch
-    per = [[] for _ in layers]
-    ev = []
-    for s in range(nk):
-        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b.record()  # torch creates the HIP event on first record
-        e.record()
-        ev.append((b, e))
-        per[s % len(layers)].append((b, e))
-    torch.cuda.synchronize()
+
+    import activation_sparse_gated_gate_amd as sf
+    hip = _hip()
+
+    def mk():
+        e = C.c_void_p()
+        if hip.hipEventCreateWithFlags(C.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e.value
+    pairs = [(mk(), mk()) for _ in range(nk)]
+    arrays = []
     for i, L in enumerate(layers):
-        L.arm_kernel_timer(per[i])
+        mine = pairs[i::len(layers)]
+        b = (C.c_void_p * len(mine))(*[p[0] for p in mine])
+        e = (C.c_void_p * len(mine))(*[p[1] for p in mine])
+        arrays.append((b, e))
+        if sf.sffn_set_kernel_timer(L.handle, b, e, len(mine)) != 0:
+            raise RuntimeError("sffn_set_kernel_timer failed")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * 1e-3 * 2.4e9))
     run(0, nk)
     torch.cuda.synchronize()
     for L in layers:
-        L.arm_kernel_timer([])
-    return float(np.mean([b.elapsed_time(e) * 1e3 for b, e in ev]))
+        sf.sffn_set_kernel_timer(L.handle, None, None, 0)
+    us = []
+    for b, e in pairs:
+        v = C.c_float()
+        hip.hipEventElapsedTime(C.byref(v), b, e)
+        us.append(v.value * 1e3)
+        hip.hipEventDestroy(b)
+        hip.hipEventDestroy(e)
+    return float(np.mean(us))
 
 
 def line(metric, value, unit, steps, warmup, ms_per_step, dtype, config, roofline, cpu, higher=True):
@@ -209,10 +247,12 @@ def bench_decode(args):
         # neuron + x in and y out (fp32)
         return f * d * 2 + n_active * (2 * d * 2 + 8) + 2 * d * 4
 
-    dense_us = time_policy(sf.make_policy("dense"))
+    dense_us = float("nan") if args.no_dense else time_policy(sf.make_policy("dense"))
     log("dense: %.2f us/layer (%.0f GB/s on %.1f MB)" % (dense_us, 3 * f * d * 2 / dense_us / 1e3,
                                                           3 * f * d * 2 / 1e6))
-    a_list = [1.0, 0.6, 0.3, 0.1]
+    a_list = list(args.a) if args.a else [1.0, 0.6, 0.3, 0.1]
+    if 0.1 not in a_list:
+        a_list.append(0.1)
     if args.sweep:
         a_list += [round(0.5 + 0.05 * i, 2) for i in range(10)]
     rows = {}
@@ -229,15 +269,19 @@ def bench_decode(args):
         log("a=%.2f  n_active=%.0f  %.2f us/layer  %.0f GB/s (%.1f%% of peak)  speedup %.2fx (ideal %.2fx)"
             % (a, n_act, us, r["GBps"], r["pct_peak"], r["speedup_vs_dense"], r["ideal"]))
 
-    pts = [(rows[a]["a_realized"], rows[a]["us_per_layer"]) for a in (1.0, 0.6, 0.3, 0.1)]
-    c, t0f = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
-    breakeven = float((dense_us - t0f) / c) if c > 0 else float("inf")
+    fit_a = [a for a in (1.0, 0.6, 0.3, 0.1) if a in rows]
+    if len(fit_a) >= 2 and dense_us == dense_us:
+        pts = [(rows[a]["a_realized"], rows[a]["us_per_layer"]) for a in fit_a]
+        c, t0f = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
+        breakeven = float((dense_us - t0f) / c) if c > 0 else float("inf")
+    else:
+        c, t0f, breakeven = float("nan"), float("nan"), float("nan")
 
     pol = policy(0.1)
     run = runner(pol)
     run(0, args.warmup)
     torch.cuda.synchronize()
-    kus = main_kernel_us(layers, run, min(args.steps, 1024))
+    kus = main_kernel_us(layers, run, min(args.steps, 512))
     k_bytes = bytes_alg(rows[0.1]["n_active"])
     achieved = k_bytes / kus / 1e3
     log("main kernel (fused gate/selection/up/down): %.2f us avg, %.0f GB/s" % (kus, achieved))
@@ -551,6 +595,32 @@ def bench_prefill(args):
     layer.close()
 
 
+# ---------------------------------------------------------------------------
+# counter calibration: a plain device-to-device copy of known size
+# ---------------------------------------------------------------------------
+
+def bench_copy(args):
+    import torch
+    n = 256 << 20  # 256 MiB per copy, 8 copies per run
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(8):
+        dst.copy_(src)
+    en.record()
+    torch.cuda.synchronize()
+    us = st.elapsed_time(en) * 1e3 / 8
+    gbps = 2 * n / us / 1e3
+    out = line("device copy GB/s (read + write), counter calibration", round(gbps, 1), "GB/s", 8, 8,
+               round(us / 1e3, 4), "f32", {"workload": "torch copy of 256 MiB, read 256 MiB + write 256 MiB per launch"},
+               None, None)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -559,7 +629,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
-     "prefill": bench_prefill}[args.workload](args)
+     "prefill": bench_prefill, "copy": bench_copy}[args.workload](args)
 
 
 if __name__ == "__main__":

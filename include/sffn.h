@@ -207,9 +207,10 @@ const char *sffn_last_hip_error(void);
 /*
  * Diagnostics for benchmarks: arm per-launch timing of the path's main kernel
  * (the decode gate/selection kernel, the prefill gate-up GEMM).  The next n
- * sffn_forward calls on this handle record begin_events[i] / end_events[i]
- * (hipEvent_t, created by the caller with timing enabled) on the call's stream
- * immediately before and after that kernel; later calls record nothing.  The
+ * sffn_forward calls on this handle launch that kernel with begin_events[i] /
+ * end_events[i] (hipEvent_t, created by the caller with timing enabled) as its
+ * dispatch start / stop events (hipExtLaunchKernel), so the pair brackets the
+ * kernel's own execution; later calls record nothing.  The
  * arrays are host memory and must stay valid until those n calls are made.
  * n = 0 disarms.  Not thread-safe: do not arm a handle used by two threads.
  */
