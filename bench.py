@@ -37,6 +37,32 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_FP32_PEAK_TFLOPS = 78.6   # non-packed fp32 FMA: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; breakeven a"
 
+# HBM bytes per dispatch of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per
+# dispatch), FETCH scaled by what the counter reads for a plain 256 MiB copy (1.9998), WRITE by 1.0.
+# Each entry is valid only for the kernel sources it was taken on (sha256 prefix over the listed
+# files); after any change the figure is reported as null until the counters are taken again.
+COUNTER_TRAFFIC = {
+    "k_decode_b1": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
+                    "sha256_16": "27a6418a9c4f561f",
+                    "workload": "a = 0.1, bf16 4096 x 11008, batch 1",
+                    "fetch_kib": 52947.49, "write_kib": 4180.68, "fetch_factor": 1.9998, "write_factor": 1.0},
+}
+
+
+def counter_traffic(name):
+    """Measured HBM bytes per dispatch for `name`, or None if its sources changed since."""
+    import hashlib
+    e = COUNTER_TRAFFIC.get(name)
+    if e is None:
+        return None
+    h = hashlib.sha256()
+    for f in e["sources"]:
+        with open(os.path.join(ROOT, "activation_sparse_gated_gate_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != e["sha256_16"]:
+        return None
+    return int(round((e["fetch_kib"] * e["fetch_factor"] + e["write_kib"] * e["write_factor"]) * 1024))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -313,7 +339,7 @@ def bench_decode(args):
            "breakeven_a": round(breakeven, 3),
            "breakeven_fit": {"t0_us": round(float(t0f), 3), "slope_us": round(float(c), 3)}}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("k_decode_b1"),
             "kernel": "k_decode_b1<1,8> (gate GEMV + selection + compaction + up + down partial)",
             "kernel_us": round(kus, 3), "bytes_per_launch": int(k_bytes)}
     out = line(METRIC, head["GBps"], "GB/s", args.steps, args.warmup, round(head["us_per_layer"] / 1e3, 6),
