@@ -23,7 +23,7 @@ SFFN_OK, SFFN_ERR_INVALID_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ER
 W_F32, W_BF16, W_INT4_G128 = 0, 1, 2
 ACT_RELU, ACT_SILU = 0, 1
 MODE_ALL, MODE_EXACT, MODE_THRESH, MODE_TOPK, MODE_TOKENS, MODE_DENSE = 0, 1, 2, 3, 4, 5
-LAYOUT_DECODE, LAYOUT_PREFILL = 1, 2
+LAYOUT_DECODE, LAYOUT_PREFILL, LAYOUT_BATCH = 1, 2, 4
 MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MODE_TOPK,
          "tokens": MODE_TOKENS, "dense": MODE_DENSE}
 

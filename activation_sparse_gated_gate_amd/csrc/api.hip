@@ -47,6 +47,9 @@ PersistentLayout persistent_layout(const sffn_layer_desc &D)
     P.sd = take(scl_d);
     P.wgu = pre ? take(2 * mat) : 0;
     P.wdp = P.wd;
+    const bool bat = dec && (D.layouts & SFFN_LAYOUT_BATCH);
+    P.wut = bat ? take(mat) : 0;
+    P.wdtl = bat ? take(mat) : 0;
     P.total = o;
     return P;
 }
@@ -94,7 +97,12 @@ static bool desc_ok(const sffn_layer_desc *D, sffn_status *why)
     if (D->wtype < SFFN_W_F32 || D->wtype > SFFN_W_INT4_G128) return false;
     if (D->act != SFFN_ACT_RELU && D->act != SFFN_ACT_SILU) return false;
     if ((D->rmsnorm != 0 && D->rmsnorm != 1) || (D->residual != 0 && D->residual != 1)) return false;
-    if (D->layouts <= 0 || (D->layouts & ~(SFFN_LAYOUT_DECODE | SFFN_LAYOUT_PREFILL))) return false;
+    if (D->layouts <= 0 || (D->layouts & ~(SFFN_LAYOUT_DECODE | SFFN_LAYOUT_PREFILL | SFFN_LAYOUT_BATCH))) return false;
+    if (D->layouts == SFFN_LAYOUT_BATCH) return false;
+    if ((D->layouts & SFFN_LAYOUT_BATCH) && (!(D->layouts & SFFN_LAYOUT_DECODE) || D->wtype != SFFN_W_BF16)) {
+        *why = SFFN_ERR_UNSUPPORTED;
+        return false;
+    }
     if (D->rmsnorm && !(D->eps >= 0.0f)) return false;
     if (D->max_rows < 1) return false;
     if (D->layouts & SFFN_LAYOUT_DECODE) {
@@ -183,6 +191,10 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
     if (desc->layouts & SFFN_LAYOUT_PREFILL) {
         L.wgu = (const uint16_t *)(base + P.wgu);
         L.wdp = (const uint16_t *)(base + P.wdp);
+    }
+    if (dec && (desc->layouts & SFFN_LAYOUT_BATCH)) {
+        L.wut = (const uint16_t *)(base + P.wut);
+        L.wdtl = (const uint16_t *)(base + P.wdtl);
     }
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_relayout(L, w_gate, w_up, w_down, s_gate, s_up, s_down, base, st);

@@ -674,14 +674,17 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
 // up projection and the down projection only produce values, so they run on
 // v_mfma_f32_16x16x32_bf16 with their fp32 operand split into bf16 hi + lo
 // (x = hi + lo to about 2^-17 relative), two MFMAs per step, fp32 accumulate.
-//   k_split_x   x_hat [B][d] -> X_hi, X_lo [16][d] bf16 (tokens >= B are 0)
-//   k_up_mfma   one wave per gate block of 16 neurons: u for its active rows
-//               (gathered W_up rows are the A operand), h = m act(g') u ->
-//               H_hi, H_lo [16][f] (0 outside the selection)
-//   k_down_mfma one workgroup per 16 output columns: y = H W_down^T over all
-//               d_ff with h = 0 outside the union (W_down rows are read in full,
-//               the union-masked dense form), 16 waves split d_ff and are summed
-//               in a fixed order; epilogue adds the residual.
+// W_up and W_down are read from copies stored as 16 x 32 operand tiles, so
+// every load of a wave is one contiguous kilobyte; the activations use the
+// same lane order ([cols/32][64 lanes][8], lane = (k-group << 4) | token).
+//   k_split_x   x_hat [B][d] -> X_hi, X_lo in lane order (tokens >= B are 0)
+//   k_up_tiled  one wave per 16 neurons (one gate block): u for the block's
+//               rows, h = act(g') u for the selected (token, neuron) pairs and
+//               0 elsewhere -> H_hi, H_lo in lane order over d_ff; blocks with
+//               no selected neuron skip the weight stream
+//   k_down_tiled one wave per (16 output columns, d_ff split): partial y of
+//               H W_down^T over its share of d_ff (H is 0 outside the selection)
+//   k_down_sum  fixed-order sum over the splits, plus the residual
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -693,55 +696,55 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v)
     return (uint16_t)(u >> 16);
 }
 
+// one thread per lane slot of 8 values: (d/32) * 64 threads
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ x, int B, int d, uint16_t *__restrict__ xh,
                                                  uint16_t *__restrict__ xl)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= 16 * d) return;
-    const int t = i / d;
-    const float v = t < B ? x[i] : 0.0f;
-    const uint16_t h = bf16_rne_bits(v);
-    xh[i] = h;
-    xl[i] = bf16_rne_bits(v - bf16_lo(h));
+    if (i >= (d / 32) * 64) return;
+    const int s = i >> 6, l = i & 63, n = l & 15;
+    const int c = s * 32 + 8 * (l >> 4);
+    uint16_t h[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = n < B ? x[(size_t)n * d + c + e] : 0.0f;
+        h[e] = bf16_rne_bits(v);
+        lo[e] = bf16_rne_bits(v - bf16_lo(h[e]));
+    }
+    uint4 ph, pl;
+    __builtin_memcpy(&ph, h, 16);
+    __builtin_memcpy(&pl, lo, 16);
+    *(uint4 *)(xh + (size_t)i * 8) = ph;
+    *(uint4 *)(xl + (size_t)i * 8) = pl;
 }
 
-struct UpMfmaArgs {
-    const uint16_t *wu;        // [f][d] bf16
-    const uint16_t *xh, *xl;   // [16][d]
-    const float *G;            // [B][f]
+struct UpTiledArgs {
+    const uint16_t *wut;             // W_up tiles [f/16][d/32][64][8]
+    const uint16_t *xh, *xl;         // [d/32][64][8]
+    const float *G;                  // [B][f]
     const int *list_cnt, *list_idx;  // per gate block of 16 neurons
-    int nblk, d, f, B, mode, act, use_union;
+    int d, f, B, mode, act, use_union;
     float theta;
-    uint16_t *hh, *hl;         // [16][f]
+    uint16_t *hh, *hl;               // [f/32][64][8]
 };
 
-__global__ __launch_bounds__(256) void k_up_mfma(const UpMfmaArgs a)
+template <int U>
+__device__ __forceinline__ f32x4_t mfma_stream(const uint16_t *__restrict__ w, const uint16_t *__restrict__ xh,
+                                               const uint16_t *__restrict__ xl, int k0, int k1, f32x4_t acc)
 {
-    const int lane = threadIdx.x & 63;
-    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= a.nblk) return;
-    const int n = a.list_cnt[blk];
-    const int r = lane & 15;           // A row = neuron slot, B col = token
-    const int kq = (lane >> 4) * 8;    // k offset of this lane within a 32-step
-    const int j = r < n ? a.list_idx[blk * 16 + r] : -1;
-    const uint16_t *wrow = a.wu + (size_t)(j < 0 ? 0 : j) * a.d;
-    const uint16_t *xhr = a.xh + (size_t)r * a.d;
-    const uint16_t *xlr = a.xl + (size_t)r * a.d;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int KS = a.d / 32;
-    constexpr int U = 8;
-    for (int k0 = 0; k0 < KS; k0 += U) {
+    // w, xh, xl already offset by lane * 8; step k is 512 elements further
+    for (int k = k0; k < k1; k += U) {
         bf16x8_t av[U], bh[U], bl[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = (k0 + u) * 32 + kq;
-            const bool ok = k0 + u < KS;
-            uint4 w = (ok && j >= 0) ? *(const uint4 *)(wrow + k) : make_uint4(0, 0, 0, 0);
-            uint4 xh = ok ? *(const uint4 *)(xhr + k) : make_uint4(0, 0, 0, 0);
-            uint4 xl = ok ? *(const uint4 *)(xlr + k) : make_uint4(0, 0, 0, 0);
-            __builtin_memcpy(&av[u], &w, 16);
-            __builtin_memcpy(&bh[u], &xh, 16);
-            __builtin_memcpy(&bl[u], &xl, 16);
+            const bool ok = k + u < k1;
+            const size_t o = (size_t)(k + u) * 512;
+            uint4 wa = ok ? *(const uint4 *)(w + o) : make_uint4(0, 0, 0, 0);
+            uint4 xa = ok ? *(const uint4 *)(xh + o) : make_uint4(0, 0, 0, 0);
+            uint4 xb = ok ? *(const uint4 *)(xl + o) : make_uint4(0, 0, 0, 0);
+            __builtin_memcpy(&av[u], &wa, 16);
+            __builtin_memcpy(&bh[u], &xa, 16);
+            __builtin_memcpy(&bl[u], &xb, 16);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -749,96 +752,71 @@ __global__ __launch_bounds__(256) void k_up_mfma(const UpMfmaArgs a)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[u], acc, 0, 0, 0);
         }
     }
-    // C[neuron slot][token]: lane holds token = lane & 15, slots 4 * (lane >> 4) + e
-    const int t = lane & 15;
-    // write H rows: every neuron of the block gets a value (0 when inactive)
+    return acc;
+}
+
+__global__ __launch_bounds__(64) void k_up_tiled(const UpTiledArgs a)
+{
+    const int t = blockIdx.x, lane = threadIdx.x;
+    const int cnt = a.list_cnt[t];
+    uint32_t m = 0;
+    for (int s2 = 0; s2 < cnt; ++s2) m |= 1u << (a.list_idx[t * 16 + s2] - t * 16);
+    const int KS = a.d / 32;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (cnt > 0)
+        acc = mfma_stream<8>(a.wut + (size_t)t * KS * 512 + lane * 8, a.xh + lane * 8, a.xl + lane * 8, 0, KS, acc);
+    // C[neuron 4q + e][token n]
+    const int n = lane & 15, q = lane >> 4;
+    uint16_t hb[4], lb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int slot = 4 * (lane >> 4) + e;
+        const int r = 4 * q + e, j = t * 16 + r;
         float h = 0.0f;
-        int js = -1;
-        if (slot < n) {
-            js = a.list_idx[blk * 16 + slot];
-            if (t < a.B) {
-                const float gp = a.G[(size_t)t * a.f + js];
-                const bool on = a.use_union || gate_pred(a.mode, gp, a.theta);
-                h = on ? act_f32(a.act, gp) * acc[e] : 0.0f;
-            }
+        if (n < a.B && ((m >> r) & 1u)) {
+            const float gp = a.G[(size_t)n * a.f + j];
+            if (a.use_union || gate_pred(a.mode, gp, a.theta)) h = act_f32(a.act, gp) * acc[e];
         }
-        if (js >= 0) {
-            const uint16_t hb = bf16_rne_bits(h);
-            a.hh[(size_t)t * a.f + js] = hb;
-            a.hl[(size_t)t * a.f + js] = bf16_rne_bits(h - bf16_lo(hb));
-        }
+        hb[e] = bf16_rne_bits(h);
+        lb[e] = bf16_rne_bits(h - bf16_lo(hb[e]));
     }
-    // neurons of the block that are not selected: h = 0
-    for (int q = lane; q < 16 * 16; q += 64) {
-        const int tt = q >> 4, rr = q & 15;
-        const int jn = blk * 16 + rr;
-        if (jn >= a.f) continue;
-        bool active = false;
-        for (int s2 = 0; s2 < n; ++s2) active |= a.list_idx[blk * 16 + s2] == jn;
-        if (!active) {
-            a.hh[(size_t)tt * a.f + jn] = 0;
-            a.hl[(size_t)tt * a.f + jn] = 0;
-        }
-    }
+    // lane order over d_ff: step t/2, k-group 2(t&1) + (q>>1), elements 4(q&1) .. +4
+    const int g = 2 * (t & 1) + (q >> 1);
+    const size_t o = ((size_t)(t >> 1) * 64 + (g << 4) + n) * 8 + 4 * (q & 1);
+    uint2 ph, pl;
+    __builtin_memcpy(&ph, hb, 8);
+    __builtin_memcpy(&pl, lb, 8);
+    *(uint2 *)(a.hh + o) = ph;
+    *(uint2 *)(a.hl + o) = pl;
 }
 
-struct DownMfmaArgs {
-    const uint16_t *wd;        // W_down [d][f] bf16
-    const uint16_t *hh, *hl;   // [16][f]
-    int d, f, B;
-    const float *resid;        // [B][d] or null
-    float *out;                // [B][d]
+struct DownTiledArgs {
+    const uint16_t *wdtl;            // W_down tiles [d/16][f/32][64][8]
+    const uint16_t *hh, *hl;         // [f/32][64][8]
+    int d, f, per;                   // per: k-steps per split (multiple of 4)
+    float *partial;                  // [splits][16][d]
 };
 
-__global__ __launch_bounds__(1024) void k_down_mfma(const DownMfmaArgs a)
+__global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
 {
-    __shared__ float red[16][16][17];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i0 = blockIdx.x * 16;
-    const int r = lane & 15, kq = (lane >> 4) * 8;
+    const int t = blockIdx.x, p = blockIdx.y, lane = threadIdx.x;
     const int KS = a.f / 32;
-    const int per = (KS + 15) / 16;
-    const int ks0 = wave * per, ks1 = min(KS, ks0 + per);
-    const uint16_t *wrow = a.wd + (size_t)(i0 + r) * a.f;
-    const uint16_t *hhr = a.hh + (size_t)r * a.f;
-    const uint16_t *hlr = a.hl + (size_t)r * a.f;
+    const int k0 = min(KS, p * a.per), k1 = min(KS, k0 + a.per);
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int U = 8;
-    for (int k0 = ks0; k0 < ks1; k0 += U) {
-        bf16x8_t av[U], bh[U], bl[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = (k0 + u) * 32 + kq;
-            const bool ok = k0 + u < ks1;
-            uint4 w = ok ? *(const uint4 *)(wrow + k) : make_uint4(0, 0, 0, 0);
-            uint4 xh = ok ? *(const uint4 *)(hhr + k) : make_uint4(0, 0, 0, 0);
-            uint4 xl = ok ? *(const uint4 *)(hlr + k) : make_uint4(0, 0, 0, 0);
-            __builtin_memcpy(&av[u], &w, 16);
-            __builtin_memcpy(&bh[u], &xh, 16);
-            __builtin_memcpy(&bl[u], &xl, 16);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bh[u], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[u], acc, 0, 0, 0);
-        }
-    }
-    // C[output column i0 + row][token]: lane holds token = lane & 15, rows 4*(lane>>4)+e
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][4 * (lane >> 4) + e][lane & 15] = acc[e];
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int row = threadIdx.x >> 4, t = threadIdx.x & 15;
-        float y = 0.0f;
-        for (int w = 0; w < 16; ++w) y += red[w][row][t];
-        if (t < a.B) {
-            const size_t o = (size_t)t * a.d + i0 + row;
-            a.out[o] = a.resid ? y + a.resid[o] : y;
-        }
-    }
+    acc = mfma_stream<8>(a.wdtl + (size_t)t * KS * 512 + lane * 8, a.hh + lane * 8, a.hl + lane * 8, k0, k1, acc);
+    // C[output column 16t + 4q + e][token n]
+    const int n = lane & 15, q = lane >> 4;
+    *(float4 *)(a.partial + ((size_t)p * 16 + n) * a.d + t * 16 + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+__global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ partial, int ns, int B, int d,
+                                                  const float *__restrict__ resid, float *__restrict__ out)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * d) return;
+    const int n = i / d, c = i - n * d;
+    float y = 0.0f;
+    for (int p = 0; p < ns; ++p) y += partial[((size_t)p * 16 + n) * d + c];
+    out[i] = resid ? y + resid[i] : y;
 }
 
 // ---------------------------------------------------------------------------
@@ -1290,14 +1268,15 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     }
 
     if constexpr (WT == SFFN_W_BF16 && BT >= 8) {
-        if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE) {
+        if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && L.wut) {
             // fixed-order gate with per-block lists, then MFMA up and down
             r.w0 = L.wg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
             r.list_cnt = lcnt; r.list_idx = lidx;
             hipEvent_t evb = nullptr, eve = nullptr;
             if (forward) L.timer->take(&evb, &eve);
             if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st, evb, eve)) != hipSuccess) return e;
-            const int R = gate_rows_per_block<WT, BT>();  // 16
+            static_assert(Cfg<WT, BT>::NW * Cfg<WT, BT>::RPW == 16, "one gate block per MFMA tile of 16 neurons");
+            const int R = gate_rows_per_block<WT, BT>();
             const int nblk = (f + R - 1) / R;
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
@@ -1308,14 +1287,22 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             if (!forward) return hipSuccess;
             uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
             uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
-            hipLaunchKernelGGL(k_split_x, dim3((16 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl);
+            hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            UpMfmaArgs ua{(const uint16_t *)L.wu, xh, xl, G, lcnt, lidx, nblk, d, f, B, c.mode, D.act, c.use_union,
-                          c.theta, hh, hl};
-            hipLaunchKernelGGL(k_up_mfma, dim3((nblk + 3) / 4), dim3(256), 0, st, ua);
+            UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl};
+            hipLaunchKernelGGL(k_up_tiled, dim3(f / 16), dim3(64), 0, st, ua);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            DownMfmaArgs da{(const uint16_t *)L.wd, hh, hl, d, f, B, D.residual ? c.x : nullptr, c.out};
-            hipLaunchKernelGGL(k_down_mfma, dim3(d / 16), dim3(1024), 0, st, da);
+            // about 1800 waves in flight: split d_ff so that (d/16) x splits fills the chip
+            const int KS = f / 32, T = d / 16;
+            const int ns0 = std::max(1, std::min(std::min(KS / 4, kMaxDownSplits), (1792 + T - 1) / T));
+            const int per = ((KS + ns0 - 1) / ns0 + 3) / 4 * 4;
+            const int ns = (KS + per - 1) / per;
+            float *partial = (float *)(sc + S.partial);
+            DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial};
+            hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_down_sum, dim3((B * d + 255) / 256), dim3(256), 0, st, (const float *)partial, ns, B,
+                               d, D.residual ? c.x : nullptr, c.out);
             return hipGetLastError();
         }
     }

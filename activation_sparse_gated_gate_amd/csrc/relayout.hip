@@ -83,6 +83,25 @@ __global__ __launch_bounds__(256) void k_interleave(const uint16_t *__restrict__
     for (int i = threadIdx.x * 8; i < d; i += 256 * 8) *(uint4 *)(o + i) = *(const uint4 *)(src + i);
 }
 
+// [R][C] bf16 row-major -> 16 x 32 MFMA operand tiles [R/16][C/32][64][8]: lane l of tile (t, s)
+// holds row 16t + (l & 15), columns 32s + 8(l >> 4) .. +8 (R % 16 == 0, C % 32 == 0).  One thread
+// per 16-byte lane slot; reads are 16 bytes of one row, writes are contiguous.
+__global__ __launch_bounds__(256) void k_tile_mfma(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
+                                                   int R, int C)
+{
+    const size_t nslot = (size_t)R * C / 8;
+    const int ks = C / 32;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nslot; i += (size_t)gridDim.x * 256) {
+        const int l = (int)(i & 63);
+        const size_t ts = i >> 6;
+        const int s = (int)(ts % ks);
+        const size_t t = ts / ks;
+        const size_t r = t * 16 + (l & 15);
+        const int c = s * 32 + 8 * (l >> 4);
+        *(uint4 *)(dst + i * 8) = *(const uint4 *)(src + r * C + c);
+    }
+}
+
 hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up, const void *w_down,
                            const void *s_gate, const void *s_up, const void *s_down, uint8_t *base,
                            hipStream_t st)
@@ -133,6 +152,14 @@ hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up,
     if ((e = hipMemcpyAsync(base + P.wd, w_down, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
     if (wt == SFFN_W_INT4_G128)
         if ((e = hipMemcpyAsync(base + P.sd, s_down, scl_d, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
+
+    if ((D.layouts & SFFN_LAYOUT_DECODE) && (D.layouts & SFFN_LAYOUT_BATCH)) {
+        hipLaunchKernelGGL(k_tile_mfma, dim3(4096), dim3(256), 0, st, (const uint16_t *)w_up,
+                           (uint16_t *)(base + P.wut), f, d);
+        hipLaunchKernelGGL(k_tile_mfma, dim3(4096), dim3(256), 0, st, (const uint16_t *)w_down,
+                           (uint16_t *)(base + P.wdtl), d, f);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         hipLaunchKernelGGL(k_interleave, dim3(2 * f), dim3(256), 0, st,

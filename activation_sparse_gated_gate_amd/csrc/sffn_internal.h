@@ -20,6 +20,7 @@ constexpr int kMaxTopkNeurons = 16384;  // d_ff limit of the top-k mode (sort in
 constexpr int kGatherWGs = 256;      // partitions of the active list (partial sums)
 constexpr int kListRowsTopk = 64;    // neurons per compaction block after top-k
 constexpr int kMassBlock = 256;      // sorted scores per block of the fp64 mass prefix
+constexpr int kMaxDownSplits = 64;     // d_ff splits of the batched MFMA down projection
 constexpr int kIlvRows = 32;         // prefill: W_gate / W_up interleave granularity
 
 // weight bytes per row of `cols` elements
@@ -76,12 +77,15 @@ struct Layer {
     // prefill layouts (bf16)
     const uint16_t *wgu = nullptr;                // [f/32][2][32][d]: gate rows then up rows
     const uint16_t *wdp = nullptr;                // W_down natural [d][f]
+    // batched-decode MFMA tiles (bf16): [rows/16][cols/32][64 lanes][8], lane = (k-group << 4) | row
+    const uint16_t *wut = nullptr;                // W_up   [f][d] as tiles
+    const uint16_t *wdtl = nullptr;               // W_down [d][f] as tiles
     KernelTimer *timer = nullptr;                 // owned by the handle
 };
 
 // persistent-buffer layout, in creation order
 struct PersistentLayout {
-    size_t wg, sg, wu, su, wdt, sdt, wd, sd, wdn, wgu, wdp, total;
+    size_t wg, sg, wu, su, wdt, sdt, wd, sd, wdn, wgu, wdp, wut, wdtl, total;
 };
 PersistentLayout persistent_layout(const sffn_layer_desc &d);
 

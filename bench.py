@@ -459,7 +459,8 @@ def bench_schedule(args):
     for l in range(NL):
         w = synth.cfg4_layer_weights(l, d, f)
         wt = weights_dev(w)
-        layers.append(sf.Layer(d, f, B, sf.W_BF16, sf.ACT_SILU, wt, rmsnorm=True, residual=True))
+        layers.append(sf.Layer(d, f, B, sf.W_BF16, sf.ACT_SILU, wt, rmsnorm=True, residual=True,
+                               layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH))
         del wt, w
         mode, a = synth.cfg4_schedule(l)
         th = synth.gate_threshold_for_active_fraction(a) if mode == "thresh" else 0.0

@@ -83,8 +83,15 @@ enum {
     SFFN_MODE_DENSE = 5
 };
 
-/* which internal layouts sffn_create builds */
-enum { SFFN_LAYOUT_DECODE = 1, SFFN_LAYOUT_PREFILL = 2 };
+/*
+ * Which internal layouts sffn_create builds.
+ *  DECODE   row-major W_gate, W_up, W_down^T and the W_down column norms (decode at every batch size)
+ *  PREFILL  interleaved W_gate / W_up rows for the token-selective prefill GEMMs
+ *  BATCH    with DECODE and bf16 weights only: W_up and W_down copied once more as 16 x 32 MFMA
+ *           operand tiles (2 * d_model * d_ff * 2 bytes more), used by decode calls of 5..16 tokens
+ *           in the ALL / EXACT / THRESH modes; without it those calls run the VALU gather path
+ */
+enum { SFFN_LAYOUT_DECODE = 1, SFFN_LAYOUT_PREFILL = 2, SFFN_LAYOUT_BATCH = 4 };
 
 /*
  * Layer descriptor.

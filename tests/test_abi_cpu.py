@@ -53,6 +53,9 @@ def test_workspace_sizes_cover_the_layouts():
     assert st == sf.SFFN_OK
     assert pb5 >= 3 * 5120 * 25600 * 2
     assert sb5 >= 16384 * 25600 * 2
+    # the MFMA tile copies of W_up and W_down for batched decode
+    st, pbb, sbb = sf.sffn_workspace_size(_desc(layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH, max_rows=16))
+    assert st == sf.SFFN_OK and pbb >= pb + 2 * mat
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,6 +63,8 @@ def test_workspace_sizes_cover_the_layouts():
     (dict(wtype=3), 1), (dict(act=2), 1), (dict(layouts=0), 1), (dict(layouts=4), 1),
     (dict(wtype=2, max_rows=16), 2), (dict(layouts=2, wtype=0, act=1), 2),
     (dict(layouts=2, act=0), 2), (dict(layouts=2, max_rows=16385, act=1), 1),
+    (dict(layouts=8), 1), (dict(layouts=5, wtype=0), 2), (dict(layouts=5, wtype=2, act=1), 2),
+    (dict(layouts=6, act=1), 2),
 ])
 def test_descriptor_validation(kw, status):
     import activation_sparse_gated_gate_amd as sf

@@ -145,24 +145,54 @@ def test_batches_thresh_and_exact(wt, B):
     x = synth.normal_f32(950 + B, (B, d))
     if wt == synth.WT_BF16:
         x = synth.round_to_bf16(x)
-    layer = make_layer(w, 16)
     th = synth.gate_threshold_for_active_fraction(0.13)
     tol = TOL[wt]
-    _check(layer, w, x, "thresh", tol, theta=th, union=True)
-    _check(layer, w, x, "thresh", tol, theta=th, union=False)
-    _check(layer, w, x, "all", tol)
     relu = synth._make_weights(wt, d, f, synth.ACT_RELU, (900 + B, 901 + B, 902 + B))
-    lr = make_layer(relu, 16)
-    _check(lr, relu, x, "exact", tol, bias=synth.gate_offset_for_active_fraction(0.3), union=False)
+    # bf16 runs twice: the VALU gather path and, with the MFMA tile layout, the batched MFMA path
+    for layouts in _layouts(wt):
+        layer = make_layer(w, 16, layouts=layouts)
+        _check(layer, w, x, "thresh", tol, theta=th, union=True)
+        _check(layer, w, x, "thresh", tol, theta=th, union=False)
+        _check(layer, w, x, "all", tol)
+        layer.close()
+        lr = make_layer(relu, 16, layouts=layouts)
+        _check(lr, relu, x, "exact", tol, bias=synth.gate_offset_for_active_fraction(0.3), union=False)
+        lr.close()
+
+
+def _layouts(wt):
+    sf = _sf()
+    if wt == synth.WT_BF16:
+        return (sf.LAYOUT_DECODE, sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+    return (sf.LAYOUT_DECODE,)
+
+
+@pytest.mark.parametrize("B", [5, 8, 16])
+def test_batched_mfma_sparse_blocks(B):
+    # very few selected neurons: most gate blocks of 16 are empty and skip their weights
+    sf = _sf()
+    d, f = 1024, 2048
+    w = synth._make_weights(synth.WT_BF16, d, f, synth.ACT_RELU, (1901, 1902, 1903))
+    x = synth.round_to_bf16(synth.normal_f32(1904 + B, (B, d)))
+    layer = make_layer(w, 16, layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+    for a in (0.002, 0.02):
+        b = synth.gate_offset_for_active_fraction(a)
+        _check(layer, w, x, "exact", 2e-3, bias=b, union=True)
+        _check(layer, w, x, "exact", 2e-3, bias=b, union=False)
+    y, idx, n = run_decode(layer, sf.make_policy("exact", gate_bias=-40.0), x)
+    assert n == 0 and np.all(y == 0.0)
+    layer.close()
 
 
 def test_rmsnorm_residual_batch16():
     w = synth._make_weights(synth.WT_BF16, 1024, 2048, synth.ACT_SILU, (961, 962, 963))
     x = synth.normal_f32(964, (16, 1024)) * np.float32(2.5)
-    layer = make_layer(w, 16, rmsnorm=True, residual=True)
     th = synth.gate_threshold_for_active_fraction(0.3)
-    _check(layer, w, x, "thresh", 2e-3, theta=th, union=True)
-    _check(layer, w, x[:7], "all", 2e-3)
+    for layouts in _layouts(synth.WT_BF16):
+        layer = make_layer(w, 16, rmsnorm=True, residual=True, layouts=layouts)
+        _check(layer, w, x, "thresh", 2e-3, theta=th, union=True)
+        _check(layer, w, x[:7], "all", 2e-3)
+        layer.close()
 
 
 def test_no_active_neuron_gives_zero_output():

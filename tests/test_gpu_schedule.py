@@ -30,7 +30,7 @@ def _run_stack(n_layers, d, f, B, seed_shift=0):
         w = synth.cfg4_layer_weights(l + seed_shift, d, f)
         mode, a = synth.cfg4_schedule(l)
         th = synth.gate_threshold_for_active_fraction(a) if mode == "thresh" else 0.0
-        layer = make_layer(w, B, rmsnorm=True, residual=True)
+        layer = make_layer(w, B, rmsnorm=True, residual=True, layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
         pol = sf.make_policy(mode, theta=th, use_union=True)
         y, idx, n = run_decode(layer, pol, x_gpu)
         ref = oracle.decode(w, x_gpu, mode=mode, theta=th, union=True, rmsnorm=True, residual=True)
