@@ -50,6 +50,8 @@ PersistentLayout persistent_layout(const sffn_layer_desc &D)
     const bool bat = dec && (D.layouts & SFFN_LAYOUT_BATCH);
     P.wut = bat ? take(mat) : 0;
     P.wdtl = bat ? take(mat) : 0;
+    // class-tiled W_gate: 4 x ceil(d / 512) x f x 256 bytes (d % 512 == 256 pads a half slice)
+    P.wgt = bat ? take((size_t)4 * ((d / 8 + 63) / 64) * f * 256) : 0;
     P.total = o;
     return P;
 }
@@ -78,6 +80,8 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         S.partial = take(std::max((size_t)kGatherWGs * B, (size_t)(f + 47) / 48 + 256) * d * 4);
         S.xsplit = take((size_t)2 * 16 * d * 2);   // x_hat as bf16 hi / lo, 16 token slots
         S.hsplit = take((size_t)2 * 16 * f * 2);   // h as bf16 hi / lo, 16 token slots
+        // four partial gate sums per (token, neuron) of the row-per-lane gate kernel
+        S.gpart = (D.layouts & SFFN_LAYOUT_BATCH) ? take((size_t)4 * B * f * 4) : 0;
     }
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         S.tscore = take(B * 4 * 2);   // scores and their sorted copy
@@ -195,6 +199,7 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
     if (dec && (desc->layouts & SFFN_LAYOUT_BATCH)) {
         L.wut = (const uint16_t *)(base + P.wut);
         L.wdtl = (const uint16_t *)(base + P.wdtl);
+        L.wgt = (const uint16_t *)(base + P.wgt);
     }
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_relayout(L, w_gate, w_up, w_down, s_gate, s_up, s_down, base, st);

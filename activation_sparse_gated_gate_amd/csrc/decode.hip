@@ -40,8 +40,10 @@ template <int WT, int BT> struct Cfg {
         WT == SFFN_W_F32 ? (BT == 1 ? 4 : BT == 4 ? 2 : 1)
         : WT == SFFN_W_BF16 ? (BT == 1 ? 8 : BT == 4 ? 2 : 1)
                             : (BT == 1 ? 2 : 1);
-    static constexpr int RPW = BT == 1 ? 4 : 2;      // rows per wave
-    static constexpr int NW = BT >= 8 ? 8 : 4;       // waves per workgroup
+    // rows per wave: each lane reuses its x values (read from LDS) over RPW rows,
+    // which keeps the LDS reads below the FMA rate at 8-16 tokens
+    static constexpr int RPW = (BT == 1 || BT >= 8) ? 4 : 2;
+    static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int CPT = (WT == SFFN_W_BF16 && BT == 1) ? 16 : (WT == SFFN_W_F32 ? 4 : 8);
     static constexpr int UNR = BT >= 8 ? 2 : 4;      // down rows in flight per thread
 };
@@ -132,13 +134,8 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotA
         const int e0 = k0 * 64 * E;
         const int ne = min(SL, a.cols - e0);
         const int n4 = ne >> 2;
-        __syncthreads();
-        for (int i = threadIdx.x; i < B * n4; i += NW * 64) {
-            const int t = i / n4, c4 = i - t * n4;
-            *(float4 *)&xs[t * SL + 4 * c4] = *(const float4 *)&a.x[(size_t)t * a.cols + e0 + 4 * c4];
-        }
-        __syncthreads();
 
+        // weight loads first: they stay in flight while x is staged
         uint4 w0v[KMAX][RPW], w1v[TWO ? KMAX : 1][TWO ? RPW : 1];
         float s0v[KMAX][RPW], s1v[TWO ? KMAX : 1][TWO ? RPW : 1];
 #pragma unroll
@@ -161,6 +158,19 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotA
                 }
             }
         }
+
+        // x slice in LDS as [token][chunk column][E/4][lane] float4s: lane l of a
+        // wave reads consecutive 16-byte words (no bank conflicts)
+        __syncthreads();
+        for (int i = threadIdx.x; i < B * n4; i += NW * 64) {
+            const int t = i / n4, c4 = i - t * n4;
+            const int q = 4 * c4, cl = q / E, e4 = (q - cl * E) >> 2;
+            const int kk = cl >> 6, ln = cl & 63;
+            *(float4 *)&xs[t * SL + ((kk * (E / 4) + e4) * 64 + ln) * 4] =
+                *(const float4 *)&a.x[(size_t)t * a.cols + e0 + q];
+        }
+        __syncthreads();
+
 #pragma unroll
         for (int kk = 0; kk < KMAX; ++kk) {
             const int c = (k0 + kk) * 64 + lane;
@@ -169,10 +179,9 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotA
                 for (int t = 0; t < BT; ++t) {
                     if (t < B) {
                         float xv[E];
-                        const float4 *xp = (const float4 *)&xs[t * SL + kk * 64 * E + lane * E];
 #pragma unroll
                         for (int e4 = 0; e4 < E / 4; ++e4) {
-                            const float4 v = xp[e4];
+                            const float4 v = *(const float4 *)&xs[t * SL + ((kk * (E / 4) + e4) * 64 + lane) * 4];
                             xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
                             xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
                         }
@@ -820,6 +829,254 @@ __global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ part
 }
 
 // ---------------------------------------------------------------------------
+// batched gate GEMV in the fixed order (5..16 tokens, bf16, BATCH layout).
+// The fixed order splits a row into 64 lane accumulators (accumulator c sums
+// chunks c, c + 64, ... with an fma chain per chunk) and adds them in a halving
+// tree that pairs c with c ^ 32, then ^ 16, ^ 8, ^ 4, ^ 2, ^ 1.  The last two
+// levels join the four classes c mod 4, so a workgroup can own one class m: it
+// stages only that quarter of x (the chunks m + 4i + 64k), its lanes are the 16
+// accumulators i of the class times 4 row groups, every lane keeps its x values
+// for RPW rows, and the class's tree levels (c ^ 32 ... c ^ 4 = lane ^ 8 ... ^ 1)
+// are shuffles inside 16 lanes.  W_gate is read from a copy laid out
+// [class][k][row][i] (16 bytes each), so four consecutive rows' 256-byte pieces
+// form one contiguous kilobyte per wave load.  k_gate_combine adds the classes
+// (0 with 2, 1 with 3, then the two) and the bias: bit for bit the fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kGateClsRPW = 4;                   // rows per lane
+constexpr int kGateClsRows = 16 * kGateClsRPW;   // rows per workgroup (4 waves x 4 groups x RPW)
+
+struct GateClsArgs {
+    const uint16_t *wgc;   // [4][K][f][16][8]
+    int d, f, B;
+    float *part;           // [4][B][f]
+};
+
+template <int BT>
+__global__ __launch_bounds__(256) void k_gate_cls(const GateClsArgs a, const float *__restrict__ x)
+{
+    constexpr int RPW = kGateClsRPW;
+    __shared__ __align__(16) float xs[2][BT][16][8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int i = lane & 15, r = lane >> 4;
+    const int m = blockIdx.y;
+    const int nch = a.d / 8, K = (nch + 63) / 64, B = a.B, f = a.f;
+    const int j0 = blockIdx.x * kGateClsRows + w * 4 * RPW + r;   // rows j0 + 4q
+    const uint16_t *wb = a.wgc + ((size_t)m * K * f + j0) * 128 + i * 8;
+    const size_t kstride = (size_t)f * 128;
+
+    // staging: 2 float4 per thread per slice; token slots >= B repeat token B - 1
+    auto stage_load = [&](int k, float4 (&v)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int item = tid + 256 * h;          // [t][i'][half]
+            const int t = item >> 5, ii = (item >> 1) & 15, half = item & 1;
+            const int ch = m + 4 * ii + 64 * k;
+            v[h] = (t < BT && ch < nch)
+                       ? *(const float4 *)(x + (size_t)min(t, B - 1) * a.d + ch * 8 + 4 * half)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    };
+    auto stage_store = [&](int buf, const float4 (&v)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int item = tid + 256 * h;
+            if ((item >> 5) < BT) *(float4 *)&xs[buf][item >> 5][(item >> 1) & 15][4 * (item & 1)] = v[h];
+        }
+    };
+    auto w_load = [&](int k, uint4 (&v)[RPW]) {
+        const bool ok = m + 4 * i + 64 * k < nch;
+#pragma unroll
+        for (int q = 0; q < RPW; ++q)
+            v[q] = ok ? *(const uint4 *)(wb + k * kstride + (size_t)q * 4 * 128) : make_uint4(0, 0, 0, 0);
+    };
+
+    float acc[RPW][BT];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int t = 0; t < BT; ++t) acc[q][t] = 0.0f;
+
+    float4 xr[2];
+    uint4 wc[RPW], wn[RPW];
+    stage_load(0, xr);
+    w_load(0, wc);
+    stage_store(0, xr);
+    __syncthreads();
+    for (int k = 0; k < K; ++k) {
+        if (k + 1 < K) {
+            stage_load(k + 1, xr);   // issued before the next weights: waiting for it
+            w_load(k + 1, wn);       // leaves those loads in flight
+        }
+        if (m + 4 * i + 64 * k < nch) {
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                const float4 x0 = *(const float4 *)&xs[k & 1][t][i][0];
+                const float4 x1 = *(const float4 *)&xs[k & 1][t][i][4];
+                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) acc[q][t] = chunk_dot<SFFN_W_BF16>(wc[q], 0.0f, xv, acc[q][t]);
+            }
+        }
+        if (k + 1 < K) {
+            stage_store((k + 1) & 1, xr);
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) wc[q] = wn[q];
+        }
+        __syncthreads();
+    }
+    // class tree: accumulators c ^ 32, ^ 16, ^ 8, ^ 4 are lanes i ^ 8, ^ 4, ^ 2, ^ 1
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            float v = acc[q][t];
+            v = v + __shfl_xor(v, 8, 64);
+            v = v + __shfl_xor(v, 4, 64);
+            v = v + __shfl_xor(v, 2, 64);
+            v = v + __shfl_xor(v, 1, 64);
+            acc[q][t] = v;
+        }
+    // lane i of each row group writes token i
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        float v = 0.0f;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) v = (t == i) ? acc[q][t] : v;
+        if (i < B) a.part[((size_t)m * B + i) * f + j0 + 4 * q] = v;
+    }
+}
+
+// Same order and work split as k_gate_cls, with a three-stage pipeline of
+// asynchronous global -> LDS copies (global_load_lds_dwordx4): each slice k
+// brings the workgroup's 64 W_gate rows (16 KB, each wave its own 16 rows) and
+// the class's x values (8 KB, shared) into stage k % 3, two slices ahead of the
+// FMAs, without holding registers for them.
+constexpr int kGateStages = 2;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their no-wait maxima)
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ void lds_copy16(const void *g, void *lds_wave_base)
+{
+    // lane l writes bytes [16 l, 16 l + 16) of the wave's 1 KB LDS block, whose
+    // (wave-uniform) LDS address goes in M0.  Issued as inline assembly so the
+    // compiler's wait insertion, which cannot tell the stages apart, does not
+    // drain every copy in flight before each LDS read; the kernel waits on the
+    // vector-memory counter itself.  Nothing else in these kernels uses M0.
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
+}
+
+template <int BT>
+__global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const float *__restrict__ x)
+{
+    constexpr int RPW = kGateClsRPW, S = kGateStages;
+    __shared__ __align__(16) uint4 wsm[S][4][4 * RPW][16];   // [stage][wave][row in wave][i]
+    __shared__ __align__(16) float xs[S][16][2][16][4];      // [stage][token][half][i][4]: conflict-free reads
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 15, r = lane >> 4;
+    const int m = blockIdx.y;
+    const int nch = a.d / 8, K = (nch + 63) / 64, B = a.B, f = a.f;
+    const int jw = blockIdx.x * kGateClsRows + w * 4 * RPW;   // first row of this wave
+    const size_t kstride = (size_t)f * 128;
+    const uint16_t *wsrc = a.wgc + ((size_t)m * K * f + jw) * 128 + lane * 8;
+
+    auto issue = [&](int k) {
+        const int st = k % S;
+        // this wave's 4 RPW rows: 4 RPW x 256 B = RPW loads of 1 KB
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) lds_copy16(wsrc + k * kstride + q * 512, &wsm[st][w][4 * q][0]);
+        // x: 8 KB = 8 loads of 1 KB, two per wave; item = [t][half][i'], t < 16
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int item = (w * 2 + h) * 64 + lane;
+            const int t = item >> 5, half = (item >> 4) & 1, ii = item & 15;
+            const int ch = min(m + 4 * ii + 64 * k, nch - 1);   // past the row: any valid chunk (never used)
+            lds_copy16(x + (size_t)min(t, B - 1) * a.d + ch * 8 + 4 * half, &xs[st][0][0][0][0] + (w * 2 + h) * 256);
+        }
+    };
+
+    float acc[RPW][BT];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int t = 0; t < BT; ++t) acc[q][t] = 0.0f;
+
+    issue(0);
+    for (int k = 0; k < K; ++k) {
+        // slice k has landed once at most the next slice's loads are outstanding
+        if (k + 1 < K) {
+            issue(k + 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(RPW + 2));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        // this wave's copies of slice k are in LDS; the barrier (no fence, so the
+        // later slices stay in flight) waits for every wave's
+        __builtin_amdgcn_s_barrier();
+        const int st = k % S;
+        if (m + 4 * i + 64 * k < nch) {
+            uint4 wv[RPW];
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) wv[q] = wsm[st][w][4 * q + r][i];
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                const float4 x0 = *(const float4 *)&xs[st][t][0][i][0];
+                const float4 x1 = *(const float4 *)&xs[st][t][1][i][0];
+                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) acc[q][t] = chunk_dot<SFFN_W_BF16>(wv[q], 0.0f, xv, acc[q][t]);
+            }
+        }
+        __builtin_amdgcn_s_barrier();   // stage st is refilled by the next iteration's issue
+    }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            float v = acc[q][t];
+            v = v + __shfl_xor(v, 8, 64);
+            v = v + __shfl_xor(v, 4, 64);
+            v = v + __shfl_xor(v, 2, 64);
+            v = v + __shfl_xor(v, 1, 64);
+            acc[q][t] = v;
+        }
+    const int j0 = jw + r;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        float v = 0.0f;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) v = (t == i) ? acc[q][t] : v;
+        if (i < B) a.part[((size_t)m * B + i) * f + j0 + 4 * q] = v;
+    }
+}
+
+// g' = ((class 0 + class 2) + (class 1 + class 3)) + b; selection flags; ascending
+// lists per block of 16 rows (ballot + mbcnt), the format of the gate kernels
+__global__ __launch_bounds__(64) void k_gate_combine(const float *__restrict__ part, int B, int f, float bias,
+                                                     int mode, float theta, float *__restrict__ G,
+                                                     int *__restrict__ list_cnt, int *__restrict__ list_idx)
+{
+    const int lane = threadIdx.x, j = blockIdx.x * 64 + lane;
+    int on = 0;
+    for (int t = 0; t < B; ++t) {
+        const size_t o = (size_t)t * f + j, cs = (size_t)B * f;
+        const float g = (part[o] + part[2 * cs + o]) + (part[cs + o] + part[3 * cs + o]);
+        const float gp = g + bias;
+        G[o] = gp;
+        on |= gate_pred(mode, gp, theta) ? 1 : 0;
+    }
+    const uint64_t m = __ballot(on);
+    const int sb = lane >> 4;
+    const uint64_t below = m & ((1ull << lane) - 1ull) & (0xFFFFull << (16 * sb));
+    if (on) list_idx[(size_t)(j >> 4) * 16 + __popcll(below)] = j;
+    if ((lane & 15) == 0) list_cnt[j >> 4] = __popcll(m & (0xFFFFull << (16 * sb)));
+}
+
+// ---------------------------------------------------------------------------
 // batch-1 kernels.  One 1024-thread workgroup per compute unit, every weight
 // row load issued before x is staged into LDS, so each workgroup keeps its whole
 // share of rows in flight at once (up to 3 rows x 8 KB per wave).
@@ -1270,13 +1527,16 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     if constexpr (WT == SFFN_W_BF16 && BT >= 8) {
         if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && L.wut) {
             // fixed-order gate with per-block lists, then MFMA up and down
-            r.w0 = L.wg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
-            r.list_cnt = lcnt; r.list_idx = lidx;
+            // class-split gate in the fixed order, lists per block of 16 rows
+            GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
             hipEvent_t evb = nullptr, eve = nullptr;
             if (forward) L.timer->take(&evb, &eve);
-            if ((e = run_rowdot<WT, BT, OUT_GATE>(r, st, evb, eve)) != hipSuccess) return e;
-            static_assert(Cfg<WT, BT>::NW * Cfg<WT, BT>::RPW == 16, "one gate block per MFMA tile of 16 neurons");
-            const int R = gate_rows_per_block<WT, BT>();
+            SFFN_LAUNCH((k_gate_pipe<BT>), dim3(f / kGateClsRows, 4), dim3(256), 0, st, evb, eve, ga, (const float *)xin);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_gate_combine, dim3(f / 64), dim3(64), 0, st, (const float *)ga.part, B, f, c.bias,
+                               c.mode, c.theta, G, lcnt, lidx);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const int R = 16;
             const int nblk = (f + R - 1) / R;
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;

@@ -102,6 +102,24 @@ __global__ __launch_bounds__(256) void k_tile_mfma(const uint16_t *__restrict__ 
     }
 }
 
+// W_gate [f][d] bf16 -> [4 classes][K][f][16][8] with K = ceil(d / 512): entry (m, k, j, i)
+// is chunk m + 4i + 64k (8 values) of row j, zero where that chunk is past the row.
+__global__ __launch_bounds__(256) void k_tile_gate_cls(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
+                                                       int f, int d)
+{
+    const int nch = d / 8, K = (nch + 63) / 64;
+    const size_t nslot = (size_t)4 * K * f * 16;
+    for (size_t s = (size_t)blockIdx.x * 256 + threadIdx.x; s < nslot; s += (size_t)gridDim.x * 256) {
+        const int i = (int)(s & 15);
+        const size_t rest = s >> 4;
+        const size_t j = rest % f;
+        const size_t mk = rest / f;
+        const int k = (int)(mk % K), m = (int)(mk / K);
+        const int ch = m + 4 * i + 64 * k;
+        *(uint4 *)(dst + s * 8) = ch < nch ? *(const uint4 *)(src + j * d + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
 hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up, const void *w_down,
                            const void *s_gate, const void *s_up, const void *s_down, uint8_t *base,
                            hipStream_t st)
@@ -158,6 +176,8 @@ hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up,
                            (uint16_t *)(base + P.wut), f, d);
         hipLaunchKernelGGL(k_tile_mfma, dim3(4096), dim3(256), 0, st, (const uint16_t *)w_down,
                            (uint16_t *)(base + P.wdtl), d, f);
+        hipLaunchKernelGGL(k_tile_gate_cls, dim3(4096), dim3(256), 0, st, (const uint16_t *)w_gate,
+                           (uint16_t *)(base + P.wgt), f, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 

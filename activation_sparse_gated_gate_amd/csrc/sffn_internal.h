@@ -80,19 +80,20 @@ struct Layer {
     // batched-decode MFMA tiles (bf16): [rows/16][cols/32][64 lanes][8], lane = (k-group << 4) | row
     const uint16_t *wut = nullptr;                // W_up   [f][d] as tiles
     const uint16_t *wdtl = nullptr;               // W_down [d][f] as tiles
+    const uint16_t *wgt = nullptr;                // W_gate [f][d] as [4][ceil(d/512)][f][16][8] (class-tiled)
     KernelTimer *timer = nullptr;                 // owned by the handle
 };
 
 // persistent-buffer layout, in creation order
 struct PersistentLayout {
-    size_t wg, sg, wu, su, wdt, sdt, wd, sd, wdn, wgu, wdp, wut, wdtl, total;
+    size_t wg, sg, wu, su, wdt, sdt, wd, sd, wdn, wgu, wdp, wut, wdtl, wgt, total;
 };
 PersistentLayout persistent_layout(const sffn_layer_desc &d);
 
 // scratch layout for one call
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
-    size_t xsplit, hsplit;                                               // decode, MFMA batches
+    size_t xsplit, hsplit, gpart;                                        // decode, batches (BATCH layout)
     size_t tscore, tflag, pH;                                            // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;

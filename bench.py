@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-VALU_FP32_PEAK_TFLOPS = 78.6   # non-packed fp32 FMA: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 157.3  # fp32 vector FMA: 256 CU x 128 lanes/clk x 2 flop x 2.4 GHz (unpacked v_fmac reaches it)
 METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; breakeven a"
 
 # HBM bytes per dispatch of a kernel from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per
@@ -499,7 +499,10 @@ def bench_schedule(args):
             layers[8].forward(pols[8], xs[8], xs[9])
     kus = main_kernel_us([layers[8]], gl, 64)
     flops_gate = 2.0 * B * f * d
-    achieved = flops_gate / kus / 1e6
+    # the gate kernel reads W_gate once (2 d f bytes), x_hat (B d fp32) and writes four class partials
+    bytes_gate = 2.0 * d * f + 4.0 * B * d + 4.0 * 4 * B * f
+    achieved = bytes_gate / kus / 1e3
+    alu_frac = flops_gate / kus / 1e6 / VALU_FP32_PEAK_TFLOPS
     cpu = None
     if args.cpu_tokens > 0:
         import oracle
@@ -516,10 +519,11 @@ def bench_schedule(args):
                        "RMSNorm + residual, layers 0-7 all, 8-19 a~0.3, 20-27 a~0.13, union per step",
            "us_per_layer_by_segment": seg, "union_density": [round(v, 4) for v in dens],
            "bytes_per_step": int(bytes_step)}
-    roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "k_rowdot<bf16,16,gate> (fixed-order gate GEMV, 16 tokens, fp32 FMA)",
-            "kernel_us": round(kus, 3), "flops_per_launch": flops_gate}
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_gate_cls<16> (fixed-order gate GEMV, 16 tokens, fp32 FMA, class-split)",
+            "kernel_us": round(kus, 3), "bytes_per_launch": int(bytes_gate), "flops_per_launch": flops_gate,
+            "alu_frac": round(alu_frac, 4)}
     out = line("µs per 28-layer step & effective HBM GB/s", round(gbps, 1), "GB/s", steps, 2,
                round(us_step / 1e3, 4), "bf16", cfg, roof, cpu)
     print(json.dumps(out), flush=True)

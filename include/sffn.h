@@ -87,9 +87,10 @@ enum {
  * Which internal layouts sffn_create builds.
  *  DECODE   row-major W_gate, W_up, W_down^T and the W_down column norms (decode at every batch size)
  *  PREFILL  interleaved W_gate / W_up rows for the token-selective prefill GEMMs
- *  BATCH    with DECODE and bf16 weights only: W_up and W_down copied once more as 16 x 32 MFMA
- *           operand tiles (2 * d_model * d_ff * 2 bytes more), used by decode calls of 5..16 tokens
- *           in the ALL / EXACT / THRESH modes; without it those calls run the VALU gather path
+ *  BATCH    with DECODE and bf16 weights only: W_gate copied once more with the rows of each block
+ *           of 64 interleaved per 8-column chunk, W_up and W_down as 16 x 32 MFMA operand tiles
+ *           (3 * d_model * d_ff * 2 bytes more); used by decode calls of 5..16 tokens in the
+ *           ALL / EXACT / THRESH modes; without it those calls run the VALU gather path
  */
 enum { SFFN_LAYOUT_DECODE = 1, SFFN_LAYOUT_PREFILL = 2, SFFN_LAYOUT_BATCH = 4 };
 

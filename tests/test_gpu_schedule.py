@@ -6,8 +6,17 @@ of its selected sets; each layer is RMSNorm -> FFN -> residual.
 
 Per layer (teacher-forced: the oracle gets the GPU's input x_l): x_hat and the
 gate values bit-exact, the selected union bit-exact, x_{l+1} within relative L2
-2e-3.  Over the whole stack: the GPU's x_28 against a free oracle rollout within
-relative L2 2e-3.
+2e-3.
+
+Over the whole stack the oracle also runs its own rollout.  The oracle map is
+not chaotic (a 1e-6 input perturbation stays near 3e-6 after 28 layers), but a
+union decision whose gate value lies within rounding of the threshold can fall
+either way once the two inputs differ in the last bits, and one extra union
+member moves y by about 1/sqrt(d_ff).  So wherever the oracle's own union
+differs from the GPU's, every differing neuron must be a near tie on the oracle
+side (max over tokens of g' within 1e-4 of the threshold); the rollout then
+continues from the GPU state.  The GPU's x_28 against the rollout: relative L2
+2e-3.
 """
 import numpy as np
 import pytest
@@ -20,12 +29,27 @@ from gpu_util import make_layer, rel_l2, run_decode, scratch_views
 pytestmark = pytest.mark.gpu
 
 
+TIE = 1e-4
+
+
+def _union_ties(free, idx, mode, th):
+    """Neurons whose union membership differs between the oracle rollout and the
+    GPU chain, with their decision margin on the oracle side."""
+    diff = np.setxor1d(free["idx"], idx)
+    if diff.size == 0:
+        return diff, np.zeros(0)
+    thr = th if mode == "thresh" else 0.0
+    gmax = free["g"][:, diff].max(axis=0)
+    return diff, np.abs(gmax - thr)
+
+
 def _run_stack(n_layers, d, f, B, seed_shift=0):
     import activation_sparse_gated_gate_amd as sf
     x_gpu = synth.cfg4_input(B, d)
     x_free = x_gpu.copy()
     worst = 0.0
     dens = []
+    flips = []
     for l in range(n_layers):
         w = synth.cfg4_layer_weights(l + seed_shift, d, f)
         mode, a = synth.cfg4_schedule(l)
@@ -43,9 +67,16 @@ def _run_stack(n_layers, d, f, B, seed_shift=0):
         worst = max(worst, err)
         dens.append(n / f)
         free = oracle.decode(w, x_free, mode=mode, theta=th, union=True, rmsnorm=True, residual=True)
-        x_free = free["y"].astype(np.float32)
+        diff, margin = _union_ties(free, idx, mode, th)
+        if diff.size:
+            assert mode != "all" and np.all(margin <= TIE), (l, diff, margin)
+            flips.append((l, int(diff.size), float(margin.max())))
+            x_free = y.copy()
+        else:
+            x_free = free["y"].astype(np.float32)
         x_gpu = y
         layer.close()
+    print("near-tie union flips against the oracle rollout (layer, neurons, max margin):", flips)
     return x_gpu, x_free, worst, dens
 
 
