@@ -101,7 +101,11 @@ struct RowDotArgs {
     int mode, act;
     float bias, theta;
     int *list_cnt, *list_idx;
+    const double *wdn;   // top-k: ||W_down[:, j]||_2
+    uint64_t *keys;      // top-k: fp64 score keys [B][rows] (null: not computed)
 };
+
+__device__ __forceinline__ uint64_t topk_key(float g, float u, double n);
 
 template <int WT, int BT, int OUT>
 __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotArgs a)
@@ -207,6 +211,19 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_rowdot(const RowDotA
         }
     }
 
+    if constexpr (OUT == OUT_GATE_UP) {
+        // top-k score keys, one (row, token) per lane (every lane holds the sums)
+        if (a.keys && lane < RPW * BT) {
+            const int r = lane / BT, t = lane - r * BT, row = rowA + r;
+            float gs = 0.0f, us = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+                for (int tt = 0; tt < BT; ++tt)
+                    if (rr == r && tt == t) { gs = ag[tt][rr]; us = au[tt][rr]; }
+            if (t < B && row < a.rows) a.keys[(size_t)t * a.rows + row] = topk_key(gs + a.bias, us, a.wdn[row]);
+        }
+    }
     if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
@@ -284,79 +301,149 @@ __device__ __forceinline__ uint64_t topk_key(float g, float u, double n)
 }
 
 struct TopkArgs {
-    const float *G, *U;
-    const double *wdn;
     int f, k, nw32;
-    uint64_t *keys;
+    const uint64_t *keys;   // [B][f] fp64 score keys (written by the gate / up kernel)
     uint32_t *bits;
 };
 
-// One workgroup per token: score every neuron (fp64 key = the bits of the
-// non-negative score, so the integer order is the value order), then an exact
-// radix select of the k-th largest key T over the keys held in LDS, one byte
-// per pass from the top, each wave counting into its own histogram.  Keep
-// every neuron above T and, of those equal to T, the lowest indices (an
-// index-order scan).
+// One workgroup per token: an exact radix select of the k-th largest score key
+// T (fp64 key = the bits of the non-negative score, so the integer order is the
+// value order), one byte per pass from the top.  Each thread keeps its keys
+// j = tid + 1024 q in registers; each group of four waves counts into its own
+// histogram (a quarter of the fold's reads).  In
+// the first pass, keys of one wave sharing a digit are counted with one atomic
+// (two ballot rounds take the most common digits first: the top bytes of fp64
+// scores are nearly all equal, and same-address LDS atomics serialize).  One wave folds the histograms, scans
+// them and picks the digit.  The select stops once every key of the chosen bin
+// is kept: the kept set is then all keys at or above the bin's floor.
+// Otherwise keep every neuron above T and, of those equal to T, the lowest
+// indices (an index-order scan).
 __global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
 {
-    extern __shared__ __align__(16) uint64_t skey[];  // [f]
-    __shared__ int hist[16][256];
+    constexpr int PER = kMaxTopkNeurons / 1024;
+    __shared__ int hist[4][256];   // one histogram per group of 4 waves
     __shared__ uint64_t s_prefix;
-    __shared__ int s_kk;
+    __shared__ int s_kk, s_all;
     __shared__ int tmp[17];
-    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-    const float *g = a.G + (size_t)t * a.f;
-    const float *u = a.U + (size_t)t * a.f;
-    for (int j = tid; j < a.f; j += 1024) skey[j] = topk_key(g[j], u[j], a.wdn[j]);
+    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t *keys = a.keys + (size_t)t * a.f;
+    uint64_t kv[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int j = tid + 1024 * q;
+        kv[q] = j < a.f ? keys[j] : 0;
+    }
+    for (int i = tid; i < 4 * 256; i += 1024) (&hist[0][0])[i] = 0;
+    __syncthreads();
     uint64_t prefix = 0, pmask = 0;
     int kk = a.k;
+    bool all_kept = false;   // every key >= prefix is kept (no tie rule needed)
     for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
-        for (int i = tid; i < 16 * 256; i += 1024) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        for (int j = tid; j < a.f; j += 1024) {
-            const uint64_t v = skey[j];
-            if ((v & pmask) == prefix) atomicAdd(&hist[wave][(int)((v >> shift) & 255)], 1);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q * 1024 >= a.f) break;   // uniform
+            const int j = tid + 1024 * q;
+            const uint64_t v = kv[q];
+            const int digit = (int)((v >> shift) & 255);
+            bool act = j < a.f && (v & pmask) == prefix;
+            if (pass == 0) {   // uniform: the top bytes of the keys are nearly all equal
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    const uint64_t am = __ballot(act);
+                    if (am == 0) break;
+                    const int leader = __builtin_ctzll(am);
+                    const int d0 = __builtin_amdgcn_readlane(digit, leader);
+                    const bool same = act && digit == d0;
+                    const uint64_t sm = __ballot(same);
+                    if (lane == leader) atomicAdd(&hist[wave & 3][d0], __popcll(sm));
+                    act = act && !same;
+                }
+            }
+            if (act) atomicAdd(&hist[wave & 3][digit], 1);
         }
         __syncthreads();
-        // fold the wave histograms; thread i < 256 takes digit 255 - i, so an
-        // exclusive scan over threads counts the keys with a larger digit
-        int c = 0;
-        if (tid < 256)
-            for (int w = 0; w < 16; ++w) c += hist[w][255 - tid];
-        int tot;
-        const int above = block_exclusive_scan(c, tmp, &tot);
-        if (tid < 256 && above < kk && kk <= above + c) {
-            s_kk = kk - above;
-            s_prefix = prefix | ((uint64_t)(255 - tid) << shift);
+        if (wave == 0) {
+            // lane l takes digits 255 - 4l ... 252 - 4l (descending); the
+            // counts are cleared for the next pass as they are read
+            int cd[4], cs = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dg = 255 - (4 * lane + e);
+                int c = 0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    c += hist[w][dg];
+                    hist[w][dg] = 0;
+                }
+                cd[e] = c;
+                cs += c;
+            }
+            int incl = cs;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += o;
+            }
+            int above = incl - cs;
+            if (above < kk && kk <= incl) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (above < kk && kk <= above + cd[e]) {
+                        s_kk = kk - above;
+                        s_all = (kk - above) == cd[e];
+                        s_prefix = prefix | ((uint64_t)(255 - (4 * lane + e)) << shift);
+                    }
+                    above += cd[e];
+                }
+            }
         }
         __syncthreads();
         prefix = s_prefix;
         kk = s_kk;
         pmask |= (uint64_t)255 << shift;
+        if (s_all) {   // uniform
+            all_kept = true;
+            break;
+        }
     }
     const uint64_t T = prefix;  // kk = how many keys equal to T are kept
-    const int wpt = (a.nw32 + 1023) / 1024;
-    const int w0 = min(a.nw32, tid * wpt), w1 = min(a.nw32, w0 + wpt);
-    int eq = 0;
-    for (int w = w0; w < w1; ++w)
-        for (int b = 0; b < 32; ++b) {
-            const int j = w * 32 + b;
-            if (j < a.f && skey[j] == T) ++eq;
+    // bit words from ballots: key j = 1024 q + 64 wave + lane sits in word
+    // 32 q + 2 wave + lane / 32 (f is a multiple of 32)
+    uint32_t *bits = a.bits + (size_t)t * a.nw32;
+    int base_rank = 0;   // ties before this round (index order), tie path only
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (q * 1024 >= a.f) break;   // uniform
+        const int j = tid + 1024 * q;
+        const uint64_t v = kv[q];
+        bool on;
+        if (all_kept) {
+            on = j < a.f && v >= T;
+        } else {
+            // rank of each tie among the ties in index order (a rare path: a
+            // bin that cannot be split by the remaining bytes holds equal keys)
+            const bool tie = j < a.f && v == T;
+            const uint64_t tm = __ballot(tie);
+            if (lane == 0) tmp[wave] = __popcll(tm);
+            __syncthreads();
+            int off = 0, tot = 0;
+            for (int w2 = 0; w2 < 16; ++w2) {
+                const int c2 = tmp[w2];
+                off += w2 < wave ? c2 : 0;
+                tot += c2;
+            }
+            const int below = __popcll(tm & ((1ull << lane) - 1ull));
+            on = j < a.f && (v > T || (tie && base_rank + off + below < kk));
+            base_rank += tot;
+            __syncthreads();
         }
-    int tot;
-    int rank = block_exclusive_scan(eq, tmp, &tot);
-    for (int w = w0; w < w1; ++w) {
-        uint32_t bitsw = 0;
-        for (int b = 0; b < 32; ++b) {
-            const int j = w * 32 + b;
-            if (j >= a.f) break;
-            const uint64_t v = skey[j];
-            bool on = v > T;
-            if (v == T) { on = rank < kk; ++rank; }
-            if (on) bitsw |= 1u << b;
+        const uint64_t m = __ballot(on);
+        const int w0 = 32 * q + 2 * wave;
+        if (q * 1024 + 64 * wave < a.f) {
+            if (lane == 0) bits[w0] = (uint32_t)m;
+            if (lane == 32) bits[w0 + 1] = (uint32_t)(m >> 32);
         }
-        a.bits[(size_t)t * a.nw32 + w] = bitsw;
     }
 }
 
@@ -851,106 +938,11 @@ struct GateClsArgs {
     float *part;           // [4][B][f]
 };
 
-template <int BT>
-__global__ __launch_bounds__(256) void k_gate_cls(const GateClsArgs a, const float *__restrict__ x)
-{
-    constexpr int RPW = kGateClsRPW;
-    __shared__ __align__(16) float xs[2][BT][16][8];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int i = lane & 15, r = lane >> 4;
-    const int m = blockIdx.y;
-    const int nch = a.d / 8, K = (nch + 63) / 64, B = a.B, f = a.f;
-    const int j0 = blockIdx.x * kGateClsRows + w * 4 * RPW + r;   // rows j0 + 4q
-    const uint16_t *wb = a.wgc + ((size_t)m * K * f + j0) * 128 + i * 8;
-    const size_t kstride = (size_t)f * 128;
-
-    // staging: 2 float4 per thread per slice; token slots >= B repeat token B - 1
-    auto stage_load = [&](int k, float4 (&v)[2]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int item = tid + 256 * h;          // [t][i'][half]
-            const int t = item >> 5, ii = (item >> 1) & 15, half = item & 1;
-            const int ch = m + 4 * ii + 64 * k;
-            v[h] = (t < BT && ch < nch)
-                       ? *(const float4 *)(x + (size_t)min(t, B - 1) * a.d + ch * 8 + 4 * half)
-                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-    };
-    auto stage_store = [&](int buf, const float4 (&v)[2]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int item = tid + 256 * h;
-            if ((item >> 5) < BT) *(float4 *)&xs[buf][item >> 5][(item >> 1) & 15][4 * (item & 1)] = v[h];
-        }
-    };
-    auto w_load = [&](int k, uint4 (&v)[RPW]) {
-        const bool ok = m + 4 * i + 64 * k < nch;
-#pragma unroll
-        for (int q = 0; q < RPW; ++q)
-            v[q] = ok ? *(const uint4 *)(wb + k * kstride + (size_t)q * 4 * 128) : make_uint4(0, 0, 0, 0);
-    };
-
-    float acc[RPW][BT];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q)
-#pragma unroll
-        for (int t = 0; t < BT; ++t) acc[q][t] = 0.0f;
-
-    float4 xr[2];
-    uint4 wc[RPW], wn[RPW];
-    stage_load(0, xr);
-    w_load(0, wc);
-    stage_store(0, xr);
-    __syncthreads();
-    for (int k = 0; k < K; ++k) {
-        if (k + 1 < K) {
-            stage_load(k + 1, xr);   // issued before the next weights: waiting for it
-            w_load(k + 1, wn);       // leaves those loads in flight
-        }
-        if (m + 4 * i + 64 * k < nch) {
-#pragma unroll
-            for (int t = 0; t < BT; ++t) {
-                const float4 x0 = *(const float4 *)&xs[k & 1][t][i][0];
-                const float4 x1 = *(const float4 *)&xs[k & 1][t][i][4];
-                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int q = 0; q < RPW; ++q) acc[q][t] = chunk_dot<SFFN_W_BF16>(wc[q], 0.0f, xv, acc[q][t]);
-            }
-        }
-        if (k + 1 < K) {
-            stage_store((k + 1) & 1, xr);
-#pragma unroll
-            for (int q = 0; q < RPW; ++q) wc[q] = wn[q];
-        }
-        __syncthreads();
-    }
-    // class tree: accumulators c ^ 32, ^ 16, ^ 8, ^ 4 are lanes i ^ 8, ^ 4, ^ 2, ^ 1
-#pragma unroll
-    for (int q = 0; q < RPW; ++q)
-#pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            float v = acc[q][t];
-            v = v + __shfl_xor(v, 8, 64);
-            v = v + __shfl_xor(v, 4, 64);
-            v = v + __shfl_xor(v, 2, 64);
-            v = v + __shfl_xor(v, 1, 64);
-            acc[q][t] = v;
-        }
-    // lane i of each row group writes token i
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-        float v = 0.0f;
-#pragma unroll
-        for (int t = 0; t < BT; ++t) v = (t == i) ? acc[q][t] : v;
-        if (i < B) a.part[((size_t)m * B + i) * f + j0 + 4 * q] = v;
-    }
-}
-
-// Same order and work split as k_gate_cls, with a three-stage pipeline of
-// asynchronous global -> LDS copies (global_load_lds_dwordx4): each slice k
-// brings the workgroup's 64 W_gate rows (16 KB, each wave its own 16 rows) and
-// the class's x values (8 KB, shared) into stage k % 3, two slices ahead of the
-// FMAs, without holding registers for them.
+// The class-split gate runs as a two-stage pipeline of asynchronous global ->
+// LDS copies (global_load_lds_dwordx4): each slice k brings the workgroup's 64
+// W_gate rows (16 KB, each wave its own 16 rows) and the class's x values
+// (8 KB, shared) into stage k % 2, one slice ahead of the FMAs, without holding
+// registers for them.
 constexpr int kGateStages = 2;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -1234,7 +1226,9 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
             const float4 v = ((const float4 *)(ysum + (size_t)w * D))[c];
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
-        ((float4 *)(a.partial + (size_t)blockIdx.x * D))[c] = acc;
+        // blocked layout [D / 16][P][16]: the reduce reads each 16-column block contiguously
+        const int col = 4 * c;
+        *(float4 *)(a.partial + ((size_t)(col >> 4) * gridDim.x + blockIdx.x) * 16 + (col & 15)) = acc;
     }
     // ascending list of this workgroup's active neurons (ballot + mbcnt)
     if (wave == 0) {
@@ -1368,6 +1362,38 @@ __global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ par
         for (int g = 0; g < 16; ++g) y += red2[g][l];
         if (resid) y += resid[col];
         out[col] = y;
+    }
+}
+
+// y = sum of the fused kernel's P partials (+ residual) from the blocked layout
+// [d/16][P][16]: one workgroup per 16 columns reads its 16 P floats as one
+// contiguous block; thread (column c, group g) adds partials g, g + 16, ... in
+// order, then the 16 groups are added in order through LDS.
+__global__ __launch_bounds__(256) void k_reduce_blk(const float *__restrict__ partial, int P, int d,
+                                                    const float *__restrict__ resid, float *__restrict__ out)
+{
+    __shared__ float red[16][17];
+    const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const float *base = partial + (size_t)blockIdx.x * P * 16 + c;
+    float s = 0.0f;
+    for (int p0 = g; p0 < P; p0 += 16 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = p0 + 16 * u;
+            v[u] = p < P ? base[(size_t)p * 16] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    red[g][c] = s;
+    __syncthreads();
+    if (g == 0) {
+        float y = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) y += red[q][c];
+        const int col = blockIdx.x * 16 + c;
+        out[col] = resid ? y + resid[col] : y;
     }
 }
 
@@ -1508,7 +1534,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (!forward) return hipSuccess;
-            hipLaunchKernelGGL(k_reduce16, dim3((d + 15) / 16), dim3(1024), 0, st, (const float *)(sc + S.partial), P, d,
+            hipLaunchKernelGGL(k_reduce_blk, dim3(d / 16), dim3(256), 0, st, (const float *)(sc + S.partial), P, d,
                                D.residual ? c.x : nullptr, c.out);
             return hipGetLastError();
         }
@@ -1573,18 +1599,13 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     r.w0 = L.wg; r.s0 = L.sg; r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
     if (c.mode == SFFN_MODE_TOPK) {
         r.w1 = L.wu; r.s1 = L.su; r.o1 = U;
+        r.wdn = L.wdn;
+        r.keys = (uint64_t *)(sc + S.keys);
         hipEvent_t evb = nullptr, eve = nullptr;
         if (forward) L.timer->take(&evb, &eve);
         if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st, evb, eve)) != hipSuccess) return e;
-        TopkArgs t{G, U, L.wdn, f, c.topk_k, nw32, (uint64_t *)(sc + S.keys), bits};
-        static bool attr_topk = false;
-        if (!attr_topk) {
-            if ((e = hipFuncSetAttribute((const void *)k_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         kMaxTopkNeurons * 8)) != hipSuccess)
-                return e;
-            attr_topk = true;
-        }
-        hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), (size_t)f * 8, st, t);
+        TopkArgs t{f, c.topk_k, nw32, (const uint64_t *)(sc + S.keys), bits};
+        hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), 0, st, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         nL = f / kListRowsTopk;
         R = kListRowsTopk;

@@ -521,7 +521,7 @@ def bench_schedule(args):
            "bytes_per_step": int(bytes_step)}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_gate_cls<16> (fixed-order gate GEMV, 16 tokens, fp32 FMA, class-split)",
+            "kernel": "k_gate_pipe<16> (fixed-order gate GEMV, 16 tokens, fp32 FMA, class-split, LDS-staged)",
             "kernel_us": round(kus, 3), "bytes_per_launch": int(bytes_gate), "flops_per_launch": flops_gate,
             "alu_frac": round(alu_frac, 4)}
     out = line("µs per 28-layer step & effective HBM GB/s", round(gbps, 1), "GB/s", steps, 2,
