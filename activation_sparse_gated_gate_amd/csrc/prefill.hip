@@ -204,7 +204,19 @@ struct GemmArgs {
     const uint16_t *Y;      // DOWN: residual rows
     uint16_t *X;            // DOWN: output rows (scatter)
     int ldo;                // row length of H (GATE_UP) or X/Y (DOWN)
+    int gate;               // 0: always run; else run only if (256 x 256 tiles >= gate) == (gate_big != 0)
+    int gate_big;
 };
+
+// The device-side row count decides between the two tile sizes without a host
+// round trip: with too few 256 x 256 tiles for the compute units, 128 x 128
+// tiles keep every unit busy.
+__device__ __forceinline__ bool gemm_gate_open(const GemmArgs &a, int M)
+{
+    if (a.gate == 0) return true;
+    const int big = ((M + 255) / 256) * (a.N / 256);
+    return (big >= a.gate) == (a.gate_big != 0);
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 {
@@ -221,6 +233,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
     __shared__ int rowsrc[GBM];
 
     const int M = *a.count;
+    if (!gemm_gate_open(a, M)) return;
     const int mt = (M + GBM - 1) / GBM;
     const int nt = a.N / GBN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -337,6 +350,176 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile variant: 256 x 256 tiles, four waves of 128 x 128 (4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, 16 MFMAs per 8 KB of LDS operand reads), both
+// operands copied global -> LDS asynchronously (global_load_lds_dwordx4) in
+// slices of 32 along k, four stages deep (three slices in flight while one is
+// consumed).  A copy writes one contiguous kilobyte (sixteen 64-byte rows of 32
+// bf16), so the LDS layout is chosen through the source addresses: the 16-byte
+// chunk c of row r sits at position c ^ ((r >> 2) & 3), which spreads the rows
+// that one MFMA operand read touches over all banks.
+// ---------------------------------------------------------------------------
+constexpr int BBM = 256, BBN = 256, BBK = 32, BSTAGES = 4;
+
+__device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base)
+{
+    // lane l writes bytes [16 l, 16 l + 16) of the 1 KB LDS block whose
+    // (wave-uniform) address goes in M0; inline assembly keeps the compiler's
+    // wait insertion from draining every copy in flight before each LDS read
+    // (the kernel waits on the vector-memory counter itself).  Nothing else in
+    // this kernel uses M0.
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
+}
+
+constexpr int gemm_waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
+{
+    __shared__ __align__(1024) uint16_t As[BSTAGES][BBM * BBK];
+    __shared__ __align__(1024) uint16_t Bs[BSTAGES][BBN * BBK];
+    __shared__ int rowsrc[BBM];
+
+    const int M = *a.count;
+    if (!gemm_gate_open(a, M)) return;
+    const int mt = (M + BBM - 1) / BBM;
+    const int nt = a.N / BBN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int KT = a.K / BBK;
+    // per wave and stage: 4 copies of A rows and 4 of B rows
+    constexpr int CPS = 8;
+
+    // Workgroups are dealt to the 8 XCDs round-robin; renumbering them so that
+    // each XCD walks a contiguous run of tiles (M-tiles fastest) keeps the
+    // workgroups that share a weight tile on the same L2.
+    const int G = gridDim.x;
+    const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    for (int tile = v; tile < mt * nt; tile += G) {
+        const int tm = tile % mt, tn = tile / mt;
+        const int m0 = tm * BBM, n0 = tn * BBN;
+        __syncthreads();
+        {
+            // rows past M read a valid row; their results are not written
+            const int m = min(m0 + tid, M - 1);
+            rowsrc[tid] = EPI == EPI_GATE_UP ? a.keep[m] : m;
+        }
+        __syncthreads();
+        // this wave copies rows 64 w + 16 q + (lane >> 2), q = 0..3, of both
+        // operands; lane position p = lane & 3 holds logical chunk p ^ ((r >> 2) & 3)
+        uint32_t aoff[4];   // element offsets of the gathered A rows (< 2^31 for every supported shape)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 64 * w + 16 * q + (lane >> 2);
+            aoff[q] = (uint32_t)rowsrc[r] * (uint32_t)a.K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
+        }
+        // (r >> 2) & 3 does not depend on q (16 q only changes higher bits)
+        const int rb0 = 64 * w + (lane >> 2);
+        const uint16_t *bsrc = a.B + (size_t)(n0 + rb0) * a.K + (((lane & 3) ^ ((rb0 >> 2) & 3)) * 8);
+        auto issue = [&](int kt) {
+            const int st = kt % BSTAGES;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(64 * w + 16 * q) * BBK]);
+                lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(64 * w + 16 * q) * BBK]);
+            }
+        };
+
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+        for (int p = 0; p < BSTAGES - 1; ++p)
+            if (p < KT) issue(p);
+        for (int kt = 0; kt < KT; ++kt) {
+            // slice kt has landed once only the later slices' copies are outstanding
+            const int later = min(KT - 1 - kt, BSTAGES - 2);
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(2 * CPS));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(CPS));
+            else __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(0));
+            // every wave's copies of slice kt are in LDS, and every wave has finished
+            // slice kt - 1, whose stage the next copies refill
+            __builtin_amdgcn_s_barrier();
+            if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
+            const uint16_t *as = As[kt % BSTAGES], *bs = Bs[kt % BSTAGES];
+#pragma unroll
+            for (int ks = 0; ks < BBK / 16; ++ks) {
+                const int kc = 2 * ks + (lane >> 5);
+                bf16x8 fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * 128 + i * 32 + (lane & 31);
+                    fa[i] = *(const bf16x8 *)&as[r * BBK + ((kc ^ ((r >> 2) & 3)) * 8)];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = wn * 128 + j * 32 + (lane & 31);
+                    fb[j] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_barrier();   // the next tile's first copies reuse the stages
+
+        // epilogue: lane holds col = lane & 31 and rows 8 g + 4 (lane >> 5) + e of a 32 x 32 block
+        const int ccol = lane & 31;
+        if constexpr (EPI == EPI_GATE_UP) {
+            // wave columns: [gate | up] of neurons nb .. nb + 31, then of nb + 32 .. nb + 63
+            const int nb = (n0 + wn * 128) / 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    __builtin_amdgcn_sched_barrier(0);   // bound the live values of the epilogue
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                        if (m < M) {
+#pragma unroll
+                            for (int hb = 0; hb < 2; ++hb) {
+                                const float gv = acc[i][2 * hb][4 * g + e], uv = acc[i][2 * hb + 1][4 * g + e];
+                                const float h = gv / (1.0f + expf(-gv)) * uv;
+                                a.H[(size_t)m * a.ldo + nb + 32 * hb + ccol] = f32_to_bf16_rne(h);
+                            }
+                        }
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                        if (m < M) {
+                            const int tok = a.keep[m];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int n = n0 + wn * 128 + j * 32 + ccol;
+                                const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
+                                a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
+                            }
+                        }
+                    }
+                }
+        }
+    }
+}
+
 // flags[i] = 1 iff i is in the ascending keep list (binary search per token)
 __global__ __launch_bounds__(256) void k_fill_flags(int32_t *__restrict__ flags, int L, const int32_t *__restrict__ keep,
                                                     const int32_t *__restrict__ count)
@@ -390,6 +573,20 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     return hipGetLastError();
 }
 
+// compute units of the current device (cached per device), a multiple of 8 when possible
+static int gemm_grid(hipStream_t)
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n >= 8 ? n / 8 * 8 : n;
+    }
+    return cus[dev];
+}
+
 hipError_t launch_prefill_forward(const PrefillForwardCall &c)
 {
     const Layer &L = *c.L;
@@ -410,16 +607,27 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     const int mt_max = (rows + GBM - 1) / GBM;
     GemmArgs g{};
     g.A = c.Y; g.B = L.wgu; g.K = d; g.N = 2 * f; g.keep = c.keep; g.count = c.count; g.H = H; g.ldo = f;
-    const int tiles1 = mt_max * (2 * f / GBN);
+    const int mt_big = (c.L->desc.max_rows + BBM - 1) / BBM;
+    const int tiles1 = mt_big * (2 * f / BBN);
     hipEvent_t evb = nullptr, eve = nullptr;
     L.timer->take(&evb, &eve);
-    SFFN_LAUNCH(k_gemm<EPI_GATE_UP>, dim3(std::min(tiles1, 2048)), dim3(256), 0, c.stream, evb, eve, g);
+    // one workgroup per compute unit (128 KB of LDS each), looping over tiles
+    const int G = gemm_grid(c.stream);
+    SFFN_LAUNCH(k_gemm_big<EPI_GATE_UP>, dim3(std::min(tiles1, G)), dim3(256), 0, c.stream, evb, eve, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmArgs g2{};
     g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
     g2.ldo = d;
-    const int tiles2 = mt_max * (d / GBN);
-    hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(std::min(tiles2, 2048)), dim3(256), 0, c.stream, g2);
+    // down projection: 256 x 256 tiles when they fill at least half of the compute
+    // units, else 128 x 128 tiles (both launched; the device-side count opens one)
+    const int tiles2 = mt_big * (d / BBN);
+    g2.gate = G / 2;   // measured: 220 big tiles on 256 units beat 880 small ones; 100 do not
+    g2.gate_big = 1;
+    hipLaunchKernelGGL(k_gemm_big<EPI_DOWN>, dim3(std::min(tiles2, G)), dim3(256), 0, c.stream, g2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    g2.gate_big = 0;
+    const int tiles2s = mt_max * (d / GBN);
+    hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(std::min(tiles2s, 2048)), dim3(256), 0, c.stream, g2);
     return hipGetLastError();
 }
 
