@@ -5,18 +5,19 @@
 // only on the important tokens S, Z[~S] = 0 and X_next = Y + Z.
 //   t1 k_token_norms   s_i = ||A_i||_2 (attention output row), sum of squares in
 //                      the fixed fp32 order (64 lane accumulators), IEEE sqrt.
-//   t2 k_token_select  one workgroup: sort the (score, index) keys descending,
-//                      fp64 cumulative mass in blocks of 256 sorted entries,
+//   t2 k_tsort_chunk / k_tsort_merge sort the (score, index) keys descending
+//                      (chunks of 1024 in LDS, then exact merge ranks);
+//      k_token_select  (one workgroup) fp64 cumulative mass in blocks of 256 sorted entries,
 //                      shortest prefix reaching mass * total, plus the last
 //                      recent_n tokens, plus top-ranked tokens up to min_keep;
 //                      mass >= 1 or total == 0 keeps every token.  Writes the
 //                      ascending keep list, its length and per-token flags, all
 //                      on the device (no host synchronisation).
-//   t3 k_gemm<GATE_UP> H = SiLU(Y_S W_gate^T) (.) (Y_S W_up^T), bf16 MFMA with
+//   t3 k_gemm_big<GATE_UP> H = SiLU(Y_S W_gate^T) (.) (Y_S W_up^T), bf16 MFMA with
 //                      the A rows gathered through the keep list and the gate /
 //                      up columns of the same neurons in one tile (the weights
 //                      are interleaved in blocks of 32 rows at creation).
-//   t4 k_gemm<DOWN>    Z = H W_down^T; epilogue X_next[S_m] = bf16(Y[S_m] + Z_m),
+//   t4 k_gemm_big<DOWN> / k_gemm<DOWN> Z = H W_down^T; epilogue X_next[S_m] = bf16(Y[S_m] + Z_m),
 //                      a scatter through the keep list.
 //   k_copy_unkept      X_next[i] = Y[i] for i not kept (skipped when X_next == Y).
 // Tiles whose rows start past the device-side count exit at once, so the grid
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 struct SelectArgs {
     const float *s;
+    const uint64_t *sorted;   // the L keys in descending order
     int L, recent_n, min_keep;
     double mass;
     int32_t *keep, *count;
@@ -77,6 +79,53 @@ __device__ __forceinline__ uint64_t rank_key(float s, int i)
 {
     // descending key order = score descending, then index ascending
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// t2, sort in two steps.  k_tsort_chunk: every workgroup sorts 1024 keys
+// descending in LDS (padding keys are 0, below every token's key).
+// k_tsort_merge: the keys are unique (the index is part of the key), so the
+// global rank of a key is its place in its chunk plus, for every other chunk,
+// the number of larger keys there (a binary search); the key is written to that
+// rank.  The result is the full descending order.
+__global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks)
+{
+    __shared__ uint64_t key[1024];
+    const int i = blockIdx.x * 1024 + threadIdx.x;
+    key[threadIdx.x] = i < L ? rank_key(s[i], i) : 0ull;
+    __syncthreads();
+    bitonic_sort_desc(key, 1024);
+    chunks[(size_t)blockIdx.x * 1024 + threadIdx.x] = key[threadIdx.x];
+}
+
+__global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict__ chunks, int G,
+                                                      uint64_t *__restrict__ sorted)
+{
+    extern __shared__ __align__(16) uint64_t all[];   // [G][1024]
+    {
+        constexpr int GMAX = kMaxPrefillRows / 1024;
+        uint64_t kv[GMAX];
+#pragma unroll
+        for (int q = 0; q < GMAX; ++q) kv[q] = q < G ? chunks[q * 1024 + threadIdx.x] : 0ull;
+#pragma unroll
+        for (int q = 0; q < GMAX; ++q)
+            if (q < G) all[q * 1024 + threadIdx.x] = kv[q];
+    }
+    __syncthreads();
+    const int c = blockIdx.x, p = threadIdx.x;
+    const uint64_t key = all[c * 1024 + p];
+    if (key == 0) return;   // padding
+    int rank = p;
+    for (int c2 = 0; c2 < G; ++c2) {
+        if (c2 == c) continue;
+        const uint64_t *q = all + c2 * 1024;
+        int lo = 0, hi = 1024;   // first position whose key is below this key
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (q[mid] > key) lo = mid + 1; else hi = mid;
+        }
+        rank += lo;
+    }
+    sorted[rank] = key;
 }
 
 __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
@@ -92,25 +141,60 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     __shared__ int s_m, s_all, s_cnt;
     __shared__ int tmp[17];
 
-    for (int i = tid; i < N; i += NT) key[i] = i < L ? rank_key(a.s[i], i) : 0ull;
+    {
+        // all loads first, then the LDS stores (L <= 16 * 1024)
+        constexpr int PER = kMaxPrefillRows / 1024;
+        uint64_t kv[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) kv[q] = tid + q * NT < L ? a.sorted[tid + q * NT] : 0ull;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (tid + q * NT < L) key[tid + q * NT] = kv[q];
+    }
     for (int i = tid; i < L; i += NT) in[i] = 0;
     if (tid == 0) s_m = L;
     __syncthreads();
-    bitonic_sort_desc(key, N);
-    // fp64 cumulative mass in blocks of kMassBlock sorted entries
+    // fp64 cumulative mass in blocks of kMassBlock sorted entries: thread b adds
+    // block b in order (its values loaded 32 at a time ahead of the adds) and
+    // keeps the running sum after every 32 entries, so that the threshold scan
+    // can start from the last checkpoint below the threshold
     const int nb = (L + kMassBlock - 1) / kMassBlock;
+    constexpr int NCP = kMassBlock / 32;
+    __shared__ double cpt[kMaxPrefillRows / kMassBlock][NCP];
+    auto score_at = [&](int k) { return __uint_as_float((uint32_t)(key[k] >> 32)); };
     if (tid < nb) {
         double run = 0.0;
-        const int b1 = min(L, (tid + 1) * kMassBlock);
-        for (int k = tid * kMassBlock; k < b1; ++k) run = run + (double)__uint_as_float((uint32_t)(key[k] >> 32));
+        const int b0 = tid * kMassBlock, b1 = min(L, b0 + kMassBlock);
+        for (int k0 = b0; k0 < b1; k0 += 32) {
+            float v[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v[u] = k0 + u < b1 ? score_at(k0 + u) : 0.0f;
+            __builtin_amdgcn_sched_barrier(0);   // keep the 32 reads ahead of the dependent adds
+            if (k0 + 32 <= b1) {
+#pragma unroll
+                for (int u = 0; u < 32; ++u) run = run + (double)v[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < 32; ++u)
+                    if (k0 + u < b1) run = run + (double)v[u];
+            }
+            cpt[tid][(k0 - b0) >> 5] = run;   // the sum of the block's entries up to k0 + 31
+        }
         blk_total[tid] = run;
     }
     __syncthreads();
     if (tid == 0) {
+        constexpr int NBMAX = kMaxPrefillRows / kMassBlock;
+        double tv[NBMAX];
+#pragma unroll
+        for (int b = 0; b < NBMAX; ++b) tv[b] = b < nb ? blk_total[b] : 0.0;
         double base = 0.0;
-        for (int b = 0; b < nb; ++b) {
-            blk_base[b] = base;
-            base = base + blk_total[b];
+#pragma unroll
+        for (int b = 0; b < NBMAX; ++b) {
+            if (b < nb) {
+                blk_base[b] = base;
+                base = base + tv[b];
+            }
         }
         const double total = base;  // equals the last cumulative value
         s_all = (a.mass >= 1.0 || total == 0.0) ? 1 : 0;
@@ -120,16 +204,28 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     const bool all = s_all != 0;
     if (!all && a.mass > 0.0) {
         const double thr = a.mass * blk_base[nb];
-        if (tid < nb) {
-            double run = 0.0;
-            const int b1 = min(L, (tid + 1) * kMassBlock);
-            for (int k = tid * kMassBlock; k < b1; ++k) {
-                run = run + (double)__uint_as_float((uint32_t)(key[k] >> 32));
-                if (blk_base[tid] + run >= thr) {
-                    atomicMin(&s_m, k);
-                    break;
+        // the cumulative mass only grows, and its value at the end of block b is
+        // blk_base[b + 1]: the first block whose end reaches thr holds the answer
+        if (tid < nb && blk_base[tid + 1] >= thr && (tid == 0 || blk_base[tid] < thr)) {
+            const double base = blk_base[tid];
+            const int b0 = tid * kMassBlock, b1 = min(L, b0 + kMassBlock);
+            // the 32-entry span where the cumulative mass first reaches thr
+            int j = 0;
+            while (b0 + 32 * (j + 1) < b1 && base + cpt[tid][j] < thr) ++j;
+            double run = j > 0 ? cpt[tid][j - 1] : 0.0;
+            const int k0 = b0 + 32 * j;
+            float v[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v[u] = k0 + u < b1 ? score_at(k0 + u) : 0.0f;
+            int hit = -1;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                if (hit < 0 && k0 + u < b1) {
+                    run = run + (double)v[u];
+                    if (base + run >= thr) hit = k0 + u;
                 }
             }
+            s_m = hit;
         }
         __syncthreads();
         // the shortest prefix: ranks 0..m
@@ -561,14 +657,25 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     int N = 1;
     while (N < rows) N <<= 1;
     const size_t lds = (size_t)N * 8 + (size_t)rows;
+    const int G = (rows + 1023) / 1024;   // <= kMaxPrefillRows / 1024 = 16
     static bool attr = false;
     if (!attr) {
         e = hipFuncSetAttribute((const void *)k_token_select, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)((size_t)kMaxPrefillRows * 8 + kMaxPrefillRows));
         if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)k_tsort_merge, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)((size_t)kMaxPrefillRows * 8));
+        if (e != hipSuccess) return e;
         attr = true;
     }
-    SelectArgs a{sc_s, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out, flags};
+    uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);
+    uint64_t *sorted = chunks + kMaxPrefillRows;
+    hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tsort_merge, dim3(G), dim3(1024), (size_t)G * 1024 * 8, c.stream, (const uint64_t *)chunks, G,
+                       sorted);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out, flags};
     hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
     return hipGetLastError();
 }

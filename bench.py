@@ -576,7 +576,14 @@ def bench_prefill(args):
             t_oop.append(ev[2].elapsed_time(ev[3]) * 1e3)
         flops = 6.0 * M * d * f
         us_ffn = float(np.median(t_ffn))
-        r = dict(mass=mass, kept=M, kept_frac=round(M / L, 4), select_us=round(float(np.median(t_sel)), 2),
+
+        # selection alone: HIP graphs of 8 back-to-back calls (no host launch gaps)
+        def sel(s0, n, pol=pol):
+            for _ in range(n):
+                layer.select(pol, Ad, keep, cnt)
+        us_sel = graph_time_us(sel, 32, 8, 1)
+        r = dict(mass=mass, kept=M, kept_frac=round(M / L, 4), select_us=round(us_sel, 2),
+                 select_us_eager=round(float(np.median(t_sel)), 2),
                  ffn_ms=round(us_ffn / 1e3, 4), ffn_out_of_place_ms=round(float(np.median(t_oop)) / 1e3, 4),
                  tflops=round(flops / us_ffn / 1e6, 1),
                  mfma_frac=round(flops / us_ffn / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
