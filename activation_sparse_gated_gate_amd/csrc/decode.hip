@@ -1123,13 +1123,13 @@ __device__ __forceinline__ void stage_vec(float *xs, const float *x, int n)
 }
 
 // Fused sparse layer for one token.  Each workgroup owns RB consecutive
-// neurons; wave w walks neurons w, w + 8, ... with the next gate row prefetched.
-// For an active neuron the wave loads its W_up row and W_down^T row together,
-// forms h = act(g') u and accumulates h * W_down^T[j] into a per-wave partial y
-// held in registers (lane p owns the columns of chunks p, p + 64, ...).  No
-// barrier separates gate, up and down, so the memory pipe keeps streaming
-// while some waves wait on dependent loads.  At the end the 8 wave partials are
-// summed in a fixed order through LDS into the workgroup's partial.
+// neurons.  Phase 1 streams their gate rows (wave w walks neurons w, w + 8, ...
+// with the next row's loads in flight) and records g' and the selection in LDS.
+// Phase 2 deals the workgroup's active neurons round-robin to the waves, so no
+// wave carries more than its share of gathers: each loads the W_up and W_down^T
+// rows of two neurons at a time, forms h = act(g') u and adds h * W_down^T[j]
+// into its own partial y in LDS.  The wave partials are then summed in a fixed
+// order into the workgroup's partial (blocked layout for the reduce).
 constexpr int kFusedNW = 8;
 constexpr int kFusedNT = kFusedNW * 64;
 
@@ -1144,6 +1144,9 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
     __shared__ __align__(16) float xs[D];
     __shared__ __align__(16) float ysum[NW * D];
     __shared__ int flags[kFusedMaxRB];
+    __shared__ float gsm[kFusedMaxRB];
+    __shared__ int alist[kFusedMaxRB];
+    __shared__ int s_nact;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r0 = blockIdx.x * a.RB;
@@ -1154,29 +1157,64 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
     stage_vec(xs, a.x, D);
     __syncthreads();
 
-    // this wave's partial y lives in its own LDS slice (lane p owns the columns
-    // of chunks p, p + 64, ...), so only the running rows occupy registers
-    float *yw = ysum + (size_t)wave * D;
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-        float4 *dst = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
-#pragma unroll
-        for (int e4 = 0; e4 < E / 4; ++e4) dst[e4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    // phase 1: the gate stream (wave w walks rows w, w + 8, ..., the next row's
+    // loads in flight), g' and the selection into LDS
+    auto gate = [&](const uint4 (&cur)[KC], int i) {
+        const float g = dot_row_lds<WT, KC>(cur, xs, lane);
+        const float gp = g + a.bias;
+        const bool on = gate_pred(a.mode, gp, a.theta);
+        if (lane == 0) {
+            a.G[r0 + i] = gp;
+            flags[i] = on ? 1 : 0;
+            gsm[i] = gp;
+        }
+    };
+    for (int i = wave; i < nr; i += 2 * NW) {
+        const int i2 = i + NW;
+        if (i2 < nr) load_row<WT, KC>(gb, a.wg, RBYTES, r0 + i2, lane);
+        gate(ga, i);
+        if (i2 >= nr) break;
+        const int i3 = i2 + NW;
+        if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
+        gate(gb, i2);
     }
+    __syncthreads();
+    // ascending list of this workgroup's active neurons (ballot + mbcnt)
+    if (wave == 0) {
+        const int on = lane < nr ? flags[lane] : 0;
+        const uint64_t m = __ballot(on);
+        if (on) {
+            alist[mbcnt64(m)] = lane;
+            a.list_idx[(size_t)blockIdx.x * a.RB + mbcnt64(m)] = r0 + lane;
+        }
+        if (lane == 0) {
+            s_nact = __popcll(m);
+            a.list_cnt[blockIdx.x] = __popcll(m);
+        }
+    }
+    __syncthreads();
+    const int nact = s_nact;
 
-    // Software pipeline per wave: while the W_up / W_down^T rows of the last
-    // active neuron are in flight, the wave computes the next gate row (whose
-    // load was issued one row earlier); the pending neuron is finished after.
-    uint4 ua[KC], da[KC];
-    int pend = -1;       // neuron whose up / down rows are in flight
-    float pend_g = 0.0f;
-    auto finish = [&]() {
-        const float u = dot_row_lds<WT, KC>(ua, xs, lane);
-        const float h = act_f32(a.act, pend_g) * u;
+    // phase 2: the active neurons dealt round-robin to the waves (two at a time
+    // per wave, their W_up and W_down^T rows loaded together); each wave adds
+    // h * W_down^T[j] into its own partial y (lane p owns the columns of chunks
+    // p, p + 64, ...), neurons in ascending order
+    float *yw = ysum + (size_t)wave * D;
+    if (wave < nact) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            float4 *dst = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
+#pragma unroll
+            for (int e4 = 0; e4 < E / 4; ++e4) dst[e4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    auto finish = [&](const uint4 (&ur)[KC], const uint4 (&dr)[KC], float gp) {
+        const float u = dot_row_lds<WT, KC>(ur, xs, lane);
+        const float h = act_f32(a.act, gp) * u;
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
             float w[E];
-            unpack<WT>(da[k], w);
+            unpack<WT>(dr[k], w);
             float4 *yv = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
 #pragma unroll
             for (int e4 = 0; e4 < E / 4; ++e4) {
@@ -1189,53 +1227,35 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
             }
         }
     };
-    auto neuron = [&](const uint4 (&cur)[KC], int i) {
-        const float g = dot_row_lds<WT, KC>(cur, xs, lane);
-        const float gp = g + a.bias;
-        const bool on = gate_pred(a.mode, gp, a.theta);
-        if (lane == 0) {
-            a.G[r0 + i] = gp;
-            flags[i] = on ? 1 : 0;
+    for (int q = wave; q < nact; q += 2 * NW) {
+        const int q2 = q + NW;
+        const int i1 = alist[q];
+        load_row<WT, KC>(ga, a.wu, RBYTES, r0 + i1, lane);
+        load_row<WT, KC>(gb, a.wdt, RBYTES, r0 + i1, lane);
+        uint4 uc[KC], dc[KC];
+        int i2 = -1;
+        if (q2 < nact) {
+            i2 = alist[q2];
+            load_row<WT, KC>(uc, a.wu, RBYTES, r0 + i2, lane);
+            load_row<WT, KC>(dc, a.wdt, RBYTES, r0 + i2, lane);
         }
-        if (pend >= 0) finish();
-        pend = -1;
-        if (on) {
-            load_row<WT, KC>(ua, a.wu, RBYTES, r0 + i, lane);
-            load_row<WT, KC>(da, a.wdt, RBYTES, r0 + i, lane);
-            pend = i;
-            pend_g = gp;
-        }
-    };
-    for (int i = wave; i < nr; i += 2 * NW) {
-        const int i2 = i + NW;
-        if (i2 < nr) load_row<WT, KC>(gb, a.wg, RBYTES, r0 + i2, lane);
-        neuron(ga, i);
-        if (i2 >= nr) break;
-        const int i3 = i2 + NW;
-        if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
-        neuron(gb, i2);
+        finish(ga, gb, gsm[i1]);
+        if (i2 >= 0) finish(uc, dc, gsm[i2]);
     }
-    if (pend >= 0) finish();
 
-    // fixed-order sum of the wave partials
+    // fixed-order sum of the partials of the waves that had neurons
     __syncthreads();
+    const int nwp = min(nact, NW);
     for (int c = threadIdx.x; c < D / 4; c += NT) {
-        float4 acc = ((const float4 *)ysum)[c];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) {
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (nwp > 0) acc = ((const float4 *)ysum)[c];
+        for (int w = 1; w < nwp; ++w) {
             const float4 v = ((const float4 *)(ysum + (size_t)w * D))[c];
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         // blocked layout [D / 16][P][16]: the reduce reads each 16-column block contiguously
         const int col = 4 * c;
         *(float4 *)(a.partial + ((size_t)(col >> 4) * gridDim.x + blockIdx.x) * 16 + (col & 15)) = acc;
-    }
-    // ascending list of this workgroup's active neurons (ballot + mbcnt)
-    if (wave == 0) {
-        const int on = lane < nr ? flags[lane] : 0;
-        const uint64_t m = __ballot(on);
-        if (on) a.list_idx[(size_t)blockIdx.x * a.RB + mbcnt64(m)] = r0 + lane;
-        if (lane == 0) a.list_cnt[blockIdx.x] = __popcll(m);
     }
 }
 
