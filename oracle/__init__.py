@@ -68,6 +68,8 @@ def _load():
     lib.ora_token_select.argtypes = [P, I, D, I, I, P, P, P]
     lib.ora_token_select.restype = I
     lib.ora_prefill_rows.argtypes = [I, I, P, P, P, P, P, I, P, I]
+    lib.ora_expert_select.argtypes = [P, I, I, F, I, I, P, P, P]
+    lib.ora_expert_select.restype = I
     lib.ora_prefill_rows.restype = None
     lib.ora_bf16_rne.argtypes = [D]
     lib.ora_bf16_rne.restype = C.c_uint16
@@ -196,6 +198,18 @@ def token_select(s, mass, recent_n=128, min_keep=1):
     if n < 0:
         raise ValueError("oracle token_select rejected its arguments")
     return keep[:n].copy(), order[:L].copy(), cum[:L].copy()
+
+
+def expert_select(probs, tau=0.5, kmin=3, kmax=6):
+    """Adaptive expert top-K: returns (K int32 [T], idx int32 [T, kmax], w fp32 [T, kmax])."""
+    p = _c(probs, np.float32)
+    T, E = p.shape
+    k = np.empty(max(T, 1), np.int32)
+    idx = np.empty((max(T, 1), kmax), np.int32)
+    w = np.empty((max(T, 1), kmax), np.float32)
+    if _load().ora_expert_select(_p(p), T, E, float(tau), int(kmin), int(kmax), _p(k), _p(idx), _p(w)) != 0:
+        raise ValueError("oracle expert_select rejected its arguments")
+    return k[:T].copy(), idx[:T].copy(), w[:T].copy()
 
 
 def prefill_rows(weights, Y_bf16, rows, threads=None) -> np.ndarray:

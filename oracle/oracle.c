@@ -30,6 +30,11 @@
  *    mass in descending order; the last recent_n tokens always kept; at least
  *    min_keep tokens; an all-zero score row or mass >= 1 means dense;
  *    X_next = Y + Z with Z = FFN(Y) on the kept rows and 0 elsewhere.
+ *  - Adaptive expert top-K (RedKnot article, section on adaptive expert top-K):
+ *    per token, rank the routed experts by routing probability and keep the
+ *    smallest bucket of the top-ranked experts whose probability mass reaches
+ *    the threshold (default 0.50 over buckets 3..6); the per-depth schedule
+ *    caps the largest bucket.
  *
  * Precision.  Every output value is computed in fp64 from the exact fp32
  * values of the inputs (bf16 and int4*fp16 weights convert to fp32 exactly).
@@ -48,6 +53,8 @@
  *       exp below, n_j = sqrt of the ascending fp64 sum of squares.
  *   C3  the token cumulative mass is fp64 in blocks of 256 sorted entries:
  *       sequential inside a block, block totals summed sequentially.
+ *   C8  the expert cumulative mass is fp32, summed sequentially in rank order
+ *       from the top-ranked expert.
  *
  * Build: plain C99, -O2 -ffp-contract=off, no fast-math, optional OpenMP over
  * tokens / rows.
@@ -498,6 +505,53 @@ int ora_token_select(const float *s, int L, double mass, int recent_n, int min_k
     if (cum_out) memcpy(cum_out, cum, sizeof(double) * (size_t)L);
     free(t); free(cum); free(in);
     return n;
+}
+
+/*
+ * Adaptive expert top-K (RedKnot article, section on adaptive expert top-K:
+ * the number of experts a token activates follows its routing probability
+ * mass, threshold 0.50 over the candidate buckets 3, 4, 5, 6; confident tokens
+ * take few experts, diffuse ones more).  Per token t, with p = probs[t][0..E):
+ *   rank the experts by (p desc, index asc);
+ *   c_b = the fp32 sum of the b top-ranked probabilities, added in rank order;
+ *   K = the smallest b in [kmin, kmax] with c_b >= tau, or kmax if none.
+ * k_out[t] = K; idx_out[t][0..kmax) = the top K experts in rank order then -1;
+ * w_out[t][0..kmax) = their probabilities then 0.  Probabilities are >= 0.
+ * Returns 0, or -1 on bad arguments.
+ */
+typedef struct { float p; int i; } expert_rank;
+
+static int cmp_expert(const void *a, const void *b)
+{
+    const expert_rank *x = (const expert_rank *)a, *y = (const expert_rank *)b;
+    if (x->p != y->p) return x->p > y->p ? -1 : 1;
+    return x->i < y->i ? -1 : (x->i > y->i ? 1 : 0);
+}
+
+int ora_expert_select(const float *probs, int T, int E, float tau, int kmin, int kmax,
+                      int32_t *k_out, int32_t *idx_out, float *w_out)
+{
+    if (T < 0 || E < 1 || kmin < 1 || kmax < kmin || kmax > E) return -1;
+    expert_rank *r = (expert_rank *)malloc(sizeof(expert_rank) * (size_t)E);
+    if (!r) return -1;
+    for (int t = 0; t < T; ++t) {
+        const float *p = probs + (size_t)t * E;
+        for (int j = 0; j < E; ++j) { r[j].p = p[j]; r[j].i = j; }
+        qsort(r, (size_t)E, sizeof(expert_rank), cmp_expert);
+        int K = kmax;
+        float c = 0.0f;
+        for (int b = 1; b <= kmax; ++b) {
+            c = c + r[b - 1].p;
+            if (b >= kmin && c >= tau) { K = b; break; }
+        }
+        k_out[t] = K;
+        for (int b = 0; b < kmax; ++b) {
+            idx_out[(size_t)t * kmax + b] = b < K ? r[b].i : -1;
+            w_out[(size_t)t * kmax + b] = b < K ? r[b].p : 0.0f;
+        }
+    }
+    free(r);
+    return 0;
 }
 
 /*

@@ -494,3 +494,90 @@ def test_prefill_rows_match_fp64_numpy_and_unkept_rows_pass_through():
     full = oracle.prefill(w, Y, np.arange(L, dtype=np.int32))
     ref = oracle.bf16_rne(Yf + ffn_f64(w, Yf, np.ones(f)))
     assert np.array_equal(full, ref)
+
+
+# ---------------------------------------------------------------------------
+# adaptive expert top-K (RedKnot article, section on adaptive expert top-K)
+# ---------------------------------------------------------------------------
+
+def test_expert_page_parameters():
+    g = json.load(open(GOLDEN))
+    e = g["adaptive_expert_topk"]
+    assert e["threshold"] == 0.5 and e["buckets"] == [3, 4, 5, 6] and e["native_experts_per_token"] == 6
+    sched = g["progressive_topk_schedule"]["layers"]
+    assert [k for _, _, k in sched] == [6, 5, 4]
+    assert max(k for _, _, k in sched) == e["buckets"][-1]
+
+
+def test_expert_select_hand_worked_cases():
+    # confident token: 0.40 + 0.20 + 0.15 = 0.75 >= 0.5 at the smallest bucket
+    p = np.array([[0.05, 0.40, 0.20, 0.15, 0.10, 0.05, 0.03, 0.02]], np.float32)
+    k, idx, w = oracle.expert_select(p)
+    assert k[0] == 3 and list(idx[0]) == [1, 2, 3, -1, -1, -1]
+    assert list(w[0][:3]) == [np.float32(0.40), np.float32(0.20), np.float32(0.15)] and np.all(w[0][3:] == 0)
+    # diffuse token: six of sixteen equal experts carry 6/16 < 0.5 -> the largest bucket, ties by index
+    k, idx, _ = oracle.expert_select(np.full((1, 16), 1 / 16, np.float32))
+    assert k[0] == 6 and list(idx[0]) == [0, 1, 2, 3, 4, 5]
+    # eight experts of 1/8: the mass after four is exactly 0.5, which reaches the threshold
+    k, idx, _ = oracle.expert_select(np.full((1, 8), 0.125, np.float32))
+    assert k[0] == 4 and list(idx[0]) == [0, 1, 2, 3, -1, -1]
+    # mass crosses between the third and the fourth expert: 0.2 + 3 x 0.1
+    p = np.array([[0.2] + [0.1] * 8], np.float32)
+    k, idx, _ = oracle.expert_select(p)
+    assert k[0] == 4 and list(idx[0][:4]) == [0, 1, 2, 3]
+
+
+def test_expert_select_threshold_limits_and_plain_topk():
+    rng = np.random.default_rng(17)
+    p = rng.dirichlet(np.ones(384), size=64).astype(np.float32)
+    k0, _, _ = oracle.expert_select(p, tau=0.0)
+    assert np.all(k0 == 3)
+    k2, _, _ = oracle.expert_select(p, tau=2.0)
+    assert np.all(k2 == 6)
+    # kmin = kmax: plain top-k, equal to a stable sort of -p
+    for kk in (1, 6, 16):
+        k, idx, w = oracle.expert_select(p, kmin=kk, kmax=kk)
+        assert np.all(k == kk)
+        ref = np.argsort(-p, axis=1, kind="stable")[:, :kk]
+        assert np.array_equal(idx, ref)
+        assert np.array_equal(w, np.take_along_axis(p, ref, axis=1))
+
+
+def test_expert_select_matches_exhaustive_subsets():
+    # K = the smallest bucket b whose best b-subset of experts reaches tau; checked by
+    # enumerating every subset in exact rational arithmetic (cases near a tie skipped)
+    from fractions import Fraction
+    from itertools import combinations
+    rng = np.random.default_rng(23)
+    checked = 0
+    for _ in range(60):
+        E = int(rng.integers(6, 10))
+        p = rng.dirichlet(np.ones(E) * float(rng.choice([0.3, 1.0, 3.0]))).astype(np.float32)[None, :]
+        tau = float(rng.choice([0.3, 0.5, 0.7]))
+        best = {b: max(sum(Fraction(float(p[0, j])) for j in c) for c in combinations(range(E), b))
+                for b in range(3, 7)}
+        if any(abs(float(best[b]) - tau) < 1e-5 for b in best):
+            continue
+        want = next((b for b in range(3, 7) if best[b] >= Fraction(tau)), 6)
+        k, idx, w = oracle.expert_select(p, tau=tau)
+        assert k[0] == want
+        # the chosen experts carry the best mass for that count
+        assert sum(Fraction(float(v)) for v in w[0][:want]) == best[want]
+        checked += 1
+    assert checked >= 40
+
+
+def test_expert_select_kept_experts_dominate_and_counts_follow_mass():
+    rng = np.random.default_rng(29)
+    logits = rng.standard_normal((200, 256)) * rng.uniform(0.5, 6.0, (200, 1))
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    k, idx, w = oracle.expert_select(p)
+    assert set(np.unique(k)) <= {3, 4, 5, 6} and len(np.unique(k)) >= 3
+    for t in range(p.shape[0]):
+        sel = idx[t][: k[t]]
+        rest = np.setdiff1d(np.arange(256), sel)
+        assert p[t, sel].min() >= p[t, rest].max()
+        # sharper routing (more mass in the top experts) never asks for more experts
+    top3 = np.sort(p, axis=1)[:, ::-1][:, :3].sum(axis=1)
+    assert k[top3 >= 0.5].max() == 3
