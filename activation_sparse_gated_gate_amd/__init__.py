@@ -28,7 +28,7 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
          "tokens": MODE_TOKENS, "dense": MODE_DENSE}
 
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
-           "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer")
+           "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select")
 
 
 class LayerDesc(C.Structure):
@@ -41,6 +41,10 @@ class Policy(C.Structure):
     _fields_ = [("mode", C.c_int32), ("gate_bias", C.c_float), ("theta", C.c_float),
                 ("topk_k", C.c_int32), ("use_union", C.c_int32), ("recent_n", C.c_int32),
                 ("min_keep", C.c_int32), ("reserved", C.c_int32), ("mass_thresh", C.c_double)]
+
+
+class ExpertPolicy(C.Structure):
+    _fields_ = [("tau", C.c_float), ("kmin", C.c_int32), ("kmax", C.c_int32), ("reserved", C.c_int32)]
 
 
 class SffnError(RuntimeError):
@@ -76,6 +80,8 @@ def _load():
     lib.sffn_last_hip_error.argtypes = []
     lib.sffn_last_hip_error.restype = C.c_char_p
     lib.sffn_set_kernel_timer.argtypes = [P, P, P, I]
+    lib.sffn_expert_select.restype = I
+    lib.sffn_expert_select.argtypes = [P, I, I, C.POINTER(ExpertPolicy), P, P, P, P]
     lib.sffn_set_kernel_timer.restype = I
     return lib
 
@@ -119,6 +125,29 @@ def sffn_forward(handle, policy, inp, rows, out, idx_in, count_in, idx_out, coun
 
 def sffn_destroy(handle) -> None:
     _lib.sffn_destroy(handle)
+
+
+def sffn_expert_select(probs, tokens, experts, policy, k_out, idx_out, w_out, stream) -> int:
+    return _lib.sffn_expert_select(probs, int(tokens), int(experts), C.byref(policy), k_out, idx_out, w_out,
+                                   stream)
+
+
+def expert_select(probs, tau=0.5, kmin=3, kmax=6, k_out=None, idx_out=None, w_out=None, stream=None):
+    """Adaptive expert top-K on device probabilities [T, E] (fp32): returns (K [T] int32,
+    experts [T, kmax] int32, probabilities [T, kmax] fp32), all device tensors."""
+    import torch
+    T, E = probs.shape
+    dev = probs.device
+    k_out = k_out if k_out is not None else torch.empty(T, dtype=torch.int32, device=dev)
+    idx_out = idx_out if idx_out is not None else torch.empty((T, kmax), dtype=torch.int32, device=dev)
+    w_out = w_out if w_out is not None else torch.empty((T, kmax), dtype=torch.float32, device=dev)
+    st = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+    pol = ExpertPolicy(float(tau), int(kmin), int(kmax), 0)
+    status = sffn_expert_select(probs.data_ptr(), T, E, pol, k_out.data_ptr(), idx_out.data_ptr(),
+                                w_out.data_ptr(), st)
+    if status != SFFN_OK:
+        raise SffnError(status, "sffn_expert_select")
+    return k_out, idx_out, w_out
 
 
 def sffn_set_kernel_timer(handle, begin_events, end_events, n) -> int:

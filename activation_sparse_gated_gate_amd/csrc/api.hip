@@ -215,13 +215,29 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
 
 void sffn_destroy(sffn_t layer) { delete layer; }
 
+// the timer of the entry points that take no handle (sffn_expert_select)
+static KernelTimer g_free_timer;
+
+sffn_status sffn_expert_select(const float *probs, int32_t tokens, int32_t experts, const sffn_expert_policy *policy,
+                               int32_t *k_out, int32_t *idx_out, float *w_out, void *stream)
+{
+    if (!policy || tokens < 0 || experts < 1 || experts > kMaxExpertsAbi) return SFFN_ERR_INVALID_ARG;
+    if (tokens > 0 && (!probs || !k_out || !idx_out || !w_out)) return SFFN_ERR_INVALID_ARG;
+    const int kmin = policy->kmin, kmax = policy->kmax;
+    if (kmin < 1 || kmax < kmin || kmax > experts || kmax > kMaxExpertKAbi) return SFFN_ERR_INVALID_ARG;
+    if (!(policy->tau == policy->tau)) return SFFN_ERR_INVALID_ARG;   // NaN
+    return hip_status(launch_expert_select(probs, tokens, experts, policy->tau, kmin, kmax, k_out, idx_out, w_out,
+                                           (hipStream_t)stream, &g_free_timer));
+}
+
 sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events, int32_t n)
 {
-    if (!layer || n < 0 || (n > 0 && (!begin_events || !end_events))) return SFFN_ERR_INVALID_ARG;
-    layer->timer.begin = begin_events;
-    layer->timer.end = end_events;
-    layer->timer.n = n;
-    layer->timer.next = 0;
+    if (n < 0 || (n > 0 && (!begin_events || !end_events))) return SFFN_ERR_INVALID_ARG;
+    KernelTimer &t = layer ? layer->timer : g_free_timer;
+    t.begin = begin_events;
+    t.end = end_events;
+    t.n = n;
+    t.next = 0;
     return SFFN_OK;
 }
 

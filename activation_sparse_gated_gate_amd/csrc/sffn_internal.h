@@ -127,6 +127,11 @@ struct PrefillSelectCall {
     hipStream_t stream;
 };
 hipError_t launch_prefill_select(const PrefillSelectCall &c);
+// adaptive expert top-K (experts.hip)
+constexpr int kMaxExpertsAbi = 1024;
+constexpr int kMaxExpertKAbi = 16;
+hipError_t launch_expert_select(const float *probs, int T, int E, float tau, int kmin, int kmax, int32_t *k_out,
+                                int32_t *idx_out, float *w_out, hipStream_t st, KernelTimer *timer);
 
 struct PrefillForwardCall {
     const Layer *L;

@@ -18,6 +18,8 @@ Other workloads (same JSON contract, one line each):
   --workload schedule  28 layers of 3584 / 18944 bf16 SwiGLU, batch 16, dense /
                        a ~ 0.3 / a ~ 0.13 thresholds, RMSNorm and residual
   --workload prefill   token-selective prefill, d_model 5120, d_ff 25600, L 16384
+  --workload experts   adaptive expert top-K by routing mass over 16384 tokens,
+                       384 and 256 routed experts, tau 0.5, buckets 3..6
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -74,7 +76,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "topk", "schedule", "prefill", "copy"])
+                   choices=["decode", "topk", "schedule", "prefill", "experts", "copy"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
     p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
@@ -633,6 +635,81 @@ def bench_prefill(args):
     layer.close()
 
 
+class _FREE_ENTRY_POINTS:
+    """Stands for the library's handle-free entry points in main_kernel_us."""
+    handle = None
+
+
+def bench_experts(args):
+    """Adaptive expert top-K: one call ranks the experts of 16384 tokens and picks
+    each token's K by routing-probability mass.  Algorithmic bytes per token:
+    the E fp32 probabilities read, plus K, kmax indices and kmax probabilities
+    written (4 + 8 kmax)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    T, tau, kmin, kmax = synth.EXPERT_T, synth.EXPERT_TAU, synth.EXPERT_KMIN, synth.EXPERT_KMAX
+    rows = []
+    main = None
+    for E in synth.EXPERT_E:
+        probs = synth.router_probs(T, E, seed=660 + E)
+        P0 = dev_tensor(probs)
+        # copies rotate so that the 256 MB Infinity Cache cannot hold them all
+        ncopy = -(-(320 << 20) // P0.numel() // 4)
+        Ps = [P0] + [P0.clone() for _ in range(ncopy - 1)]
+        k = torch.empty(T, dtype=torch.int32, device="cuda:0")
+        idx = torch.empty((T, kmax), dtype=torch.int32, device="cuda:0")
+        w = torch.empty((T, kmax), dtype=torch.float32, device="cuda:0")
+
+        def run(s0, n, Ps=Ps, k=k, idx=idx, w=w):
+            for i in range(s0, s0 + n):
+                sf.expert_select(Ps[i % len(Ps)], tau, kmin, kmax, k_out=k, idx_out=idx, w_out=w)
+        run(0, 8)
+        torch.cuda.synchronize()
+        us_graph = graph_time_us(run, max(args.steps // 16, 64), 16, 4)
+        # per-launch kernel time: start / stop events recorded by the kernel's own
+        # dispatch (the handle-free timer of the library)
+        kus = main_kernel_us([_FREE_ENTRY_POINTS], run, 32)
+        kmean = float(k.float().mean().item())
+        bytes_alg = T * (4 * E + 4 + 8 * kmax)
+        r = dict(experts=E, copies=ncopy, us_per_call=round(us_graph, 2), kernel_us=round(kus, 2),
+                 tokens_per_s=round(T / us_graph * 1e6, 0), gbs=round(bytes_alg / kus / 1e3, 1),
+                 mean_k=round(kmean, 4), bucket_counts=np.bincount(k.cpu().numpy(), minlength=kmax + 1)[kmin:].tolist())
+        rows.append(r)
+        log("E %d: %.2f us per call (%.2f us kernel, %.0f GB/s), mean K %.3f"
+            % (E, us_graph, kus, r["gbs"], kmean))
+        if main is None:
+            main = (r, bytes_alg, kus, probs)
+    r, bytes_alg, kus, probs = main
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        n = T
+        t1 = time.time()
+        reps = 0
+        while True:
+            oracle.expert_select(probs[:n], tau, kmin, kmax)
+            reps += 1
+            if time.time() - t1 > 10.0 or reps >= 32:
+                break
+        dt = (time.time() - t1) / reps
+        cpu = {"value": round(n / dt, 0), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "all %d tokens at E = %d, %d oracle call(s), single thread (qsort per token)"
+                         % (n, synth.EXPERT_E[0], reps)}
+    roof = {"bound": "hbm", "achieved": round(bytes_alg / kus / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(bytes_alg / kus / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_expert_select<6> (one wave per token)", "kernel_us": round(kus, 3),
+            "bytes_per_launch": bytes_alg}
+    cfg = {"workload": "adaptive expert top-K by routing mass, 16384 tokens, tau 0.5, buckets 3..6; value at "
+                       "384 routed experts", "results": rows}
+    out = line("tokens/s of adaptive expert top-K (one call over a 16384-token batch)", r["tokens_per_s"],
+               "tokens/s", max(args.steps // 16, 64), 8, round(r["us_per_call"] / 1e3, 5), "f32", cfg, roof, cpu)
+    print(json.dumps(out), flush=True)
+
+
 # ---------------------------------------------------------------------------
 # counter calibration: a plain device-to-device copy of known size
 # ---------------------------------------------------------------------------
@@ -667,7 +744,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
-     "prefill": bench_prefill, "copy": bench_copy}[args.workload](args)
+     "prefill": bench_prefill, "experts": bench_experts, "copy": bench_copy}[args.workload](args)
 
 
 if __name__ == "__main__":

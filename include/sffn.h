@@ -206,6 +206,40 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
 /* Frees the host-side handle (the persistent buffer stays the caller's). */
 void sffn_destroy(sffn_t layer);
 
+/*
+ * Adaptive expert top-K (RedKnot article, section on adaptive expert top-K:
+ * the routing-probability mass decides how many experts a token activates,
+ * threshold 0.50 over the candidate buckets 3..6; the per-depth schedule
+ * 6 / 5 / 4 caps the largest bucket).
+ *  tau   mass threshold (fp32 compare)
+ *  kmin  smallest bucket, >= 1
+ *  kmax  largest bucket, kmin..min(16, experts)
+ */
+typedef struct sffn_expert_policy {
+    float tau;
+    int32_t kmin;
+    int32_t kmax;
+    int32_t reserved;
+} sffn_expert_policy;
+
+/*
+ * For every token t: rank the experts of probs[t][0..experts) by (probability
+ * desc, index asc); c_b = the fp32 sum of the b top-ranked probabilities added
+ * in rank order; K = the smallest b in [kmin, kmax] with c_b >= tau, else kmax.
+ *  probs    device fp32 [tokens][experts], router probabilities, finite (NaN
+ *           ranks unspecified; -0 ties with +0), 1 <= experts <= 1024
+ *  k_out    device int32 [tokens]: K
+ *  idx_out  device int32 [tokens][kmax]: the K experts in rank order, then -1
+ *  w_out    device fp32 [tokens][kmax]: their probabilities as stored, then 0
+ *  One wave per token; outputs are owned by the caller and fully written.
+ * No handle and no workspace; asynchronous on `stream`; tokens = 0 is a no-op.
+ * Errors: SFFN_ERR_INVALID_ARG for a null pointer, tokens < 0, experts out of
+ * range or a bad policy (checked before any launch).
+ */
+sffn_status sffn_expert_select(const float *probs, int32_t tokens, int32_t experts,
+                               const sffn_expert_policy *policy, int32_t *k_out, int32_t *idx_out,
+                               float *w_out, void *stream);
+
 /* Static text for a status code. */
 const char *sffn_status_string(sffn_status status);
 
@@ -221,6 +255,8 @@ const char *sffn_last_hip_error(void);
  * kernel's own execution; later calls record nothing.  The
  * arrays are host memory and must stay valid until those n calls are made.
  * n = 0 disarms.  Not thread-safe: do not arm a handle used by two threads.
+ * layer = NULL arms the same timing, process-wide, for the entry points that
+ * take no handle (sffn_expert_select and its one kernel).
  */
 sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events,
                                   int32_t n);

@@ -259,3 +259,32 @@ def cfg5_activations(L=CFG5_L, d=CFG5_D):
     r = np.exp(normal_f32(553, (L,)).astype(np.float64)).astype(np.float32)
     a = f32_to_bf16_bits(eps * r[:, None])
     return y, a
+
+
+# ---------------------------------------------------------------------------
+# adaptive expert top-K: router probabilities
+# ---------------------------------------------------------------------------
+
+EXPERT_E = (384, 256)             # routed experts (Pro / Flash models of the RedKnot article)
+EXPERT_T = 16384                  # tokens per call: one prefill-sized batch
+EXPERT_TAU, EXPERT_KMIN, EXPERT_KMAX = 0.5, 3, 6
+EXPERT_DEPTH_KMAX = ((0, 15, 6), (16, 39, 5), (40, 60, 4))   # progressive per-depth cap
+
+
+def router_probs(T=EXPERT_T, E=EXPERT_E[0], seed=601):
+    """Router probabilities [T, E] fp32: per token a softmax over E of s_t * z_tj
+    with z ~ N(0, 1) and a sharpness s_t log-uniform on [2, 4], so that some
+    tokens put most of their mass on a few experts and others spread it (the
+    mass-0.5 rule then picks every bucket 3..6).  Softmax in float64, stored
+    fp32 with round-to-nearest-even."""
+    rng = np.random.default_rng(seed)
+    s = np.exp(rng.uniform(math.log(2.0), math.log(4.0), T))
+    out = np.empty((T, E), dtype=np.float32)
+    step = max(1, _CHUNK_ELEMS // max(E, 1))
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        z = rng.standard_normal((t1 - t0, E)) * s[t0:t1, None]
+        z -= z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        out[t0:t1] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return out

@@ -98,3 +98,33 @@ def test_status_strings():
     assert sf.sffn_status_string(0) == "ok"
     assert sf.sffn_status_string(3) == "workspace too small"
     assert sf.sffn_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("T,E,tau,kmin,kmax,ptrs,status", [
+    (0, 384, 0.5, 3, 6, False, 0),            # no tokens: nothing to do, no pointer needed
+    (4, 384, 0.5, 3, 6, False, 1),            # tokens without buffers
+    (-1, 384, 0.5, 3, 6, True, 1),
+    (4, 0, 0.5, 1, 1, True, 1),
+    (4, 1025, 0.5, 3, 6, True, 1),            # more experts than one wave holds
+    (4, 384, 0.5, 0, 6, True, 1),             # kmin < 1
+    (4, 384, 0.5, 4, 3, True, 1),             # kmin > kmax
+    (4, 5, 0.5, 3, 6, True, 1),               # kmax > experts
+    (4, 384, 0.5, 3, 17, True, 1),            # kmax above the per-token limit
+    (4, 384, float("nan"), 3, 6, True, 1),
+])
+def test_expert_select_validation(T, E, tau, kmin, kmax, ptrs, status):
+    import activation_sparse_gated_gate_amd as sf
+    fake = (1 << 20) if ptrs else None   # never dereferenced: validation fails first
+    pol = sf.ExpertPolicy(tau, kmin, kmax, 0)
+    if status == 0:
+        assert sf.sffn_expert_select(fake, T, E, pol, fake, fake, fake, None) == 0
+    else:
+        assert sf.sffn_expert_select(fake, T, E, pol, fake, fake, fake, None) == sf.SFFN_ERR_INVALID_ARG
+
+
+def test_expert_select_rejects_null_policy():
+    import activation_sparse_gated_gate_amd as sf
+    lib = C.CDLL(sf.LIB_PATH)
+    lib.sffn_expert_select.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p]
+    assert lib.sffn_expert_select(None, 0, 384, None, None, None, None, None) == sf.SFFN_ERR_INVALID_ARG
