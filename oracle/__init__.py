@@ -68,6 +68,10 @@ def _load():
     lib.ora_token_select.argtypes = [P, I, D, I, I, P, P, P]
     lib.ora_token_select.restype = I
     lib.ora_prefill_rows.argtypes = [I, I, P, P, P, P, P, I, P, I]
+    lib.ora_block_select.argtypes = [P, I, P, I, I, D, F, F, I, I, P]
+    lib.ora_block_select.restype = I
+    lib.ora_schedule_mass.argtypes = [I, I, I, D, D]
+    lib.ora_schedule_mass.restype = D
     lib.ora_expert_select.argtypes = [P, I, I, F, I, I, P, P, P]
     lib.ora_expert_select.restype = I
     lib.ora_prefill_rows.restype = None
@@ -198,6 +202,25 @@ def token_select(s, mass, recent_n=128, min_keep=1):
     if n < 0:
         raise ValueError("oracle token_select rejected its arguments")
     return keep[:n].copy(), order[:L].copy(), cum[:L].copy()
+
+
+def block_select(s, cu_seqlens, block=128, mass=0.5, min_full=0.10, max_full=0.50, recent_n=128, min_keep=1):
+    """Block-granular token selection over sequences [cu[q], cu[q+1]): the kept
+    token indices in ascending order (see ora_block_select)."""
+    s = _c(s, np.float32)
+    cu = _c(cu_seqlens, np.int32)
+    rows = s.size
+    keep = np.empty(max(rows, 1), dtype=np.int32)
+    n = _load().ora_block_select(_p(s), rows, _p(cu), cu.size - 1, int(block), float(mass),
+                                 float(min_full), float(max_full), int(recent_n), int(min_keep), _p(keep))
+    if n < 0:
+        raise ValueError("oracle block_select rejected its arguments")
+    return keep[:n].copy()
+
+
+def schedule_mass(layer, dense_until, deep_layer_start, mass_thresh, mass_thresh_deep) -> float:
+    return float(_load().ora_schedule_mass(int(layer), int(dense_until), int(deep_layer_start),
+                                           float(mass_thresh), float(mass_thresh_deep)))
 
 
 def expert_select(probs, tau=0.5, kmin=3, kmax=6):

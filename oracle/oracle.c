@@ -30,6 +30,13 @@
  *    mass in descending order; the last recent_n tokens always kept; at least
  *    min_keep tokens; an all-zero score row or mass >= 1 means dense;
  *    X_next = Y + Z with Z = FFN(Y) on the kept rows and 0 elsewhere.
+ *  - Block-granular token selection over a batch of sequences (RedKnot
+ *    article, section on token-selective sparse FFN: at least min_keep tokens
+ *    per sequence; and the closing paragraph of the section on adaptive expert
+ *    top-K: bounds min_full_ratio / max_full_ratio on the kept fraction and a
+ *    fixed-budget top-K over 128-token blocks, so the kept rows form a few
+ *    contiguous runs).  The three-tier layer schedule of the same section
+ *    (dense_until, deep_layer_start, mass_thresh_deep) picks each layer's mass.
  *  - Adaptive expert top-K (RedKnot article, section on adaptive expert top-K):
  *    per token, rank the routed experts by routing probability and keep the
  *    smallest bucket of the top-ranked experts whose probability mass reaches
@@ -55,6 +62,10 @@
  *       sequential inside a block, block totals summed sequentially.
  *   C8  the expert cumulative mass is fp32, summed sequentially in rank order
  *       from the top-ranked expert.
+ *   C9  block masses are fp64: the fp32 token scores of a block added in token
+ *       order; the cumulative block mass is fp64, sequential in rank order.
+ *       The block-count bounds are fp32 products: ceilf(nb * min_full_ratio),
+ *       floorf(nb * max_full_ratio).
  *
  * Build: plain C99, -O2 -ffp-contract=off, no fast-math, optional OpenMP over
  * tokens / rows.
@@ -505,6 +516,117 @@ int ora_token_select(const float *s, int L, double mass, int recent_n, int min_k
     if (cum_out) memcpy(cum_out, cum, sizeof(double) * (size_t)L);
     free(t); free(cum); free(in);
     return n;
+}
+
+/*
+ * Block-granular token selection (RedKnot article: min_keep per sequence in
+ * the section on token-selective sparse FFN; the token-level bounds and the
+ * fixed-budget selection of 128-token blocks in the last paragraph of the
+ * section on adaptive expert top-K).  The pages give the parts, not their
+ * order; this is the plainest composition, the block analogue of
+ * ora_token_select.  Sequence q holds tokens [cu[q], cu[q+1]); its nb blocks
+ * of `block` consecutive tokens start at the sequence start (the last may be
+ * short).  Per sequence:
+ *   S_b   = sum of the block's scores (C9), blocks ranked by (S_b desc, b asc);
+ *   c_k   = sum of the k top-ranked S_b (C9), total = c_nb;
+ *   mass >= 1 or total == 0: every block;
+ *   else K = smallest k with c_k >= mass * total (0 if mass <= 0), then
+ *        K = max(min(K, floorf(nb * max_full)), ceilf(nb * min_full))
+ *        (the lower bound wins when rounding crosses them), the top K blocks,
+ *        plus every block holding one of the last recent_n tokens, plus
+ *        further blocks in rank order while fewer than min(min_keep, Lq)
+ *        tokens are kept.
+ * keep receives the kept token indices of all sequences in ascending order;
+ * returns their number, or -1 on bad arguments.
+ */
+typedef struct { double m; int b; } block_rank;
+
+static int cmp_block(const void *a, const void *b)
+{
+    const block_rank *x = (const block_rank *)a, *y = (const block_rank *)b;
+    if (x->m != y->m) return x->m > y->m ? -1 : 1;
+    return x->b < y->b ? -1 : (x->b > y->b ? 1 : 0);
+}
+
+int ora_block_select(const float *s, int rows, const int32_t *cu, int nseq, int block, double mass,
+                     float min_full, float max_full, int recent_n, int min_keep, int32_t *keep)
+{
+    if (rows < 0 || nseq < 1 || block < 1 || recent_n < 0 || min_keep < 0) return -1;
+    if (!(min_full >= 0.0f && max_full <= 1.0f && min_full <= max_full)) return -1;
+    if (cu[0] != 0 || cu[nseq] != rows) return -1;
+    for (int q = 0; q < nseq; ++q)
+        if (cu[q + 1] < cu[q]) return -1;
+    int n = 0;
+    for (int q = 0; q < nseq; ++q) {
+        const int o0 = cu[q], Lq = cu[q + 1] - cu[q];
+        if (Lq == 0) continue;
+        const int nb = (Lq + block - 1) / block;
+        block_rank *r = (block_rank *)malloc(sizeof(block_rank) * (size_t)nb);
+        uint8_t *in = (uint8_t *)calloc((size_t)nb, 1);
+        if (!r || !in) { free(r); free(in); return -1; }
+        for (int b = 0; b < nb; ++b) {
+            const int t1 = (b + 1) * block < Lq ? (b + 1) * block : Lq;
+            double m = 0.0;
+            for (int t = b * block; t < t1; ++t) m = m + (double)s[o0 + t];
+            r[b].m = m;
+            r[b].b = b;
+        }
+        qsort(r, (size_t)nb, sizeof(block_rank), cmp_block);
+        double total = 0.0;
+        for (int k = 0; k < nb; ++k) total = total + r[k].m;
+        if (mass >= 1.0 || total == 0.0) {
+            for (int b = 0; b < nb; ++b) in[b] = 1;
+        } else {
+            int K = 0;
+            if (mass > 0.0) {
+                const double thr = mass * total;
+                double c = 0.0;
+                while (K < nb) {
+                    c = c + r[K].m;
+                    ++K;
+                    if (c >= thr) break;
+                }
+            }
+            const int lo = (int)ceilf((float)nb * min_full);
+            const int hi = (int)floorf((float)nb * max_full);
+            if (K > hi) K = hi;
+            if (K < lo) K = lo;
+            for (int k = 0; k < K; ++k) in[r[k].b] = 1;
+            if (recent_n > 0) {
+                const int first = (Lq - recent_n > 0 ? Lq - recent_n : 0) / block;
+                for (int b = first; b < nb; ++b) in[b] = 1;
+            }
+            const int need = min_keep < Lq ? min_keep : Lq;
+            int kept = 0;
+            for (int b = 0; b < nb; ++b)
+                if (in[b]) kept += ((b + 1) * block < Lq ? block : Lq - b * block);
+            for (int k = 0; k < nb && kept < need; ++k)
+                if (!in[r[k].b]) {
+                    const int b = r[k].b;
+                    in[b] = 1;
+                    kept += ((b + 1) * block < Lq ? block : Lq - b * block);
+                }
+        }
+        for (int t = 0; t < Lq; ++t)
+            if (in[t / block]) keep[n++] = o0 + t;
+        free(r);
+        free(in);
+    }
+    return n;
+}
+
+/*
+ * Three-tier layer schedule (RedKnot article, section on token-selective
+ * sparse FFN, the schedule table): layers below dense_until run dense (mass
+ * 1), layers from dense_until up to deep_layer_start use mass_thresh, deeper
+ * layers mass_thresh_deep.
+ */
+double ora_schedule_mass(int layer, int dense_until, int deep_layer_start, double mass_thresh,
+                         double mass_thresh_deep)
+{
+    if (layer < dense_until) return 1.0;
+    if (layer < deep_layer_start) return mass_thresh;
+    return mass_thresh_deep;
 }
 
 /*

@@ -581,3 +581,103 @@ def test_expert_select_kept_experts_dominate_and_counts_follow_mass():
         # sharper routing (more mass in the top experts) never asks for more experts
     top3 = np.sort(p, axis=1)[:, ::-1][:, :3].sum(axis=1)
     assert k[top3 >= 0.5].max() == 3
+
+
+# ---------------------------------------------------------------------------
+# block-granular token selection and the layer schedule
+# ---------------------------------------------------------------------------
+
+def test_block_select_page_parameters():
+    g = json.load(open(GOLDEN))["token_block_selection"]
+    assert (g["block_tokens"], g["min_full_ratio"], g["max_full_ratio"]) == (128, 0.10, 0.50)
+    assert g["min_keep_per_sequence"] >= 1
+
+
+def test_block_select_hand_worked():
+    s = np.arange(1, 9, dtype=np.float32)          # blocks of 2: masses 3, 7, 11, 15; total 36
+    kw = dict(block=2, min_full=0.0, max_full=1.0, recent_n=0, min_keep=0)
+    assert list(oracle.block_select(s, [0, 8], mass=0.5, **kw)) == [4, 5, 6, 7]        # 15 + 11 >= 18
+    assert list(oracle.block_select(s, [0, 8], mass=0.4, **kw)) == [6, 7]              # 15 >= 14.4
+    assert list(oracle.block_select(s, [0, 8], mass=0.42, **kw)) == [4, 5, 6, 7]       # 15 < 15.12
+    assert oracle.block_select(s, [0, 8], mass=0.0, **kw).size == 0
+    kw_recent = dict(kw, recent_n=1)                                                   # last token's block
+    assert list(oracle.block_select(s, [0, 8], mass=0.0, **kw_recent)) == [6, 7]
+    assert list(oracle.block_select(s, [0, 8], mass=0.0, **dict(kw, min_keep=3))) == [4, 5, 6, 7]
+    # ragged last block: [1,2,3] [4,5,6] [7] -> masses 6, 15, 7
+    s7 = np.arange(1, 8, dtype=np.float32)
+    assert list(oracle.block_select(s7, [0, 7], block=3, mass=0.6, min_full=0.0, max_full=1.0,
+                                    recent_n=0, min_keep=0)) == [3, 4, 5, 6]           # 15 + 7 >= 16.8
+
+
+def test_block_select_bounds_and_their_fp32_rounding():
+    L, B = 1280, 128                                # nb = 10
+    s = np.ones(L, dtype=np.float32)
+    kw = dict(block=B, recent_n=0, min_keep=0)
+    # mass 0: the lower bound alone, ceilf(10 * 0.1f) = 1 (an fp64 product would give 2)
+    assert oracle.block_select(s, [0, L], mass=0.0, min_full=0.1, max_full=0.5, **kw).size == B
+    # equal masses: K = ceil(10 * mass) blocks, ties to the lower block index
+    k = oracle.block_select(s, [0, L], mass=0.35, min_full=0.1, max_full=0.5, **kw)
+    assert list(k) == list(range(4 * B))
+    # the upper bound: 0.99 would need 10 blocks, capped at floor(10 * 0.5) = 5
+    assert oracle.block_select(s, [0, L], mass=0.99, min_full=0.1, max_full=0.5, **kw).size == 5 * B
+    # bounds that cross after rounding: nb = 3, ceilf(1.2) = 2 > floorf(1.5) = 1, the lower one wins
+    s3 = np.ones(3 * B, dtype=np.float32)
+    assert oracle.block_select(s3, [0, 3 * B], mass=0.0, min_full=0.4, max_full=0.5, **kw).size == 2 * B
+    # mass >= 1 and all-zero scores are dense, whatever the upper bound
+    assert oracle.block_select(s, [0, L], mass=1.0, min_full=0.1, max_full=0.5, **kw).size == L
+    assert oracle.block_select(np.zeros(L, np.float32), [0, L], mass=0.3, min_full=0.1, max_full=0.5,
+                               **kw).size == L
+    with pytest.raises(ValueError):
+        oracle.block_select(s, [0, L], min_full=0.6, max_full=0.5)
+    with pytest.raises(ValueError):
+        oracle.block_select(s, [0, L - 1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_block_select_with_one_token_blocks_is_token_select(seed):
+    # block = 1, no bounds: block masses are the token scores and the cumulative
+    # mass is sequential; for L <= 256 the token path's blocked sum is that same
+    # sequence, so both selections must agree exactly
+    rng = np.random.default_rng(900 + seed)
+    L = int(rng.integers(1, 257))
+    s = rng.integers(0, 6, size=L).astype(np.float32) * np.float32(0.25) if seed % 2 else \
+        rng.random(L).astype(np.float32)
+    for mass in (0.0, 0.3, 0.7, 1.0):
+        for recent, mk in ((0, 0), (5, 1), (0, 40)):
+            a = oracle.block_select(s, [0, L], block=1, mass=mass, min_full=0.0, max_full=1.0,
+                                    recent_n=recent, min_keep=mk)
+            b, _, _ = oracle.token_select(s, mass, recent, mk)
+            assert np.array_equal(a, b), (L, mass, recent, mk)
+
+
+def test_block_select_sequences_are_independent_and_runs_are_few():
+    rng = np.random.default_rng(950)
+    lens = [0, 1, 127, 128, 129, 700, 5000, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    s = (np.exp(rng.standard_normal(cu[-1])) * rng.random(cu[-1])).astype(np.float32)
+    kw = dict(block=128, mass=0.5, min_full=0.1, max_full=0.5, recent_n=128, min_keep=1)
+    whole = oracle.block_select(s, cu, **kw)
+    parts = [oracle.block_select(s[cu[q]:cu[q + 1]], [0, lens[q]], **kw) + cu[q] for q in range(len(lens))]
+    assert np.array_equal(whole, np.concatenate(parts))
+    for q, Lq in enumerate(lens):
+        mine = whole[(whole >= cu[q]) & (whole < cu[q + 1])] - cu[q]
+        if Lq:
+            assert mine.size >= 1                                  # min_keep per sequence
+            assert Lq - 1 in mine                                   # the recent tail
+        nb = -(-Lq // 128)
+        blocks = np.unique(mine // 128)
+        assert all(np.array_equal(mine[mine // 128 == b], np.arange(b * 128, min(b * 128 + 128, Lq)))
+                   for b in blocks)                                 # whole blocks only
+        if nb >= 10:
+            assert blocks.size <= math.floor(nb * 0.5) + 2          # budget + recent blocks
+
+
+def test_layer_schedule_tiers_and_presets():
+    g = json.load(open(GOLDEN))["ffn_layer_schedule"]
+    du, mt, rn = g["presets"]["balanced"]
+    assert (du, mt, rn) == (20, 0.5, 128)
+    assert [oracle.schedule_mass(l, du, 40, mt, 0.2) for l in (0, 19, 20, 39, 40, 63)] == \
+        [1.0, 1.0, 0.5, 0.5, 0.2, 0.2]
+    # the dense preset keeps every layer of an 80-layer model dense
+    du, mt, _ = g["presets"]["dense"]
+    assert all(oracle.schedule_mass(l, du, du, mt, mt) == 1.0 for l in range(80))
