@@ -28,7 +28,8 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
          "tokens": MODE_TOKENS, "dense": MODE_DENSE}
 
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
-           "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select")
+           "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
+           "sffn_select_blocks", "sffn_schedule_mass")
 
 
 class LayerDesc(C.Structure):
@@ -45,6 +46,11 @@ class Policy(C.Structure):
 
 class ExpertPolicy(C.Structure):
     _fields_ = [("tau", C.c_float), ("kmin", C.c_int32), ("kmax", C.c_int32), ("reserved", C.c_int32)]
+
+
+class BlockPolicy(C.Structure):
+    _fields_ = [("mass_thresh", C.c_double), ("min_full_ratio", C.c_float), ("max_full_ratio", C.c_float),
+                ("block", C.c_int32), ("recent_n", C.c_int32), ("min_keep", C.c_int32), ("reserved", C.c_int32)]
 
 
 class SffnError(RuntimeError):
@@ -80,6 +86,10 @@ def _load():
     lib.sffn_last_hip_error.argtypes = []
     lib.sffn_last_hip_error.restype = C.c_char_p
     lib.sffn_set_kernel_timer.argtypes = [P, P, P, I]
+    lib.sffn_select_blocks.restype = I
+    lib.sffn_select_blocks.argtypes = [P, C.POINTER(BlockPolicy), P, I, P, I, P, P, P, Z, P]
+    lib.sffn_schedule_mass.restype = C.c_double
+    lib.sffn_schedule_mass.argtypes = [I, I, I, C.c_double, C.c_double]
     lib.sffn_expert_select.restype = I
     lib.sffn_expert_select.argtypes = [P, I, I, C.POINTER(ExpertPolicy), P, P, P, P]
     lib.sffn_set_kernel_timer.restype = I
@@ -125,6 +135,23 @@ def sffn_forward(handle, policy, inp, rows, out, idx_in, count_in, idx_out, coun
 
 def sffn_destroy(handle) -> None:
     _lib.sffn_destroy(handle)
+
+
+def sffn_select_blocks(handle, policy, A, rows, cu_seqlens, nseq, idx_out, count_out, scratch, scratch_bytes,
+                       stream) -> int:
+    return _lib.sffn_select_blocks(handle, C.byref(policy), A, int(rows), cu_seqlens, int(nseq), idx_out,
+                                   count_out, scratch, scratch_bytes, stream)
+
+
+def sffn_schedule_mass(layer, dense_until, deep_layer_start, mass_thresh, mass_thresh_deep) -> float:
+    return float(_lib.sffn_schedule_mass(int(layer), int(dense_until), int(deep_layer_start), float(mass_thresh),
+                                         float(mass_thresh_deep)))
+
+
+def make_block_policy(mass_thresh=0.5, min_full_ratio=0.10, max_full_ratio=0.50, block=128, recent_n=128,
+                      min_keep=1) -> BlockPolicy:
+    return BlockPolicy(float(mass_thresh), float(min_full_ratio), float(max_full_ratio), int(block), int(recent_n),
+                       int(min_keep), 0)
 
 
 def sffn_expert_select(probs, tokens, experts, policy, k_out, idx_out, w_out, stream) -> int:
@@ -211,6 +238,13 @@ class Layer:
                          self._stream(stream))
         if st != SFFN_OK:
             raise SffnError(st, "sffn_select")
+
+    def select_blocks(self, policy: BlockPolicy, A, cu_seqlens, idx_out, count_out, stream=None):
+        st = sffn_select_blocks(self.handle, policy, A.data_ptr(), A.shape[0], cu_seqlens.data_ptr(),
+                                cu_seqlens.shape[0] - 1, idx_out.data_ptr(), count_out.data_ptr(),
+                                self.scratch.data_ptr(), self.scratch_bytes, self._stream(stream))
+        if st != SFFN_OK:
+            raise SffnError(st, "sffn_select_blocks")
 
     def forward(self, policy: Policy, inp, out, idx_in=None, count_in=None, idx_out=None,
                 count_out=None, stream=None):

@@ -288,6 +288,36 @@ sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in,
     return hip_status(launch_decode(c, false));
 }
 
+sffn_status sffn_select_blocks(sffn_t layer, const sffn_block_policy *policy, const void *A, int32_t rows,
+                               const int32_t *cu_seqlens, int32_t nseq, int32_t *idx_out, int32_t *count_out,
+                               void *scratch, size_t scratch_bytes, void *stream)
+{
+    if (!layer || !policy || !A || !cu_seqlens || !idx_out || !count_out || !scratch) return SFFN_ERR_INVALID_ARG;
+    const sffn_layer_desc &D = layer->L.desc;
+    if (!(D.layouts & SFFN_LAYOUT_PREFILL)) return SFFN_ERR_INVALID_ARG;
+    if (rows < 1 || rows > D.max_rows || nseq < 1 || nseq > rows) return SFFN_ERR_INVALID_ARG;
+    const sffn_block_policy &p = *policy;
+    if (p.block < kMinTokenBlock || p.block > kMaxPrefillRows) return SFFN_ERR_INVALID_ARG;
+    if (!(p.mass_thresh == p.mass_thresh)) return SFFN_ERR_INVALID_ARG;   // NaN
+    if (!(p.min_full_ratio >= 0.0f && p.max_full_ratio <= 1.0f && p.min_full_ratio <= p.max_full_ratio))
+        return SFFN_ERR_INVALID_ARG;
+    if (p.recent_n < 0 || p.min_keep < 0) return SFFN_ERR_INVALID_ARG;
+    if (((uintptr_t)scratch & 255) || ((uintptr_t)A & 15)) return SFFN_ERR_INVALID_ARG;
+    if (scratch_bytes < scratch_layout(D).total) return SFFN_ERR_WORKSPACE;
+    BlockSelectCall c{&layer->L, (const uint16_t *)A, rows, cu_seqlens, nseq, p.block, p.mass_thresh,
+                      p.min_full_ratio, p.max_full_ratio, p.recent_n, p.min_keep, idx_out, count_out,
+                      (uint8_t *)scratch, (hipStream_t)stream};
+    return hip_status(launch_block_select(c));
+}
+
+double sffn_schedule_mass(int32_t layer, int32_t dense_until, int32_t deep_layer_start, double mass_thresh,
+                          double mass_thresh_deep)
+{
+    if (layer < dense_until) return 1.0;
+    if (layer < deep_layer_start) return mass_thresh;
+    return mass_thresh_deep;
+}
+
 sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows, void *out,
                          const int32_t *idx_in, const int32_t *count_in, int32_t *idx_out, int32_t *count_out,
                          void *scratch, size_t scratch_bytes, void *stream)

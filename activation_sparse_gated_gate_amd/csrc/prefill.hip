@@ -644,6 +644,12 @@ __global__ __launch_bounds__(256) void k_copy_unkept(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_token_norms(const uint16_t *A, int rows, int d, float *s, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, st, A, rows, d, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_select(const PrefillSelectCall &c)
 {
     const Layer &L = *c.L;

@@ -127,6 +127,27 @@ struct PrefillSelectCall {
     hipStream_t stream;
 };
 hipError_t launch_prefill_select(const PrefillSelectCall &c);
+// t1 alone: s_i = ||A_i||_2 for rows bf16 rows of d_model d
+hipError_t launch_token_norms(const uint16_t *A, int rows, int d, float *s, hipStream_t st);
+
+// block-granular token selection over a batch of sequences (blocks.hip)
+constexpr int kMinTokenBlock = 16;
+constexpr int kMaxBlocksPerSeq = (kMaxPrefillRows + kMinTokenBlock - 1) / kMinTokenBlock;   // 1024
+struct BlockSelectCall {
+    const Layer *L;
+    const uint16_t *A;
+    int rows;
+    const int32_t *cu;   // device [nseq + 1]
+    int nseq;
+    int block;
+    double mass;
+    float min_full, max_full;
+    int recent_n, min_keep;
+    int32_t *idx_out, *count_out;
+    uint8_t *scratch;
+    hipStream_t stream;
+};
+hipError_t launch_block_select(const BlockSelectCall &c);
 // adaptive expert top-K (experts.hip)
 constexpr int kMaxExpertsAbi = 1024;
 constexpr int kMaxExpertKAbi = 16;

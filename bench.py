@@ -45,9 +45,13 @@ METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; break
 # files); after any change the figure is reported as null until the counters are taken again.
 COUNTER_TRAFFIC = {
     "k_decode_b1": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
-                    "sha256_16": "ea0e322d8543f882",
+                    "sha256_16": "da5dcc349138c0b5",
                     "workload": "a = 0.1, bf16 4096 x 11008, batch 1",
-                    "fetch_kib": 52947.21, "write_kib": 4180.75, "fetch_factor": 1.9998, "write_factor": 1.0},
+                    "fetch_kib": 52930.27, "write_kib": 4179.15, "fetch_factor": 1.9998, "write_factor": 1.0000},
+    "k_expert_select": {"sources": ("experts.hip", "dev_common.h", "sffn_internal.h"),
+                        "sha256_16": "c3290f4643503ce3",
+                        "workload": "16384 tokens x 384 experts, tau 0.5, buckets 3..6",
+                        "fetch_kib": 12305.71, "write_kib": 896.26, "fetch_factor": 1.9998, "write_factor": 1.0000},
 }
 
 
@@ -595,6 +599,36 @@ def bench_prefill(args):
     dense_ms = rows[-1]["ffn_ms"]
     for r in rows:
         r["speedup_vs_mass1"] = round(dense_ms / r["ffn_ms"], 3)
+    # block-granular selection (128-token blocks, kept fraction bounded to
+    # [0.10, 0.50]) over the same activations, one sequence and a varlen batch
+    cu_sets = {"1 sequence": [0, L], "7 sequences": [0, 8192, 12288, 14336, 15360, 15872, 16383, 16384]}
+    brows = []
+    for name, cu in cu_sets.items():
+        cut = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+        for mass in synth.CFG5_MASS:
+            bpol = sf.make_block_policy(mass, 0.10, 0.50, 128, synth.CFG5_RECENT, synth.CFG5_MIN_KEEP)
+            layer.select_blocks(bpol, Ad, cut, keep, cnt)
+            torch.cuda.synchronize()
+            M = int(cnt.item())
+
+            def bsel(s0, n, bpol=bpol, cut=cut):
+                for _ in range(n):
+                    layer.select_blocks(bpol, Ad, cut, keep, cnt)
+            us_bsel = graph_time_us(bsel, 32, 8, 1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            t_ffn = []
+            for _ in range(reps):
+                ev[0].record()
+                layer.forward(fwd, Xd, Xd, idx_in=keep, count_in=cnt)
+                ev[1].record()
+                torch.cuda.synchronize()
+                t_ffn.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            us_ffn = float(np.median(t_ffn))
+            br = dict(batch=name, mass=mass, kept=M, kept_frac=round(M / L, 4), select_us=round(us_bsel, 2),
+                      ffn_ms=round(us_ffn / 1e3, 4), speedup_vs_mass1=round(dense_ms * 1e3 / us_ffn, 3))
+            brows.append(br)
+            log("blocks, %s, mass %.1f: kept %d, select %.1f us, FFN %.3f ms"
+                % (name, mass, M, br["select_us"], br["ffn_ms"]))
     pol = sf.make_policy("tokens", mass_thresh=0.5, recent_n=synth.CFG5_RECENT, min_keep=1)
     layer.select(pol, Ad, keep, cnt)
     torch.cuda.synchronize()
@@ -624,10 +658,11 @@ def bench_prefill(args):
                          "scaled to all kept rows" % (L, t_sel, n, k_ref.size, dt)}
     mid = rows[1]
     cfg = {"workload": "token-selective prefill FFN, d_model 5120, d_ff 25600, L 16384, bf16 SwiGLU, "
-                       "top-P mass with recent_n 128, min_keep 1; value at mass 0.5", "results": rows}
+                       "top-P mass with recent_n 128, min_keep 1; value at mass 0.5", "results": rows,
+           "block_selection": brows}
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "k_gemm<gate_up> (gathered rows x interleaved W_gate/W_up, SwiGLU epilogue)",
+            "kernel": "k_gemm_big<gate_up> (gathered rows x interleaved W_gate/W_up, SwiGLU epilogue)",
             "kernel_us": round(kus, 3), "flops_per_launch": fl}
     out = line("ms per prefill FFN layer & TFLOP/s vs mass", mid["tflops"], "TFLOP/s", reps, 1, mid["ffn_ms"],
                "bf16", cfg, roof, cpu)
@@ -700,7 +735,7 @@ def bench_experts(args):
                "sample": "all %d tokens at E = %d, %d oracle call(s), single thread (qsort per token)"
                          % (n, synth.EXPERT_E[0], reps)}
     roof = {"bound": "hbm", "achieved": round(bytes_alg / kus / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(bytes_alg / kus / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(bytes_alg / kus / 1e3 / HBM_PEAK_GBS, 4), "traffic": counter_traffic("k_expert_select"),
             "kernel": "k_expert_select<6> (one wave per token)", "kernel_us": round(kus, 3),
             "bytes_per_launch": bytes_alg}
     cfg = {"workload": "adaptive expert top-K by routing mass, 16384 tokens, tau 0.5, buckets 3..6; value at "

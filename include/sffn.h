@@ -203,6 +203,65 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
                          int32_t *idx_out, int32_t *count_out, void *scratch,
                          size_t scratch_bytes, void *stream);
 
+/*
+ * Block-granular token selection over a batch of sequences (RedKnot article:
+ * at least min_keep tokens per sequence, section on the token-selective sparse
+ * FFN; bounds min_full_ratio 0.10 / max_full_ratio 0.50 on the kept fraction
+ * and a fixed-budget top-K over blocks of 128 tokens so that the kept rows
+ * form a few contiguous runs, computed on the GPU without host
+ * synchronisation, last paragraph of the section on adaptive expert top-K).
+ *  mass_thresh     fraction of each sequence's block mass (fp64); >= 1 keeps all
+ *  min_full_ratio  lower bound, as a fraction of the sequence's blocks, 0..1
+ *  max_full_ratio  upper bound, min_full_ratio..1
+ *  block           tokens per block, 16..16384 (the pages use 128)
+ *  recent_n        trailing tokens of each sequence always kept (their blocks)
+ *  min_keep        minimum kept tokens per sequence
+ */
+typedef struct sffn_block_policy {
+    double mass_thresh;
+    float min_full_ratio;
+    float max_full_ratio;
+    int32_t block;
+    int32_t recent_n;
+    int32_t min_keep;
+    int32_t reserved;
+} sffn_block_policy;
+
+/*
+ * For each sequence q = [cu_seqlens[q], cu_seqlens[q+1]) of the rows tokens:
+ * scores s_i = ||A_i||_2 as for SFFN_MODE_TOKENS; blocks of `block` tokens
+ * from the sequence start (the last may be short), S_b = fp64 sum of the
+ * block's scores in token order; blocks ranked by (S_b desc, b asc); c_k =
+ * fp64 sum of the k top-ranked S_b in rank order.  mass >= 1 or c_nb = 0 keeps
+ * the whole sequence; otherwise K = the smallest k with c_k >= mass * c_nb (0
+ * when mass <= 0), then K = max(min(K, floorf(nb * max_full_ratio)),
+ * ceilf(nb * min_full_ratio)) in fp32; kept: the top K blocks, the blocks
+ * holding the last recent_n tokens, then further blocks in rank order until
+ * min(min_keep, length) tokens are kept.
+ *  A           device bf16 [rows][d_model], 16-byte aligned; the layer needs
+ *              SFFN_LAYOUT_PREFILL; 1 <= rows <= max_rows
+ *  cu_seqlens  device int32 [nseq + 1], 0 = cu[0] <= cu[1] <= ... <= cu[nseq] =
+ *              rows; 1 <= nseq <= rows (other contents are clamped to [0, rows]
+ *              and made non-decreasing, never read or written out of bounds)
+ *  idx_out     device int32, capacity rows: kept token indices, ascending
+ *              (sequence by sequence); count_out (device, one int32) their number
+ * Asynchronous on `stream`; no host synchronisation.  Errors: INVALID_ARG for
+ * a null pointer, a size or policy out of range or a layer without the prefill
+ * layout; WORKSPACE for a small scratch.
+ */
+sffn_status sffn_select_blocks(sffn_t layer, const sffn_block_policy *policy, const void *A, int32_t rows,
+                               const int32_t *cu_seqlens, int32_t nseq, int32_t *idx_out,
+                               int32_t *count_out, void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * Three-tier layer schedule (RedKnot article, section on the token-selective
+ * sparse FFN): the mass for layer `layer` is 1 (dense) below dense_until,
+ * mass_thresh below deep_layer_start and mass_thresh_deep from there on.
+ * Host only.
+ */
+double sffn_schedule_mass(int32_t layer, int32_t dense_until, int32_t deep_layer_start, double mass_thresh,
+                          double mass_thresh_deep);
+
 /* Frees the host-side handle (the persistent buffer stays the caller's). */
 void sffn_destroy(sffn_t layer);
 

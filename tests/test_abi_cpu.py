@@ -128,3 +128,25 @@ def test_expert_select_rejects_null_policy():
     lib.sffn_expert_select.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p]
     assert lib.sffn_expert_select(None, 0, 384, None, None, None, None, None) == sf.SFFN_ERR_INVALID_ARG
+
+
+def test_select_blocks_rejects_null_handle_and_policy():
+    import activation_sparse_gated_gate_amd as sf
+    fake = 1 << 20   # never dereferenced: validation fails first
+    pol = sf.make_block_policy()
+    assert sf.sffn_select_blocks(None, pol, fake, 16, fake, 1, fake, fake, fake, 1 << 20, None) == \
+        sf.SFFN_ERR_INVALID_ARG
+    lib = C.CDLL(sf.LIB_PATH)
+    lib.sffn_select_blocks.argtypes = [C.c_void_p] * 4 + [C.c_void_p, C.c_int32] + [C.c_void_p] * 3 + \
+        [C.c_size_t, C.c_void_p]
+    lib.sffn_select_blocks.argtypes[3] = C.c_int32
+    assert lib.sffn_select_blocks(fake, None, fake, 16, fake, 1, fake, fake, fake, 1 << 20, None) == \
+        sf.SFFN_ERR_INVALID_ARG
+
+
+def test_schedule_mass_matches_the_oracle():
+    import activation_sparse_gated_gate_amd as sf
+    import oracle
+    for du, deep in ((3, 40), (20, 40), (32, 48), (80, 80), (0, 0)):
+        for layer in range(0, 82, 3):
+            assert sf.sffn_schedule_mass(layer, du, deep, 0.5, 0.2) == oracle.schedule_mass(layer, du, deep, 0.5, 0.2)
