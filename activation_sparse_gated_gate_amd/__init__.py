@@ -41,7 +41,7 @@ class LayerDesc(C.Structure):
 class Policy(C.Structure):
     _fields_ = [("mode", C.c_int32), ("gate_bias", C.c_float), ("theta", C.c_float),
                 ("topk_k", C.c_int32), ("use_union", C.c_int32), ("recent_n", C.c_int32),
-                ("min_keep", C.c_int32), ("reserved", C.c_int32), ("mass_thresh", C.c_double)]
+                ("min_keep", C.c_int32), ("batch_path", C.c_int32), ("mass_thresh", C.c_double)]
 
 
 class ExpertPolicy(C.Structure):
@@ -186,11 +186,14 @@ def sffn_set_kernel_timer(handle, begin_events, end_events, n) -> int:
 # convenience wrapper over torch-owned memory
 # ---------------------------------------------------------------------------
 
+BATCH_PATH_AUTO, BATCH_PATH_TILED, BATCH_PATH_GATHER = 0, 1, 2
+
+
 def make_policy(mode="all", gate_bias=0.0, theta=0.0, topk_k=1, use_union=False, mass_thresh=1.0,
-                recent_n=0, min_keep=1) -> Policy:
+                recent_n=0, min_keep=1, batch_path=BATCH_PATH_AUTO) -> Policy:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     return Policy(m, float(gate_bias), float(theta), int(topk_k), int(bool(use_union)), int(recent_n),
-                  int(min_keep), 0, float(mass_thresh))
+                  int(min_keep), int(batch_path), float(mass_thresh))
 
 
 def _ptr(t):

@@ -82,6 +82,7 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         S.hsplit = take((size_t)2 * 16 * f * 2);   // h as bf16 hi / lo, 16 token slots
         // four partial gate sums per (token, neuron) of the row-per-lane gate kernel
         S.gpart = (D.layouts & SFFN_LAYOUT_BATCH) ? take((size_t)4 * B * f * 4) : 0;
+        S.path = (D.layouts & SFFN_LAYOUT_BATCH) ? take(256) : 0;   // the chosen forward path
     }
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         S.tscore = take(B * 4 * 2);   // scores and their sorted copy
@@ -259,6 +260,7 @@ static sffn_status policy_ok(const sffn_layer *h, const sffn_policy *p)
     if (!(D.layouts & SFFN_LAYOUT_DECODE)) return SFFN_ERR_INVALID_ARG;
     if (p->mode == SFFN_MODE_TOPK && (p->topk_k < 1 || p->topk_k > D.d_ff)) return SFFN_ERR_INVALID_ARG;
     if (p->use_union != 0 && p->use_union != 1) return SFFN_ERR_INVALID_ARG;
+    if (p->batch_path < 0 || p->batch_path > 2) return SFFN_ERR_INVALID_ARG;
     if (p->mode == SFFN_MODE_TOPK && D.act != SFFN_ACT_SILU) return SFFN_ERR_UNSUPPORTED;
     if (p->mode == SFFN_MODE_TOPK && D.d_ff > kMaxTopkNeurons) return SFFN_ERR_UNSUPPORTED;
     return SFFN_OK;
@@ -283,7 +285,7 @@ sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in,
         return hip_status(launch_prefill_select(c));
     }
     if ((uintptr_t)in & 15) return SFFN_ERR_INVALID_ARG;
-    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->gate_bias, policy->theta,
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->gate_bias, policy->theta,
                  rows, (const float *)in, nullptr, idx_out, count_out, (uint8_t *)scratch, st};
     return hip_status(launch_decode(c, false));
 }
@@ -340,7 +342,7 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
     if (idx_in || count_in) return SFFN_ERR_INVALID_ARG;
     if (in == out) return SFFN_ERR_INVALID_ARG;
     if (policy->mode == SFFN_MODE_DENSE && (idx_out || count_out)) return SFFN_ERR_INVALID_ARG;
-    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->gate_bias, policy->theta,
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->gate_bias, policy->theta,
                  rows, (const float *)in, (float *)out, idx_out, count_out, (uint8_t *)scratch, st};
     return hip_status(launch_decode(c, true));
 }

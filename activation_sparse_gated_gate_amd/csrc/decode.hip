@@ -33,6 +33,18 @@ enum { OUT_GATE = 0, OUT_GATE_UP = 1, OUT_DENSE_GU = 2, OUT_DENSE_DOWN = 3 };
 // ---------------------------------------------------------------------------
 // launch configuration per weight type and batch bucket
 // ---------------------------------------------------------------------------
+// Batched bf16 decode with the BATCH layout: the row gather reads only the
+// union's rows but its work per row grows with the batch, while the MFMA tiles
+// stream whole matrices at nearly the same cost for 5..16 tokens.  Union
+// fraction (per mille) below which the gather was measured faster, per batch
+// size, at 3584 x 18944 (a layer larger than the Infinity Cache): 5 tokens
+// about 0.25, 8 tokens about 0.18, 16 tokens never.
+static int gather_below_permille(int B)
+{
+    static const int t[17] = {0, 0, 0, 0, 0, 250, 220, 200, 180, 0, 0, 0, 0, 0, 0, 0, 0};
+    return B >= 0 && B <= 16 ? t[B] : 0;
+}
+
 template <int WT, int BT> struct Cfg {
     static constexpr int E = Chunk<WT>::E;
     // chunk-columns staged per slice: keeps x in LDS at <= 32 KB (64 KB int4 x 8)
@@ -485,6 +497,8 @@ struct GatherArgs {
     int32_t *idx_out, *count_out;
     int maxs;        // capacity of the share arrays
     int stage_x;     // 1: the up projection runs here (x slices in LDS)
+    const int *path; // run only when *path == want (nullptr: always)
+    int want;
 };
 
 // Share of the concatenated per-block lists for this workgroup: writes the
@@ -546,6 +560,7 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
     int *pref = jl + a.maxs;
     __shared__ int tmp[17];
 
+    if (a.path && *a.path != a.want) return;   // uniform, before any barrier
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int B = a.B, d = a.d, f = a.f;
     const int ns = share_of_lists(a.list_cnt, a.list_idx, a.nL, a.R, pref, jl, a.idx_out, a.count_out, tmp);
@@ -794,8 +809,9 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v)
 
 // one thread per lane slot of 8 values: (d/32) * 64 threads
 __global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ x, int B, int d, uint16_t *__restrict__ xh,
-                                                 uint16_t *__restrict__ xl)
+                                                 uint16_t *__restrict__ xl, const int *__restrict__ path, int want)
 {
+    if (path && *path != want) return;   // the other batched path was picked
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= (d / 32) * 64) return;
     const int s = i >> 6, l = i & 63, n = l & 15;
@@ -822,6 +838,8 @@ struct UpTiledArgs {
     int d, f, B, mode, act, use_union;
     float theta;
     uint16_t *hh, *hl;               // [f/32][64][8]
+    const int *path;                 // run only when *path == want (nullptr: always)
+    int want;
 };
 
 template <int U>
@@ -853,6 +871,7 @@ __device__ __forceinline__ f32x4_t mfma_stream(const uint16_t *__restrict__ w, c
 
 __global__ __launch_bounds__(64) void k_up_tiled(const UpTiledArgs a)
 {
+    if (a.path && *a.path != a.want) return;
     const int t = blockIdx.x, lane = threadIdx.x;
     const int cnt = a.list_cnt[t];
     uint32_t m = 0;
@@ -890,10 +909,13 @@ struct DownTiledArgs {
     const uint16_t *hh, *hl;         // [f/32][64][8]
     int d, f, per;                   // per: k-steps per split (multiple of 4)
     float *partial;                  // [splits][16][d]
+    const int *path;                 // run only when *path == want (nullptr: always)
+    int want;
 };
 
 __global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
 {
+    if (a.path && *a.path != a.want) return;
     const int t = blockIdx.x, p = blockIdx.y, lane = threadIdx.x;
     const int KS = a.f / 32;
     const int k0 = min(KS, p * a.per), k1 = min(KS, k0 + a.per);
@@ -905,8 +927,10 @@ __global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
 }
 
 __global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ partial, int ns, int B, int d,
-                                                  const float *__restrict__ resid, float *__restrict__ out)
+                                                  const float *__restrict__ resid, float *__restrict__ out,
+                                                  const int *__restrict__ path, int want)
 {
+    if (path && *path != want) return;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= B * d) return;
     const int n = i / d, c = i - n * d;
@@ -1044,6 +1068,26 @@ __global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const fl
         for (int t = 0; t < BT; ++t) v = (t == i) ? acc[q][t] : v;
         if (i < B) a.part[((size_t)m * B + i) * f + j0 + 4 * q] = v;
     }
+}
+
+// Batched forward path from the selected union: |U| = the sum of the block
+// counts; the row gather when |U| * den < num * f (below the measured
+// breakeven fraction num / den), else the MFMA tiles; a caller's choice
+// (force != 0) wins.
+__global__ __launch_bounds__(256) void k_path_pick(const int *__restrict__ list_cnt, int nL, int f, int force,
+                                                   int num, int den, int *__restrict__ path)
+{
+    __shared__ int red[256];
+    int s = 0;
+    for (int i = threadIdx.x; i < nL; i += 256) s += list_cnt[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        *path = force ? force : ((long long)red[0] * den < (long long)num * f ? kPathGather : kPathTiled);
 }
 
 // g' = ((class 0 + class 2) + (class 1 + class 3)) + b; selection flags; ascending
@@ -1349,8 +1393,10 @@ __global__ __launch_bounds__(kB1NT) void k_dense_down_b1(const uint8_t *__restri
 // with all of its loads issued before the first add, then the 64 groups are
 // combined in a fixed order through LDS.
 __global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ partial, int P, int BD,
-                                                   const float *__restrict__ resid, float *__restrict__ out)
+                                                   const float *__restrict__ resid, float *__restrict__ out,
+                                                   const int *__restrict__ path, int want)
 {
+    if (path && *path != want) return;   // uniform: the whole workgroup leaves before any barrier
     __shared__ float red[64][17];
     __shared__ float red2[16][17];
     const int l = threadIdx.x & 15, qg = threadIdx.x >> 4;
@@ -1591,11 +1637,20 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (!forward) return hipSuccess;
+            // the device picks the forward path from the union size (no host round trip);
+            // both paths are launched and the one not picked exits at its first instruction
+            int *path = (int *)(sc + S.path);
+            hipLaunchKernelGGL(k_path_pick, dim3(1), dim3(256), 0, st, (const int *)lcnt, nblk, f, c.batch_path,
+                               gather_below_permille(B), 1000, path);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            // (1) MFMA tiles: up on every W_up block with a selected neuron, down on all of W_down
             uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
             uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
-            hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl);
+            hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl,
+                               (const int *)path, (int)kPathTiled);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl};
+            UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl,
+                           path, kPathTiled};
             hipLaunchKernelGGL(k_up_tiled, dim3(f / 16), dim3(64), 0, st, ua);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             // about 1800 waves in flight: split d_ff so that (d/16) x splits fills the chip
@@ -1604,11 +1659,26 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             const int per = ((KS + ns0 - 1) / ns0 + 3) / 4 * 4;
             const int ns = (KS + per - 1) / per;
             float *partial = (float *)(sc + S.partial);
-            DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial};
+            DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial, path, kPathTiled};
             hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             hipLaunchKernelGGL(k_down_sum, dim3((B * d + 255) / 256), dim3(256), 0, st, (const float *)partial, ns, B,
-                               d, D.residual ? c.x : nullptr, c.out);
+                               d, D.residual ? c.x : nullptr, c.out, (const int *)path, (int)kPathTiled);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            // (2) row gather over the union's W_up and W_down^T rows, then the fixed-order reduce
+            GatherArgs g{};
+            g.list_cnt = lcnt; g.list_idx = lidx; g.nL = nblk; g.R = R;
+            g.G = G; g.U = U; g.bits = nullptr; g.nw32 = f / 32;
+            g.x = xin; g.B = B; g.d = d; g.f = f;
+            g.wu = L.wu; g.su = L.su; g.wdt = L.wdt; g.sdt = L.sdt;
+            g.mode = c.mode; g.act = D.act; g.use_union = c.use_union; g.theta = c.theta;
+            g.partial = partial;
+            g.idx_out = nullptr; g.count_out = nullptr;
+            g.path = path; g.want = kPathGather;
+            if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_reduce16, dim3((B * d + 15) / 16), dim3(1024), 0, st, (const float *)partial,
+                               kGatherWGs, B * d, D.residual ? c.x : nullptr, c.out, (const int *)path,
+                               (int)kPathGather);
             return hipGetLastError();
         }
     }
@@ -1662,7 +1732,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
 
     const int BD = B * d;
     hipLaunchKernelGGL(k_reduce16, dim3((BD + 15) / 16), dim3(1024), 0, st, (const float *)partial, kGatherWGs, BD,
-                       D.residual ? c.x : nullptr, c.out);
+                       D.residual ? c.x : nullptr, c.out, (const int *)nullptr, 0);
     return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ PersistentLayout persistent_layout(const sffn_layer_desc &d);
 // scratch layout for one call
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
-    size_t xsplit, hsplit, gpart;                                        // decode, batches (BATCH layout)
+    size_t xsplit, hsplit, gpart, path;                                  // decode, batches (BATCH layout)
     size_t tscore, tflag, pH, tkeys;                                     // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;
@@ -103,9 +103,14 @@ ScratchLayout scratch_layout(const sffn_layer_desc &d);
 // ---------------------------------------------------------------------------
 // kernel launchers (return hipError_t of the launch)
 // ---------------------------------------------------------------------------
+// batched decode with the BATCH layout: which forward path the device-side
+// union size picked (or the caller forced)
+enum { kPathTiled = 1, kPathGather = 2 };
+
 struct DecodeCall {
     const Layer *L;
     int mode, use_union, topk_k;
+    int batch_path;     // 0 auto, kPathTiled, kPathGather
     float bias, theta;
     int B;
     const float *x;     // [B][d] caller input

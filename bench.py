@@ -20,6 +20,8 @@ Other workloads (same JSON contract, one line each):
   --workload prefill   token-selective prefill, d_model 5120, d_ff 25600, L 16384
   --workload experts   adaptive expert top-K by routing mass over 16384 tokens,
                        384 and 256 routed experts, tau 0.5, buckets 3..6
+  --workload breakeven batched decode (5 / 8 / 16 tokens): tile path, row gather and
+                       the device's automatic choice against the union fraction
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -80,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "topk", "schedule", "prefill", "experts", "copy"])
+                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
     p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
@@ -670,6 +672,54 @@ def bench_prefill(args):
     layer.close()
 
 
+def bench_breakeven(args):
+    """Batched decode (BATCH layout, 5 / 8 / 16 tokens): the MFMA tile path and
+    the row gather forced in turn, and the device's automatic choice, against the
+    selected union's fraction of d_ff (THRESH on RMSNorm-ed inputs, union rule)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+    rows = []
+    for (d, f) in ((3584, 18944), (4096, 11008)):
+        w = synth.cfg4_layer_weights(8, d, f)
+        wt = weights_dev(w)
+        layer = sf.Layer(d, f, 16, sf.W_BF16, sf.ACT_SILU, wt, rmsnorm=True, residual=True,
+                         layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+        del wt
+        for B in (5, 8, 16):
+            xs = [dev_tensor(synth.cfg4_input(B, d) * np.float32(1 + 0.1 * i)) for i in range(4)]
+            ys = [torch.empty_like(x) for x in xs]
+            for a in (0.002, 0.01, 0.02, 0.04, 0.07, 0.1, 0.3):
+                th = synth.gate_threshold_for_active_fraction(a)
+                row = {"d": d, "f": f, "B": B, "a": a}
+                for name, bp in (("tiled", 1), ("gather", 2), ("auto", 0)):
+                    pol = sf.make_policy("thresh", theta=th, use_union=True, batch_path=bp)
+
+                    def run(s0, n, pol=pol):
+                        for i in range(s0, s0 + n):
+                            layer.forward(pol, xs[i % 4], ys[i % 4])
+                    run(0, 4)
+                    torch.cuda.synchronize()
+                    row[name + "_us"] = round(graph_time_us(run, 64, 16, 4), 2)
+                idx = torch.empty(f, dtype=torch.int32, device="cuda:0")
+                cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+                layer.select(sf.make_policy("thresh", theta=th, use_union=True), xs[0], idx, cnt)
+                torch.cuda.synchronize()
+                row["union"] = round(int(cnt.item()) / f, 4)
+                row["auto_vs_best"] = round(min(row["tiled_us"], row["gather_us"]) / row["auto_us"], 3)
+                rows.append(row)
+                log(json.dumps(row))
+        layer.close()
+    worst = min(r["auto_vs_best"] for r in rows)
+    cfg = {"workload": "batched decode layer (3584 x 18944 and 4096 x 11008 bf16 SwiGLU, RMSNorm + residual), "
+                       "5 / 8 / 16 tokens, union rule, tile vs gather vs automatic path", "results": rows}
+    out = line("worst ratio of the best forced path's time to the automatic choice's", worst, "ratio", 64, 4,
+               None, "bf16", cfg, None, None)
+    print(json.dumps(out), flush=True)
+
+
 class _FREE_ENTRY_POINTS:
     """Stands for the library's handle-free entry points in main_kernel_us."""
     handle = None
@@ -779,7 +829,8 @@ def main():
     import torch
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
-     "prefill": bench_prefill, "experts": bench_experts, "copy": bench_copy}[args.workload](args)
+     "prefill": bench_prefill, "experts": bench_experts, "breakeven": bench_breakeven,
+     "copy": bench_copy}[args.workload](args)
 
 
 if __name__ == "__main__":

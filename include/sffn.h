@@ -132,6 +132,13 @@ typedef struct sffn_layer_desc {
  *  mass_thresh  TOKENS: fraction of the total importance mass (fp64)
  *  recent_n     TOKENS: trailing tokens always kept (>= 0)
  *  min_keep     TOKENS: minimum kept tokens (>= 0)
+ *  batch_path   decode calls that use the BATCH layout (5..16 tokens): 0 = the
+ *               device picks, from the size of the selected union, between
+ *               the MFMA tile path (every W_up block with a selected neuron
+ *               and all of W_down) and the row gather (only the union's
+ *               W_up and W_down^T rows) at the measured breakeven; 1 forces
+ *               the tiles, 2 the gather (both give the same results within
+ *               the bf16 / fp32 tolerance).  Other calls ignore it.
  */
 typedef struct sffn_policy {
     int32_t mode;
@@ -141,7 +148,7 @@ typedef struct sffn_policy {
     int32_t use_union;
     int32_t recent_n;
     int32_t min_keep;
-    int32_t reserved;
+    int32_t batch_path;
     double mass_thresh;
 } sffn_policy;
 

@@ -26,7 +26,8 @@ def _check(layer, w, x, mode, tol, **kw):
     """Run one call on the GPU and the oracle; compare everything unique."""
     sf = _sf()
     pol = sf.make_policy(mode, gate_bias=kw.get("bias", 0.0), theta=kw.get("theta", 0.0),
-                         topk_k=kw.get("topk_k", 1), use_union=kw.get("union", False))
+                         topk_k=kw.get("topk_k", 1), use_union=kw.get("union", False),
+                         batch_path=kw.get("batch_path", 0))
     y, idx, n = run_decode(layer, pol, x)
     ref = oracle.decode(w, x, mode=mode, bias=kw.get("bias", 0.0), theta=kw.get("theta", 0.0),
                         topk_k=kw.get("topk_k", 1), union=kw.get("union", False),
@@ -182,6 +183,32 @@ def test_batched_mfma_sparse_blocks(B):
     y, idx, n = run_decode(layer, sf.make_policy("exact", gate_bias=-40.0), x)
     assert n == 0 and np.all(y == 0.0)
     layer.close()
+
+
+@pytest.mark.parametrize("B", [5, 8, 16])
+def test_batched_tile_and_gather_paths_match_the_oracle(B):
+    # the device picks the tile or the gather path from the union size; both forced
+    # paths and the automatic choice must match the oracle, from nearly empty to
+    # nearly full unions, with and without the union rule
+    sf = _sf()
+    d, f = 1024, 2048
+    w = synth._make_weights(synth.WT_BF16, d, f, synth.ACT_RELU, (1911, 1912, 1913))
+    x = synth.round_to_bf16(synth.normal_f32(1914 + B, (B, d)))
+    layer = make_layer(w, 16, layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+    for a in (0.002, 0.05, 0.3):
+        b = synth.gate_offset_for_active_fraction(a)
+        for union in (True, False):
+            ys = [_check(layer, w, x, "exact", 2e-3, bias=b, union=union, batch_path=p)[0] for p in (1, 2, 0)]
+            assert rel_l2(ys[0], ys[1]) <= 2e-3
+    th = synth.gate_threshold_for_active_fraction(0.1)
+    wt = synth._make_weights(synth.WT_BF16, d, f, synth.ACT_SILU, (1921, 1922, 1923))
+    layer_t = make_layer(wt, 16, rmsnorm=True, residual=True, layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+    for p in (1, 2, 0):
+        _check(layer_t, wt, x, "thresh", 2e-3, theta=th, union=True, batch_path=p)
+    with pytest.raises(sf.SffnError):
+        run_decode(layer, sf.make_policy("exact", batch_path=3), x)
+    layer.close()
+    layer_t.close()
 
 
 def test_rmsnorm_residual_batch16():
