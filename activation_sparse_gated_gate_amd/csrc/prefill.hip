@@ -544,28 +544,31 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
             // every wave's copies of slice kt are in LDS, and every wave has finished
             // slice kt - 1, whose stage the next copies refill
             __builtin_amdgcn_s_barrier();
-            if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
             const uint16_t *as = As[kt % BSTAGES], *bs = Bs[kt % BSTAGES];
+            // every operand fragment of the slice is read from LDS before the first
+            // product, so only the first two reads' latency is exposed; the refill of
+            // the stage finished two slices ago goes out behind them
+            bf16x8 fa[BBK / 16][4], fb[BBK / 16][4];
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks) {
                 const int kc = 2 * ks + (lane >> 5);
-                bf16x8 fa[4], fb[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 128 + i * 32 + (lane & 31);
-                    fa[i] = *(const bf16x8 *)&as[r * BBK + ((kc ^ ((r >> 2) & 3)) * 8)];
+                    fa[ks][i] = *(const bf16x8 *)&as[r * BBK + ((kc ^ ((r >> 2) & 3)) * 8)];
+                    const int c = wn * 128 + i * 32 + (lane & 31);
+                    fb[ks][i] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
                 }
+            }
+            if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = wn * 128 + j * 32 + (lane & 31);
-                    fb[j] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
-                }
+            for (int ks = 0; ks < BBK / 16; ++ks)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
         }
         __builtin_amdgcn_s_barrier();   // the next tile's first copies reuse the stages
 
