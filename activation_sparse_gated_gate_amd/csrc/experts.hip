@@ -54,13 +54,38 @@ __device__ __forceinline__ int wave_min(int v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// The two best keys of one lane in (key desc, slot asc) order, optionally only
+// among the keys that rank after (hl, ql), the last expert the lane gave up.
+template <int PER>
+__device__ __forceinline__ void lane_top2(const int (&key)[PER], bool after, int hl, int ql, int &h1, int &q1,
+                                          int &h2, int &q2)
+{
+    h1 = INT_MIN;
+    q1 = PER;
+    h2 = INT_MIN;
+    q2 = PER;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        int k = key[q];
+        if (after) k = (k < hl || (k == hl && q > ql)) ? k : INT_MIN;
+        // strict comparisons keep the lower slot first among equal keys
+        const bool g1 = k > h1, g2 = k > h2;
+        h2 = g1 ? h1 : (g2 ? k : h2);
+        q2 = g1 ? q1 : (g2 ? q : q2);
+        h1 = g1 ? k : h1;
+        q1 = g1 ? q : q1;
+    }
+}
+
 // One wave per token; lane l holds the keys of experts l, l + 64, ... (PER of
-// them, PER = ceil(E / 64)).  Round r takes the wave-wide maximum key m, then
-// the lowest expert index whose key is m (a minimum over the lanes' lowest
-// matching slot), and removes that expert; the mass c of the ranked
-// probabilities is added in rank order and the rounds stop at the first
-// b >= kmin with c >= tau.  Lanes past E load expert E - 1 (in bounds) and
-// hold the lowest key instead.
+// them, PER = ceil(E / 64)) and keeps its two best.  Round r takes the
+// wave-wide maximum m of the lanes' best keys (DPP); the lane holding it (the
+// lowest expert index if several lanes tie: a DPP minimum of their indices)
+// gives it up and promotes its second best, and only a lane that gives up a
+// second expert recomputes its two best among the keys ranking after the last
+// one it gave up.  The mass c of the ranked probabilities is added in rank
+// order and the rounds stop at the first b >= kmin with c >= tau.  Lanes past E
+// load expert E - 1 (in bounds) and hold the lowest key instead.
 template <int PER>
 __global__ __launch_bounds__(256) void k_expert_select(const float *__restrict__ probs, int T, int E, float tau,
                                                        int kmin, int kmax, int32_t *__restrict__ k_out,
@@ -76,23 +101,51 @@ __global__ __launch_bounds__(256) void k_expert_select(const float *__restrict__
     int key[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) key[q] = lane + 64 * q < E ? order_key(x[q]) : INT_MIN;
-    int sel_j = -1;   // lane r keeps the rank-r expert
+    int h1, q1, h2, q2;
+    lane_top2<PER>(key, false, 0, 0, h1, q1, h2, q2);
+    bool have2 = true;           // h2 / q2 hold this lane's next expert
+    int hl = INT_MAX, ql = -1;   // the last expert this lane gave up
+    int sel_j = -1;              // lane r keeps the rank-r expert and its probability
+    float sel_p = 0.0f;
     int K = kmax;
     float c = 0.0f;
     for (int r = 0; r < kmax; ++r) {
-        int best = key[0];
-#pragma unroll
-        for (int q = 1; q < PER; ++q) best = max(best, key[q]);
-        const int m = wave_max(best);
-        int cand = INT_MAX;
-#pragma unroll
-        for (int q = PER - 1; q >= 0; --q) cand = key[q] == m ? lane + 64 * q : cand;
-        // clamped: only a non-finite input could leave it past E - 1
-        const int j = min(wave_min(cand), E - 1);
-#pragma unroll
-        for (int q = 0; q < PER; ++q) key[q] = lane + 64 * q == j ? INT_MIN : key[q];
-        if (lane == r) sel_j = j;
-        c = c + order_value(m);
+        const int m = wave_max(h1);
+        const uint64_t hit = __ballot(h1 == m);   // never empty: some lane holds m
+        int owner;
+        if (__builtin_popcountll(hit) == 1) {
+            owner = (int)__builtin_ctzll(hit);
+        } else {
+            const int cand = h1 == m ? lane + 64 * q1 : INT_MAX;
+            owner = wave_min(cand) & 63;
+        }
+        // clamped: only a non-finite input could point past E - 1
+        const int j = min(64 * __builtin_amdgcn_readlane(q1, owner) + owner, E - 1);
+        const bool refill = __builtin_amdgcn_readlane((int)!have2, owner) != 0;
+        if (lane == owner) {
+            hl = h1;
+            ql = q1;
+            h1 = h2;
+            q1 = q2;
+            have2 = false;
+        }
+        if (refill) {   // uniform: the owner had already given up its second best
+            int a1, b1, a2, b2;
+            lane_top2<PER>(key, true, hl, ql, a1, b1, a2, b2);
+            if (lane == owner) {
+                h1 = a1;
+                q1 = b1;
+                h2 = a2;
+                q2 = b2;
+                have2 = true;
+            }
+        }
+        const float v = order_value(m);
+        if (lane == r) {
+            sel_j = j;
+            sel_p = v;
+        }
+        c = c + v;
         if (r + 1 >= kmin && c >= tau) {
             K = r + 1;
             break;
@@ -100,8 +153,8 @@ __global__ __launch_bounds__(256) void k_expert_select(const float *__restrict__
     }
     if (lane < kmax) {
         idx_out[(size_t)t * kmax + lane] = lane < K ? sel_j : -1;
-        // the stored probability itself (a -0 input stays -0; the key only ranks)
-        w_out[(size_t)t * kmax + lane] = lane < K ? p[sel_j] : 0.0f;
+        // the key's value is the stored probability except for a stored -0
+        w_out[(size_t)t * kmax + lane] = lane < K ? (sel_p == 0.0f ? p[sel_j] : sel_p) : 0.0f;
     }
     if (lane == 0) k_out[t] = K;
 }
