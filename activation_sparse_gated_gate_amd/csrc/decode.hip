@@ -808,10 +808,34 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v)
 }
 
 // one thread per lane slot of 8 values: (d/32) * 64 threads
-__global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ x, int B, int d, uint16_t *__restrict__ xh,
-                                                 uint16_t *__restrict__ xl, const int *__restrict__ path, int want)
+// Union size -> forward path: the row gather when |U| * 1000 < thr * f, else
+// the tiles.  Every workgroup that calls it computes the same value.
+__device__ int pick_path(const int *__restrict__ list_cnt, int nL, int f, int thr)
 {
-    if (path && *path != want) return;   // the other batched path was picked
+    __shared__ int red[256];
+    int s = 0;
+    for (int i = threadIdx.x; i < nL; i += 256) s += list_cnt[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    return (long long)red[0] * 1000 < (long long)thr * f ? kPathGather : kPathTiled;
+}
+
+// x_hat as bf16 hi / lo in MFMA lane order.  With path != nullptr the path is
+// picked here first (workgroup 0 stores it for the later kernels) and the
+// split is skipped when the gather was picked.
+__global__ __launch_bounds__(256) void k_split_x(const float *__restrict__ x, int B, int d, uint16_t *__restrict__ xh,
+                                                 uint16_t *__restrict__ xl, const int *__restrict__ list_cnt, int nL,
+                                                 int f, int thr, int *__restrict__ path)
+{
+    if (path) {
+        const int pk = pick_path(list_cnt, nL, f, thr);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *path = pk;
+        if (pk != kPathTiled) return;
+    }
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= (d / 32) * 64) return;
     const int s = i >> 6, l = i & 63, n = l & 15;
@@ -926,18 +950,23 @@ __global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
     *(float4 *)(a.partial + ((size_t)p * 16 + n) * a.d + t * 16 + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
-__global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ partial, int ns, int B, int d,
-                                                  const float *__restrict__ resid, float *__restrict__ out,
-                                                  const int *__restrict__ path, int want)
+__device__ __forceinline__ void down_sum_elem(const float *__restrict__ partial, int ns, int d, int i,
+                                              const float *__restrict__ resid, float *__restrict__ out)
 {
-    if (path && *path != want) return;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= B * d) return;
     const int n = i / d, c = i - n * d;
     float y = 0.0f;
     for (int p = 0; p < ns; ++p) y += partial[((size_t)p * 16 + n) * d + c];
     out[i] = resid ? y + resid[i] : y;
 }
+
+__global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ partial, int ns, int B, int d,
+                                                  const float *__restrict__ resid, float *__restrict__ out)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < B * d) down_sum_elem(partial, ns, d, i, resid, out);
+}
+
+
 
 // ---------------------------------------------------------------------------
 // batched gate GEMV in the fixed order (5..16 tokens, bf16, BATCH layout).
@@ -1068,26 +1097,6 @@ __global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const fl
         for (int t = 0; t < BT; ++t) v = (t == i) ? acc[q][t] : v;
         if (i < B) a.part[((size_t)m * B + i) * f + j0 + 4 * q] = v;
     }
-}
-
-// Batched forward path from the selected union: |U| = the sum of the block
-// counts; the row gather when |U| * den < num * f (below the measured
-// breakeven fraction num / den), else the MFMA tiles; a caller's choice
-// (force != 0) wins.
-__global__ __launch_bounds__(256) void k_path_pick(const int *__restrict__ list_cnt, int nL, int f, int force,
-                                                   int num, int den, int *__restrict__ path)
-{
-    __shared__ int red[256];
-    int s = 0;
-    for (int i = threadIdx.x; i < nL; i += 256) s += list_cnt[i];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0)
-        *path = force ? force : ((long long)red[0] * den < (long long)num * f ? kPathGather : kPathTiled);
 }
 
 // g' = ((class 0 + class 2) + (class 1 + class 3)) + b; selection flags; ascending
@@ -1392,11 +1401,9 @@ __global__ __launch_bounds__(kB1NT) void k_dense_down_b1(const uint8_t *__restri
 // workgroup; thread (column, group g) sums partials g, g + 64, g + 128, ...
 // with all of its loads issued before the first add, then the 64 groups are
 // combined in a fixed order through LDS.
-__global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ partial, int P, int BD,
-                                                   const float *__restrict__ resid, float *__restrict__ out,
-                                                   const int *__restrict__ path, int want)
+__device__ __forceinline__ void reduce16_block(const float *__restrict__ partial, int P, int BD,
+                                               const float *__restrict__ resid, float *__restrict__ out)
 {
-    if (path && *path != want) return;   // uniform: the whole workgroup leaves before any barrier
     __shared__ float red[64][17];
     __shared__ float red2[16][17];
     const int l = threadIdx.x & 15, qg = threadIdx.x >> 4;
@@ -1429,6 +1436,27 @@ __global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ par
         if (resid) y += resid[col];
         out[col] = y;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_reduce16(const float *__restrict__ partial, int P, int BD,
+                                                   const float *__restrict__ resid, float *__restrict__ out)
+{
+    reduce16_block(partial, P, BD, resid, out);
+}
+
+// The output of a batched call whose path the device picked: the tile path's
+// split sums (as k_down_sum) or the gather path's partials (as k_reduce16), one
+// launch for either; the branch is uniform.
+__global__ __launch_bounds__(1024) void k_batched_out(const float *__restrict__ partial, int ns, int P, int B, int d,
+                                                      const float *__restrict__ resid, float *__restrict__ out,
+                                                      const int *__restrict__ path)
+{
+    if (*path == kPathTiled) {
+        const int i = blockIdx.x * 16 + (int)threadIdx.x;
+        if (threadIdx.x < 16 && i < B * d) down_sum_elem(partial, ns, d, i, resid, out);
+        return;
+    }
+    reduce16_block(partial, P, B * d, resid, out);
 }
 
 // y = sum of the fused kernel's P partials (+ residual) from the blocked layout
@@ -1637,35 +1665,42 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (!forward) return hipSuccess;
-            // the device picks the forward path from the union size (no host round trip);
-            // both paths are launched and the one not picked exits at its first instruction
-            int *path = (int *)(sc + S.path);
-            hipLaunchKernelGGL(k_path_pick, dim3(1), dim3(256), 0, st, (const int *)lcnt, nblk, f, c.batch_path,
-                               gather_below_permille(B), 1000, path);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            // (1) MFMA tiles: up on every W_up block with a selected neuron, down on all of W_down
-            uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
-            uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
-            hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl,
-                               (const int *)path, (int)kPathTiled);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl,
-                           path, kPathTiled};
-            hipLaunchKernelGGL(k_up_tiled, dim3(f / 16), dim3(64), 0, st, ua);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            // about 1800 waves in flight: split d_ff so that (d/16) x splits fills the chip
+            // Which forward path: forced by the caller, fixed by the batch size when the
+            // gather never wins at it, or else picked on the device from the union size
+            // (no host round trip) by the first tile kernel; then both paths are
+            // launched, the kernels of the one not picked exit at once, and one output
+            // kernel sums whichever partials were written.
+            const int thr = gather_below_permille(B);
+            const int fixed = c.batch_path ? c.batch_path : (thr == 0 ? (int)kPathTiled : 0);
+            int *path = fixed ? nullptr : (int *)(sc + S.path);
+            float *partial = (float *)(sc + S.partial);
+            const float *resid = D.residual ? c.x : nullptr;
             const int KS = f / 32, T = d / 16;
+            // about 1800 waves in flight for the down tiles: split d_ff so that (d/16) x splits fills the chip
             const int ns0 = std::max(1, std::min(std::min(KS / 4, kMaxDownSplits), (1792 + T - 1) / T));
             const int per = ((KS + ns0 - 1) / ns0 + 3) / 4 * 4;
             const int ns = (KS + per - 1) / per;
-            float *partial = (float *)(sc + S.partial);
-            DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial, path, kPathTiled};
-            hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_down_sum, dim3((B * d + 255) / 256), dim3(256), 0, st, (const float *)partial, ns, B,
-                               d, D.residual ? c.x : nullptr, c.out, (const int *)path, (int)kPathTiled);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            // (2) row gather over the union's W_up and W_down^T rows, then the fixed-order reduce
+            if (fixed != kPathGather) {
+                // (1) MFMA tiles: up on every W_up block with a selected neuron, down on all of W_down
+                uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
+                uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
+                hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl,
+                                   (const int *)lcnt, nblk, f, thr, path);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl,
+                               path, kPathTiled};
+                hipLaunchKernelGGL(k_up_tiled, dim3(f / 16), dim3(64), 0, st, ua);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial, path, kPathTiled};
+                hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                if (fixed == kPathTiled) {
+                    hipLaunchKernelGGL(k_down_sum, dim3((B * d + 255) / 256), dim3(256), 0, st,
+                                       (const float *)partial, ns, B, d, resid, c.out);
+                    return hipGetLastError();
+                }
+            }
+            // (2) row gather over the union's W_up and W_down^T rows
             GatherArgs g{};
             g.list_cnt = lcnt; g.list_idx = lidx; g.nL = nblk; g.R = R;
             g.G = G; g.U = U; g.bits = nullptr; g.nw32 = f / 32;
@@ -1676,9 +1711,12 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             g.idx_out = nullptr; g.count_out = nullptr;
             g.path = path; g.want = kPathGather;
             if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_reduce16, dim3((B * d + 15) / 16), dim3(1024), 0, st, (const float *)partial,
-                               kGatherWGs, B * d, D.residual ? c.x : nullptr, c.out, (const int *)path,
-                               (int)kPathGather);
+            if (fixed == kPathGather)
+                hipLaunchKernelGGL(k_reduce16, dim3((B * d + 15) / 16), dim3(1024), 0, st, (const float *)partial,
+                                   kGatherWGs, B * d, resid, c.out);
+            else
+                hipLaunchKernelGGL(k_batched_out, dim3((B * d + 15) / 16), dim3(1024), 0, st, (const float *)partial,
+                                   ns, kGatherWGs, B, d, resid, c.out, (const int *)path);
             return hipGetLastError();
         }
     }
@@ -1732,7 +1770,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
 
     const int BD = B * d;
     hipLaunchKernelGGL(k_reduce16, dim3((BD + 15) / 16), dim3(1024), 0, st, (const float *)partial, kGatherWGs, BD,
-                       D.residual ? c.x : nullptr, c.out, (const int *)nullptr, 0);
+                       D.residual ? c.x : nullptr, c.out);
     return hipGetLastError();
 }
 
