@@ -57,7 +57,9 @@ template <int WT, int BT> struct Cfg {
     static constexpr int RPW = (BT == 1 || BT >= 8) ? 4 : 2;
     static constexpr int NW = 4;                     // waves per workgroup
     static constexpr int CPT = (WT == SFFN_W_BF16 && BT == 1) ? 16 : (WT == SFFN_W_F32 ? 4 : 8);
-    static constexpr int UNR = BT >= 8 ? 2 : 4;      // down rows in flight per thread
+    // down rows in flight per thread: an int4 row gives a thread 4 bytes, so it
+    // keeps 16 rows in flight (fewer only costs latency: one workgroup per CU)
+    static constexpr int UNR = WT == SFFN_W_INT4_G128 ? 16 : (BT >= 16 ? 2 : 4);
 };
 
 // ---------------------------------------------------------------------------
