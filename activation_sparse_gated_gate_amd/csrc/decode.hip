@@ -1177,61 +1177,75 @@ __device__ __forceinline__ void stage_vec(float *xs, const float *x, int n)
     for (int i = threadIdx.x; i < n / 4; i += blockDim.x) ((float4 *)xs)[i] = ((const float4 *)x)[i];
 }
 
-// Fused sparse layer for one token.  Each workgroup owns RB consecutive
-// neurons.  Phase 1 streams their gate rows (wave w walks neurons w, w + 8, ...
-// with the next row's loads in flight) and records g' and the selection in LDS.
-// Phase 2 deals the workgroup's active neurons round-robin to the waves, so no
-// wave carries more than its share of gathers: each loads the W_up and W_down^T
-// rows of two neurons at a time, forms h = act(g') u and adds h * W_down^T[j]
-// into its own partial y in LDS.  The wave partials are then summed in a fixed
-// order into the workgroup's partial (blocked layout for the reduce).
+// Fused sparse layer for one token.  Each workgroup owns RB <= 48 consecutive
+// neurons and runs 8 waves.
+// Phase 1: the gate stream.  Wave w walks the rows w, w + 8, ... with the next
+// row's loads in flight (a deeper prefetch, or every row requested at once,
+// measured slower), forms g' in the fixed order and the predicate, and records
+// g' and the flag in LDS.
+// Phase 2: the ascending list of active neurons (ballot + mbcnt).  Wave q loads
+// the W_up rows of active neurons q, q + 8, ... (two in flight) and forms
+// h = act(g') u.  Before the first of those products is waited for, every
+// wave also requests its slice of the active neurons' W_down^T rows: wave w
+// owns the chunks [w CW, (w + 1) CW) of a row (CW = 8 KC), lane (s, c) chunk c
+// of the neurons s, s + S, ... (S = 64 / CW slots; one slot at d_model 4096
+// bf16).  Once every h is in LDS, each lane adds h_q * W_down^T[j_q] for its
+// chunk in ascending q, the slots of a chunk are summed in slot order, and the
+// workgroup's partial y is written in the blocked layout [D / 16][P][16] that
+// the reduce reads.  No per-wave copy of y is kept, so LDS holds only x and
+// the workgroup's neuron bookkeeping.
 constexpr int kFusedNW = 8;
 constexpr int kFusedNT = kFusedNW * 64;
+constexpr int kFusedDB = 8;  // W_down^T chunks per lane per batch (two batches in flight)
 
 template <int WT, int KC>
 __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
 {
     constexpr int E = Chunk<WT>::E;
-    constexpr int NW = kFusedNW, NT = kFusedNT;
+    constexpr int NW = kFusedNW;
     constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
     constexpr int D = KC * 64 * E;
     constexpr size_t RBYTES = (size_t)D * EB;
+    constexpr int CW = KC * 64 / NW;       // chunks of a W_down^T row per wave
+    constexpr int S = CW >= 64 ? 1 : 64 / CW;  // neuron slots per wave
+    constexpr int DB = kFusedDB;
+    static_assert(NW * CW == KC * 64 && CW <= 64, "column split of the down rows");
     __shared__ __align__(16) float xs[D];
-    __shared__ __align__(16) float ysum[NW * D];
     __shared__ int flags[kFusedMaxRB];
     __shared__ float gsm[kFusedMaxRB];
     __shared__ int alist[kFusedMaxRB];
+    __shared__ float hs[kFusedMaxRB];
     __shared__ int s_nact;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r0 = blockIdx.x * a.RB;
     const int nr = min(a.RB, a.f - r0);
 
-    uint4 ga[KC], gb[KC];
-    if (wave < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + wave, lane);
-    stage_vec(xs, a.x, D);
-    __syncthreads();
-
-    // phase 1: the gate stream (wave w walks rows w, w + 8, ..., the next row's
+    // phase 1: the gate stream (wave w walks rows w, w + NW, ..., the next row's
     // loads in flight), g' and the selection into LDS
     auto gate = [&](const uint4 (&cur)[KC], int i) {
-        const float g = dot_row_lds<WT, KC>(cur, xs, lane);
-        const float gp = g + a.bias;
-        const bool on = gate_pred(a.mode, gp, a.theta);
+        const float gp = dot_row_lds<WT, KC>(cur, xs, lane) + a.bias;
         if (lane == 0) {
             a.G[r0 + i] = gp;
-            flags[i] = on ? 1 : 0;
+            flags[i] = gate_pred(a.mode, gp, a.theta) ? 1 : 0;
             gsm[i] = gp;
         }
     };
-    for (int i = wave; i < nr; i += 2 * NW) {
-        const int i2 = i + NW;
-        if (i2 < nr) load_row<WT, KC>(gb, a.wg, RBYTES, r0 + i2, lane);
-        gate(ga, i);
-        if (i2 >= nr) break;
-        const int i3 = i2 + NW;
-        if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
-        gate(gb, i2);
+    {
+        uint4 ga[KC];
+        if (wave < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + wave, lane);
+        stage_vec(xs, a.x, D);
+        __syncthreads();
+        uint4 gb[KC];
+        for (int i = wave; i < nr; i += 2 * NW) {
+            const int i2 = i + NW;
+            if (i2 < nr) load_row<WT, KC>(gb, a.wg, RBYTES, r0 + i2, lane);
+            gate(ga, i);
+            if (i2 >= nr) break;
+            const int i3 = i2 + NW;
+            if (i3 < nr) load_row<WT, KC>(ga, a.wg, RBYTES, r0 + i3, lane);
+            gate(gb, i2);
+        }
     }
     __syncthreads();
     // ascending list of this workgroup's active neurons (ballot + mbcnt)
@@ -1250,67 +1264,76 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
     __syncthreads();
     const int nact = s_nact;
 
-    // phase 2: the active neurons dealt round-robin to the waves (two at a time
-    // per wave, their W_up and W_down^T rows loaded together); each wave adds
-    // h * W_down^T[j] into its own partial y (lane p owns the columns of chunks
-    // p, p + 64, ...), neurons in ascending order
-    float *yw = ysum + (size_t)wave * D;
-    if (wave < nact) {
+    // phase 2
+    const int s = lane / CW, c = lane - s * CW;  // lanes with s >= S (when CW does not divide 64) idle
+    const bool dl = s < S;
+    const size_t coff = (size_t)(wave * CW + c) * 16;  // byte offset of this lane's chunk in a row
+    constexpr int PER = S * DB;                        // neurons per batch
+    auto load_down = [&](uint4 (&dst)[DB], int q0) {
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-            float4 *dst = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
-#pragma unroll
-            for (int e4 = 0; e4 < E / 4; ++e4) dst[e4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int t = 0; t < DB; ++t) {
+            const int q = q0 + s + S * t;
+            if (dl && q < nact) dst[t] = ld16(a.wdt + (size_t)(r0 + alist[q]) * RBYTES + coff);
         }
-    }
-    auto finish = [&](const uint4 (&ur)[KC], const uint4 (&dr)[KC], float gp) {
-        const float u = dot_row_lds<WT, KC>(ur, xs, lane);
-        const float h = act_f32(a.act, gp) * u;
+    };
+    float yacc[E];
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-            float w[E];
-            unpack<WT>(dr[k], w);
-            float4 *yv = (float4 *)(yw + (size_t)(k * 64 + lane) * E);
+    for (int e = 0; e < E; ++e) yacc[e] = 0.0f;
+    auto fma_down = [&](const uint4 (&src)[DB], int q0) {
 #pragma unroll
-            for (int e4 = 0; e4 < E / 4; ++e4) {
-                float4 v = yv[e4];
-                v.x = __builtin_fmaf(h, w[4 * e4 + 0], v.x);
-                v.y = __builtin_fmaf(h, w[4 * e4 + 1], v.y);
-                v.z = __builtin_fmaf(h, w[4 * e4 + 2], v.z);
-                v.w = __builtin_fmaf(h, w[4 * e4 + 3], v.w);
-                yv[e4] = v;
+        for (int t = 0; t < DB; ++t) {
+            const int q = q0 + s + S * t;
+            if (dl && q < nact) {
+                const float h = hs[q];
+                float w[E];
+                unpack<WT>(src[t], w);
+#pragma unroll
+                for (int e = 0; e < E; ++e) yacc[e] = __builtin_fmaf(h, w[e], yacc[e]);
             }
         }
     };
-    for (int q = wave; q < nact; q += 2 * NW) {
-        const int q2 = q + NW;
-        const int i1 = alist[q];
-        load_row<WT, KC>(ga, a.wu, RBYTES, r0 + i1, lane);
-        load_row<WT, KC>(gb, a.wdt, RBYTES, r0 + i1, lane);
-        uint4 uc[KC], dc[KC];
-        int i2 = -1;
-        if (q2 < nact) {
-            i2 = alist[q2];
-            load_row<WT, KC>(uc, a.wu, RBYTES, r0 + i2, lane);
-            load_row<WT, KC>(dc, a.wdt, RBYTES, r0 + i2, lane);
+    auto up_h = [&](const uint4 (&ur)[KC], int q) {
+        const float u = dot_row_lds<WT, KC>(ur, xs, lane);
+        if (lane == 0) hs[q] = act_f32(a.act, gsm[alist[q]]) * u;
+    };
+    uint4 da[DB], db[DB];
+    {
+        uint4 ua[KC], ub[KC];
+        int q = wave;
+        if (q < nact) load_row<WT, KC>(ua, a.wu, RBYTES, r0 + alist[q], lane);
+        if (q + NW < nact) load_row<WT, KC>(ub, a.wu, RBYTES, r0 + alist[q + NW], lane);
+        load_down(da, 0);
+        for (; q < nact; q += 2 * NW) {
+            up_h(ua, q);
+            if (q + 2 * NW < nact) load_row<WT, KC>(ua, a.wu, RBYTES, r0 + alist[q + 2 * NW], lane);
+            if (q + NW >= nact) break;
+            up_h(ub, q + NW);
+            if (q + 3 * NW < nact) load_row<WT, KC>(ub, a.wu, RBYTES, r0 + alist[q + 3 * NW], lane);
         }
-        finish(ga, gb, gsm[i1]);
-        if (i2 >= 0) finish(uc, dc, gsm[i2]);
     }
-
-    // fixed-order sum of the partials of the waves that had neurons
     __syncthreads();
-    const int nwp = min(nact, NW);
-    for (int c = threadIdx.x; c < D / 4; c += NT) {
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (nwp > 0) acc = ((const float4 *)ysum)[c];
-        for (int w = 1; w < nwp; ++w) {
-            const float4 v = ((const float4 *)(ysum + (size_t)w * D))[c];
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
-        // blocked layout [D / 16][P][16]: the reduce reads each 16-column block contiguously
-        const int col = 4 * c;
-        *(float4 *)(a.partial + ((size_t)(col >> 4) * gridDim.x + blockIdx.x) * 16 + (col & 15)) = acc;
+    for (int q0 = 0; q0 < nact; q0 += 2 * PER) {
+        if (q0 + PER < nact) load_down(db, q0 + PER);
+        fma_down(da, q0);
+        if (q0 + PER >= nact) break;
+        if (q0 + 2 * PER < nact) load_down(da, q0 + 2 * PER);
+        fma_down(db, q0 + PER);
+    }
+    // slots summed in slot order (lanes with s = 0 keep the result)
+    float ys[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ys[e] = yacc[e];
+#pragma unroll
+    for (int t = 1; t < S; ++t) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) ys[e] += __shfl(yacc[e], t * CW + c, 64);
+    }
+    if (s == 0) {
+        const int col = (wave * CW + c) * E;
+        float *dst = a.partial + ((size_t)(col >> 4) * gridDim.x + blockIdx.x) * 16 + (col & 15);
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4)
+            *(float4 *)(dst + 4 * e4) = make_float4(ys[4 * e4], ys[4 * e4 + 1], ys[4 * e4 + 2], ys[4 * e4 + 3]);
     }
 }
 
