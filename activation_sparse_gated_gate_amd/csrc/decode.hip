@@ -1169,7 +1169,7 @@ __device__ __forceinline__ float dot_row_lds(const uint4 (&w)[KC], const float *
         }
         acc = chunk_dot<WT>(w[k], 0.0f, xv, acc);
     }
-    return wave_tree_sum(acc);
+    return wave_tree_sum_dpp(acc);
 }
 
 __device__ __forceinline__ void stage_vec(float *xs, const float *x, int n)

@@ -82,6 +82,31 @@ __device__ __forceinline__ float wave_tree_sum(float v)
     return v;
 }
 
+// The same halving tree without LDS traffic: xor 32 and xor 16 through the
+// gfx950 lane swaps (each returns both halves; a lane takes its partner's),
+// xor 8 as a rotation by 8 inside a row of 16, then a rotation by 4, which
+// reads lane i + 4 or i - 4 -- after the xor-8 step both hold the value of
+// lane i ^ 4 -- and xor 2, xor 1 as quad permutations.  Each step adds the
+// partner's value exactly as the shuffle tree does, so the result is the same
+// bit for bit.  Every lane of the wave must be active.
+__device__ __forceinline__ float wave_tree_sum_dpp(float v)
+{
+    const int lane = threadIdx.x & 63;
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = v + __uint_as_float(lane < 32 ? p[1] : p[0]);
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = v + __uint_as_float((lane & 16) ? p[0] : p[1]);
+    }
+    v = v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+    v = v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+    v = v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x4E, 0xf, 0xf, false));   // quad [2,3,0,1]
+    v = v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0xB1, 0xf, 0xf, false));   // quad [1,0,3,2]
+    return v;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ int mbcnt64(uint64_t m)
