@@ -296,3 +296,27 @@ def test_topk_ties_lower_index_first():
     layer = make_layer(w, 1)
     _, ref, _ = _check(layer, w, x, "topk", 2e-3, topk_k=ahead + 2)
     assert 17 in ref["idx"] and 90 in ref["idx"] and 200 not in ref["idx"]
+
+
+def test_int4_sparse_union_scales_of_a_third_group():
+    """int4 gather with a union so sparse (about 1.5 % of d_ff = 65536) that a
+    batch of 16 consecutive rows of one workgroup's share spans three or more
+    128-neuron scale groups; the rows past the batch's first and last group
+    load their scales on their own."""
+    w = synth._make_weights(synth.WT_I4, 256, 65536, synth.ACT_RELU, (981, 982, 983))
+    x = synth.normal_f32(985, (2, 256))
+    b = synth.gate_offset_for_active_fraction(0.015)
+    layer = make_layer(w, 1)
+    for t in range(2):
+        _, ref, _ = _check(layer, w, x[t:t + 1], "exact", 5e-3, bias=b)
+        # the batched gather splits the list into 256 equal shares, rows in
+        # batches of 16: the case must occur
+        idx, n, P = ref["idx"], ref["idx"].size, 256
+        spans = []
+        for q in range(P):
+            lo, hi = q * n // P, (q + 1) * n // P
+            for b0 in range(lo, hi, 16):
+                rows = idx[b0:min(hi, b0 + 16)]
+                spans.append(len(set((rows >> 7).tolist())))
+        assert max(spans) >= 3, "no batch reaches a third scale group"
+    layer.close()
