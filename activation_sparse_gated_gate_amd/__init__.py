@@ -29,7 +29,8 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
 
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
            "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
-           "sffn_select_blocks", "sffn_schedule_mass")
+           "sffn_select_blocks", "sffn_schedule_mass", "sffn_neuron_counts", "sffn_frequency_order",
+           "sffn_decode_block_rows", "sffn_create_permuted")
 
 
 class LayerDesc(C.Structure):
@@ -93,6 +94,14 @@ def _load():
     lib.sffn_expert_select.restype = I
     lib.sffn_expert_select.argtypes = [P, I, I, C.POINTER(ExpertPolicy), P, P, P, P]
     lib.sffn_set_kernel_timer.restype = I
+    lib.sffn_neuron_counts.restype = I
+    lib.sffn_neuron_counts.argtypes = [P, P, I, P, P]
+    lib.sffn_frequency_order.restype = I
+    lib.sffn_frequency_order.argtypes = [P, I, I, I, P]
+    lib.sffn_decode_block_rows.restype = I
+    lib.sffn_decode_block_rows.argtypes = [I]
+    lib.sffn_create_permuted.restype = I
+    lib.sffn_create_permuted.argtypes = [C.POINTER(LayerDesc), P, P, P, P, P, Z, P, C.POINTER(P)]
     return lib
 
 
@@ -200,6 +209,34 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+ORDER_CLUSTER, ORDER_BALANCE = 0, 1
+
+
+def neuron_counts(idx, count, counts, stream=None):
+    """counts[idx[q]] += 1 for q < count (device int32 tensors; sffn_neuron_counts)."""
+    import torch
+    s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+    st = _lib.sffn_neuron_counts(idx.data_ptr(), count.data_ptr(), int(counts.numel()), counts.data_ptr(), s)
+    if st != SFFN_OK:
+        raise SffnError(st, "sffn_neuron_counts")
+
+
+def frequency_order(counts, mode=ORDER_CLUSTER, block=1):
+    """Host int32 counts [d_ff] -> perm [d_ff] (sffn_frequency_order)."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    perm = np.empty(c.size, np.int32)
+    st = _lib.sffn_frequency_order(c.ctypes.data, int(c.size), int(mode), int(block), perm.ctypes.data)
+    if st != SFFN_OK:
+        raise SffnError(st, "sffn_frequency_order")
+    return perm
+
+
+def decode_block_rows(d_ff: int) -> int:
+    """Consecutive neurons per workgroup of the batch-1 kernel (sffn_decode_block_rows)."""
+    return int(_lib.sffn_decode_block_rows(int(d_ff)))
+
+
 class Layer:
     """One FFN layer on the current CUDA (HIP) device.
 
@@ -210,7 +247,7 @@ class Layer:
     """
 
     def __init__(self, d_model, d_ff, max_rows, wtype, act, weights, rmsnorm=False, residual=False,
-                 eps=1e-6, layouts=LAYOUT_DECODE, stream=None):
+                 eps=1e-6, layouts=LAYOUT_DECODE, stream=None, perm=None):
         import torch
         self.desc = LayerDesc(int(d_model), int(d_ff), int(max_rows), int(wtype), int(act),
                               int(bool(rmsnorm)), int(bool(residual)), float(eps), int(layouts))
@@ -222,10 +259,18 @@ class Layer:
         self.scratch = torch.empty(sb, dtype=torch.uint8, device=dev)
         self.persistent_bytes, self.scratch_bytes = pb, sb
         s = self._stream(stream)
-        st, h = sffn_create(self.desc, _ptr(weights["w_gate"]), _ptr(weights["w_up"]),
-                            _ptr(weights["w_down"]), _ptr(weights.get("s_gate")),
-                            _ptr(weights.get("s_up")), _ptr(weights.get("s_down")),
-                            self.persistent.data_ptr(), pb, s)
+        if perm is None:
+            st, h = sffn_create(self.desc, _ptr(weights["w_gate"]), _ptr(weights["w_up"]),
+                                _ptr(weights["w_down"]), _ptr(weights.get("s_gate")),
+                                _ptr(weights.get("s_up")), _ptr(weights.get("s_down")),
+                                self.persistent.data_ptr(), pb, s)
+        else:
+            # perm: device int32 [d_ff], new neuron j = original neuron perm[j]
+            hh = C.c_void_p()
+            st = _lib.sffn_create_permuted(C.byref(self.desc), _ptr(weights["w_gate"]), _ptr(weights["w_up"]),
+                                           _ptr(weights["w_down"]), perm.data_ptr(), self.persistent.data_ptr(),
+                                           pb, s, C.byref(hh))
+            h = hh.value
         if st != SFFN_OK:
             raise SffnError(st, "sffn_create")
         self.handle = h

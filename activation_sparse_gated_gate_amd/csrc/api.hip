@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "sffn_internal.h"
 
 namespace sffn {
@@ -160,9 +162,10 @@ sffn_status sffn_workspace_size(const sffn_layer_desc *desc, size_t *persistent_
     return SFFN_OK;
 }
 
-sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const void *w_up, const void *w_down,
-                        const void *s_gate, const void *s_up, const void *s_down, void *persistent,
-                        size_t persistent_bytes, void *stream, sffn_t *out)
+static sffn_status create_layer(const sffn_layer_desc *desc, const void *w_gate, const void *w_up,
+                               const void *w_down, const void *s_gate, const void *s_up, const void *s_down,
+                               const int32_t *perm, void *persistent, size_t persistent_bytes, void *stream,
+                               sffn_t *out)
 {
     sffn_status why;
     if (!desc_ok(desc, &why)) return why;
@@ -204,7 +207,20 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
         L.wgt = (const uint16_t *)(base + P.wgt);
     }
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_relayout(L, w_gate, w_up, w_down, s_gate, s_up, s_down, base, st);
+    hipError_t e = hipSuccess;
+    const int32_t *ilv_perm = nullptr;
+    if (perm) {
+        // the permuted natural copies first; every other layout is built from them
+        e = launch_permute_weights(*desc, w_gate, w_up, w_down, perm, base, st);
+        if (dec) {
+            w_gate = base + P.wg;
+            w_up = base + P.wu;
+        } else {
+            ilv_perm = perm;
+        }
+        w_down = base + P.wd;
+    }
+    if (e == hipSuccess) e = launch_relayout(L, w_gate, w_up, w_down, s_gate, s_up, s_down, base, st, ilv_perm);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
         delete h;
@@ -212,6 +228,38 @@ sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const v
     }
     *out = h;
     return SFFN_OK;
+}
+
+sffn_status sffn_create(const sffn_layer_desc *desc, const void *w_gate, const void *w_up, const void *w_down,
+                        const void *s_gate, const void *s_up, const void *s_down, void *persistent,
+                        size_t persistent_bytes, void *stream, sffn_t *out)
+{
+    return create_layer(desc, w_gate, w_up, w_down, s_gate, s_up, s_down, nullptr, persistent, persistent_bytes,
+                        stream, out);
+}
+
+sffn_status sffn_create_permuted(const sffn_layer_desc *desc, const void *w_gate, const void *w_up,
+                                 const void *w_down, const int32_t *perm, void *persistent, size_t persistent_bytes,
+                                 void *stream, sffn_t *out)
+{
+    sffn_status why;
+    if (!desc_ok(desc, &why)) return why;
+    if (desc->wtype == SFFN_W_INT4_G128) return SFFN_ERR_UNSUPPORTED;
+    if (!perm) return SFFN_ERR_INVALID_ARG;
+    // the permutation is checked on the host before any kernel indexes with it
+    const int f = desc->d_ff;
+    std::vector<int32_t> hp(f);
+    std::vector<char> seen(f, 0);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(hp.data(), perm, (size_t)f * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e);
+    for (int j = 0; j < f; ++j) {
+        if (hp[j] < 0 || hp[j] >= f || seen[hp[j]]) return SFFN_ERR_INVALID_ARG;
+        seen[hp[j]] = 1;
+    }
+    return create_layer(desc, w_gate, w_up, w_down, nullptr, nullptr, nullptr, perm, persistent, persistent_bytes,
+                        stream, out);
 }
 
 void sffn_destroy(sffn_t layer) { delete layer; }

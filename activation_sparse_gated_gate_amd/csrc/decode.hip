@@ -1567,7 +1567,7 @@ static hipError_t run_dense_gu_b1(int KC, const uint8_t *wg, const uint8_t *wu, 
 
 // rows per workgroup of the fused batch-1 kernel: one workgroup per CU when
 // d_ff allows it, never more than 48 rows
-inline int fused_rows_per_wg(int f) { return std::min(kFusedMaxRB, std::max(1, (f + 255) / 256)); }
+int fused_rows_per_wg(int f) { return std::min(kFusedMaxRB, std::max(1, (f + 255) / 256)); }
 
 // ---------------------------------------------------------------------------
 // host launchers

@@ -73,12 +73,15 @@ __global__ __launch_bounds__(256) void k_col_norms(const uint8_t *__restrict__ w
 }
 
 // prefill interleave: dst block b = [gate rows 32b..32b+31][up rows 32b..32b+31]
+// (neuron n read from source row perm[n] when a permutation is given)
 __global__ __launch_bounds__(256) void k_interleave(const uint16_t *__restrict__ wg, const uint16_t *__restrict__ wu,
-                                                    uint16_t *__restrict__ dst, int f, int d)
+                                                    uint16_t *__restrict__ dst, int f, int d,
+                                                    const int32_t *__restrict__ perm)
 {
     const int r = blockIdx.x;  // destination row, 0..2f-1
     const int b = r / (2 * kIlvRows), w = (r / kIlvRows) & 1, rr = r % kIlvRows;
-    const uint16_t *src = (w ? wu : wg) + (size_t)(b * kIlvRows + rr) * d;
+    const int n = b * kIlvRows + rr;
+    const uint16_t *src = (w ? wu : wg) + (size_t)(perm ? perm[n] : n) * d;
     uint16_t *o = dst + (size_t)r * d;
     for (int i = threadIdx.x * 8; i < d; i += 256 * 8) *(uint4 *)(o + i) = *(const uint4 *)(src + i);
 }
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void k_tile_gate_cls(const uint16_t *__restric
 
 hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up, const void *w_down,
                            const void *s_gate, const void *s_up, const void *s_down, uint8_t *base,
-                           hipStream_t st)
+                           hipStream_t st, const int32_t *ilv_perm)
 {
     const sffn_layer_desc &D = L.desc;
     const int d = D.d_model, f = D.d_ff, wt = D.wtype;
@@ -133,8 +136,11 @@ hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up,
     const size_t scl_d = (size_t)d * (f / 128) * 2;
 
     if (D.layouts & SFFN_LAYOUT_DECODE) {
-        if ((e = hipMemcpyAsync(base + P.wg, w_gate, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
-        if ((e = hipMemcpyAsync(base + P.wu, w_up, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
+        // (a permuted layer's copies are already in place)
+        if (w_gate != base + P.wg)
+            if ((e = hipMemcpyAsync(base + P.wg, w_gate, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
+        if (w_up != base + P.wu)
+            if ((e = hipMemcpyAsync(base + P.wu, w_up, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
         if (wt == SFFN_W_INT4_G128) {
             if ((e = hipMemcpyAsync(base + P.sg, s_gate, scl, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
             if ((e = hipMemcpyAsync(base + P.su, s_up, scl, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
@@ -167,7 +173,8 @@ hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // W_down natural [d][f]: dense baseline (decode) and prefill
-    if ((e = hipMemcpyAsync(base + P.wd, w_down, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
+    if (w_down != base + P.wd)
+        if ((e = hipMemcpyAsync(base + P.wd, w_down, mat, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
     if (wt == SFFN_W_INT4_G128)
         if ((e = hipMemcpyAsync(base + P.sd, s_down, scl_d, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
 
@@ -183,7 +190,8 @@ hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up,
 
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
         hipLaunchKernelGGL(k_interleave, dim3(2 * f), dim3(256), 0, st,
-                           (const uint16_t *)w_gate, (const uint16_t *)w_up, (uint16_t *)(base + P.wgu), f, d);
+                           (const uint16_t *)w_gate, (const uint16_t *)w_up, (uint16_t *)(base + P.wgu), f, d,
+                           ilv_perm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -170,8 +170,20 @@ struct PrefillForwardCall {
 };
 hipError_t launch_prefill_forward(const PrefillForwardCall &c);
 
+// ilv_perm (device, or null): the prefill interleave reads neuron n from row
+// ilv_perm[n] of w_gate / w_up
 hipError_t launch_relayout(const Layer &L, const void *w_gate, const void *w_up, const void *w_down,
                            const void *s_gate, const void *s_up, const void *s_down,
-                           uint8_t *persistent, hipStream_t stream);
+                           uint8_t *persistent, hipStream_t stream, const int32_t *ilv_perm);
+
+// gathers the neurons in the order perm (fp32 / bf16) into the persistent
+// natural-layout copies: W_down's columns always, W_gate's and W_up's rows
+// when the DECODE layout holds copies of them
+hipError_t launch_permute_weights(const sffn_layer_desc &D, const void *w_gate, const void *w_up,
+                                  const void *w_down, const int32_t *perm, uint8_t *persistent,
+                                  hipStream_t stream);
+
+// consecutive neurons per workgroup of the batch-1 fused decode kernel
+int fused_rows_per_wg(int f);
 
 }  // namespace sffn

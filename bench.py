@@ -47,13 +47,13 @@ METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; break
 # files); after any change the figure is reported as null until the counters are taken again.
 COUNTER_TRAFFIC = {
     "k_decode_b1": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
-                    "sha256_16": "2eabddc81e4918bc",
+                    "sha256_16": "c575d5597ba7db74",
                     "workload": "a = 0.1, bf16 4096 x 11008, batch 1",
-                    "fetch_kib": 52935.55, "write_kib": 4178.66, "fetch_factor": 1.9998, "write_factor": 1.0000},
+                    "fetch_kib": 52935.45, "write_kib": 4178.58, "fetch_factor": 1.9998, "write_factor": 1.0000},
     "k_expert_select": {"sources": ("experts.hip", "dev_common.h", "sffn_internal.h"),
-                        "sha256_16": "4bfc86eb8cf166e2",
+                        "sha256_16": "702342adcd26b1c6",
                         "workload": "16384 tokens x 384 experts, tau 0.5, buckets 3..6",
-                        "fetch_kib": 12313.12, "write_kib": 896.06, "fetch_factor": 1.9998, "write_factor": 1.0000},
+                        "fetch_kib": 12313.17, "write_kib": 896.07, "fetch_factor": 1.9998, "write_factor": 1.0000},
 }
 
 
@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy"])
+                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
     p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
@@ -799,6 +799,88 @@ def bench_experts(args):
 # counter calibration: a plain device-to-device copy of known size
 # ---------------------------------------------------------------------------
 
+def bench_reorder(args):
+    """Neuron order by activation frequency (WiSparse notes, section 5) on a
+    4096 x 11008 bf16 ReLU layer whose gate rows have log-normal scales (hot and
+    cold neurons): calibrate the counts on 256 tokens, then time the batch-1
+    kernel and the 8-token MFMA tile path with the neurons in their original,
+    BALANCE and CLUSTER orders (HIP graph replay, 4 rotating weight copies)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    d, f, copies = 4096, 11008, 4
+    w = synth.skewed_weights(synth.WT_BF16, d, f, synth.ACT_RELU, (1001, 1002, 1003, 1004))
+    X = synth.round_to_bf16(synth.normal_f32(1005, (args.tokens, d)))
+    b = synth.gate_offset_for_active_fraction(0.1)
+    wt = weights_dev(w)
+    lay = sf.LAYOUT_DECODE | sf.LAYOUT_BATCH
+    plain = [sf.Layer(d, f, 8, sf.W_BF16, sf.ACT_RELU, wt, layouts=lay) for _ in range(copies)]
+    Xd = dev_tensor(X)
+    pol1 = sf.make_policy("exact", gate_bias=b)
+    idx = torch.empty(f, dtype=torch.int32, device="cuda:0")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    counts = torch.zeros(f, dtype=torch.int32, device="cuda:0")
+    y1 = torch.empty((1, d), dtype=torch.float32, device="cuda:0")
+    for t in range(256):
+        plain[0].forward(pol1, Xd[t:t + 1], y1, idx_out=idx, count_out=cnt)
+        sf.neuron_counts(idx, cnt, counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    orders = {"original": np.arange(f, dtype=np.int32),
+              "balance": sf.frequency_order(c, sf.ORDER_BALANCE, sf.decode_block_rows(f)),
+              "cluster": sf.frequency_order(c, sf.ORDER_CLUSTER)}
+    layers = {"original": plain}
+    for name in ("balance", "cluster"):
+        pt = torch.from_numpy(orders[name]).to("cuda:0")
+        layers[name] = [sf.Layer(d, f, 8, sf.W_BF16, sf.ACT_RELU, wt, layouts=lay, perm=pt) for _ in range(copies)]
+    del wt
+    T = args.tokens
+    steps = min(args.steps, 1024)
+    Y = torch.empty_like(Xd)
+    res = {"calibration_tokens": 256, "mean_active": round(float(c.sum()) / 256 / f, 4),
+           "hot_share": round(float(np.sort(c)[::-1][:f // 10].sum()) / max(1, int(c.sum())), 4)}
+    rb = sf.decode_block_rows(f)
+    for name, ls in layers.items():
+        # load per batch-1 workgroup (expected active neurons of its block) and per 16-row tile at 8 tokens
+        cc = c[orders[name]].astype(np.float64) / 256
+        blk = np.add.reduceat(cc, np.arange(0, f, rb))
+        tiles = cc.reshape(-1, 16)
+        p_tile = 1.0 - np.prod(1.0 - np.minimum(tiles, 1.0), axis=1) ** 8
+
+        def run1(s0, n, ls=ls):
+            for s_ in range(s0, s0 + n):
+                ls[s_ % copies].forward(pol1, Xd[s_ % T:s_ % T + 1], Y[:1])
+        run1(0, args.warmup)
+        torch.cuda.synchronize()
+        us1 = graph_time_us(run1, steps, 64, 4)
+        out = {"b1_us": round(us1, 3), "b1_max_block_load": round(float(blk.max()), 2),
+               "b1_mean_block_load": round(float(blk.mean()), 2),
+               "b8_expected_tiles_touched": round(float(p_tile.mean()), 4)}
+        for path, key in ((1, "b8_tiles_us"), (0, "b8_auto_us")):
+            pol8 = sf.make_policy("exact", gate_bias=b, use_union=True, batch_path=path)
+
+            def run8(s0, n, ls=ls, pol8=pol8):
+                for s_ in range(s0, s0 + n):
+                    q = (8 * s_) % (T - 8)
+                    ls[s_ % copies].forward(pol8, Xd[q:q + 8], Y[q:q + 8])
+            run8(0, 8)
+            torch.cuda.synchronize()
+            out[key] = round(graph_time_us(run8, min(steps, 256), 32, 4), 3)
+        res[name] = out
+        log("reorder %s: batch 1 %.2f us, 8 tokens tiles %.2f us, auto %.2f us" %
+            (name, out["b1_us"], out["b8_tiles_us"], out["b8_auto_us"]))
+    cfg = {"workload": "neuron order by activation frequency: 4096 x 11008 bf16 ReLU layer, gate rows scaled by "
+                       "exp(0.6 z), exact gating at the offset for a = 0.1; batch 1 and 8 tokens (union)",
+           "tokens": T, "weight_copies": copies, "timing": "HIP graph replay", **res}
+    out = line("µs/layer, 8-token MFMA tile path, neurons in CLUSTER order", res["cluster"]["b8_tiles_us"], "us",
+               steps, args.warmup, round(res["cluster"]["b8_tiles_us"] / 1e3, 6), "bf16", cfg, None, None,
+               higher=False)
+    print(json.dumps(out), flush=True)
+
+
 def bench_copy(args):
     import torch
     n = 256 << 20  # 256 MiB per copy, 8 copies per run
@@ -830,7 +912,7 @@ def main():
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
      "prefill": bench_prefill, "experts": bench_experts, "breakeven": bench_breakeven,
-     "copy": bench_copy}[args.workload](args)
+     "copy": bench_copy, "reorder": bench_reorder}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -306,6 +306,54 @@ sffn_status sffn_expert_select(const float *probs, int32_t tokens, int32_t exper
                                const sffn_expert_policy *policy, int32_t *k_out, int32_t *idx_out,
                                float *w_out, void *stream);
 
+/*
+ * Neuron reordering by activation frequency (WiSparse reproduction notes,
+ * section 5: count how often each neuron is active, sort the neurons by that
+ * frequency and store the weights in that order).
+ *
+ * sffn_neuron_counts: counts[idx[q]] += 1 for q < min(*count, d_ff), on the
+ *   device; idx / count are an active list and its length as written by
+ *   sffn_select / sffn_forward (device), counts a device int32 [d_ff] the
+ *   caller zero-fills once and passes for every calibration token.  Entries
+ *   outside [0, d_ff) are ignored.  Asynchronous on `stream`.
+ *   Errors: SFFN_ERR_INVALID_ARG (null pointer, d_ff outside 1..65536).
+ *
+ * sffn_frequency_order (host memory, synchronous, no GPU work): perm[j] = the
+ *   original neuron placed at position j, from counts[d_ff] >= 0.
+ *   SFFN_ORDER_CLUSTER: neurons by (count desc, index asc), the page's order;
+ *     frequently active neurons share the 16-row tiles of the batched path.
+ *   SFFN_ORDER_BALANCE: neurons in rank order dealt in a snake
+ *     (0, 1, ..., G-1, G-1, ..., 0, 0, ...) over G = ceil(d_ff / block) blocks
+ *     of `block` consecutive positions (the last one shorter, full blocks
+ *     passed over), each block in ascending index order; with block =
+ *     sffn_decode_block_rows(d_ff) every workgroup of the batch-1 kernel gets
+ *     an equal share of hot and cold neurons.
+ *   Errors: SFFN_ERR_INVALID_ARG (null pointer, d_ff < 1, unknown mode,
+ *   block outside 1..d_ff for BALANCE, a negative count).
+ *
+ * sffn_decode_block_rows: consecutive neurons per workgroup of the batch-1
+ *   decode kernel for this d_ff (0 for d_ff < 1).
+ *
+ * sffn_create_permuted: as sffn_create for fp32 / bf16 weights (no scales),
+ *   with the neurons stored in the order perm (device int32 [d_ff], new neuron
+ *   j = original neuron perm[j]; read once, not retained).  The layer computes
+ *   the same FFN; selections, lists and g' use the new numbering (map them
+ *   back through perm).  The permutation is copied to the host and checked
+ *   before any kernel uses it.  Errors: as sffn_create, SFFN_ERR_UNSUPPORTED
+ *   for int4 weights (W_down's scale groups run along d_ff, so moving a neuron
+ *   would change its quantisation), SFFN_ERR_INVALID_ARG if perm is null or
+ *   not a permutation of 0..d_ff-1.
+ */
+enum { SFFN_ORDER_CLUSTER = 0, SFFN_ORDER_BALANCE = 1 };
+
+sffn_status sffn_neuron_counts(const int32_t *idx, const int32_t *count, int32_t d_ff, int32_t *counts,
+                               void *stream);
+sffn_status sffn_frequency_order(const int32_t *counts, int32_t d_ff, int32_t mode, int32_t block, int32_t *perm);
+int32_t sffn_decode_block_rows(int32_t d_ff);
+sffn_status sffn_create_permuted(const sffn_layer_desc *desc, const void *w_gate, const void *w_up,
+                                 const void *w_down, const int32_t *perm, void *persistent, size_t persistent_bytes,
+                                 void *stream, sffn_t *out);
+
 /* Static text for a status code. */
 const char *sffn_status_string(sffn_status status);
 

@@ -73,6 +73,8 @@ def _load():
     lib.ora_schedule_mass.argtypes = [I, I, I, D, D]
     lib.ora_schedule_mass.restype = D
     lib.ora_expert_select.argtypes = [P, I, I, F, I, I, P, P, P]
+    lib.ora_frequency_order.restype = C.c_int
+    lib.ora_frequency_order.argtypes = [P, I, I, I, P]
     lib.ora_expert_select.restype = I
     lib.ora_prefill_rows.restype = None
     lib.ora_bf16_rne.argtypes = [D]
@@ -233,6 +235,17 @@ def expert_select(probs, tau=0.5, kmin=3, kmax=6):
     if _load().ora_expert_select(_p(p), T, E, float(tau), int(kmin), int(kmax), _p(k), _p(idx), _p(w)) != 0:
         raise ValueError("oracle expert_select rejected its arguments")
     return k[:T].copy(), idx[:T].copy(), w[:T].copy()
+
+
+def frequency_order(counts, mode="cluster", block=1) -> np.ndarray:
+    """Neuron order by activation count: perm[j] = the neuron at position j
+    (mode 'cluster' or 'balance' over blocks of `block` positions)."""
+    c = _c(counts, np.int32)
+    perm = np.empty(max(c.size, 1), np.int32)
+    m = {"cluster": 0, "balance": 1}[mode]
+    if _load().ora_frequency_order(_p(c), int(c.size), m, int(block), _p(perm)) != 0:
+        raise ValueError("oracle frequency_order rejected its arguments")
+    return perm[:c.size].copy()
 
 
 def prefill_rows(weights, Y_bf16, rows, threads=None) -> np.ndarray:

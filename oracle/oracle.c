@@ -37,6 +37,8 @@
  *    fixed-budget top-K over 128-token blocks, so the kept rows form a few
  *    contiguous runs).  The three-tier layer schedule of the same section
  *    (dense_until, deep_layer_start, mass_thresh_deep) picks each layer's mass.
+ *  - Neuron order by activation frequency (WiSparse notes, section 5: count how
+ *    often each neuron is active and store the neurons sorted by that count).
  *  - Adaptive expert top-K (RedKnot article, section on adaptive expert top-K):
  *    per token, rank the routed experts by routing probability and keep the
  *    smallest bucket of the top-ranked experts whose probability mass reaches
@@ -749,4 +751,74 @@ uint16_t ora_bf16_rne(double v)
 void ora_bf16_rne_array(const double *v, size_t n, uint16_t *out)
 {
     for (size_t i = 0; i < n; ++i) out[i] = ora_bf16_rne(v[i]);
+}
+
+/*
+ * Neuron order by activation frequency (WiSparse notes, section 5, second
+ * trick: sort the neurons by how often they are active).  counts[f] >= 0.
+ *   mode 0 (cluster): perm = the neurons ranked by (count desc, index asc).
+ *   mode 1 (balance): the same ranking handed out one neuron at a time to
+ *     G = ceil(f / block) blocks of `block` positions (the last block holds
+ *     the remainder), visiting the blocks 0..G-1, then G-1..0, then 0..G-1 and
+ *     so on, and skipping a block that is full; each block lists its neurons
+ *     in ascending index, the blocks follow each other in order.
+ * Returns 0, or -1 on bad arguments.
+ */
+typedef struct { int32_t c; int32_t j; } neuron_rank;
+
+static int cmp_neuron(const void *a, const void *b)
+{
+    const neuron_rank *x = (const neuron_rank *)a, *y = (const neuron_rank *)b;
+    if (x->c != y->c) return x->c > y->c ? -1 : 1;
+    return x->j < y->j ? -1 : (x->j > y->j ? 1 : 0);
+}
+
+static int cmp_int32(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+int ora_frequency_order(const int32_t *counts, int f, int mode, int block, int32_t *perm)
+{
+    if (f < 1 || (mode != 0 && mode != 1) || (mode == 1 && (block < 1 || block > f))) return -1;
+    neuron_rank *r = (neuron_rank *)malloc((size_t)f * sizeof *r);
+    if (!r) return -1;
+    for (int j = 0; j < f; ++j) {
+        if (counts[j] < 0) { free(r); return -1; }
+        r[j].c = counts[j];
+        r[j].j = j;
+    }
+    qsort(r, (size_t)f, sizeof *r, cmp_neuron);
+    if (mode == 0) {
+        for (int k = 0; k < f; ++k) perm[k] = r[k].j;
+        free(r);
+        return 0;
+    }
+    const int G = (f + block - 1) / block;
+    int *fill = (int *)calloc((size_t)G, sizeof *fill);
+    if (!fill) { free(r); return -1; }
+    /* block g owns perm[g * block .. g * block + size_g) */
+    int g = 0, dir = 1;
+    for (int k = 0; k < f; ++k) {
+        for (;;) {
+            const int size = g == G - 1 ? f - (G - 1) * block : block;
+            const int here = g, room = fill[g] < size;
+            /* step along the snake: ... G-2, G-1, G-1, G-2 ... 1, 0, 0, 1 ... */
+            if (dir > 0) { if (g == G - 1) dir = -1; else ++g; }
+            else { if (g == 0) dir = 1; else --g; }
+            if (room) {
+                perm[here * block + fill[here]] = r[k].j;
+                ++fill[here];
+                break;
+            }
+        }
+    }
+    for (int b = 0; b < G; ++b) {
+        const int size = b == G - 1 ? f - (G - 1) * block : block;
+        qsort(perm + (size_t)b * block, (size_t)size, sizeof *perm, cmp_int32);
+    }
+    free(fill);
+    free(r);
+    return 0;
 }

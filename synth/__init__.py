@@ -182,6 +182,30 @@ def _make_weights(wtype, d, f, act, seeds, sigma_in=None, rows_sub=None):
     return FFNWeights(wtype, d, f, act, pg, pu, pd, qg, qu, qd)
 
 
+def skewed_weights(wtype, d, f, act, seeds, sigma_row=0.6):
+    """As _make_weights (fp32 / bf16), with row j of W_gate scaled by
+    exp(sigma_row * z_j), z ~ N(0, 1) from seeds[3]: neurons then differ in how
+    often they pass the gate, the skew that neuron reordering by activation
+    frequency works on (real models have hot and cold neurons; the plain
+    workloads' neurons are all alike)."""
+    sg = math.sqrt(1.0 / d)
+    sd = math.sqrt(1.0 / f)
+    scale = np.exp(sigma_row * np.random.Generator(np.random.PCG64(seeds[3])).standard_normal(f))
+    wg = (normal_f32(seeds[0], (f, d), sg).astype(np.float64) * scale[:, None]).astype(np.float32)
+    wu = normal_f32(seeds[1], (f, d), sg)
+    wd = normal_f32(seeds[2], (d, f), sd)
+    if wtype == WT_F32:
+        return FFNWeights(wtype, d, f, act, wg, wu, wd)
+    assert wtype == WT_BF16
+    return FFNWeights(wtype, d, f, act, f32_to_bf16_bits(wg), f32_to_bf16_bits(wu), f32_to_bf16_bits(wd))
+
+
+def permuted_weights(w, perm):
+    """The same layer with its neurons stored in the order perm (new j = old perm[j])."""
+    return FFNWeights(w.wtype, w.d_model, w.d_ff, w.act, np.ascontiguousarray(w.w_gate[perm]),
+                      np.ascontiguousarray(w.w_up[perm]), np.ascontiguousarray(w.w_down[:, perm]))
+
+
 # ---------------------------------------------------------------------------
 # the five workloads
 # ---------------------------------------------------------------------------

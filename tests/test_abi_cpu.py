@@ -150,3 +150,46 @@ def test_schedule_mass_matches_the_oracle():
     for du, deep in ((3, 40), (20, 40), (32, 48), (80, 80), (0, 0)):
         for layer in range(0, 82, 3):
             assert sf.sffn_schedule_mass(layer, du, deep, 0.5, 0.2) == oracle.schedule_mass(layer, du, deep, 0.5, 0.2)
+
+
+# ---------------------------------------------------------------------------
+# neuron reordering: host logic (no GPU)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("f,block,seed", [(6, 2, 1), (1408, 6, 2), (11008, 43, 3), (1000, 48, 4), (777, 1, 5),
+                                          (512, 512, 6)])
+def test_frequency_order_matches_the_oracle(f, block, seed):
+    import numpy as np
+
+    import activation_sparse_gated_gate_amd as sf
+    import oracle
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, 40, f).astype(np.int32)   # many ties
+    for mode, name in ((sf.ORDER_CLUSTER, "cluster"), (sf.ORDER_BALANCE, "balance")):
+        got = sf.frequency_order(counts, mode, block)
+        ref = oracle.frequency_order(counts, name, block)
+        assert np.array_equal(got, ref), name
+
+
+def test_frequency_order_and_create_permuted_validation():
+    import numpy as np
+
+    import activation_sparse_gated_gate_amd as sf
+    lib = sf._lib
+    c = np.zeros(8, np.int32)
+    p = np.zeros(8, np.int32)
+    assert lib.sffn_frequency_order(None, 8, 0, 1, p.ctypes.data) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_frequency_order(c.ctypes.data, 8, 2, 1, p.ctypes.data) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_frequency_order(c.ctypes.data, 8, 1, 0, p.ctypes.data) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_frequency_order(c.ctypes.data, 8, 1, 9, p.ctypes.data) == sf.SFFN_ERR_INVALID_ARG
+    c[3] = -1
+    assert lib.sffn_frequency_order(c.ctypes.data, 8, 0, 1, p.ctypes.data) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_neuron_counts(None, None, 8, None, None) == sf.SFFN_ERR_INVALID_ARG
+    assert [sf.decode_block_rows(f) for f in (0, 128, 1408, 11008, 12288, 18944)] == [0, 1, 6, 43, 48, 48]
+    h = C.c_void_p()
+    d = _desc(wtype=sf.W_INT4_G128)
+    assert lib.sffn_create_permuted(C.byref(d), 16, 16, 16, 16, 256, 1 << 40, None, C.byref(h)) == \
+        sf.SFFN_ERR_UNSUPPORTED
+    d = _desc()
+    assert lib.sffn_create_permuted(C.byref(d), 16, 16, 16, None, 256, 1 << 40, None, C.byref(h)) == \
+        sf.SFFN_ERR_INVALID_ARG

@@ -681,3 +681,49 @@ def test_layer_schedule_tiers_and_presets():
     # the dense preset keeps every layer of an 80-layer model dense
     du, mt, _ = g["presets"]["dense"]
     assert all(oracle.schedule_mass(l, du, du, mt, mt) == 1.0 for l in range(80))
+
+
+# ---------------------------------------------------------------------------
+# neuron order by activation frequency (WiSparse notes, section 5)
+# ---------------------------------------------------------------------------
+
+def test_frequency_order_hand_worked():
+    # counts 5 1 4 2 3 0: ranks 0, 2, 4, 3, 1, 5.  Balance over 3 blocks of 2:
+    # snake 0 1 2 2 1 0 -> {0, 5}, {2, 1}, {4, 3}, each block ascending.
+    c = np.array([5, 1, 4, 2, 3, 0], np.int32)
+    assert oracle.frequency_order(c, "cluster").tolist() == [0, 2, 4, 3, 1, 5]
+    assert oracle.frequency_order(c, "balance", 2).tolist() == [0, 5, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("f,seed", [(97, 1), (1408, 2), (4096, 3)])
+def test_frequency_order_cluster_is_the_ranking(f, seed):
+    c = np.random.default_rng(seed).integers(0, 9, f).astype(np.int32)
+    p = oracle.frequency_order(c, "cluster")
+    assert sorted(p.tolist()) == list(range(f))
+    cc = c[p]
+    assert np.all(cc[:-1] >= cc[1:])                      # counts never increase
+    tie = cc[:-1] == cc[1:]
+    assert np.all(p[:-1][tie] < p[1:][tie])               # ties: lower index first
+
+
+@pytest.mark.parametrize("f,block,seed", [(1408, 11, 1), (11008, 43, 2), (960, 48, 3)])
+def test_frequency_order_balance_spreads_the_counts(f, block, seed):
+    c = (np.random.default_rng(seed).pareto(1.2, f) * 10).astype(np.int32)   # a few very hot neurons
+    p = oracle.frequency_order(c, "balance", block)
+    assert sorted(p.tolist()) == list(range(f))
+    blocks = p.reshape(-1, block)
+    assert np.all(np.diff(blocks, axis=1) > 0)            # each block ascending
+    sums = c[blocks].sum(axis=1)
+    # a snake over a non-increasing sequence keeps any two blocks within one count of each other
+    assert sums.max() - sums.min() <= c.max()
+    # contiguous blocks of the original order are far less even
+    orig = c.reshape(-1, block).sum(axis=1)
+    assert sums.max() - sums.min() < orig.max() - orig.min()
+
+
+def test_frequency_order_balance_special_cases():
+    c = np.random.default_rng(7).integers(0, 5, 300).astype(np.int32)
+    # one block: every neuron in it, ascending -> the identity
+    assert np.array_equal(oracle.frequency_order(c, "balance", 300), np.arange(300))
+    # blocks of one: the first pass of the snake hands out the ranking in order
+    assert np.array_equal(oracle.frequency_order(c, "balance", 1), oracle.frequency_order(c, "cluster"))
