@@ -181,10 +181,10 @@ __global__ __launch_bounds__((RdCfg<WT, BT, OUT>::NW * 64)) void k_rowdot(const 
                 s0v[kk][r] = 0.0f;
                 if constexpr (TWO) { w1v[kk][r] = make_uint4(0, 0, 0, 0); s1v[kk][r] = 0.0f; }
                 if (ok && row < a.rows) {
-                    w0v[kk][r] = ld16(a.w0 + (size_t)row * rb + (size_t)c * 16);
+                    w0v[kk][r] = ld16_nt(a.w0 + (size_t)row * rb + (size_t)c * 16);
                     if constexpr (WT == SFFN_W_INT4_G128) s0v[kk][r] = half_bits_to_float(a.s0[(size_t)row * sst + (c >> 2)]);
                     if constexpr (TWO) {
-                        w1v[kk][r] = ld16(a.w1 + (size_t)row * rb + (size_t)c * 16);
+                        w1v[kk][r] = ld16_nt(a.w1 + (size_t)row * rb + (size_t)c * 16);
                         if constexpr (WT == SFFN_W_INT4_G128) s1v[kk][r] = half_bits_to_float(a.s1[(size_t)row * sst + (c >> 2)]);
                     }
                 }
@@ -629,7 +629,7 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
                         wv[kk][r] = make_uint4(0, 0, 0, 0);
                         sv[kk][r] = 0.0f;
                         if (ok && jrow[r] >= 0) {
-                            wv[kk][r] = ld16(a.wu + (size_t)jrow[r] * rb + (size_t)c * 16);
+                            wv[kk][r] = ld16_nt(a.wu + (size_t)jrow[r] * rb + (size_t)c * 16);
                             if constexpr (WT == SFFN_W_INT4_G128) sv[kk][r] = half_bits_to_float(a.su[(size_t)jrow[r] * sst + (c >> 2)]);
                         }
                     }
@@ -711,7 +711,7 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
     do {                                                                                         \
         const int last_ = min(ns, (jj0) + UNR) - 1;                                              \
         _Pragma("unroll") for (int u = 0; u < UNR; ++u)                                          \
-            Q[u] = *(const uint32_t *)(wcol + (size_t)jl[min((jj0) + u, last_)] * rbd);          \
+            Q[u] = __builtin_nontemporal_load((const uint32_t *)(wcol + (size_t)jl[min((jj0) + u, last_)] * rbd)); \
         G0 = jl[(jj0)] >> 7;                                                                     \
         G1 = jl[last_] >> 7;                                                                     \
         S0 = ld16(scol + (size_t)G0 * d);                                                        \
@@ -766,7 +766,7 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
                     const int j = ok ? jl[jj] : 0;
 #pragma unroll
                     for (int v = 0; v < NV; ++v)
-                        wv[u][v] = ok ? ld16(a.wdt + (size_t)j * rbd + (size_t)col * EB + 16 * v) : make_uint4(0, 0, 0, 0);
+                        wv[u][v] = ok ? ld16_nt(a.wdt + (size_t)j * rbd + (size_t)col * EB + 16 * v) : make_uint4(0, 0, 0, 0);
                 }
 #pragma unroll
                 for (int u = 0; u < UNR; ++u) {
@@ -1167,7 +1167,7 @@ template <int WT, int KC>
 __device__ __forceinline__ void load_row(uint4 (&w)[KC], const uint8_t *base, size_t rb, int row, int lane)
 {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) w[k] = ld16(base + (size_t)row * rb + (size_t)(k * 64 + lane) * 16);
+    for (int k = 0; k < KC; ++k) w[k] = ld16_nt(base + (size_t)row * rb + (size_t)(k * 64 + lane) * 16);
 }
 
 // fixed-order dot of one row (chunks in registers) with x in LDS
@@ -1292,7 +1292,7 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
 #pragma unroll
         for (int t = 0; t < DB; ++t) {
             const int q = q0 + s + S * t;
-            if (dl && q < nact) dst[t] = ld16(a.wdt + (size_t)(r0 + alist[q]) * RBYTES + coff);
+            if (dl && q < nact) dst[t] = ld16_nt(a.wdt + (size_t)(r0 + alist[q]) * RBYTES + coff);
         }
     };
     float yacc[E];
@@ -1404,7 +1404,7 @@ __global__ __launch_bounds__(kB1NT) void k_dense_down_b1(const uint8_t *__restri
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             const int c = (k0 + k) * 64 + lane;
-            w[k] = (i < d && c < nch) ? ld16(wd + (size_t)i * rb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+            w[k] = (i < d && c < nch) ? ld16_nt(wd + (size_t)i * rb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
         }
     };
     auto dot = [&](const uint4 (&w)[KG], int k0, float acc) {

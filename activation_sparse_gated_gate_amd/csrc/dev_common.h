@@ -29,6 +29,15 @@ __device__ __forceinline__ int nib(uint32_t w, int e) { return ((int)(w << (28 -
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *(const uint4 *)p; }
 
+// 16-byte load with the non-temporal (streaming) cache policy, for weights
+// that are read once per call
+typedef unsigned int sffn_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void *p)
+{
+    const sffn_u32x4 v = __builtin_nontemporal_load((const sffn_u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Unpack a 16-byte chunk of fp32 or bf16 weights into E floats (int4 is
 // consumed nibble by nibble by its callers).
 template <int WT>

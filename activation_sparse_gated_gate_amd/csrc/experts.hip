@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_expert_select(const float *__restrict__
     const float *p = probs + (size_t)t * E;
     float x[PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) x[q] = p[min(lane + 64 * q, E - 1)];   // every load issued before any use
+    for (int q = 0; q < PER; ++q) x[q] = __builtin_nontemporal_load(p + min(lane + 64 * q, E - 1));   // every load issued before any use
     int key[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) key[q] = lane + 64 * q < E ? order_key(x[q]) : INT_MIN;

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict_
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             const int c = (k0 + k) * 64 + lane;
-            v[k] = c < nch ? ld16(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+            v[k] = c < nch ? ld16_nt(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
