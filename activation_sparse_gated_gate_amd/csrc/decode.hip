@@ -898,7 +898,7 @@ __device__ __forceinline__ f32x4_t mfma_stream(const uint16_t *__restrict__ w, c
         for (int u = 0; u < U; ++u) {
             const bool ok = k + u < k1;
             const size_t o = (size_t)(k + u) * 512;
-            uint4 wa = ok ? *(const uint4 *)(w + o) : make_uint4(0, 0, 0, 0);
+            uint4 wa = ok ? ld16_nt(w + o) : make_uint4(0, 0, 0, 0);
             uint4 xa = ok ? *(const uint4 *)(xh + o) : make_uint4(0, 0, 0, 0);
             uint4 xb = ok ? *(const uint4 *)(xl + o) : make_uint4(0, 0, 0, 0);
             __builtin_memcpy(&av[u], &wa, 16);
@@ -1023,6 +1023,7 @@ constexpr int kGateStages = 2;
 // outstanding (expcnt and lgkmcnt left at their no-wait maxima)
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+template <bool NT = false>
 __device__ __forceinline__ void lds_copy16(const void *g, void *lds_wave_base)
 {
     // lane l writes bytes [16 l, 16 l + 16) of the wave's 1 KB LDS block, whose
@@ -1032,7 +1033,11 @@ __device__ __forceinline__ void lds_copy16(const void *g, void *lds_wave_base)
     // vector-memory counter itself.  Nothing else in these kernels uses M0.
     const uint32_t la = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
+    // NT: the streaming (non-temporal) cache policy, for weights read once per call
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(la) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
 }
 
 template <int BT>
@@ -1054,7 +1059,7 @@ __global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const fl
         const int st = k % S;
         // this wave's 4 RPW rows: 4 RPW x 256 B = RPW loads of 1 KB
 #pragma unroll
-        for (int q = 0; q < RPW; ++q) lds_copy16(wsrc + k * kstride + q * 512, &wsm[st][w][4 * q][0]);
+        for (int q = 0; q < RPW; ++q) lds_copy16<true>(wsrc + k * kstride + q * 512, &wsm[st][w][4 * q][0]);
         // x: 8 KB = 8 loads of 1 KB, two per wave; item = [t][half][i'], t < 16
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
