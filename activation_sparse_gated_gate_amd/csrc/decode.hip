@@ -1519,15 +1519,16 @@ __global__ __launch_bounds__(256) void k_reduce_blk(const float *__restrict__ pa
     const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
     const float *base = partial + (size_t)blockIdx.x * P * 16 + c;
     float s = 0.0f;
-    for (int p0 = g; p0 < P; p0 += 16 * 8) {
-        float v[8];
+    // 16 loads in flight per thread: one round trip for P <= 256
+    for (int p0 = g; p0 < P; p0 += 16 * 16) {
+        float v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
             const int p = p0 + 16 * u;
             v[u] = p < P ? base[(size_t)p * 16] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < 16; ++u) s += v[u];
     }
     red[g][c] = s;
     __syncthreads();
