@@ -90,7 +90,9 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         S.tscore = take(B * 4 * 2);   // scores and their sorted copy
         S.tflag = take(B * 4);
         S.pH = take(B * f * 2);       // H (bf16) for up to L gathered rows
-        S.tkeys = take(B * 8 * 2);    // token sort keys: sorted chunks of 1024, then the full order
+        // token sort keys: the sorted chunks of 1024 (the last one padded), then the full order
+        S.tkeys = take((B + 1023) / 1024 * 1024 * 8);
+        S.tsorted = take(B * 8);
     }
     S.total = o;
     return S;

@@ -677,8 +677,8 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
         if (e != hipSuccess) return e;
         attr = true;
     }
-    uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);
-    uint64_t *sorted = chunks + kMaxPrefillRows;
+    uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);     // ceil(rows / 1024) * 1024 keys
+    uint64_t *sorted = (uint64_t *)(c.scratch + S.tsorted);   // rows keys
     hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_tsort_merge, dim3(G), dim3(1024), (size_t)G * 1024 * 8, c.stream, (const uint64_t *)chunks, G,

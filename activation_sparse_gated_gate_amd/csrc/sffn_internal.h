@@ -94,7 +94,7 @@ PersistentLayout persistent_layout(const sffn_layer_desc &d);
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
     size_t xsplit, hsplit, gpart, path;                                  // decode, batches (BATCH layout)
-    size_t tscore, tflag, pH, tkeys;                                     // prefill
+    size_t tscore, tflag, pH, tkeys, tsorted;                            // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;
 };

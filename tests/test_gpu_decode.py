@@ -320,3 +320,32 @@ def test_int4_sparse_union_scales_of_a_third_group():
                 spans.append(len(set((rows >> 7).tolist())))
         assert max(spans) >= 3, "no batch reaches a third scale group"
     layer.close()
+
+
+@pytest.mark.parametrize("case", ["bf16_b1_exact", "int4_b8_topk", "bf16_b16_tiles", "bf16_b16_gather"])
+def test_decode_writes_stay_inside_the_scratch(case):
+    import torch
+    sf = _sf()
+    if case == "int4_b8_topk":
+        w = synth._make_weights(synth.WT_I4, 512, 1408, synth.ACT_SILU, (731, 732, 733))
+        B, layouts, kw = 8, None, dict(mode="topk", topk_k=300, union=True)
+    elif case == "bf16_b1_exact":
+        w = synth._make_weights(synth.WT_BF16, 1024, 2816, synth.ACT_RELU, (734, 735, 736))
+        B, layouts, kw = 1, None, dict(mode="exact", bias=synth.gate_offset_for_active_fraction(0.1))
+    else:
+        w = synth._make_weights(synth.WT_BF16, 1024, 2816, synth.ACT_SILU, (737, 738, 739))
+        B, layouts = 16, sf.LAYOUT_DECODE | sf.LAYOUT_BATCH
+        kw = dict(mode="thresh", theta=synth.gate_threshold_for_active_fraction(0.1), union=True,
+                  batch_path=1 if case.endswith("tiles") else 2)
+    x = synth.round_to_bf16(synth.normal_f32(740, (B, w.d_model)))
+    layer = make_layer(w, B, layouts=layouts)
+    guard = 1 << 20
+    sb = layer.scratch_bytes
+    big = torch.full((sb + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    layer.scratch = big[guard:guard + sb]
+    mode = kw.pop("mode")
+    _check(layer, w, x, mode, TOL[w.wtype], **kw)
+    torch.cuda.synchronize()
+    assert bool((big[:guard] == 0xA5).all()) and bool((big[guard + sb:] == 0xA5).all()), \
+        "a kernel wrote outside the scratch"
+    layer.close()

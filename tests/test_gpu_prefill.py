@@ -155,3 +155,34 @@ def test_cfg5_selection_and_sampled_rows(cfg5, mass):
     assert np.array_equal(X[rest], Y[rest])
     frac = keep.size / Y.shape[0]
     print("mass %.1f kept %d (%.4f)" % (mass, keep.size, frac))
+
+
+def _guarded_scratch(layer, guard=1 << 20):
+    """Replace the layer's scratch by a view with 1 MiB of 0xA5 on each side."""
+    import torch
+    sb = layer.scratch_bytes
+    big = torch.full((sb + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    layer.scratch = big[guard:guard + sb]
+    return big, guard, sb
+
+
+def _guards_intact(big, guard, sb):
+    import torch
+    torch.cuda.synchronize()
+    return bool((big[:guard] == 0xA5).all()) and bool((big[guard + sb:] == 0xA5).all())
+
+
+@pytest.mark.parametrize("L", [256, 1000])
+def test_prefill_writes_stay_inside_the_scratch(L):
+    # the token sort once wrote its merged order 16384 keys past its chunks,
+    # beyond the scratch of any layer with a smaller max_rows
+    w = synth._make_weights(synth.WT_BF16, 512, 1024, synth.ACT_SILU, (721, 722, 723))
+    Y, A = synth.cfg5_activations(L=L, d=512)
+    layer = make_prefill_layer(w, L)
+    big, guard, sb = _guarded_scratch(layer)
+    keep_t, cnt_t, keep = check_select(layer, A, 0.5, 64, 1)
+    X = gpu_forward(layer, Y, keep_t, cnt_t)
+    assert _guards_intact(big, guard, sb), "a kernel wrote outside the scratch"
+    ref = oracle.prefill(w, Y, keep)
+    assert rel_l2(synth.bf16_bits_to_f32(X), synth.bf16_bits_to_f32(ref)) <= 2e-3
+    layer.close()
