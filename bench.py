@@ -51,9 +51,9 @@ COUNTER_TRAFFIC = {
                     "workload": "a = 0.1, bf16 4096 x 11008, batch 1",
                     "fetch_kib": 52935.62, "write_kib": 4169.65, "fetch_factor": 1.9998, "write_factor": 1.0000},
     "k_expert_select": {"sources": ("experts.hip", "dev_common.h", "sffn_internal.h"),
-                        "sha256_16": "7ff6372d43f31d10",
+                        "sha256_16": "ed04238792f59b9f",
                         "workload": "16384 tokens x 384 experts, tau 0.5, buckets 3..6",
-                        "fetch_kib": 12313.19, "write_kib": 896.00, "fetch_factor": 1.9998, "write_factor": 1.0000},
+                        "fetch_kib": 12313.13, "write_kib": 896.00, "fetch_factor": 1.9998, "write_factor": 1.0000},
 }
 
 

@@ -151,3 +151,23 @@ def test_full_length_page_policy(big, mass):
     for cu in (cu_of([synth.CFG5_L]), cu_of([8192, 4096, 2048, 1024, 512, 511, 1])):
         keep = check(layer, A, cu, mass)[2]
         print("mass %.1f, %d sequences: kept %d (%.3f)" % (mass, cu.size - 1, keep.size, keep.size / synth.CFG5_L))
+
+
+def test_block_select_writes_stay_inside_the_scratch():
+    # a small layer (max_rows 300) with many one- and two-token sequences, the
+    # most per-sequence bookkeeping per scratch byte; 1 MiB of guard bytes
+    # around the scratch must stay untouched
+    import torch
+    w = synth._make_weights(synth.WT_BF16, 512, 1024, synth.ACT_SILU, (741, 742, 743))
+    Y, A = synth.cfg5_activations(L=300, d=512)
+    layer = make_layer(w, 300)
+    guard, sb = 1 << 20, layer.scratch_bytes
+    big = torch.full((sb + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    layer.scratch = big[guard:guard + sb]
+    for cu in (cu_of([300]), cu_of([1] * 150 + [2] * 75), cu_of([129, 1, 170])):
+        for mass in (0.3, 1.0):
+            check(layer, A, cu, mass)
+    torch.cuda.synchronize()
+    assert bool((big[:guard] == 0xA5).all()) and bool((big[guard + sb:] == 0xA5).all()), \
+        "a kernel wrote outside the scratch"
+    layer.close()
