@@ -30,7 +30,7 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
            "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
            "sffn_select_blocks", "sffn_schedule_mass", "sffn_neuron_counts", "sffn_frequency_order",
-           "sffn_decode_block_rows", "sffn_create_permuted")
+           "sffn_decode_block_rows", "sffn_create_permuted", "sffn_read_probe")
 
 
 class LayerDesc(C.Structure):
@@ -100,6 +100,8 @@ def _load():
     lib.sffn_frequency_order.argtypes = [P, I, I, I, P]
     lib.sffn_decode_block_rows.restype = I
     lib.sffn_decode_block_rows.argtypes = [I]
+    lib.sffn_read_probe.restype = I
+    lib.sffn_read_probe.argtypes = [P, Z, I, P, P]
     lib.sffn_create_permuted.restype = I
     lib.sffn_create_permuted.argtypes = [C.POINTER(LayerDesc), P, P, P, P, P, Z, P, C.POINTER(P)]
     return lib

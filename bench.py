@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder"])
+                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder", "read"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
     p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
@@ -881,6 +881,48 @@ def bench_reorder(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_read(args):
+    """HBM read ceiling for the decode kernels' access policy (non-temporal
+    16-byte loads): sffn_read_probe over four rotating 90.2 MB buffers (the
+    4096 x 11008 bf16 gate matrix, past the Infinity Cache together) and over
+    one 4 GiB buffer, for several grid sizes."""
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    nbytes = 11008 * 4096 * 2
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    big = torch.ones((4 << 30) // 4, dtype=torch.float32, device="cuda:0")
+    out = torch.empty(65536, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for wg in (256, 512, 1024, 2048, 4096):
+        for name, bl, nb in (("4 x 90.2 MB", bufs, nbytes), ("4 GiB", [big], 4 << 30)):
+            reps = 256 if nb == nbytes else 8
+
+            def run(n):
+                for i in range(n):
+                    if sf._lib.sffn_read_probe(bl[i % len(bl)].data_ptr(), nb, wg, out.data_ptr(), s) != 0:
+                        raise RuntimeError("sffn_read_probe failed")
+            run(8)
+            torch.cuda.synchronize()
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.record()
+            run(reps)
+            en.record()
+            torch.cuda.synchronize()
+            us = st.elapsed_time(en) * 1e3 / reps
+            rows.append({"buffer": name, "workgroups": wg, "us": round(us, 3), "GBps": round(nb / us / 1e3, 1)})
+            log("read %s, %d workgroups: %.2f us, %.0f GB/s" % (name, wg, us, nb / us / 1e3))
+    best = max((r for r in rows if r["buffer"] != "4 GiB"), key=lambda r: r["GBps"])
+    cfg = {"workload": "HBM read ceiling: non-temporal 16-byte loads, 8 in flight per thread, 256-thread "
+                       "workgroups; 4 rotating 90.2 MB buffers and one 4 GiB buffer", "results": rows}
+    out_line = line("HBM read GB/s (non-temporal 16-byte loads)", best["GBps"], "GB/s", 256, 8,
+                    round(best["us"] / 1e3, 6), "u32", cfg,
+                    {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}, None)
+    print(json.dumps(out_line), flush=True)
+
+
 def bench_copy(args):
     import torch
     n = 256 << 20  # 256 MiB per copy, 8 copies per run
@@ -912,7 +954,7 @@ def main():
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
      "prefill": bench_prefill, "experts": bench_experts, "breakeven": bench_breakeven,
-     "copy": bench_copy, "reorder": bench_reorder}[args.workload](args)
+     "copy": bench_copy, "reorder": bench_reorder, "read": bench_read}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -354,6 +354,17 @@ sffn_status sffn_create_permuted(const sffn_layer_desc *desc, const void *w_gate
                                  const void *w_down, const int32_t *perm, void *persistent, size_t persistent_bytes,
                                  void *stream, sffn_t *out);
 
+/*
+ * Diagnostics for benchmarks: reads `bytes` (a multiple of 16, 16-byte aligned
+ * device memory) once with the non-temporal 16-byte loads the decode kernels
+ * use for weights, `workgroups` x 256 threads with 8 loads in flight each, and
+ * writes one xor of the data per workgroup to out (device, `workgroups` words),
+ * so that the read is the whole work: its time gives the HBM read ceiling for
+ * that access policy.  Asynchronous on `stream`.  SFFN_ERR_INVALID_ARG for a
+ * null pointer, a misaligned buffer or size, or workgroups outside 1..65536.
+ */
+sffn_status sffn_read_probe(const void *buf, size_t bytes, int32_t workgroups, uint32_t *out, void *stream);
+
 /* Static text for a status code. */
 const char *sffn_status_string(sffn_status status);
 
