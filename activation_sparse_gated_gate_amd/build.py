@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsffn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "relayout.hip", "experts.hip", "blocks.hip", "reorder.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "relayout.hip", "experts.hip", "blocks.hip", "reorder.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
