@@ -193,3 +193,13 @@ def test_frequency_order_and_create_permuted_validation():
     d = _desc()
     assert lib.sffn_create_permuted(C.byref(d), 16, 16, 16, None, 256, 1 << 40, None, C.byref(h)) == \
         sf.SFFN_ERR_INVALID_ARG
+
+
+def test_read_probe_validation():
+    import activation_sparse_gated_gate_amd as sf
+    lib = sf._lib
+    assert lib.sffn_read_probe(None, 1024, 1, 16, None) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_read_probe(256, 1000, 1, 16, None) == sf.SFFN_ERR_INVALID_ARG     # size not a multiple of 16
+    assert lib.sffn_read_probe(264, 1024, 1, 16, None) == sf.SFFN_ERR_INVALID_ARG     # misaligned
+    assert lib.sffn_read_probe(256, 1024, 0, 16, None) == sf.SFFN_ERR_INVALID_ARG     # no workgroups
+    assert lib.sffn_read_probe(256, 1024, 1, None, None) == sf.SFFN_ERR_INVALID_ARG
