@@ -203,3 +203,12 @@ def test_read_probe_validation():
     assert lib.sffn_read_probe(264, 1024, 1, 16, None) == sf.SFFN_ERR_INVALID_ARG     # misaligned
     assert lib.sffn_read_probe(256, 1024, 0, 16, None) == sf.SFFN_ERR_INVALID_ARG     # no workgroups
     assert lib.sffn_read_probe(256, 1024, 1, None, None) == sf.SFFN_ERR_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: the benchmark exits with a message before it touches a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr
