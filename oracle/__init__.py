@@ -143,14 +143,14 @@ def down_col_norms(weights) -> np.ndarray:
 
 
 def decode(weights, x, mode="all", bias=0.0, theta=0.0, topk_k=1, union=False,
-           rmsnorm=False, eps=1e-6, residual=False, threads=None):
+           rmsnorm=False, eps=1e-6, residual=False, threads=None, outputs=True):
     """One gated-FFN layer over the rows of x (fp32 [B, d]).
 
     Returns a dict: y (fp64 [B, d]; x + y when residual), xhat, g (gate
     pre-activation + bias in the fixed fp32 order), u (TOPK only), sel (each
     token's own selection, bool [B, f]), used (the mask its output sums over),
     idx (ascending indices of the union of the used masks), wdn (TOPK column
-    norms).
+    norms).  outputs=False computes the selection only (y is None).
     """
     w = weights
     lib = _load()
@@ -167,7 +167,7 @@ def decode(weights, x, mode="all", bias=0.0, theta=0.0, topk_k=1, union=False,
     u = np.zeros((B, f), np.float32)
     sel = np.empty((B, f), np.uint8)
     used = np.empty((B, f), np.uint8)
-    y = np.empty((B, d), np.float64)
+    y = np.empty((B, d), np.float64) if outputs else None
     wdn = np.zeros(f, np.float64)
     rc = lib.ora_decode(w.wtype, d, f, w.act, _p(wg), _p(sg), _p(wu), _p(su), _p(wd), _p(sd),
                         int(rmsnorm), float(eps), int(residual), m, float(bias), float(theta),

@@ -317,7 +317,8 @@ static double act64(int act, double z)
  *   used  [rows][f]   1 where the token's output sums neuron j, may be NULL
  *   y     [rows][d]   fp64: W_down (used (.) act(W_gate x_hat + b) (.) (W_up x_hat)),
  *                     plus x when residual is set.  Every dot product here is a
- *                     plain ascending fp64 sum.
+ *                     plain ascending fp64 sum.  NULL: the selection only (the
+ *                     outputs are not computed).
  *   wdn   [f]         column norms used by TOPK, may be NULL
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
@@ -392,7 +393,7 @@ int ora_decode(int wt, int d, int f, int act,
 
     /* outputs in fp64 over the used neurons, ascending j */
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int t = 0; t < rows; ++t) {
+    for (int t = 0; t < (y ? rows : 0); ++t) {
         const float *xht = xh + (size_t)t * d;
         const uint8_t *use = use_union ? uni : sel + (size_t)t * f;
         double *yt = y + (size_t)t * d;
@@ -463,7 +464,10 @@ static int cmp_tok(const void *a, const void *b)
  * prefix of the sorted scores; total = cum[L-1]; P = the shortest prefix of the
  * sorted order with cum >= mass * total (empty when mass <= 0); S = P plus the
  * last recent_n tokens; then the highest-ranked tokens not yet in S are added
- * until |S| >= min_keep; mass >= 1 or total == 0 selects every token.
+ * until |S| >= min_keep; mass >= 1 or total == 0 selects every token.  The
+ * pages define the mass only for finite scores; a total that is not finite (a
+ * NaN or infinite score) is read like the degenerate all-zero row: every token
+ * is kept, so the FFN runs densely rather than on an arbitrary prefix.
  *
  * keep [L] receives S in ascending token order; returns |S| (or -1).
  * order [L] (optional) receives the sorted token order, cum [L] (optional) the
@@ -493,7 +497,7 @@ int ora_token_select(const float *s, int L, double mass, int recent_n, int min_k
     }
     double total = cum[L - 1];
 
-    if (mass >= 1.0 || total == 0.0) {
+    if (mass >= 1.0 || total == 0.0 || !isfinite(total)) {
         for (int i = 0; i < L; ++i) in[i] = 1;
     } else {
         if (mass > 0.0) {
@@ -531,7 +535,7 @@ int ora_token_select(const float *s, int L, double mass, int recent_n, int min_k
  * short).  Per sequence:
  *   S_b   = sum of the block's scores (C9), blocks ranked by (S_b desc, b asc);
  *   c_k   = sum of the k top-ranked S_b (C9), total = c_nb;
- *   mass >= 1 or total == 0: every block;
+ *   mass >= 1, total == 0 or a total that is not finite: every block;
  *   else K = smallest k with c_k >= mass * total (0 if mass <= 0), then
  *        K = max(min(K, floorf(nb * max_full)), ceilf(nb * min_full))
  *        (the lower bound wins when rounding crosses them), the top K blocks,
@@ -576,7 +580,7 @@ int ora_block_select(const float *s, int rows, const int32_t *cu, int nseq, int 
         qsort(r, (size_t)nb, sizeof(block_rank), cmp_block);
         double total = 0.0;
         for (int k = 0; k < nb; ++k) total = total + r[k].m;
-        if (mass >= 1.0 || total == 0.0) {
+        if (mass >= 1.0 || total == 0.0 || !isfinite(total)) {
             for (int b = 0; b < nb; ++b) in[b] = 1;
         } else {
             int K = 0;

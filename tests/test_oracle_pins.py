@@ -471,6 +471,38 @@ def test_token_select_guards_and_degenerate_rows():
     assert list(oracle.token_select(tie, 0.0, 0, 3)[0]) == [0, 1, 2]        # ties: lower index
 
 
+@pytest.mark.parametrize("bad", [np.nan, np.inf])
+def test_token_select_non_finite_total_keeps_every_token(bad):
+    # a NaN or infinite score makes the total mass non-finite; the selection
+    # then keeps every token, like the all-zero row (the pages define the mass
+    # only for finite scores)
+    s = np.exp(synth.normal_f32(11, (300,))).astype(np.float32)
+    for pos in (0, 137, 299):
+        t = s.copy()
+        t[pos] = bad
+        for mass, recent, mk in ((0.3, 0, 1), (0.0, 5, 3), (0.7, 128, 1)):
+            assert list(oracle.token_select(t, mass, recent, mk)[0]) == list(range(300))
+    # one sequence with a NaN keeps all of its tokens; the other one is unaffected
+    t = s.copy()
+    t[10] = bad
+    cu = np.array([0, 150, 300], np.int32)
+    keep = oracle.block_select(t, cu, block=16, mass=0.3, min_full=0.1, max_full=0.5, recent_n=0, min_keep=1)
+    other = oracle.block_select(s[150:], np.array([0, 150], np.int32), block=16, mass=0.3, min_full=0.1,
+                                max_full=0.5, recent_n=0, min_keep=1)
+    assert list(keep) == list(range(150)) + [150 + int(i) for i in other]
+
+
+def test_selection_only_decode_equals_the_full_call():
+    w = tiny_weights(2, 256, 512, synth.ACT_SILU, seed=61)
+    x = synth.normal_f32(62, (3, 256))
+    for kw in (dict(mode="topk", topk_k=77, union=True), dict(mode="thresh", theta=0.52)):
+        full = oracle.decode(w, x, **kw)
+        sel = oracle.decode(w, x, outputs=False, **kw)
+        assert sel["y"] is None
+        for k in ("g", "u", "sel", "used", "idx"):
+            assert np.array_equal(sel[k], full[k]), k
+
+
 def test_token_select_blocked_cum_equals_exact_prefix_for_integer_scores():
     s = np.arange(1, 1001, dtype=np.float32)[::-1].copy()
     keep, order, cum = oracle.token_select(s, 0.5, 0, 0)
