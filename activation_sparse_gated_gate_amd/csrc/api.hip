@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "sffn_internal.h"
+#include "../../include/sffn_diag.h"
 
 namespace sffn {
 
@@ -93,6 +94,10 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         // token sort keys: the sorted chunks of 1024 (the last one padded), then the full order
         S.tkeys = take((B + 1023) / 1024 * 1024 * 8);
         S.tsorted = take(B * 8);
+        // the keep list and count of the last selection made with this scratch
+        // (sffn_forward in TOKENS mode reads them when it is given no list)
+        S.tkeep = take(B * 4);
+        S.tkcnt = take(4);
     }
     S.total = o;
     return S;
@@ -127,6 +132,23 @@ static bool desc_ok(const sffn_layer_desc *D, sffn_status *why)
         }
     }
     return true;
+}
+
+hipError_t allow_full_dynamic_lds(const void *kernel, std::once_flag &once, hipError_t &err, int &limit)
+{
+    std::call_once(once, [&]() {
+        int dev = 0, per_block = 0;
+        hipFuncAttributes fa{};
+        err = hipGetDevice(&dev);
+        if (err == hipSuccess) err = hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (err == hipSuccess) err = hipFuncGetAttributes(&fa, kernel);
+        if (err == hipSuccess) {
+            limit = per_block - (int)fa.sharedSizeBytes;
+            err = limit > 0 ? hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, limit)
+                            : hipErrorInvalidConfiguration;
+        }
+    });
+    return err;
 }
 
 }  // namespace sffn
@@ -312,6 +334,14 @@ static sffn_status policy_ok(const sffn_layer *h, const sffn_policy *p)
     if (p->use_union != 0 && p->use_union != 1) return SFFN_ERR_INVALID_ARG;
     if (p->batch_path < 0 || p->batch_path > 2) return SFFN_ERR_INVALID_ARG;
     if (p->mode == SFFN_MODE_TOPK && D.act != SFFN_ACT_SILU) return SFFN_ERR_UNSUPPORTED;
+    if (p->mode == SFFN_MODE_THRESH) {
+        // THRESH stands for |act(g')| > tau, taken in the gate domain as g' > theta.
+        // For SiLU the two agree only when tau exceeds SiLU's minimum depth
+        // (0.27846...), i.e. theta > 0.45511541... on the positive branch:
+        // 0.4551154f is the largest float below that bound.  For ReLU, theta >= 0.
+        if (!(p->theta == p->theta)) return SFFN_ERR_INVALID_ARG;   // NaN
+        if (D.act == SFFN_ACT_SILU ? !(p->theta > 0.4551154f) : !(p->theta >= 0.0f)) return SFFN_ERR_UNSUPPORTED;
+    }
     if (p->mode == SFFN_MODE_TOPK && D.d_ff > kMaxTopkNeurons) return SFFN_ERR_UNSUPPORTED;
     return SFFN_OK;
 }
@@ -384,7 +414,13 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
     if (scratch_bytes < scratch_layout(D).total) return SFFN_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (policy->mode == SFFN_MODE_TOKENS) {
-        if (!idx_in || !count_in || idx_out || count_out) return SFFN_ERR_INVALID_ARG;
+        if ((idx_in == nullptr) != (count_in == nullptr) || idx_out || count_out) return SFFN_ERR_INVALID_ARG;
+        if (!idx_in) {
+            // no list given: the keep list the last selection on this scratch left there
+            const ScratchLayout S = scratch_layout(D);
+            idx_in = (const int32_t *)((const uint8_t *)scratch + S.tkeep);
+            count_in = (const int32_t *)((const uint8_t *)scratch + S.tkcnt);
+        }
         PrefillForwardCall c{&layer->L, (const uint16_t *)in, (uint16_t *)out, rows, idx_in, count_in,
                              (uint8_t *)scratch, st};
         return hip_status(launch_prefill_forward(c));

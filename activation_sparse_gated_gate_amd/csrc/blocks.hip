@@ -8,7 +8,8 @@
 // Per sequence [cu[q], cu[q+1]) split into nb blocks from its first token:
 //   S_b  = fp64 sum of the block's token scores in token order;
 //   rank the blocks by (S_b desc, b asc); c_k = fp64 sum of the k top-ranked
-//   S_b in rank order; mass >= 1 or c_nb == 0 keeps every block; otherwise
+//   S_b in rank order; mass >= 1, c_nb == 0 or a non-finite block mass keeps
+//   every block; otherwise
 //   K = smallest k with c_k >= mass * c_nb (0 for mass <= 0), capped at
 //   floorf(nb * max_full) and then raised to ceilf(nb * min_full); the top K
 //   blocks, every block holding one of the last recent_n tokens, and further
@@ -54,6 +55,7 @@ struct BlkArgs {
     uint8_t *flags;          // kept flag per block, sequence q's at o0 / block + q
     int32_t *counts;         // kept tokens per sequence [nseq]
     int32_t *idx_out, *count_out;
+    int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
 };
 
 __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
@@ -64,7 +66,9 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
     __shared__ uint8_t kept[kMaxBlocksPerSeq];
     __shared__ int red[256];
     const int q = blockIdx.x, tid = threadIdx.x, B = a.block;
+    __shared__ int s_bad;   // a non-finite block mass (from a NaN or infinite score)
     int o0, o1;
+    if (tid == 0) s_bad = 0;
     seq_range(a.cu, q, a.rows, &o0, &o1, red);
     const int Lq = o1 - o0;
     const int nb = (Lq + B - 1) / B;   // <= kMaxBlocksPerSeq (block >= 16, rows <= 16384)
@@ -82,6 +86,7 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
         }
         S[b] = m;
         kept[b] = 0;
+        if (!isfinite(m)) s_bad = 1;
     }
     __syncthreads();
     // rank of each block by counting; the masses are also stored in rank order
@@ -113,7 +118,10 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
     }
     __syncthreads();
     const double total = nb > 0 ? cum[nb - 1] : 0.0;
-    const bool dense = a.mass >= 1.0 || total == 0.0;
+    // a non-finite total keeps the sequence.  It is taken from the block masses
+    // themselves: a NaN mass has no rank, so the rank-order sums above do not
+    // hold it (the fp64 sum of finite fp32 scores cannot overflow)
+    const bool dense = a.mass >= 1.0 || total == 0.0 || s_bad != 0;
     if (dense) {
         for (int b = tid; b < nb; b += 256) kept[b] = 1;
     } else {
@@ -188,7 +196,10 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
         __syncthreads();
     }
     const int base_out = red[0];
-    if (q == a.nseq - 1 && tid == 0) *a.count_out = base_out + a.counts[q];
+    if (q == a.nseq - 1 && tid == 0) {
+        *a.count_out = base_out + a.counts[q];
+        *a.count_copy = base_out + a.counts[q];
+    }
     // exclusive prefix of kept block sizes: 4 blocks per thread, then the 256 partials
     const uint8_t *fl = a.flags + (size_t)(o0 / B + q);
     int v[4], sum = 0;
@@ -218,7 +229,10 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
     __syncthreads();
     for (int t = tid; t < Lq; t += 256) {
         const int b = t / B;
-        if (pos[b + 1] != pos[b]) a.idx_out[base_out + pos[b] + (t - b * B)] = o0 + t;
+        if (pos[b + 1] != pos[b]) {
+            a.idx_out[base_out + pos[b] + (t - b * B)] = o0 + t;
+            a.keep_copy[base_out + pos[b] + (t - b * B)] = o0 + t;
+        }
     }
 }
 
@@ -230,7 +244,8 @@ hipError_t launch_block_select(const BlockSelectCall &c)
     hipError_t e = launch_token_norms(c.A, c.rows, L.desc.d_model, sc, c.stream);
     if (e != hipSuccess) return e;
     BlkArgs a{sc, c.cu, c.rows, c.nseq, c.block, c.mass, c.min_full, c.max_full, c.recent_n, c.min_keep,
-              c.scratch + S.tkeys, (int32_t *)(c.scratch + S.tflag), c.idx_out, c.count_out};
+              c.scratch + S.tkeys, (int32_t *)(c.scratch + S.tflag), c.idx_out, c.count_out,
+              (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt)};
     hipLaunchKernelGGL(k_blk_select, dim3(c.nseq), dim3(256), 0, c.stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_blk_emit, dim3(c.nseq), dim3(256), 0, c.stream, a);

@@ -1610,13 +1610,15 @@ static hipError_t run_gather(const GatherArgs &a0, hipStream_t st)
     a.stage_x = a.mode != SFFN_MODE_TOPK;
     const size_t lds = (a.stage_x ? (size_t)BT * C::KMAX * 64 * C::E * 4 : 0) + (size_t)a.maxs * BT * 4 +
                        (size_t)a.maxs * 4 + (size_t)(a.nL + 1) * 4;
-    static bool attr_set = false;
-    if (lds > 65536 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gather<WT, BT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // the limit is raised once to the most any call can need (the device's LDS
+    // per workgroup), never to one call's request, so a later layer with a
+    // larger d_ff or batch still launches
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    static int lds_limit = 0;
+    hipError_t e = allow_full_dynamic_lds((const void *)k_gather<WT, BT>, once, attr_err, lds_limit);
+    if (e != hipSuccess) return e;
+    if (lds > (size_t)lds_limit) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_gather<WT, BT>), dim3(P), dim3(C::NW * 64), lds, st, a);
     return hipGetLastError();
 }

@@ -10,7 +10,8 @@
 //      k_token_select  (one workgroup) fp64 cumulative mass in blocks of 256 sorted entries,
 //                      shortest prefix reaching mass * total, plus the last
 //                      recent_n tokens, plus top-ranked tokens up to min_keep;
-//                      mass >= 1 or total == 0 keeps every token.  Writes the
+//                      mass >= 1, total == 0 or a non-finite total keeps every
+//                      token.  Writes the
 //                      ascending keep list, its length and per-token flags, all
 //                      on the device (no host synchronisation).
 //   t3 k_gemm_big<GATE_UP> H = SiLU(Y_S W_gate^T) (.) (Y_S W_up^T), bf16 MFMA with
@@ -72,6 +73,7 @@ struct SelectArgs {
     int L, recent_n, min_keep;
     double mass;
     int32_t *keep, *count;
+    int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
     int32_t *flags;  // [L] 1 = kept
 };
 
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
             if (tid + q * NT < L) key[tid + q * NT] = kv[q];
     }
     for (int i = tid; i < L; i += NT) in[i] = 0;
-    if (tid == 0) s_m = L;
+    if (tid == 0) s_m = -1;   // no prefix unless a block finds the threshold
     __syncthreads();
     // fp64 cumulative mass in blocks of kMassBlock sorted entries: thread b adds
     // block b in order (its values loaded 32 at a time ahead of the adds) and
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
             }
         }
         const double total = base;  // equals the last cumulative value
-        s_all = (a.mass >= 1.0 || total == 0.0) ? 1 : 0;
+        // a non-finite total (a NaN or infinite score) keeps every token, like an all-zero row
+        s_all = (a.mass >= 1.0 || total == 0.0 || !isfinite(total)) ? 1 : 0;
         blk_base[nb] = total;
     }
     __syncthreads();
@@ -274,9 +277,16 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     for (int i = i0; i < i1; ++i) {
         const int on = in[i] ? 1 : 0;
         a.flags[i] = on;
-        if (on) a.keep[pos++] = i;
+        if (on) {
+            a.keep[pos] = i;
+            a.keep_copy[pos] = i;
+            ++pos;
+        }
     }
-    if (tid == 0) *a.count = tot;
+    if (tid == 0) {
+        *a.count = tot;
+        *a.count_copy = tot;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -302,7 +312,14 @@ struct GemmArgs {
     int ldo;                // row length of H (GATE_UP) or X/Y (DOWN)
     int gate;               // 0: always run; else run only if (256 x 256 tiles >= gate) == (gate_big != 0)
     int gate_big;
+    int rows;               // tokens of the call: the count and the kept indices are clamped to it
 };
+
+// The device-side count and kept indices, clamped to the call's rows: a list
+// that did not come from a selection over these rows gives wrong rows, never
+// an access outside Y, X or H.
+__device__ __forceinline__ int gemm_rows(const GemmArgs &a) { return min(max(*a.count, 0), a.rows); }
+__device__ __forceinline__ int kept_row(const GemmArgs &a, int m) { return min(max(a.keep[m], 0), a.rows - 1); }
 
 // The device-side row count decides between the two tile sizes without a host
 // round trip: with too few 256 x 256 tiles for the compute units, 128 x 128
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
     __shared__ __align__(16) uint16_t Bs[GBN * GLDA];
     __shared__ int rowsrc[GBM];
 
-    const int M = *a.count;
+    const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
     const int mt = (M + GBM - 1) / GBM;
     const int nt = a.N / GBN;
@@ -342,7 +359,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
         __syncthreads();
         if (tid < GBM) {
             const int m = m0 + tid;
-            rowsrc[tid] = m < M ? (EPI == EPI_GATE_UP ? a.keep[m] : m) : -1;
+            rowsrc[tid] = m < M ? (EPI == EPI_GATE_UP ? kept_row(a, m) : m) : -1;
         }
         __syncthreads();
 
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
                             const int rl = wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
                             const int m = m0 + rl;
                             if (m < M) {
-                                const int tok = a.keep[m];
+                                const int tok = kept_row(a, m);
                                 const int n = n0 + wn * 64 + j * 32 + ccol;
                                 const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
                                 a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
@@ -479,7 +496,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
     __shared__ __align__(1024) uint16_t Bs[BSTAGES][BBN * BBK];
     __shared__ int rowsrc[BBM];
 
-    const int M = *a.count;
+    const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
     const int mt = (M + BBM - 1) / BBM;
     const int nt = a.N / BBN;
@@ -502,7 +519,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
         {
             // rows past M read a valid row; their results are not written
             const int m = min(m0 + tid, M - 1);
-            rowsrc[tid] = EPI == EPI_GATE_UP ? a.keep[m] : m;
+            rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
         }
         __syncthreads();
         // this wave copies rows 64 w + 16 q + (lane >> 2), q = 0..3, of both
@@ -605,7 +622,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
                     for (int e = 0; e < 4; ++e) {
                         const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
                         if (m < M) {
-                            const int tok = a.keep[m];
+                            const int tok = kept_row(a, m);
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 const int n = n0 + wn * 128 + j * 32 + ccol;
@@ -625,12 +642,13 @@ __global__ __launch_bounds__(256) void k_fill_flags(int32_t *__restrict__ flags,
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= L) return;
-    int lo = 0, hi = *count;  // search [lo, hi)
+    const int n = min(max(*count, 0), L);
+    int lo = 0, hi = n;  // search [lo, hi)
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (keep[mid] < i) lo = mid + 1; else hi = mid;
     }
-    flags[i] = (lo < *count && keep[lo] == i) ? 1 : 0;
+    flags[i] = (lo < n && keep[lo] == i) ? 1 : 0;
 }
 
 // X_next rows of tokens that are not kept: a copy of Y
@@ -667,16 +685,13 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     while (N < rows) N <<= 1;
     const size_t lds = (size_t)N * 8 + (size_t)rows;
     const int G = (rows + 1023) / 1024;   // <= kMaxPrefillRows / 1024 = 16
-    static bool attr = false;
-    if (!attr) {
-        e = hipFuncSetAttribute((const void *)k_token_select, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)((size_t)kMaxPrefillRows * 8 + kMaxPrefillRows));
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)k_tsort_merge, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)((size_t)kMaxPrefillRows * 8));
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::once_flag once_sel, once_merge;
+    static hipError_t err_sel = hipSuccess, err_merge = hipSuccess;
+    static int lim_sel = 0, lim_merge = 0;
+    if ((e = allow_full_dynamic_lds((const void *)k_token_select, once_sel, err_sel, lim_sel)) != hipSuccess) return e;
+    if ((e = allow_full_dynamic_lds((const void *)k_tsort_merge, once_merge, err_merge, lim_merge)) != hipSuccess)
+        return e;
+    if (lds > (size_t)lim_sel || (size_t)G * 1024 * 8 > (size_t)lim_merge) return hipErrorInvalidConfiguration;
     uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);     // ceil(rows / 1024) * 1024 keys
     uint64_t *sorted = (uint64_t *)(c.scratch + S.tsorted);   // rows keys
     hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks);
@@ -684,7 +699,8 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     hipLaunchKernelGGL(k_tsort_merge, dim3(G), dim3(1024), (size_t)G * 1024 * 8, c.stream, (const uint64_t *)chunks, G,
                        sorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out, flags};
+    SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
+                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), flags};
     hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
     return hipGetLastError();
 }
@@ -723,6 +739,7 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     const int mt_max = (rows + GBM - 1) / GBM;
     GemmArgs g{};
     g.A = c.Y; g.B = L.wgu; g.K = d; g.N = 2 * f; g.keep = c.keep; g.count = c.count; g.H = H; g.ldo = f;
+    g.rows = rows;
     const int mt_big = (c.L->desc.max_rows + BBM - 1) / BBM;
     const int tiles1 = mt_big * (2 * f / BBN);
     hipEvent_t evb = nullptr, eve = nullptr;
@@ -734,6 +751,7 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     GemmArgs g2{};
     g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
     g2.ldo = d;
+    g2.rows = rows;
     // down projection: 256 x 256 tiles when they fill at least half of the compute
     // units, else 128 x 128 tiles (both launched; the device-side count opens one)
     const int tiles2 = mt_big * (d / BBN);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "dev_common.h"
+#include "../../include/sffn_diag.h"
 
 namespace sffn {
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sffn.h"
 
 namespace sffn {
@@ -30,6 +32,12 @@ inline size_t row_bytes(int wtype, int cols)
 }
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Raises a kernel's dynamic-LDS limit, once per process (thread-safe), to all
+// the LDS a workgroup may hold on the current device minus the kernel's static
+// LDS.  *limit receives that number of bytes; a launch asking for more must be
+// refused by the caller.
+hipError_t allow_full_dynamic_lds(const void *kernel, std::once_flag &once, hipError_t &err, int &limit);
 
 // ---------------------------------------------------------------------------
 // the handle
@@ -94,7 +102,7 @@ PersistentLayout persistent_layout(const sffn_layer_desc &d);
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
     size_t xsplit, hsplit, gpart, path;                                  // decode, batches (BATCH layout)
-    size_t tscore, tflag, pH, tkeys, tsorted;                            // prefill
+    size_t tscore, tflag, pH, tkeys, tsorted, tkeep, tkcnt;              // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;
 };

@@ -15,8 +15,13 @@
  *                     equals the dense FFN (denseflux, sections 3 and 5.1-5.3);
  *   SFFN_MODE_THRESH  a threshold on |SiLU(W_gate x)| (denseflux, section 4.1),
  *                     given in the gate domain: neurons with fl32(g + b) > theta.
- *                     For theta > 0 this equals |SiLU(g + b)| > SiLU(theta)
- *                     whenever SiLU(theta) exceeds SiLU's minimum depth 0.2785;
+ *                     This equals |SiLU(g + b)| > SiLU(theta) exactly when
+ *                     SiLU(theta) exceeds SiLU's minimum depth 0.27846..., i.e.
+ *                     theta > 0.45511541...: for SiLU layers a theta at or below
+ *                     that bound (theta <= 0.4551154f, the largest float below
+ *                     it) is SFFN_ERR_UNSUPPORTED; for ReLU layers theta must be
+ *                     >= 0 (|ReLU(g)| > theta), else SFFN_ERR_UNSUPPORTED; a
+ *                     NaN theta is SFFN_ERR_INVALID_ARG;
  *   SFFN_MODE_TOPK    weight-aware top-k: the topk_k neurons with the largest
  *                     score |SiLU(g + b) * u| * ||W_down[:, j]||_2, ties to the
  *                     lower index (WiSparse reproduction notes, sections 2.3 and
@@ -30,7 +35,9 @@
  *                     mass reaches mass_thresh of the total, plus the last
  *                     recent_n tokens, plus top-ranked tokens up to min_keep;
  *                     mass_thresh >= 1 or an all-zero score row keeps every
- *                     token; X_next = Y + FFN(Y) on kept rows, Y elsewhere.
+ *                     token (so does a NaN or infinite score, which makes the
+ *                     total mass non-finite); X_next = Y + FFN(Y) on kept
+ *                     rows, Y elsewhere.
  *
  * Conventions for every entry point:
  *  - Every pointer named *device* is HIP device memory; descriptors and
@@ -44,7 +51,11 @@
  *  - Argument validation happens before any launch and returns a status;
  *    no exception or abort crosses the ABI.  After SFFN_ERR_HIP the outputs
  *    are undefined and the handle stays valid.
- *  - Non-finite inputs are undefined behaviour (not detected).
+ *  - Non-finite inputs give undefined values (not detected), except that a
+ *    non-finite token score keeps every token (see SFFN_MODE_TOKENS); no
+ *    input makes a kernel access memory outside the buffers it was given.
+ *  - Diagnostics used by benchmarks (a read-bandwidth probe, per-launch kernel
+ *    timing) are declared in sffn_diag.h.
  *  - Calls on one handle from different streams need distinct scratch buffers.
  */
 #ifndef SFFN_H
@@ -201,9 +212,16 @@ sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in,
  *    alias in.  idx_in / count_in must be NULL.  idx_out / count_out
  *    (optional, device) receive the ascending union list as in sffn_select.
  *  TOKENS: `in` = Y bf16 [rows][d_model]; `out` = X_next bf16 [rows][d_model];
- *    idx_in / count_in (device, required) = the keep list from sffn_select.
- *    X_next may alias Y: then only kept rows are written.  Otherwise un-kept
- *    rows are copied bit for bit.  idx_out / count_out must be NULL.
+ *    idx_in / count_in (device) = the keep list from sffn_select or
+ *    sffn_select_blocks.  Both NULL: the forward runs on the selection that
+ *    the last sffn_select (TOKENS) or sffn_select_blocks call made with this
+ *    same scratch buffer left in it (stream-ordered; the attention output A is
+ *    only ever passed to the selection call); the result is undefined if no
+ *    such call preceded it on this scratch (the kernels clamp the count and
+ *    the indices to [0, rows), so no access leaves the buffers).  One NULL and
+ *    the other not is SFFN_ERR_INVALID_ARG.  X_next may alias Y: then only
+ *    kept rows are written.  Otherwise un-kept rows are copied bit for bit.
+ *    idx_out / count_out must be NULL.
  */
 sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows,
                          void *out, const int32_t *idx_in, const int32_t *count_in,
@@ -354,37 +372,11 @@ sffn_status sffn_create_permuted(const sffn_layer_desc *desc, const void *w_gate
                                  const void *w_down, const int32_t *perm, void *persistent, size_t persistent_bytes,
                                  void *stream, sffn_t *out);
 
-/*
- * Diagnostics for benchmarks: reads `bytes` (a multiple of 16, 16-byte aligned
- * device memory) once with the non-temporal 16-byte loads the decode kernels
- * use for weights, `workgroups` x 256 threads with 8 loads in flight each, and
- * writes one xor of the data per workgroup to out (device, `workgroups` words),
- * so that the read is the whole work: its time gives the HBM read ceiling for
- * that access policy.  Asynchronous on `stream`.  SFFN_ERR_INVALID_ARG for a
- * null pointer, a misaligned buffer or size, or workgroups outside 1..65536.
- */
-sffn_status sffn_read_probe(const void *buf, size_t bytes, int32_t workgroups, uint32_t *out, void *stream);
-
 /* Static text for a status code. */
 const char *sffn_status_string(sffn_status status);
 
 /* Last HIP error text recorded by this thread, or "" (diagnostics only). */
 const char *sffn_last_hip_error(void);
-
-/*
- * Diagnostics for benchmarks: arm per-launch timing of the path's main kernel
- * (the decode gate/selection kernel, the prefill gate-up GEMM).  The next n
- * sffn_forward calls on this handle launch that kernel with begin_events[i] /
- * end_events[i] (hipEvent_t, created by the caller with timing enabled) as its
- * dispatch start / stop events (hipExtLaunchKernel), so the pair brackets the
- * kernel's own execution; later calls record nothing.  The
- * arrays are host memory and must stay valid until those n calls are made.
- * n = 0 disarms.  Not thread-safe: do not arm a handle used by two threads.
- * layer = NULL arms the same timing, process-wide, for the entry points that
- * take no handle (sffn_expert_select and its one kernel).
- */
-sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events,
-                                  int32_t n);
 
 #ifdef __cplusplus
 }

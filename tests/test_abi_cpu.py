@@ -10,11 +10,12 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sffn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"\b(sffn_[a-z_]+)\s*\(", src)))
 
 

@@ -87,25 +87,60 @@ def test_cfg1_repeat_is_bitwise_deterministic():
 # config 2: bf16 Llama-2-7B FFN shape, a in {1.0, 0.6, 0.3, 0.1}
 # ---------------------------------------------------------------------------
 
+CFG2_TOKENS = 1024     # the benchmark's 1024 seeded tokens per active fraction
+CFG2_Y_SAMPLE = 64     # tokens whose output y is compared as well
+
+
 @pytest.fixture(scope="module")
 def cfg2():
     w = synth.cfg2_weights()
-    x = synth.cfg2_tokens(6)
+    x = synth.cfg2_tokens(CFG2_TOKENS)
     layer = make_layer(w, 1)
     yield w, x, layer
     layer.close()
 
 
+def _run_tokens_b1(layer, pol, x, keep_y):
+    """One batch-1 forward per token (the benchmark's launch configuration);
+    returns g' [T, f] (fp32 bits), the selected lists (count, idx [T, f]) and
+    y for the first keep_y tokens.  Everything stays on the device until one
+    synchronisation at the end."""
+    import torch
+    from gpu_util import tensor
+    T, f = x.shape[0], layer.desc.d_ff
+    xt = tensor(np.ascontiguousarray(x, np.float32))
+    yt = torch.empty_like(xt)
+    g_all = torch.empty((T, f), dtype=torch.float32, device=xt.device)
+    idx = torch.full((T, f), -1, dtype=torch.int32, device=xt.device)
+    cnt = torch.full((T,), -1, dtype=torch.int32, device=xt.device)
+    _, g, _ = scratch_views(layer, 1)
+    for t in range(T):
+        layer.forward(pol, xt[t:t + 1], yt[t:t + 1], idx_out=idx[t], count_out=cnt[t:t + 1])
+        g_all[t].copy_(g[0])
+    torch.cuda.synchronize()
+    return (g_all.cpu().numpy(), cnt.cpu().numpy(), idx.cpu().numpy(), yt[:keep_y].cpu().numpy())
+
+
 @pytest.mark.parametrize("a", [1.0, 0.6, 0.3, 0.1])
-def test_cfg2_full_shape(cfg2, a):
+def test_cfg2_every_token_gate_and_selection_bitwise(cfg2, a):
+    """All 1024 tokens of the benchmark at each active fraction, through the
+    batch-1 fused kernel: g' and the selected index sets bit-exact against the
+    oracle's fixed-order gate; y within 2e-3 on the first 64 tokens."""
+    sf = _sf()
     w, x, layer = cfg2
     mode = "all" if a == 1.0 else "exact"
     b = 0.0 if a == 1.0 else synth.gate_offset_for_active_fraction(a)
-    fr = []
-    for t in range(x.shape[0]):
-        y, ref, err = _check(layer, w, x[t:t + 1], mode, 2e-3, bias=b)
-        fr.append(ref["idx"].size / w.d_ff)
-    assert abs(np.mean(fr) - a) < 0.03, fr
+    g, cnt, idx, y = _run_tokens_b1(layer, sf.make_policy(mode, gate_bias=b), x, CFG2_Y_SAMPLE)
+    sel = oracle.decode(w, x, mode=mode, bias=b, outputs=False)
+    assert np.array_equal(g.view(np.uint32), sel["g"].view(np.uint32)), "gate values differ"
+    bad = [t for t in range(x.shape[0])
+           if not np.array_equal(idx[t, :cnt[t]], np.flatnonzero(sel["sel"][t]))]
+    assert not bad, "selected sets differ for tokens %s" % bad[:10]
+    fr = sel["sel"].mean()
+    assert abs(fr - a) < 0.01, fr
+    ref = oracle.decode(w, x[:CFG2_Y_SAMPLE], mode=mode, bias=b)
+    errs = [rel_l2(y[t], ref["y"][t]) for t in range(CFG2_Y_SAMPLE)]
+    assert max(errs) <= 2e-3, max(errs)
 
 
 def test_cfg2_dense_mode_matches_oracle(cfg2):
@@ -249,10 +284,14 @@ def test_all_neurons_active_exact_equals_all():
 # config 3: int4 weight-aware top-k, batch 1 and 8 (union)
 # ---------------------------------------------------------------------------
 
+CFG3_B1_TOKENS = 32    # batch-1 tokens checked per keep fraction
+CFG3_B8_BATCHES = 8    # batches of 8 checked per keep fraction
+
+
 @pytest.fixture(scope="module")
 def cfg3():
     w = synth.cfg3_weights()
-    x = synth.cfg3_tokens(16)
+    x = synth.cfg3_tokens(8 * CFG3_B8_BATCHES)
     layer = make_layer(w, 8)
     yield w, x, layer
     layer.close()
@@ -260,19 +299,86 @@ def cfg3():
 
 @pytest.mark.parametrize("pct", synth.CFG3_KEEP_PCT)
 def test_cfg3_topk_batch1(cfg3, pct):
+    """32 single-token calls per keep fraction: g', u and the top-k sets
+    bit-exact, y within 5e-3 of the oracle on the same dequantised weights."""
+    sf = _sf()
     w, x, layer = cfg3
     k = synth.topk_count(w.d_ff, pct)
-    for t in range(3):
-        _check(layer, w, x[t:t + 1], "topk", 5e-3, topk_k=k)
+    pol = sf.make_policy("topk", topk_k=k)
+    ref = oracle.decode(w, x[:CFG3_B1_TOKENS], mode="topk", topk_k=k)
+    for t in range(CFG3_B1_TOKENS):
+        y, idx, n = run_decode(layer, pol, x[t:t + 1])
+        _, g, u = scratch_views(layer, 1)
+        assert np.array_equal(g.cpu().numpy()[0].view(np.uint32), ref["g"][t].view(np.uint32)), t
+        assert np.array_equal(u.cpu().numpy()[0].view(np.uint32), ref["u"][t].view(np.uint32)), t
+        assert n == k and np.array_equal(idx, np.flatnonzero(ref["sel"][t])), t
+        assert rel_l2(y[0], ref["y"][t]) <= 5e-3, t
 
 
 @pytest.mark.parametrize("pct", synth.CFG3_KEEP_PCT)
 def test_cfg3_topk_batch8_union(cfg3, pct):
     w, x, layer = cfg3
     k = synth.topk_count(w.d_ff, pct)
-    y, ref, err = _check(layer, w, x[8:16], "topk", 5e-3, topk_k=k, union=True)
-    dens = ref["idx"].size / w.d_ff
-    assert dens > oracle.group_active_probability(pct / 100, 8) - 0.15
+    for q in range(CFG3_B8_BATCHES):
+        y, ref, err = _check(layer, w, x[8 * q:8 * q + 8], "topk", 5e-3, topk_k=k, union=True)
+        dens = ref["idx"].size / w.d_ff
+        assert dens > oracle.group_active_probability(pct / 100, 8) - 0.15
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_cfg3_int4_dense_mode_matches_all(cfg3, B):
+    """The int4 dense baseline (plain fixed-order GEMVs over W_gate, W_up and the
+    natural W_down with its [d_model][d_ff / 128] scales) against the oracle's
+    every-neuron FFN."""
+    sf = _sf()
+    w, x, layer = cfg3
+    y, _, _ = run_decode(layer, sf.make_policy("dense"), x[:B], want_list=False)
+    ref = oracle.decode(w, x[:B], mode="all")
+    assert rel_l2(y, ref["y"]) <= 5e-3
+
+
+@pytest.mark.parametrize("wt,B", [(synth.WT_F32, 4), (synth.WT_BF16, 8), (synth.WT_BF16, 16)])
+def test_dense_mode_batches(wt, B):
+    sf = _sf()
+    w = synth._make_weights(wt, 1024, 2816, synth.ACT_SILU, (1931, 1932, 1933))
+    x = synth.normal_f32(1934, (B, 1024))
+    if wt == synth.WT_BF16:
+        x = synth.round_to_bf16(x)
+    layer = make_layer(w, B)
+    y, _, _ = run_decode(layer, sf.make_policy("dense", gate_bias=0.25), x, want_list=False)
+    ref = oracle.decode(w, x, mode="all", bias=0.25)
+    assert rel_l2(y, ref["y"]) <= TOL[wt]
+    layer.close()
+
+
+def test_thresh_theta_must_express_a_threshold_on_the_activation():
+    """THRESH is |act(g')| > tau taken as g' > theta: for SiLU that needs theta
+    above 0.45511541... (SiLU(theta) beyond SiLU's minimum depth), for ReLU
+    theta >= 0; other values are refused before any launch."""
+    sf = _sf()
+    w = synth._make_weights(synth.WT_BF16, 512, 1408, synth.ACT_SILU, (1941, 1942, 1943))
+    x = synth.round_to_bf16(synth.normal_f32(1944, (1, 512)))
+    layer = make_layer(w, 1)
+    bound = np.float32(0.4551154)   # the largest float below the bound
+    for th in (0.0, 0.3, float(bound)):
+        with pytest.raises(sf.SffnError) as e:
+            run_decode(layer, sf.make_policy("thresh", theta=th), x)
+        assert e.value.status == sf.SFFN_ERR_UNSUPPORTED
+    with pytest.raises(sf.SffnError) as e:
+        run_decode(layer, sf.make_policy("thresh", theta=float("nan")), x)
+    assert e.value.status == sf.SFFN_ERR_INVALID_ARG
+    _check(layer, w, x, "thresh", 2e-3, theta=float(np.nextafter(bound, np.float32(1))))
+    layer.close()
+    wr = synth._make_weights(synth.WT_BF16, 512, 1408, synth.ACT_RELU, (1945, 1946, 1947))
+    lr = make_layer(wr, 1)
+    with pytest.raises(sf.SffnError) as e:
+        run_decode(lr, sf.make_policy("thresh", theta=-0.1), x)
+    assert e.value.status == sf.SFFN_ERR_UNSUPPORTED
+    # theta = 0 on ReLU is exact gating
+    _, i0, _ = run_decode(lr, sf.make_policy("thresh", theta=0.0), x)
+    _, i1, _ = run_decode(lr, sf.make_policy("exact"), x)
+    assert np.array_equal(i0, i1)
+    lr.close()
 
 
 def test_topk_k_equals_f_and_k_one(cfg3):
