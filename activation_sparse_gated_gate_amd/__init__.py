@@ -30,7 +30,8 @@ MODES = {"all": MODE_ALL, "exact": MODE_EXACT, "thresh": MODE_THRESH, "topk": MO
 EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", "sffn_destroy",
            "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
            "sffn_select_blocks", "sffn_schedule_mass", "sffn_neuron_counts", "sffn_frequency_order",
-           "sffn_decode_block_rows", "sffn_create_permuted", "sffn_read_probe")
+           "sffn_decode_block_rows", "sffn_create_permuted", "sffn_read_probe", "sffn_forward_noalloc",
+           "sffn_noalloc_scratch_bytes")
 
 
 class LayerDesc(C.Structure):
@@ -80,6 +81,10 @@ def _load():
     lib.sffn_select.restype = I
     lib.sffn_forward.argtypes = [P, C.POINTER(Policy), P, I, P, P, P, P, P, P, Z, P]
     lib.sffn_forward.restype = I
+    lib.sffn_forward_noalloc.argtypes = [P, C.POINTER(Policy), P, I, P, P, P, P, P, P]
+    lib.sffn_forward_noalloc.restype = I
+    lib.sffn_noalloc_scratch_bytes.argtypes = []
+    lib.sffn_noalloc_scratch_bytes.restype = Z
     lib.sffn_destroy.argtypes = [P]
     lib.sffn_destroy.restype = None
     lib.sffn_status_string.argtypes = [I]
@@ -142,6 +147,15 @@ def sffn_forward(handle, policy, inp, rows, out, idx_in, count_in, idx_out, coun
                  scratch_bytes, stream) -> int:
     return _lib.sffn_forward(handle, C.byref(policy), inp, int(rows), out, idx_in, count_in, idx_out,
                              count_out, scratch, scratch_bytes, stream)
+
+
+def sffn_forward_noalloc(handle, policy, inp, rows, out, idx_in, count_in, idx_out, count_out, stream) -> int:
+    return _lib.sffn_forward_noalloc(handle, C.byref(policy), inp, int(rows), out, idx_in, count_in, idx_out,
+                                     count_out, stream)
+
+
+def sffn_noalloc_scratch_bytes() -> int:
+    return int(_lib.sffn_noalloc_scratch_bytes())
 
 
 def sffn_destroy(handle) -> None:
@@ -303,6 +317,15 @@ class Layer:
                           self.scratch.data_ptr(), self.scratch_bytes, self._stream(stream))
         if st != SFFN_OK:
             raise SffnError(st, "sffn_forward")
+
+    def forward_noalloc(self, policy: Policy, inp, out, idx_in=None, count_in=None, idx_out=None,
+                        count_out=None, stream=None):
+        """sffn_forward_noalloc: as forward, on the library's built-in scratch."""
+        st = sffn_forward_noalloc(self.handle, policy, inp.data_ptr(), inp.shape[0], out.data_ptr(),
+                                  _ptr(idx_in), _ptr(count_in), _ptr(idx_out), _ptr(count_out),
+                                  self._stream(stream))
+        if st != SFFN_OK:
+            raise SffnError(st, "sffn_forward_noalloc")
 
     def close(self):
         if getattr(self, "handle", None):

@@ -151,6 +151,38 @@ hipError_t allow_full_dynamic_lds(const void *kernel, std::once_flag &once, hipE
     return err;
 }
 
+// ---------------------------------------------------------------------------
+// built-in scratch of sffn_forward_noalloc: one file-scope device array, which
+// every GPU the library runs on holds (its own copy) until the process ends.
+// In host code the array's name is only a host-side stand-in, never a device
+// address: the address is taken once per device with hipGetSymbolAddress and
+// only that pointer is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;   // 80 MiB
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t noalloc_scratch[kNoAllocScratchBytes];
+
+// the calling thread's current device's copy of the array (set up on the first
+// call made with that device current)
+static hipError_t noalloc_scratch_ptr(void **out)
+{
+    static std::once_flag once[kNoAllocMaxDevices];
+    static hipError_t err[kNoAllocMaxDevices];
+    static void *ptr[kNoAllocMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev]() {
+        void *p = nullptr;
+        err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+        ptr[dev] = err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (err[dev] != hipSuccess) return err[dev];
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace sffn
 
 using namespace sffn;
@@ -432,5 +464,22 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
                  rows, (const float *)in, (float *)out, idx_out, count_out, (uint8_t *)scratch, st};
     return hip_status(launch_decode(c, true));
 }
+
+sffn_status sffn_forward_noalloc(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows, void *out,
+                                 const int32_t *idx_in, const int32_t *count_in, int32_t *idx_out, int32_t *count_out,
+                                 void *stream)
+{
+    sffn_status s = policy_ok(layer, policy);
+    if (s != SFFN_OK) return s;
+    const size_t need = scratch_layout(layer->L.desc).total;
+    if (need > kNoAllocScratchBytes) return SFFN_ERR_WORKSPACE;
+    void *p = nullptr;
+    hipError_t e = noalloc_scratch_ptr(&p);
+    if (e != hipSuccess) return hip_status(e);
+    // the same validation and kernels as sffn_forward, on the built-in array
+    return sffn_forward(layer, policy, in, rows, out, idx_in, count_in, idx_out, count_out, p, need, stream);
+}
+
+size_t sffn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 }  // extern "C"

@@ -229,6 +229,28 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
                          size_t scratch_bytes, void *stream);
 
 /*
+ * sffn_forward without a scratch argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It runs exactly sffn_forward (same arguments,
+ * validation, kernels and results, bit for bit) on a scratch array built into
+ * the library: sffn_noalloc_scratch_bytes() = 80 MiB, which every GPU the
+ * library runs on holds until the process ends.  The call itself allocates
+ * nothing.  A layer whose scratch (sffn_workspace_size) exceeds the array is
+ * refused with SFFN_ERR_WORKSPACE before any launch (every decode workload
+ * here fits: the largest, d_model 3584 x d_ff 18944 at 16 tokens with the
+ * BATCH layout, needs 67 MB; long prefill layers do not).
+ * The layer's device must be current.  All calls on one GPU share that GPU's
+ * array, which keeps the last call's contents (a TOKENS forward without a keep
+ * list reads the selection left there): calls that overlap on one GPU
+ * (different streams or threads) race and must be serialised by the caller.
+ * No kernel needs the array cleared: every call writes what it reads.
+ */
+sffn_status sffn_forward_noalloc(sffn_t layer, const sffn_policy *policy, const void *in, int32_t rows,
+                                 void *out, const int32_t *idx_in, const int32_t *count_in,
+                                 int32_t *idx_out, int32_t *count_out, void *stream);
+size_t sffn_noalloc_scratch_bytes(void);
+
+/*
  * Block-granular token selection over a batch of sequences (RedKnot article:
  * at least min_keep tokens per sequence, section on the token-selective sparse
  * FFN; bounds min_full_ratio 0.10 / max_full_ratio 0.50 on the kept fraction
