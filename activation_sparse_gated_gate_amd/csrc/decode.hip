@@ -18,8 +18,10 @@
 //              only its neurons' W_up rows (u, then h = act(g') u) and W_down^T
 //              rows, accumulating a partial y with coalesced 16-byte loads.
 //   reduce     y = sum of the partials in a fixed order (+ x for the residual).
-// The dense baseline (mode DENSE) is two plain GEMV launches: gate+up fused
-// (h for every neuron), then W_down rows dotted with h.
+// The dense baseline (mode DENSE) at batch 1 is the fused kernel over every
+// neuron without a selection; at other batch sizes and for int4 it is two
+// plain fixed-order GEMV launches: gate + up (h for every neuron), then the
+// rows of the natural W_down dotted with h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1152,9 +1154,6 @@ __global__ __launch_bounds__(64) void k_gate_combine(const float *__restrict__ p
 // row load issued before x is staged into LDS, so each workgroup keeps its whole
 // share of rows in flight at once (up to 3 rows x 8 KB per wave).
 // ---------------------------------------------------------------------------
-constexpr int kB1NW = 16;                    // waves per workgroup
-constexpr int kB1NT = kB1NW * 64;
-constexpr int kB1RPW = 3;                    // rows per wave per phase
 constexpr int kFusedMaxRB = 48;              // neurons per workgroup of the fused kernel
 
 struct FusedArgs {
@@ -1365,91 +1364,6 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
     }
 }
 
-// Dense baseline, step 1: h_j = act(W_gate[j] . x + b) * (W_up[j] . x) for every
-// neuron, one row pair per wave.
-template <int WT, int KC>
-__global__ __launch_bounds__(kB1NT) void k_dense_gu_b1(const uint8_t *__restrict__ wg, const uint8_t *__restrict__ wu,
-                                                       const float *__restrict__ x, float *__restrict__ H, int f,
-                                                       int act, float bias)
-{
-    constexpr int E = Chunk<WT>::E;
-    constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
-    constexpr int D = KC * 64 * E;
-    constexpr size_t RBYTES = (size_t)D * EB;
-    __shared__ __align__(16) float xs[D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = blockIdx.x * kB1NW + wave;
-    uint4 w0[KC], w1[KC];
-    if (j < f) {
-        load_row<WT, KC>(w0, wg, RBYTES, j, lane);
-        load_row<WT, KC>(w1, wu, RBYTES, j, lane);
-    }
-    stage_vec(xs, x, D);
-    __syncthreads();
-    if (j < f) {
-        const float g = dot_row_lds<WT, KC>(w0, xs, lane);
-        const float u = dot_row_lds<WT, KC>(w1, xs, lane);
-        if (lane == 0) H[j] = act_f32(act, g + bias) * u;
-    }
-}
-
-// Dense baseline, step 2: y_i = W_down[i, :] . h (+ x_i), one row per wave,
-// chunk groups of 12 double-buffered; h staged in LDS (f <= 16384).
-template <int WT>
-__global__ __launch_bounds__(kB1NT) void k_dense_down_b1(const uint8_t *__restrict__ wd, const float *__restrict__ H,
-                                                         int d, int f, const float *__restrict__ resid,
-                                                         float *__restrict__ out)
-{
-    constexpr int E = Chunk<WT>::E;
-    constexpr int EB = WT == SFFN_W_F32 ? 4 : 2;
-    constexpr int KG = 12;
-    extern __shared__ __align__(16) float hs[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i = blockIdx.x * kB1NW + wave;
-    const int nch = f / E;
-    const size_t rb = (size_t)f * EB;
-    uint4 wa[KG], wb[KG];
-    auto load = [&](uint4 (&w)[KG], int k0) {
-#pragma unroll
-        for (int k = 0; k < KG; ++k) {
-            const int c = (k0 + k) * 64 + lane;
-            w[k] = (i < d && c < nch) ? ld16_nt(wd + (size_t)i * rb + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto dot = [&](const uint4 (&w)[KG], int k0, float acc) {
-#pragma unroll
-        for (int k = 0; k < KG; ++k) {
-            const int c = (k0 + k) * 64 + lane;
-            if (c < nch) {
-                float xv[E];
-                const float4 *xp = (const float4 *)(hs + (size_t)c * E);
-#pragma unroll
-                for (int e4 = 0; e4 < E / 4; ++e4) {
-                    const float4 v = xp[e4];
-                    xv[4 * e4 + 0] = v.x; xv[4 * e4 + 1] = v.y;
-                    xv[4 * e4 + 2] = v.z; xv[4 * e4 + 3] = v.w;
-                }
-                acc = chunk_dot<WT>(w[k], 0.0f, xv, acc);
-            }
-        }
-        return acc;
-    };
-    const int K = (nch + 63) / 64;
-    load(wa, 0);
-    stage_vec(hs, H, f);
-    __syncthreads();
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += 2 * KG) {
-        if (k0 + KG < K) load(wb, k0 + KG);
-        acc = dot(wa, k0, acc);
-        if (k0 + KG >= K) break;
-        if (k0 + 2 * KG < K) load(wa, k0 + 2 * KG);
-        acc = dot(wb, k0 + KG, acc);
-    }
-    acc = wave_tree_sum(acc);
-    if (lane == 0 && i < d) out[i] = resid ? acc + resid[i] : acc;
-}
-
 // y = sum over the partials in a fixed order (+ residual): 16 columns per
 // workgroup; thread (column, group g) sums partials g, g + 64, g + 128, ...
 // with all of its loads issued before the first add, then the 64 groups are
@@ -1559,22 +1473,6 @@ static hipError_t run_decode_b1(const FusedArgs &a, int KC, int P, hipStream_t s
     return hipErrorInvalidValue;
 }
 
-template <int WT>
-static hipError_t run_dense_gu_b1(int KC, const uint8_t *wg, const uint8_t *wu, const float *x, float *H, int f,
-                                  int act, float bias, hipStream_t st)
-{
-    const int grid = (f + kB1NW - 1) / kB1NW;
-    switch (KC) {
-#define CASE_KC(k)                                                                                         \
-    case k:                                                                                                \
-        hipLaunchKernelGGL((k_dense_gu_b1<WT, k>), dim3(grid), dim3(kB1NT), 0, st, wg, wu, x, H, f, act, bias); \
-        return hipGetLastError();
-        CASE_KC(1) CASE_KC(2) CASE_KC(3) CASE_KC(4) CASE_KC(5) CASE_KC(6) CASE_KC(7) CASE_KC(8)
-#undef CASE_KC
-    }
-    return hipErrorInvalidValue;
-}
-
 // rows per workgroup of the fused batch-1 kernel: one workgroup per CU when
 // d_ff allows it, never more than 48 rows
 int fused_rows_per_wg(int f) { return std::min(kFusedMaxRB, std::max(1, (f + 255) / 256)); }
@@ -1657,13 +1555,10 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         constexpr int E = Chunk<WT>::E;
         const int KC = d / (64 * E);
         const bool fits = d % (64 * E) == 0 && KC >= 1 && KC <= 8;
-        if (c.mode == SFFN_MODE_DENSE && fits && f <= 16384) {
-            if ((e = run_dense_gu_b1<WT>(KC, L.wg, L.wu, xin, G, f, D.act, c.bias, st)) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_dense_down_b1<WT>, dim3((d + kB1NW - 1) / kB1NW), dim3(kB1NT), (size_t)f * 4, st,
-                               L.wd, (const float *)G, d, f, D.residual ? c.x : nullptr, c.out);
-            return hipGetLastError();
-        }
-        if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && fits) {
+        // DENSE at batch 1 is the same streaming kernel over every neuron with
+        // no selection, so the dense reference reads its 3 d_model d_ff weights
+        // as fast as the sparse path reads its share
+        if (c.mode != SFFN_MODE_TOPK && fits) {
             FusedArgs fa{};
             fa.wg = L.wg; fa.wu = L.wu; fa.wdt = L.wdt;
             fa.x = xin;
@@ -1672,7 +1567,8 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             fa.list_cnt = lcnt; fa.list_idx = lidx;
             fa.f = f;
             fa.RB = fused_rows_per_wg(f);
-            fa.mode = c.mode; fa.act = D.act; fa.bias = c.bias; fa.theta = c.theta;
+            fa.mode = c.mode == SFFN_MODE_DENSE ? SFFN_MODE_ALL : c.mode;
+            fa.act = D.act; fa.bias = c.bias; fa.theta = c.theta;
             const int P = (f + fa.RB - 1) / fa.RB;
             hipEvent_t evb = nullptr, eve = nullptr;
             if (forward) L.timer->take(&evb, &eve);

@@ -85,12 +85,12 @@ def parse():
                    choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder", "read"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
-    p.add_argument("--no-dense", action="store_true", help="decode: skip the dense baseline")
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--tokens", type=int, default=1024)
     p.add_argument("--graph-steps", type=int, default=64, help="steps captured per HIP graph")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens timed on the CPU oracle (0 = skip)")
-    p.add_argument("--sweep", action="store_true", help="also time a = 0.50..1.00 in steps of 0.05")
+    p.add_argument("--no-sweep", action="store_true", help="decode: skip the a = 0.50..1.00 sweep (steps of 0.05)")
+    p.add_argument("--no-torch", action="store_true", help="decode: skip the torch F.linear dense figure")
     p.add_argument("--no-graph", action="store_true")
     return p.parse_args()
 
@@ -99,33 +99,58 @@ def parse():
 # shared timing helpers
 # ---------------------------------------------------------------------------
 
-def graph_time_us(run, n_steps, graph_steps, n_graph_variants):
-    """Mean microseconds per step: run(s0, n) launches steps s0..s0+n-1; they are
-    captured into HIP graphs of graph_steps steps and replayed."""
+def graph_time_us(run, n_steps, graph_steps, n_graph_variants=None, spread=None):
+    """Mean microseconds per step over exactly n_steps steps.  run(s0, n)
+    launches steps s0 .. s0 + n - 1; the n_steps steps are captured into HIP
+    graphs of graph_steps steps (the last one holding the remainder), each graph
+    is replayed once untimed, then every graph once in order between two
+    synchronisations: that pass is the timed one.  With a dict `spread`, events
+    recorded between the replays of the timed pass, and further untimed passes
+    until there are at least 16 replays, give the per-replay microseconds per step
+    (p10 / median / p90 in spread).  n_graph_variants is accepted for callers that
+    cap the number of distinct graphs; the steps of every graph are distinct."""
+    import numpy as np
     import torch
-    G = graph_steps
-    n_graphs = max(1, n_steps // G)
+    K = max(1, int(n_steps))
+    G = max(1, min(int(graph_steps), K))
+    sizes = [G] * (K // G) + ([K % G] if K % G else [])
     graphs = []
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for gi in range(min(n_graphs, max(1, n_graph_variants))):
+        s0 = 0
+        for n in sizes:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
-                run(gi * G, G)
+                run(s0, n)
             graphs.append(g)
+            s0 += n
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    for g in graphs[:2]:
+    for g in graphs:
         g.replay()
     torch.cuda.synchronize()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.record()
-    for i in range(n_graphs):
-        graphs[i % len(graphs)].replay()
-    en.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    ev[0].record()
+    for i, g in enumerate(graphs):
+        g.replay()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return st.elapsed_time(en) * 1e3 / (n_graphs * G)
+    total_us = ev[0].elapsed_time(ev[-1]) * 1e3
+    if spread is not None:
+        per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / sizes[i] for i in range(len(graphs))]
+        while len(per) < 16:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            i = len(per) % len(graphs)
+            e0.record()
+            graphs[i].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / sizes[i])
+        q = np.percentile(per, [10, 50, 90])
+        spread.update(p10=round(float(q[0]), 3), median=round(float(q[1]), 3), p90=round(float(q[2]), 3),
+                      replays=len(per), steps_per_replay=G)
+    return total_us / K
 
 
 def eager_time_us(run, n_steps):
@@ -224,6 +249,32 @@ def weights_dev(w):
 # decode, Llama-2-7B FFN shape, batch 1 (the headline)
 # ---------------------------------------------------------------------------
 
+def torch_dense_us(w, X, copies, steps, warmup, graph_steps):
+    """Sanity figure: the same dense ReGLU layer as three torch F.linear calls in
+    bf16 (hipBLASLt / rocBLAS GEMV at batch 1), weights rotating over `copies`
+    copies like the library's, graph-replayed over exactly `steps` steps."""
+    import torch
+    import torch.nn.functional as F
+    Wg = [dev_tensor(w.w_gate).view(torch.bfloat16) for _ in range(copies)]
+    Wu = [dev_tensor(w.w_up).view(torch.bfloat16) for _ in range(copies)]
+    Wd = [dev_tensor(w.w_down).view(torch.bfloat16) for _ in range(copies)]
+    Xb = dev_tensor(X).to(torch.bfloat16)
+    Yb = torch.empty_like(Xb)
+    T = X.shape[0]
+
+    def run(s0, n):
+        for st in range(s0, s0 + n):
+            c, t = st % copies, st % T
+            x = Xb[t:t + 1]
+            h = torch.relu(F.linear(x, Wg[c])) * F.linear(x, Wu[c])
+            Yb[t:t + 1] = F.linear(h, Wd[c])
+    run(0, warmup)
+    torch.cuda.synchronize()
+    us = graph_time_us(run, steps, graph_steps)
+    del Wg, Wu, Wd
+    return us
+
+
 def bench_decode(args):
     import numpy as np
     import torch
@@ -246,6 +297,7 @@ def bench_decode(args):
     ys = [Yd[i:i + 1] for i in range(T)]
     idx_buf = torch.empty(f, dtype=torch.int32, device="cuda:0")
     torch.cuda.synchronize()
+    K = args.steps
 
     def policy(a):
         if a >= 1.0:
@@ -262,13 +314,13 @@ def bench_decode(args):
                     L.forward(pol, xs[s % T], ys[s % T], idx_out=idx_buf, count_out=counts[s - s0:s - s0 + 1])
         return run
 
-    def time_policy(pol):
+    def time_policy(pol, spread=None):
         run = runner(pol)
         run(0, args.warmup)
         torch.cuda.synchronize()
         if args.no_graph:
-            return eager_time_us(run, args.steps)
-        return graph_time_us(run, args.steps, args.graph_steps, T // args.graph_steps)
+            return eager_time_us(run, K)
+        return graph_time_us(run, K, args.graph_steps, spread=spread)
 
     def realized_active(pol, n):
         cnt = torch.zeros(n, dtype=torch.int32, device="cuda:0")
@@ -281,41 +333,61 @@ def bench_decode(args):
         # neuron + x in and y out (fp32)
         return f * d * 2 + n_active * (2 * d * 2 + 8) + 2 * d * 4
 
-    dense_us = float("nan") if args.no_dense else time_policy(sf.make_policy("dense"))
-    log("dense: %.2f us/layer (%.0f GB/s on %.1f MB)" % (dense_us, 3 * f * d * 2 / dense_us / 1e3,
-                                                          3 * f * d * 2 / 1e6))
-    a_list = list(args.a) if args.a else [1.0, 0.6, 0.3, 0.1]
+    dense_bytes = 3 * f * d * 2 + 2 * d * 4
+    dense_spread = {}
+    dense_us = time_policy(sf.make_policy("dense"), dense_spread)
+    log("dense (fused streaming kernel, every neuron): %.2f us/layer (%.0f GB/s on %.1f MB)"
+        % (dense_us, dense_bytes / dense_us / 1e3, dense_bytes / 1e6))
+    torch_us = float("nan")
+    if not args.no_torch:
+        torch_us = torch_dense_us(w, X, args.copies, K, args.warmup, args.graph_steps)
+        log("torch F.linear dense (bf16): %.2f us/layer" % torch_us)
+    a_main = [1.0, 0.6, 0.3, 0.1]
+    a_list = list(args.a) if args.a else list(a_main)
     if 0.1 not in a_list:
         a_list.append(0.1)
-    if args.sweep:
-        a_list += [round(0.5 + 0.05 * i, 2) for i in range(10)]
+    if not args.no_sweep:
+        a_list += [a for a in [round(0.5 + 0.05 * i, 2) for i in range(10)] if a not in a_list]
     rows = {}
     for a in a_list:
         pol = policy(a)
         n_act = realized_active(pol, min(T, 256))
-        us = time_policy(pol)
-        B = bytes_alg(n_act)
-        r = dict(a=a, a_realized=round(n_act / f, 4), n_active=round(n_act, 1), us_per_layer=round(us, 3),
-                 bytes_alg=int(B), GBps=round(B / us / 1e3, 1), pct_peak=round(B / us / 1e3 / HBM_PEAK_GBS * 100, 1),
-                 speedup_vs_dense=round(dense_us / us, 3), ideal=round(3.0 / (1.0 + 2.0 * n_act / f), 3))
+        sp = {}
+        us = time_policy(pol, sp)
+        rows[a] = dict(a=a, a_realized=round(n_act / f, 4), n_active=round(n_act, 1), us_per_layer=round(us, 3),
+                       spread_us=sp, bytes_alg=int(bytes_alg(n_act)))
+    # the dense reference: the faster of the dense kernel and the sparse kernels with every neuron
+    dense_ref = min(dense_us, rows[1.0]["us_per_layer"]) if 1.0 in rows else dense_us
+    for a in a_list:
+        r = rows[a]
+        us, n_act, B = r["us_per_layer"], r["n_active"], r["bytes_alg"]
+        r.update(GBps=round(B / us / 1e3, 1), pct_peak=round(B / us / 1e3 / HBM_PEAK_GBS * 100, 1),
+                 speedup_vs_dense=round(dense_ref / us, 3), ideal=round(3.0 / (1.0 + 2.0 * n_act / f), 3))
         r["frac_of_ideal"] = round(r["speedup_vs_dense"] / r["ideal"], 3)
-        rows[a] = r
-        log("a=%.2f  n_active=%.0f  %.2f us/layer  %.0f GB/s (%.1f%% of peak)  speedup %.2fx (ideal %.2fx)"
-            % (a, n_act, us, r["GBps"], r["pct_peak"], r["speedup_vs_dense"], r["ideal"]))
+        log("a=%.2f  n_active=%.0f  %.2f us/layer (p10 %.2f, p90 %.2f)  %.0f GB/s (%.1f%% of peak)  speedup %.2fx "
+            "(ideal %.2fx)" % (a, n_act, us, r["spread_us"].get("p10", us), r["spread_us"].get("p90", us), r["GBps"],
+                              r["pct_peak"], r["speedup_vs_dense"], r["ideal"]))
 
-    fit_a = [a for a in (1.0, 0.6, 0.3, 0.1) if a in rows]
-    if len(fit_a) >= 2 and dense_us == dense_us:
+    # breakeven: the linear fit of sparse time against the realised a over the four main points, solved
+    # against the dense reference; a crossing outside [0, 1] is no breakeven.  The sweep gives the
+    # smallest measured a at which the sparse layer is no faster than dense.
+    fit_a = [a for a in a_main if a in rows]
+    breakeven, fit = None, None
+    if len(fit_a) >= 2:
         pts = [(rows[a]["a_realized"], rows[a]["us_per_layer"]) for a in fit_a]
         c, t0f = np.polyfit([p[0] for p in pts], [p[1] for p in pts], 1)
-        breakeven = float((dense_us - t0f) / c) if c > 0 else float("inf")
-    else:
-        c, t0f, breakeven = float("nan"), float("nan"), float("nan")
+        fit = {"t0_us": round(float(t0f), 3), "slope_us": round(float(c), 3)}
+        if c > 0:
+            x0 = float((dense_ref - t0f) / c)
+            breakeven = round(x0, 3) if 0.0 <= x0 <= 1.0 else None
+    swept = sorted(a for a in rows)
+    sweep_be = next((a for a in swept if rows[a]["us_per_layer"] >= dense_ref), None)
 
     pol = policy(0.1)
     run = runner(pol)
     run(0, args.warmup)
     torch.cuda.synchronize()
-    kus = main_kernel_us(layers, run, min(args.steps, 512))
+    kus = main_kernel_us(layers, run, min(max(K, 256), 512))
     k_bytes = bytes_alg(rows[0.1]["n_active"])
     achieved = k_bytes / kus / 1e3
     log("main kernel (fused gate/selection/up/down): %.2f us avg, %.0f GB/s" % (kus, achieved))
@@ -342,15 +414,26 @@ def bench_decode(args):
     cfg = {"workload": "decode gated-FFN layer, d_model 4096, d_ff 11008, bf16 weights, fp32 accumulate, "
                        "batch 1, ReLU exact gating, a = 0.1 headline",
            "tokens": T, "weight_copies": len(layers),
-           "timing": "eager" if args.no_graph else "HIP graph replay of %d-step captures" % args.graph_steps,
-           "dense_us_per_layer": round(dense_us, 3), "sweep": [rows[a] for a in a_list],
-           "breakeven_a": round(breakeven, 3),
-           "breakeven_fit": {"t0_us": round(float(t0f), 3), "slope_us": round(float(c), 3)}}
+           "timing": "eager" if args.no_graph else
+                     "exactly %d steps per point, HIP graphs of %d steps replayed once each; spread = "
+                     "microseconds per step of single graph replays" % (K, min(args.graph_steps, K)),
+           "dense_us_per_layer": round(dense_us, 3), "dense_spread_us": dense_spread,
+           "dense_kernel": "mode DENSE: the fused streaming kernel over every neuron, no selection",
+           "torch_flinear_us_per_layer": None if torch_us != torch_us else round(torch_us, 3),
+           "dense_reference_us": round(dense_ref, 3),
+           "dense_reference": "min(DENSE, sparse kernels at a = 1.0)",
+           "sweep": [rows[a] for a in sorted(rows, reverse=True)],
+           "breakeven_a": breakeven,
+           "breakeven_note": None if breakeven is not None else
+                             "none within [0, 1]: the fit of sparse time against a does not reach the dense "
+                             "reference below a = 1",
+           "breakeven_fit": fit,
+           "sweep_first_a_not_faster_than_dense": sweep_be}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("k_decode_b1"),
             "kernel": "k_decode_b1<1,8> (gate GEMV + selection + compaction + up + down partial)",
             "kernel_us": round(kus, 3), "bytes_per_launch": int(k_bytes)}
-    out = line(METRIC, head["GBps"], "GB/s", args.steps, args.warmup, round(head["us_per_layer"] / 1e3, 6),
+    out = line(METRIC, head["GBps"], "GB/s", K, args.warmup, round(head["us_per_layer"] / 1e3, 6),
                "bf16", cfg, roof, cpu)
     print(json.dumps(out), flush=True)
     for L in layers:

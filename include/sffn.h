@@ -27,7 +27,9 @@
  *                     lower index (WiSparse reproduction notes, sections 2.3 and
  *                     3.2); with use_union a batch runs over the union of its
  *                     tokens' sets (same notes, section 5, batch > 1);
- *   SFFN_MODE_DENSE   the dense FFN through plain dense GEMV kernels (baseline);
+ *   SFFN_MODE_DENSE   the dense FFN with no selection (the baseline): at batch 1
+ *                     (fp32 / bf16) the streaming kernel of the sparse path over
+ *                     every neuron, otherwise plain fixed-order GEMV kernels;
  *   SFFN_MODE_TOKENS  token-selective prefill (RedKnot article, Algorithm 1 and
  *                     the section on the token-selective sparse FFN): token
  *                     importance = L2 norm of the attention output row; keep the
