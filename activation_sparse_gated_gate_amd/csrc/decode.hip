@@ -32,6 +32,9 @@ namespace sffn {
 
 enum { OUT_GATE = 0, OUT_GATE_UP = 1, OUT_DENSE_GU = 2, OUT_DENSE_DOWN = 3 };
 
+constexpr int kFusedMaxRB = 48;   // neurons per workgroup of the batch-1 streaming kernels
+constexpr int kGuI4Waves = 8;     // waves per workgroup of the batch-1 int4 gate + up kernel
+
 // ---------------------------------------------------------------------------
 // launch configuration per weight type and batch bucket
 // ---------------------------------------------------------------------------
@@ -336,162 +339,188 @@ struct TopkArgs {
     uint32_t *bits;
 };
 
-// One workgroup per token: an exact radix select of the k-th largest score key
-// T (fp64 key = the bits of the non-negative score, so the integer order is the
-// value order), one byte per pass from the top.  Each thread keeps its keys
-// j = tid + 1024 q in registers; each group of four waves counts into its own
-// histogram (a quarter of the fold's reads).  In
-// the first pass, keys of one wave sharing a digit are counted with one atomic
-// (two ballot rounds take the most common digits first: the top bytes of fp64
-// scores are nearly all equal, and same-address LDS atomics serialize).  One wave folds the histograms, scans
-// them and picks the digit.  The select stops once every key of the chosen bin
-// is kept: the kept set is then all keys at or above the bin's floor.
-// Otherwise keep every neuron above T and, of those equal to T, the lowest
-// indices (an index-order scan).
-__global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
+// The exact top k of one token's f fp64 score keys (key = the bits of the
+// non-negative score, so the integer order is the value order), ties to the
+// lower index, decided by the 1024 threads of a workgroup: thread tid holds
+// keys j = tid + 1024 q.  Radix select from the top in 12-bit digits (key bits
+// 63..52, 51..40, 39..28, 27..16, 15..4, then 3..0): each pass counts in an LDS
+// histogram the keys that share the digits chosen so far, and a block scan in
+// descending digit order finds the digit of the k-th key; keys in higher digits
+// are kept.  It stops as soon as
+//   - the chosen bin is kept whole (every key at or above it is kept), or
+//   - the bin holds at most kTopkCand keys: these candidates are ranked exactly
+//     by pairwise comparison of (key desc, index asc) and the best ones kept.
+// Only a bin of more than kTopkCand identical keys is resolved by an
+// index-order scan (the lowest indices of the equal keys).  With scores spread
+// over many octaves two passes leave a handful of candidates.  The two
+// histograms alternate between passes and each bin is cleared as it is read.
+// Returns the thread's decisions: bit q set = key q kept.
+constexpr int kTopkCand = 256;
+
+struct TopkLds {
+    uint32_t hist[2][4096];
+    int wsum[16];
+    int s_digit, s_above, s_cnt, s_ncand;
+    uint64_t ckey[kTopkCand];
+    int cidx[kTopkCand];
+    uint32_t kept_bm[kMaxTopkNeurons / 32];
+};
+
+constexpr int kTopkPer = kMaxTopkNeurons / 1024;   // keys per thread
+
+__device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, TopkLds &L)
 {
-    constexpr int PER = kMaxTopkNeurons / 1024;
-    __shared__ int hist[4][256];   // one histogram per group of 4 waves
-    __shared__ uint64_t s_prefix;
-    __shared__ int s_kk, s_all;
-    __shared__ int tmp[17];
-    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const uint64_t *keys = a.keys + (size_t)t * a.f;
-    uint64_t kv[PER];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int j = tid + 1024 * q;
-        kv[q] = j < a.f ? keys[j] : 0;
-    }
-    for (int i = tid; i < 4 * 256; i += 1024) (&hist[0][0])[i] = 0;
+    constexpr int PER = kTopkPer, NT = 1024;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < 2 * 4096; i += NT) (&L.hist[0][0])[i] = 0;
+    for (int i = tid; i < kMaxTopkNeurons / 32; i += NT) L.kept_bm[i] = 0;
+    if (tid == 0) L.s_ncand = 0;
     __syncthreads();
     uint64_t prefix = 0, pmask = 0;
-    int kk = a.k;
-    bool all_kept = false;   // every key >= prefix is kept (no tie rule needed)
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
+    int kk = k;
+    int mode = 3;   // 1: keep the chosen bin whole, 2: rank the candidates, 3: equal keys by index
+    for (int pass = 0; pass < 6; ++pass) {
+        const int width = pass < 5 ? 12 : 4;
+        const int shift = pass < 5 ? 52 - 12 * pass : 0;
+        const int nb = 1 << width;
+        uint32_t *h = L.hist[pass & 1];
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            if (q * 1024 >= a.f) break;   // uniform
-            const int j = tid + 1024 * q;
-            const uint64_t v = kv[q];
-            const int digit = (int)((v >> shift) & 255);
-            bool act = j < a.f && (v & pmask) == prefix;
-            if (pass == 0) {   // uniform: the top bytes of the keys are nearly all equal
-#pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const uint64_t am = __ballot(act);
-                    if (am == 0) break;
-                    const int leader = __builtin_ctzll(am);
-                    const int d0 = __builtin_amdgcn_readlane(digit, leader);
-                    const bool same = act && digit == d0;
-                    const uint64_t sm = __ballot(same);
-                    if (lane == leader) atomicAdd(&hist[wave & 3][d0], __popcll(sm));
-                    act = act && !same;
-                }
-            }
-            if (act) atomicAdd(&hist[wave & 3][digit], 1);
+            if (q * NT >= f) break;   // uniform
+            const int j = tid + NT * q;
+            if (j < f && (kv[q] & pmask) == prefix) atomicAdd(&h[(int)(kv[q] >> shift) & (nb - 1)], 1u);
         }
         __syncthreads();
-        if (wave == 0) {
-            // lane l takes digits 255 - 4l ... 252 - 4l (descending); the
-            // counts are cleared for the next pass as they are read
-            int cd[4], cs = 0;
+        // thread tid owns digits nb-1-4tid .. nb-4-4tid (descending) and clears
+        // them for the pass after next; a block scan in thread order gives the
+        // keys above each digit
+        int c4[4], cs = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int dg = nb - 1 - (4 * tid + e);
+            c4[e] = 0;
+            if (dg >= 0) {
+                c4[e] = (int)h[dg];
+                h[dg] = 0;
+            }
+            cs += c4[e];
+        }
+        int incl = wave_incl_scan(cs);
+        if (lane == 63) L.wsum[wave] = incl;
+        __syncthreads();
+#pragma unroll
+        for (int w2 = 0; w2 < 16; ++w2) incl += w2 < wave ? L.wsum[w2] : 0;
+        int above = incl - cs;
+        if (above < kk && kk <= incl) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int dg = 255 - (4 * lane + e);
-                int c = 0;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    c += hist[w][dg];
-                    hist[w][dg] = 0;
+                if (above < kk && kk <= above + c4[e]) {
+                    L.s_digit = nb - 1 - (4 * tid + e);
+                    L.s_above = above;
+                    L.s_cnt = c4[e];
                 }
-                cd[e] = c;
-                cs += c;
-            }
-            int incl = cs;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
-            int above = incl - cs;
-            if (above < kk && kk <= incl) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (above < kk && kk <= above + cd[e]) {
-                        s_kk = kk - above;
-                        s_all = (kk - above) == cd[e];
-                        s_prefix = prefix | ((uint64_t)(255 - (4 * lane + e)) << shift);
-                    }
-                    above += cd[e];
-                }
+                above += c4[e];
             }
         }
         __syncthreads();
-        prefix = s_prefix;
-        kk = s_kk;
-        pmask |= (uint64_t)255 << shift;
-        if (s_all) {   // uniform
-            all_kept = true;
-            break;
-        }
+        kk -= L.s_above;   // still to keep from the chosen bin
+        prefix |= (uint64_t)L.s_digit << shift;
+        pmask |= (uint64_t)(nb - 1) << shift;
+        const int cnt = L.s_cnt;
+        if (cnt == kk) { mode = 1; break; }       // uniform
+        if (cnt <= kTopkCand) { mode = 2; break; }
     }
-    const uint64_t T = prefix;  // kk = how many keys equal to T are kept
-    // bit words from ballots: key j = 1024 q + 64 wave + lane sits in word
-    // 32 q + 2 wave + lane / 32 (f is a multiple of 32)
-    uint32_t *bits = a.bits + (size_t)t * a.nw32;
-    int base_rank = 0;   // ties before this round (index order), tie path only
+    if (mode == 2) {
+        // the candidates (keys of the chosen bin) into LDS, then each one's rank
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q * NT >= f) break;
+            const int j = tid + NT * q;
+            const bool c = j < f && (kv[q] & pmask) == prefix;
+            const uint64_t m = __ballot(c);
+            if (m == 0) continue;   // uniform in the wave
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&L.s_ncand, __popcll(m));
+            base = __shfl(base, 0, 64);
+            if (c) {
+                const int pos = base + mbcnt64(m);
+                L.ckey[pos] = kv[q];
+                L.cidx[pos] = j;
+            }
+        }
+        __syncthreads();
+        const int nc = L.s_ncand;
+        if (tid < nc) {
+            const uint64_t my = L.ckey[tid];
+            const int mi = L.cidx[tid];
+            int r = 0;
+            for (int i = 0; i < nc; ++i) {
+                const uint64_t o = L.ckey[i];
+                r += (o > my || (o == my && L.cidx[i] < mi)) ? 1 : 0;
+            }
+            if (r < kk) atomicOr(&L.kept_bm[mi >> 5], 1u << (mi & 31));
+        }
+        __syncthreads();
+    }
+    uint32_t dm = 0;
+    int base_rank = 0;   // equal keys before this round (index order), mode 3 only
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        if (q * 1024 >= a.f) break;   // uniform
-        const int j = tid + 1024 * q;
-        const uint64_t v = kv[q];
+        if (q * NT >= f) break;   // uniform
+        const int j = tid + NT * q;
+        const uint64_t v = kv[q] & pmask;
         bool on;
-        if (all_kept) {
-            on = j < a.f && v >= T;
+        if (mode == 1) {
+            on = j < f && v >= prefix;
+        } else if (mode == 2) {
+            on = j < f && (v > prefix || ((L.kept_bm[j >> 5] >> (j & 31)) & 1u));
         } else {
-            // rank of each tie among the ties in index order (a rare path: a
-            // bin that cannot be split by the remaining bytes holds equal keys)
-            const bool tie = j < a.f && v == T;
+            // more than kTopkCand keys equal to the threshold: the lowest indices
+            const bool tie = j < f && v == prefix;
             const uint64_t tm = __ballot(tie);
-            if (lane == 0) tmp[wave] = __popcll(tm);
+            if (lane == 0) L.wsum[wave] = __popcll(tm);
             __syncthreads();
             int off = 0, tot = 0;
             for (int w2 = 0; w2 < 16; ++w2) {
-                const int c2 = tmp[w2];
+                const int c2 = L.wsum[w2];
                 off += w2 < wave ? c2 : 0;
                 tot += c2;
             }
             const int below = __popcll(tm & ((1ull << lane) - 1ull));
-            on = j < a.f && (v > T || (tie && base_rank + off + below < kk));
+            on = j < f && (v > prefix || (tie && base_rank + off + below < kk));
             base_rank += tot;
             __syncthreads();
         }
-        const uint64_t m = __ballot(on);
-        const int w0 = 32 * q + 2 * wave;
-        if (q * 1024 + 64 * wave < a.f) {
-            if (lane == 0) bits[w0] = (uint32_t)m;
-            if (lane == 32) bits[w0 + 1] = (uint32_t)(m >> 32);
-        }
+        dm |= on ? (1u << q) : 0u;
+    }
+    return dm;
+}
+
+__device__ __forceinline__ void load_token_keys(uint64_t (&kv)[kTopkPer], const uint64_t *keys, int f)
+{
+#pragma unroll
+    for (int q = 0; q < kTopkPer; ++q) {
+        const int j = threadIdx.x + 1024 * q;
+        kv[q] = j < f ? keys[j] : 0;
     }
 }
 
-// union of the per-token top-k bits, compacted per 64 neurons (one wave each)
-__global__ __launch_bounds__(256) void k_mask_lists(const uint32_t *__restrict__ bits, int nw32, int B,
-                                                    int f, int *__restrict__ list_cnt,
-                                                    int *__restrict__ list_idx)
+// One workgroup per token: the token's selection as bit words (key j in bit
+// j % 64 of 64-bit word j / 64; f is a multiple of 64)
+__global__ __launch_bounds__(1024) void k_topk(const TopkArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk * 64 >= f) return;
-    const int j = blk * 64 + lane;
-    int on = 0;
-    if (j < f)
-        for (int t = 0; t < B; ++t) on |= (bits[(size_t)t * nw32 + (j >> 5)] >> (j & 31)) & 1;
-    const uint64_t m = __ballot(on);
-    if (on) list_idx[(size_t)blk * 64 + mbcnt64(m)] = j;
-    if (lane == 0) list_cnt[blk] = __popcll(m);
+    __shared__ TopkLds L;
+    const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint64_t kv[kTopkPer];
+    load_token_keys(kv, a.keys + (size_t)t * a.f, a.f);
+    const uint32_t dm = topk_decide(kv, a.f, a.k, L);
+    uint64_t *bits = (uint64_t *)(a.bits + (size_t)t * a.nw32);
+#pragma unroll
+    for (int q = 0; q < kTopkPer; ++q) {
+        if (q * 1024 >= a.f) break;   // uniform
+        const uint64_t m = __ballot((dm >> q) & 1u);
+        if (lane == 0 && q * 1024 + 64 * wave < a.f) bits[16 * q + wave] = m;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -517,7 +546,93 @@ struct GatherArgs {
     int stage_x;     // 1: the up projection runs here (x slices in LDS)
     const int *path; // run only when *path == want (nullptr: always)
     int want;
+    int share_bits;  // top-k: 1 = equal shares of the union's ascending list (from the bit words),
+                     // 2 = workgroup q owns the neurons [q R, q R + R), R = ceil(f / P) <= 64
 };
+
+// Top-k share by neuron range: wave 0 of workgroup q takes the neurons
+// [q R, q R + R) (R <= 64, one per lane), loads each one's bit words, g' and u
+// for every token in one round trip, forms h = act(g') u for the tokens whose
+// set holds the neuron (all tokens with the union rule) and compacts the
+// neurons of the union into jl / hs in ascending order (ballot + mbcnt).
+// Returns the number of neurons (all threads).
+template <int BT>
+__device__ int share_of_range(const GatherArgs &a, int R, int *jl, float *hs, int *s_ns)
+{
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        const int j = blockIdx.x * R + lane;
+        const bool in = lane < R && j < a.f;
+        uint32_t tb = 0;       // bit t: neuron j is in token t's set
+        float h[BT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            h[t] = 0.0f;
+            if (in && t < a.B) {
+                const uint32_t w = a.bits[(size_t)t * a.nw32 + (j >> 5)];
+                const float gp = a.G[(size_t)t * a.f + j], u = a.U[(size_t)t * a.f + j];
+                if ((w >> (j & 31)) & 1u) tb |= 1u << t;
+                h[t] = act_f32(a.act, gp) * u;
+            }
+        }
+        const bool on = tb != 0;
+        const uint64_t m = __ballot(on);
+        if (on) {
+            const int pos = mbcnt64(m);
+            jl[pos] = j;
+#pragma unroll
+            for (int t = 0; t < BT; ++t)
+                if (t < a.B) hs[pos * BT + t] = (a.use_union || ((tb >> t) & 1u)) ? h[t] : 0.0f;
+        }
+        if (lane == 0) *s_ns = __popcll(m);
+    }
+    __syncthreads();
+    return *s_ns;
+}
+
+// Share of the union of the tokens' top-k bit words for this workgroup: the
+// selected neurons in ascending order are cut into gridDim.x equal shares;
+// writes this share's neuron indices to jl (and to idx_out), returns their
+// number.  pref needs nw32 + 1 ints.
+__device__ int share_of_bits(const uint32_t *bits, int nw32, int B, int *pref, int *jl, int32_t *idx_out,
+                             int32_t *count_out, int *tmp)
+{
+    const int NT = blockDim.x, tid = threadIdx.x;
+    auto word = [&](int w) {
+        uint32_t u = 0;
+        for (int t = 0; t < B; ++t) u |= bits[(size_t)t * nw32 + w];
+        return u;
+    };
+    const int per = (nw32 + NT - 1) / NT;
+    const int w0 = min(nw32, tid * per), w1 = min(nw32, w0 + per);
+    int s = 0;
+    for (int w = w0; w < w1; ++w) s += __popc(word(w));
+    int total;
+    int run = block_exclusive_scan(s, tmp, &total);
+    for (int w = w0; w < w1; ++w) {
+        pref[w] = run;
+        run += __popc(word(w));
+    }
+    if (tid == 0) pref[nw32] = total;
+    __syncthreads();
+    const int P = gridDim.x, q = blockIdx.x;
+    const int lo = (int)((int64_t)q * total / P), hi = (int)((int64_t)(q + 1) * total / P);
+    for (int p = lo + tid; p < hi; p += NT) {
+        int a = 0, b = nw32 - 1;   // the last word whose prefix is <= p
+        while (a < b) {
+            const int mid = (a + b + 1) >> 1;
+            if (pref[mid] <= p) a = mid; else b = mid - 1;
+        }
+        uint32_t u = word(a);
+        for (int r = p - pref[a]; r > 0; --r) u &= u - 1u;   // drop the lower set bits
+        const int j = 32 * a + __builtin_ctz(u);
+        jl[p - lo] = j;
+        if (idx_out) idx_out[p] = j;
+    }
+    if (q == 0 && tid == 0 && count_out) *count_out = total;
+    __syncthreads();
+    return hi - lo;
+}
 
 // Share of the concatenated per-block lists for this workgroup: writes the
 // neuron indices to jl[0..ns) (and to idx_out), returns ns.  pref needs nL+1 ints.
@@ -554,13 +669,19 @@ __device__ int share_of_lists(const int *cnt, const int *idx, int nL, int R, int
     return hi - lo;
 }
 
+// the ascending list of the selected union (select calls): from the per-block
+// lists, or (bits != nullptr) from the tokens' top-k bit words
 __global__ __launch_bounds__(256) void k_emit_list(const int *cnt, const int *idx, int nL, int R,
-                                                   int32_t *idx_out, int32_t *count_out, int maxs)
+                                                   int32_t *idx_out, int32_t *count_out, int maxs,
+                                                   const uint32_t *bits, int B)
 {
     extern __shared__ __align__(16) int lds_e[];
     __shared__ int tmp[17];
     int *jl = lds_e, *pref = lds_e + maxs;
-    share_of_lists(cnt, idx, nL, R, pref, jl, idx_out, count_out, tmp);
+    if (bits)
+        share_of_bits(bits, nL, B, pref, jl, idx_out, count_out, tmp);
+    else
+        share_of_lists(cnt, idx, nL, R, pref, jl, idx_out, count_out, tmp);
 }
 
 template <int WT, int BT>
@@ -581,10 +702,16 @@ __global__ __launch_bounds__((Cfg<WT, BT>::NW * 64)) void k_gather(const GatherA
     if (a.path && *a.path != a.want) return;   // uniform, before any barrier
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int B = a.B, d = a.d, f = a.f;
-    const int ns = share_of_lists(a.list_cnt, a.list_idx, a.nL, a.R, pref, jl, a.idx_out, a.count_out, tmp);
+    __shared__ int s_ns;
+    const int ns = a.share_bits == 2 ? share_of_range<BT>(a, a.R, jl, hs, &s_ns)
+                   : a.share_bits ? share_of_bits(a.bits, a.nL, B, pref, jl, a.idx_out, a.count_out, tmp)
+                                  : share_of_lists(a.list_cnt, a.list_idx, a.nL, a.R, pref, jl, a.idx_out, a.count_out,
+                                                   tmp);
 
     // ---- phase A: h_tj for the share ----
-    if (a.mode == SFFN_MODE_TOPK) {
+    if (a.share_bits == 2) {
+        // formed with the share
+    } else if (a.mode == SFFN_MODE_TOPK) {
         for (int i = tid; i < ns * B; i += NT) {
             const int jj = i / B, t = i - jj * B, j = jl[jj];
             const float gp = a.G[(size_t)t * f + j];
@@ -1154,7 +1281,7 @@ __global__ __launch_bounds__(64) void k_gate_combine(const float *__restrict__ p
 // row load issued before x is staged into LDS, so each workgroup keeps its whole
 // share of rows in flight at once (up to 3 rows x 8 KB per wave).
 // ---------------------------------------------------------------------------
-constexpr int kFusedMaxRB = 48;              // neurons per workgroup of the fused kernel
+
 
 struct FusedArgs {
     const uint8_t *wg, *wu, *wdt;
@@ -1362,6 +1489,101 @@ __global__ __launch_bounds__(kFusedNT) void k_decode_b1(const FusedArgs a)
         for (int e4 = 0; e4 < E / 4; ++e4)
             *(float4 *)(dst + 4 * e4) = make_float4(ys[4 * e4], ys[4 * e4 + 1], ys[4 * e4 + 2], ys[4 * e4 + 3]);
     }
+}
+
+// int4 gate + up for one token (weight-aware top-k): a persistent streaming
+// GEMV.  A 16-byte int4 chunk holds 32 elements, so at d_model = 2048 KC each
+// lane p owns KC chunks (p, p + 64, ...) of every row, which is the fixed
+// order's accumulator p: the lane keeps its 32 KC x values in registers for
+// the whole kernel (no LDS), and a wave reads a whole row with one 16-byte load
+// per lane per chunk.  One workgroup per compute unit owns RB <= 48
+// consecutive neurons; wave w walks the rows w, w + NW, ... with three rows
+// (gate and up, with their group scales) in rotation, the next two in flight
+// while one is reduced.  (Every row requested at once with 16 waves was
+// measured slower, 11.1 against 9.2 us at 2048 x 11008: the fixed-order int4
+// dot costs about as much VALU time as the stream takes, and the rotation
+// overlaps the two.)  g' = g + b and u are stored (fixed order, bit for bit the
+// values of the generic kernel); the workgroup's fp64 score keys are formed at
+// the end, one neuron per thread.
+struct GuI4Args {
+    const uint8_t *wg, *wu;      // [f][d/2] int4
+    const uint16_t *sg, *su;     // [f][d/128] fp16
+    const float *x;              // [d]
+    const double *wdn;           // ||W_down[:, j]||_2
+    float *G, *U;                // [f]
+    uint64_t *keys;              // [f]
+    int f, RB;
+    float bias;
+};
+
+template <int KC, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gu_i4_b1(const GuI4Args a)
+{
+    constexpr size_t RBYTES = (size_t)KC * 1024;   // d / 2
+    constexpr int SST = KC * 16;                   // d / 128
+    __shared__ float gsm[kFusedMaxRB], usm[kFusedMaxRB];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = blockIdx.x * a.RB, nr = min(a.RB, a.f - r0);
+
+    float xr[KC][32];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const float4 *xp = (const float4 *)(a.x + (size_t)(k * 64 + lane) * 32);
+#pragma unroll
+        for (int e4 = 0; e4 < 8; ++e4) {
+            const float4 v = xp[e4];
+            xr[k][4 * e4] = v.x; xr[k][4 * e4 + 1] = v.y; xr[k][4 * e4 + 2] = v.z; xr[k][4 * e4 + 3] = v.w;
+        }
+    }
+    struct RowSlot {
+        uint4 g[KC], u[KC];
+        uint16_t sg[KC], su[KC];
+    };
+    auto load = [&](RowSlot &r, int i) {
+        const size_t row = (size_t)(r0 + i);
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            const int c = k * 64 + lane;
+            r.g[k] = ld16_nt(a.wg + row * RBYTES + (size_t)c * 16);
+            r.u[k] = ld16_nt(a.wu + row * RBYTES + (size_t)c * 16);
+            r.sg[k] = a.sg[row * SST + (c >> 2)];
+            r.su[k] = a.su[row * SST + (c >> 2)];
+        }
+    };
+    auto reduce = [&](const RowSlot &r, int i) {
+        float ag = 0.0f, au = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            ag = chunk_dot<SFFN_W_INT4_G128>(r.g[k], half_bits_to_float(r.sg[k]), xr[k], ag);
+            au = chunk_dot<SFFN_W_INT4_G128>(r.u[k], half_bits_to_float(r.su[k]), xr[k], au);
+        }
+        const float g = wave_tree_sum_dpp(ag), u = wave_tree_sum_dpp(au);
+        if (lane == 0) {
+            const float gp = g + a.bias;
+            a.G[r0 + i] = gp;
+            a.U[r0 + i] = u;
+            gsm[i] = gp;
+            usm[i] = u;
+        }
+    };
+    {
+        RowSlot ra, rb, rc;
+        if (wave < nr) load(ra, wave);
+        if (wave + NW < nr) load(rb, wave + NW);
+        for (int i = wave; i < nr; i += 3 * NW) {
+            if (i + 2 * NW < nr) load(rc, i + 2 * NW);
+            reduce(ra, i);
+            if (i + NW >= nr) break;
+            if (i + 3 * NW < nr) load(ra, i + 3 * NW);
+            reduce(rb, i + NW);
+            if (i + 2 * NW >= nr) break;
+            if (i + 4 * NW < nr) load(rb, i + 4 * NW);
+            reduce(rc, i + 2 * NW);
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nr)
+        a.keys[r0 + threadIdx.x] = topk_key(gsm[threadIdx.x], usm[threadIdx.x], a.wdn[r0 + threadIdx.x]);
 }
 
 // y = sum over the partials in a fixed order (+ residual): 16 columns per
@@ -1576,7 +1798,8 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
                 hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + P + 1) * 4, st,
-                                   (const int *)lcnt, (const int *)lidx, P, fa.RB, c.idx_out, c.count_out, maxs);
+                                   (const int *)lcnt, (const int *)lidx, P, fa.RB, c.idx_out, c.count_out, maxs,
+                                   (const uint32_t *)nullptr, 0);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (!forward) return hipSuccess;
@@ -1613,7 +1836,8 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
                 hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nblk + 1) * 4, st,
-                                   (const int *)lcnt, (const int *)lidx, nblk, R, c.idx_out, c.count_out, maxs);
+                                   (const int *)lcnt, (const int *)lidx, nblk, R, c.idx_out, c.count_out, maxs,
+                                   (const uint32_t *)nullptr, 0);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
             if (!forward) return hipSuccess;
@@ -1683,15 +1907,27 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         r.keys = (uint64_t *)(sc + S.keys);
         hipEvent_t evb = nullptr, eve = nullptr;
         if (forward) L.timer->take(&evb, &eve);
-        if ((e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st, evb, eve)) != hipSuccess) return e;
+        bool done = false;
+        if constexpr (WT == SFFN_W_INT4_G128 && BT == 1) {
+            if (d % 2048 == 0 && d <= 4096 && f <= kMaxTopkNeurons) {
+                GuI4Args ga{L.wg, L.wu, L.sg, L.su, xin, L.wdn, G, U, r.keys, f, fused_rows_per_wg(f), c.bias};
+                const int P = (f + ga.RB - 1) / ga.RB;
+                if (d == 2048)
+                    SFFN_LAUNCH((k_gu_i4_b1<1, kGuI4Waves>), dim3(P), dim3(kGuI4Waves * 64), 0, st, evb, eve, ga);
+                else
+                    SFFN_LAUNCH((k_gu_i4_b1<2, kGuI4Waves>), dim3(P), dim3(kGuI4Waves * 64), 0, st, evb, eve, ga);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                done = true;
+            }
+        }
+        if (!done && (e = run_rowdot<WT, BT, OUT_GATE_UP>(r, st, evb, eve)) != hipSuccess) return e;
+
         TopkArgs t{f, c.topk_k, nw32, (const uint64_t *)(sc + S.keys), bits};
         hipLaunchKernelGGL(k_topk, dim3(B), dim3(1024), 0, st, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        nL = f / kListRowsTopk;
-        R = kListRowsTopk;
-        hipLaunchKernelGGL(k_mask_lists, dim3((nL + 3) / 4), dim3(256), 0, st, (const uint32_t *)bits, nw32, B, f,
-                           lcnt, lidx);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // the gather takes its share of the union straight from the bit words
+        nL = nw32;
+        R = 32;
     } else {
         r.list_cnt = lcnt;
         r.list_idx = lidx;
@@ -1702,10 +1938,12 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         nL = (f + R - 1) / R;
     }
 
+    const bool topk = c.mode == SFFN_MODE_TOPK;
     if (!forward) {
         const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
         hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nL + 1) * 4, st,
-                           (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs);
+                           (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs,
+                           topk ? (const uint32_t *)bits : nullptr, B);
         return hipGetLastError();
     }
 
@@ -1718,6 +1956,22 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     float *partial = (float *)(sc + S.partial);
     g.partial = partial;
     g.idx_out = c.idx_out; g.count_out = c.count_out;
+    g.share_bits = 0;
+    if (topk) {
+        // each workgroup owns a range of R neurons; the ascending list, when asked
+        // for, comes from the bit words in a launch of its own
+        g.share_bits = 2;
+        g.R = (f + kGatherWGs - 1) / kGatherWGs;
+        g.idx_out = nullptr;
+        g.count_out = nullptr;
+        if (c.idx_out || c.count_out) {
+            const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
+            hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nL + 1) * 4, st,
+                               (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs,
+                               (const uint32_t *)bits, B);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
     if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
 
     const int BD = B * d;

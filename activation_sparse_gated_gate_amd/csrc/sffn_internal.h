@@ -20,7 +20,6 @@ constexpr int kMaxInt4Rows = 8;
 constexpr int kMaxPrefillRows = 16384;
 constexpr int kMaxTopkNeurons = 16384;  // d_ff limit of the top-k mode (sort in LDS)
 constexpr int kGatherWGs = 256;      // partitions of the active list (partial sums)
-constexpr int kListRowsTopk = 64;    // neurons per compaction block after top-k
 constexpr int kMassBlock = 256;      // sorted scores per block of the fp64 mass prefix
 constexpr int kMaxDownSplits = 64;     // d_ff splits of the batched MFMA down projection
 constexpr int kIlvRows = 32;         // prefill: W_gate / W_up interleave granularity

@@ -471,6 +471,29 @@ def bench_topk(args):
         # union, the scale rows of touched 128-neuron groups, the column norms
         return gate_up_bytes + n_union * (d // 2) + touched_groups * d * 2 + f * 8
 
+    dense_bytes = 3 * (f * d // 2) + 3 * f * (d // 128) * 2   # every int4 weight and its scales
+
+    def time_pol(pol, B):
+        xs = [Xd[i * B:(i + 1) * B] for i in range(T // B)]
+        ys = [Yd[i * B:(i + 1) * B] for i in range(T // B)]
+        nb = len(xs)
+
+        def run(s0, n):
+            for s in range(s0, s0 + n):
+                layers[s % copies].forward(pol, xs[s % nb], ys[s % nb])
+        run(0, args.warmup)
+        torch.cuda.synchronize()
+        return eager_time_us(run, steps) if args.no_graph else graph_time_us(run, steps, 32)
+
+    # the dense reference per batch size: the faster of the dense GEMVs (mode DENSE) and every
+    # neuron through the sparse kernels (mode ALL: the fixed-order gate, the up rows, the down rows)
+    dense = {}
+    for B in (1, 8):
+        t_dense = time_pol(sf.make_policy("dense"), B)
+        t_all = time_pol(sf.make_policy("all", use_union=True), B)
+        dense[B] = {"dense_us": round(t_dense, 3), "all_us": round(t_all, 3), "ref_us": round(min(t_dense, t_all), 3)}
+        log("int4 dense B=%d: DENSE %.2f us, ALL %.2f us" % (B, t_dense, t_all))
+
     rows = []
     for B in (1, 8):
         for pct in synth.CFG3_KEEP_PCT:
@@ -479,10 +502,6 @@ def bench_topk(args):
             xs = [Xd[i * B:(i + 1) * B] for i in range(T // B)]
             ys = [Yd[i * B:(i + 1) * B] for i in range(T // B)]
             nb = len(xs)
-
-            def run(s0, n, xs=xs, ys=ys, pol=pol, nb=nb):
-                for s in range(s0, s0 + n):
-                    layers[s % copies].forward(pol, xs[s % nb], ys[s % nb])
             nu, tg = [], []
             for i in range(min(nb, 32)):  # union size and touched groups (not timed)
                 layers[0].forward(pol, xs[i], ys[i], idx_out=idx, count_out=cnt)
@@ -491,15 +510,17 @@ def bench_topk(args):
                 sel = idx[:n].cpu().numpy()
                 nu.append(n)
                 tg.append(len(np.unique(sel // 128)))
-            run(0, args.warmup)
-            torch.cuda.synchronize()
-            us = eager_time_us(run, steps) if args.no_graph else graph_time_us(run, steps, 32, max(1, nb // 32))
+            us = time_pol(pol, B)
             Bb = bytes_alg(np.mean(nu), np.mean(tg))
+            ideal = dense_bytes / Bb
             r = dict(batch=B, keep_pct=pct, k=k, union=round(float(np.mean(nu)), 1),
                      union_frac=round(float(np.mean(nu)) / f, 4), us_per_step=round(us, 3),
-                     us_per_token=round(us / B, 3), bytes_alg=int(Bb), GBps=round(Bb / us / 1e3, 1))
+                     us_per_token=round(us / B, 3), bytes_alg=int(Bb), GBps=round(Bb / us / 1e3, 1),
+                     speedup_vs_dense=round(dense[B]["ref_us"] / us, 3), ideal=round(ideal, 3),
+                     frac_of_ideal=round(dense[B]["ref_us"] / us / ideal, 3))
             rows.append(r)
-            log("topk B=%d keep %d%%: union %.0f, %.2f us/step, %.0f GB/s" % (B, pct, r["union"], us, r["GBps"]))
+            log("topk B=%d keep %d%%: union %.0f, %.2f us/step, %.0f GB/s, %.2fx dense (ideal %.2fx)"
+                % (B, pct, r["union"], us, r["GBps"], r["speedup_vs_dense"], ideal))
     pol = sf.make_policy("topk", topk_k=synth.topk_count(f, 17))
     xs1 = [Xd[i:i + 1] for i in range(T)]
 
@@ -522,10 +543,13 @@ def bench_topk(args):
                "sample": "%d tokens at batch 1, keep 17%%, one oracle call; %.1f s wall" % (n, dt)}
     head = rows[0]
     cfg = {"workload": "weight-aware top-k decode layer, int4-g128 fp16 scales, d_model 2048, d_ff 11008, "
-                       "SwiGLU, batch 1 and 8 (union), keep 17/30/50%", "weight_copies": copies, "results": rows}
+                       "SwiGLU, batch 1 and 8 (union), keep 17/30/50%", "weight_copies": copies,
+           "dense": dense, "dense_bytes": dense_bytes,
+           "ideal": "dense bytes / the top-k path's algorithmic bytes (gate and up read in full)",
+           "results": rows}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_rowdot<int4,1,gate_up> (gate and up in the fixed order, batch 1)",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("k_gu_i4_b1"),
+            "kernel": "k_gu_i4_b1<1,8> (int4 gate and up in the fixed order + score keys, batch 1)",
             "kernel_us": round(kus, 3), "bytes_per_launch": gate_up_bytes}
     out = line("µs/step & effective HBM GB/s, weight-aware top-k", head["GBps"], "GB/s", steps, args.warmup,
                round(head["us_per_step"] / 1e3, 6), "int4", cfg, roof, cpu)

@@ -387,6 +387,22 @@ def test_topk_k_equals_f_and_k_one(cfg3):
     _check(layer, w, x[:3], "topk", 5e-3, topk_k=1, union=False)
 
 
+def test_int4_batch1_topk_edge_cases(cfg3):
+    """Batch-1 int4 top-k (the streaming gate + up kernel, then the select):
+    k = 1, k = f (every neuron), and a zero token, whose scores all tie at 0
+    (the lowest k indices win: the select's equal-key path)."""
+    w, x, layer = cfg3
+    f = w.d_ff
+    _check(layer, w, x[:1], "topk", 5e-3, topk_k=1)
+    _check(layer, w, x[1:2], "topk", 5e-3, topk_k=f)
+    z = np.zeros((1, w.d_model), np.float32)
+    sf = _sf()
+    for k in (1, 300, 4000):
+        y, idx, n = run_decode(layer, sf.make_policy("topk", topk_k=k), z)
+        assert n == k and np.array_equal(idx, np.arange(k)), k
+        assert np.all(y == 0.0)
+
+
 def test_topk_ties_lower_index_first():
     # duplicated neurons give bit-identical scores; k cuts through the tie
     w = synth._make_weights(synth.WT_BF16, 512, 256, synth.ACT_SILU, (991, 992, 993))
@@ -428,13 +444,17 @@ def test_int4_sparse_union_scales_of_a_third_group():
     layer.close()
 
 
-@pytest.mark.parametrize("case", ["bf16_b1_exact", "int4_b8_topk", "bf16_b16_tiles", "bf16_b16_gather"])
+@pytest.mark.parametrize("case", ["bf16_b1_exact", "int4_b8_topk", "int4_b1_topk", "bf16_b16_tiles",
+                                  "bf16_b16_gather"])
 def test_decode_writes_stay_inside_the_scratch(case):
     import torch
     sf = _sf()
     if case == "int4_b8_topk":
         w = synth._make_weights(synth.WT_I4, 512, 1408, synth.ACT_SILU, (731, 732, 733))
         B, layouts, kw = 8, None, dict(mode="topk", topk_k=300, union=True)
+    elif case == "int4_b1_topk":
+        w = synth._make_weights(synth.WT_I4, 2048, 1408, synth.ACT_SILU, (741, 742, 743))
+        B, layouts, kw = 1, None, dict(mode="topk", topk_k=300)
     elif case == "bf16_b1_exact":
         w = synth._make_weights(synth.WT_BF16, 1024, 2816, synth.ACT_RELU, (734, 735, 736))
         B, layouts, kw = 1, None, dict(mode="exact", bias=synth.gate_offset_for_active_fraction(0.1))
