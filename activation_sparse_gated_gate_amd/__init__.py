@@ -31,7 +31,7 @@ EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", 
            "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
            "sffn_select_blocks", "sffn_schedule_mass", "sffn_neuron_counts", "sffn_frequency_order",
            "sffn_decode_block_rows", "sffn_create_permuted", "sffn_read_probe", "sffn_forward_noalloc",
-           "sffn_noalloc_scratch_bytes")
+           "sffn_noalloc_scratch_bytes", "sffn_read_probe_cfg", "sffn_read_latency_probe")
 
 
 class LayerDesc(C.Structure):
@@ -43,7 +43,8 @@ class LayerDesc(C.Structure):
 class Policy(C.Structure):
     _fields_ = [("mode", C.c_int32), ("gate_bias", C.c_float), ("theta", C.c_float),
                 ("topk_k", C.c_int32), ("use_union", C.c_int32), ("recent_n", C.c_int32),
-                ("min_keep", C.c_int32), ("batch_path", C.c_int32), ("mass_thresh", C.c_double)]
+                ("min_keep", C.c_int32), ("batch_path", C.c_int32), ("merge_gap", C.c_int32),
+                ("reserved", C.c_int32), ("mass_thresh", C.c_double)]
 
 
 class ExpertPolicy(C.Structure):
@@ -53,6 +54,11 @@ class ExpertPolicy(C.Structure):
 class BlockPolicy(C.Structure):
     _fields_ = [("mass_thresh", C.c_double), ("min_full_ratio", C.c_float), ("max_full_ratio", C.c_float),
                 ("block", C.c_int32), ("recent_n", C.c_int32), ("min_keep", C.c_int32), ("reserved", C.c_int32)]
+
+
+class ProbeCfg(C.Structure):
+    _fields_ = [("workgroups", C.c_int32), ("threads", C.c_int32), ("pattern", C.c_int32),
+                ("in_flight", C.c_int32), ("nontemporal", C.c_int32)]
 
 
 class SffnError(RuntimeError):
@@ -107,6 +113,10 @@ def _load():
     lib.sffn_decode_block_rows.argtypes = [I]
     lib.sffn_read_probe.restype = I
     lib.sffn_read_probe.argtypes = [P, Z, I, P, P]
+    lib.sffn_read_probe_cfg.restype = I
+    lib.sffn_read_probe_cfg.argtypes = [P, Z, C.POINTER(ProbeCfg), P, P]
+    lib.sffn_read_latency_probe.restype = I
+    lib.sffn_read_latency_probe.argtypes = [P, Z, I, P, I, P, P]
     lib.sffn_create_permuted.restype = I
     lib.sffn_create_permuted.argtypes = [C.POINTER(LayerDesc), P, P, P, P, P, Z, P, C.POINTER(P)]
     return lib
@@ -215,10 +225,10 @@ BATCH_PATH_AUTO, BATCH_PATH_TILED, BATCH_PATH_GATHER = 0, 1, 2
 
 
 def make_policy(mode="all", gate_bias=0.0, theta=0.0, topk_k=1, use_union=False, mass_thresh=1.0,
-                recent_n=0, min_keep=1, batch_path=BATCH_PATH_AUTO) -> Policy:
+                recent_n=0, min_keep=1, batch_path=BATCH_PATH_AUTO, merge_gap=0) -> Policy:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     return Policy(m, float(gate_bias), float(theta), int(topk_k), int(bool(use_union)), int(recent_n),
-                  int(min_keep), int(batch_path), float(mass_thresh))
+                  int(min_keep), int(batch_path), int(merge_gap), 0, float(mass_thresh))
 
 
 def _ptr(t):

@@ -183,6 +183,13 @@ static hipError_t noalloc_scratch_ptr(void **out)
     return hipSuccess;
 }
 
+// the timer of the entry points that take no handle (sffn_expert_select, the read probe)
+KernelTimer &free_timer()
+{
+    static KernelTimer t;
+    return t;
+}
+
 }  // namespace sffn
 
 using namespace sffn;
@@ -320,8 +327,6 @@ sffn_status sffn_create_permuted(const sffn_layer_desc *desc, const void *w_gate
 
 void sffn_destroy(sffn_t layer) { delete layer; }
 
-// the timer of the entry points that take no handle (sffn_expert_select)
-static KernelTimer g_free_timer;
 
 sffn_status sffn_expert_select(const float *probs, int32_t tokens, int32_t experts, const sffn_expert_policy *policy,
                                int32_t *k_out, int32_t *idx_out, float *w_out, void *stream)
@@ -332,13 +337,13 @@ sffn_status sffn_expert_select(const float *probs, int32_t tokens, int32_t exper
     if (kmin < 1 || kmax < kmin || kmax > experts || kmax > kMaxExpertKAbi) return SFFN_ERR_INVALID_ARG;
     if (!(policy->tau == policy->tau)) return SFFN_ERR_INVALID_ARG;   // NaN
     return hip_status(launch_expert_select(probs, tokens, experts, policy->tau, kmin, kmax, k_out, idx_out, w_out,
-                                           (hipStream_t)stream, &g_free_timer));
+                                           (hipStream_t)stream, &sffn::free_timer()));
 }
 
 sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events, int32_t n)
 {
     if (n < 0 || (n > 0 && (!begin_events || !end_events))) return SFFN_ERR_INVALID_ARG;
-    KernelTimer &t = layer ? layer->timer : g_free_timer;
+    KernelTimer &t = layer ? layer->timer : sffn::free_timer();
     t.begin = begin_events;
     t.end = end_events;
     t.n = n;
@@ -365,6 +370,7 @@ static sffn_status policy_ok(const sffn_layer *h, const sffn_policy *p)
     if (p->mode == SFFN_MODE_TOPK && (p->topk_k < 1 || p->topk_k > D.d_ff)) return SFFN_ERR_INVALID_ARG;
     if (p->use_union != 0 && p->use_union != 1) return SFFN_ERR_INVALID_ARG;
     if (p->batch_path < 0 || p->batch_path > 2) return SFFN_ERR_INVALID_ARG;
+    if (p->merge_gap < 0 || p->merge_gap > 64) return SFFN_ERR_INVALID_ARG;
     if (p->mode == SFFN_MODE_TOPK && D.act != SFFN_ACT_SILU) return SFFN_ERR_UNSUPPORTED;
     if (p->mode == SFFN_MODE_THRESH) {
         // THRESH stands for |act(g')| > tau, taken in the gate domain as g' > theta.
@@ -397,7 +403,7 @@ sffn_status sffn_select(sffn_t layer, const sffn_policy *policy, const void *in,
         return hip_status(launch_prefill_select(c));
     }
     if ((uintptr_t)in & 15) return SFFN_ERR_INVALID_ARG;
-    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->gate_bias, policy->theta,
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->merge_gap, policy->gate_bias, policy->theta,
                  rows, (const float *)in, nullptr, idx_out, count_out, (uint8_t *)scratch, st};
     return hip_status(launch_decode(c, false));
 }
@@ -460,7 +466,7 @@ sffn_status sffn_forward(sffn_t layer, const sffn_policy *policy, const void *in
     if (idx_in || count_in) return SFFN_ERR_INVALID_ARG;
     if (in == out) return SFFN_ERR_INVALID_ARG;
     if (policy->mode == SFFN_MODE_DENSE && (idx_out || count_out)) return SFFN_ERR_INVALID_ARG;
-    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->gate_bias, policy->theta,
+    DecodeCall c{&layer->L, policy->mode, policy->use_union, policy->topk_k, policy->batch_path, policy->merge_gap, policy->gate_bias, policy->theta,
                  rows, (const float *)in, (float *)out, idx_out, count_out, (uint8_t *)scratch, st};
     return hip_status(launch_decode(c, true));
 }

@@ -548,6 +548,7 @@ struct GatherArgs {
     int want;
     int share_bits;  // top-k: 1 = equal shares of the union's ascending list (from the bit words),
                      // 2 = workgroup q owns the neurons [q R, q R + R), R = ceil(f / P) <= 64
+    int merge_gap;   // share 2: also read the unselected neurons of gaps of at most this many rows
 };
 
 // Top-k share by neuron range: wave 0 of workgroup q takes the neurons
@@ -576,13 +577,24 @@ __device__ int share_of_range(const GatherArgs &a, int R, int *jl, float *hs, in
             }
         }
         const bool on = tb != 0;
-        const uint64_t m = __ballot(on);
-        if (on) {
+        const uint64_t sel = __ballot(on);
+        // run merging: an unselected neuron whose gap between the selected
+        // neighbours on either side is at most merge_gap rows is read as well
+        bool rd = on;
+        if (a.merge_gap > 0 && !on && in) {
+            const uint64_t below = sel & ((1ull << lane) - 1ull), above = lane < 63 ? sel >> (lane + 1) : 0ull;
+            if (below && above) {
+                const int prev = 63 - __builtin_clzll(below), next = lane + 1 + __builtin_ctzll(above);
+                rd = next - prev - 1 <= a.merge_gap;
+            }
+        }
+        const uint64_t m = __ballot(rd);
+        if (rd) {
             const int pos = mbcnt64(m);
             jl[pos] = j;
 #pragma unroll
             for (int t = 0; t < BT; ++t)
-                if (t < a.B) hs[pos * BT + t] = (a.use_union || ((tb >> t) & 1u)) ? h[t] : 0.0f;
+                if (t < a.B) hs[pos * BT + t] = (on && (a.use_union || ((tb >> t) & 1u))) ? h[t] : 0.0f;
         }
         if (lane == 0) *s_ns = __popcll(m);
     }
@@ -1961,6 +1973,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         // each workgroup owns a range of R neurons; the ascending list, when asked
         // for, comes from the bit words in a launch of its own
         g.share_bits = 2;
+        g.merge_gap = c.merge_gap;
         g.R = (f + kGatherWGs - 1) / kGatherWGs;
         g.idx_out = nullptr;
         g.count_out = nullptr;

@@ -71,6 +71,9 @@ struct KernelTimer {
             hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                        \
     } while (0)
 
+// the timer of the entry points that take no handle (sffn_set_kernel_timer(NULL, ...))
+KernelTimer &free_timer();
+
 struct Layer {
     sffn_layer_desc desc;
     // decode layouts
@@ -118,6 +121,7 @@ struct DecodeCall {
     const Layer *L;
     int mode, use_union, topk_k;
     int batch_path;     // 0 auto, kPathTiled, kPathGather
+    int merge_gap;      // top-k gather: unselected neurons read between selected ones (0 = off)
     float bias, theta;
     int B;
     const float *x;     // [B][d] caller input

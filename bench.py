@@ -82,7 +82,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=128)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder", "read"])
+                   choices=["decode", "topk", "schedule", "prefill", "experts", "breakeven", "copy", "reorder", "read",
+                            "merge"])
     p.add_argument("--a", type=float, nargs="*", default=None,
                    help="decode: active fractions to time (default 1.0 0.6 0.3 0.1)")
     p.add_argument("--copies", type=int, default=4)
@@ -988,46 +989,227 @@ def bench_reorder(args):
     print(json.dumps(out), flush=True)
 
 
-def bench_read(args):
-    """HBM read ceiling for the decode kernels' access policy (non-temporal
-    16-byte loads): sffn_read_probe over four rotating 90.2 MB buffers (the
-    4096 x 11008 bf16 gate matrix, past the Infinity Cache together) and over
-    one 4 GiB buffer, for several grid sizes."""
+def free_kernel_us(run, nk, hold_ms=100.0):
+    """Average duration of nk launches of a handle-free entry point's kernel
+    (the read probe) from the start / stop events its own dispatch records
+    (sffn_set_kernel_timer with no handle), as main_kernel_us does for a layer."""
+    import ctypes as C
+
+    import numpy as np
     import torch
 
     import activation_sparse_gated_gate_amd as sf
-    nbytes = 11008 * 4096 * 2
-    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
-    big = torch.ones((4 << 30) // 4, dtype=torch.float32, device="cuda:0")
-    out = torch.empty(65536, dtype=torch.int32, device="cuda:0")
-    s = torch.cuda.current_stream().cuda_stream
-    rows = []
-    for wg in (256, 512, 1024, 2048, 4096):
-        for name, bl, nb in (("4 x 90.2 MB", bufs, nbytes), ("4 GiB", [big], 4 << 30)):
-            reps = 256 if nb == nbytes else 8
+    hip = _hip()
 
-            def run(n):
-                for i in range(n):
-                    if sf._lib.sffn_read_probe(bl[i % len(bl)].data_ptr(), nb, wg, out.data_ptr(), s) != 0:
-                        raise RuntimeError("sffn_read_probe failed")
-            run(8)
-            torch.cuda.synchronize()
-            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            st.record()
-            run(reps)
-            en.record()
-            torch.cuda.synchronize()
-            us = st.elapsed_time(en) * 1e3 / reps
-            rows.append({"buffer": name, "workgroups": wg, "us": round(us, 3), "GBps": round(nb / us / 1e3, 1)})
-            log("read %s, %d workgroups: %.2f us, %.0f GB/s" % (name, wg, us, nb / us / 1e3))
-    best = max((r for r in rows if r["buffer"] != "4 GiB"), key=lambda r: r["GBps"])
-    cfg = {"workload": "HBM read ceiling: non-temporal 16-byte loads, 8 in flight per thread, 256-thread "
-                       "workgroups; 4 rotating 90.2 MB buffers and one 4 GiB buffer", "results": rows}
-    out_line = line("HBM read GB/s (non-temporal 16-byte loads)", best["GBps"], "GB/s", 256, 8,
-                    round(best["us"] / 1e3, 6), "u32", cfg,
-                    {"bound": "hbm", "achieved": best["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(best["GBps"] / HBM_PEAK_GBS, 4), "traffic": None}, None)
+    def mk():
+        e = C.c_void_p()
+        if hip.hipEventCreateWithFlags(C.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e.value
+    pairs = [(mk(), mk()) for _ in range(nk)]
+    b = (C.c_void_p * nk)(*[p[0] for p in pairs])
+    e = (C.c_void_p * nk)(*[p[1] for p in pairs])
+    if sf.sffn_set_kernel_timer(None, b, e, nk) != 0:
+        raise RuntimeError("sffn_set_kernel_timer failed")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * 1e-3 * 2.4e9))
+    run(nk)
+    torch.cuda.synchronize()
+    sf.sffn_set_kernel_timer(None, None, None, 0)
+    us = []
+    for bb, ee in pairs:
+        v = C.c_float()
+        hip.hipEventElapsedTime(C.byref(v), bb, ee)
+        us.append(v.value * 1e3)
+        hip.hipEventDestroy(bb)
+        hip.hipEventDestroy(ee)
+    return float(np.median(us)), float(np.mean(us))
+
+
+def bench_read(args):
+    """What one launch can read: sffn_read_probe_cfg over four rotating buffers
+    (past the 256 MB Infinity Cache together) of 108.2 MB (the batch-1 decode
+    kernel's algorithmic bytes at a = 0.1 on the 4096 x 11008 layer) and of
+    90.2 MB (its gate matrix alone), for every access pattern, in-flight depth,
+    cache policy, workgroup size and grid size the probe offers; kernel-only
+    durations from dispatch-recorded events, as for the decode kernel.  Also a
+    4 GiB stream (the long-run rate)."""
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    s = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(65536, dtype=torch.int32, device="cuda:0")
+    rows = []
+    sizes = [("108.2 MB", 108198912), ("90.2 MB", 11008 * 4096 * 2)]
+    for name, nb in sizes:
+        bufs = [torch.ones(nb // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+        for wg in (256, 512):
+            for nt in (512, 1024):
+                for pat in (0, 1):
+                    for inf in (4, 8, 16):
+                        for ntp in (1, 0):
+                            cfg = sf.ProbeCfg(wg, nt, pat, inf, ntp)
+
+                            def run(n, cfg=cfg, bufs=bufs, nb=nb):
+                                for i in range(n):
+                                    if sf._lib.sffn_read_probe_cfg(bufs[i % 4].data_ptr(), nb, C_byref(cfg),
+                                                                   out.data_ptr(), s) != 0:
+                                        raise RuntimeError("sffn_read_probe_cfg failed")
+                            run(8)
+                            torch.cuda.synchronize()
+                            med, mean = free_kernel_us(run, 64)
+                            rows.append({"bytes": name, "workgroups": wg, "threads": nt,
+                                         "pattern": "per-workgroup block" if pat else "grid-stride",
+                                         "in_flight": inf, "nontemporal": ntp, "us_median": round(med, 3),
+                                         "us_mean": round(mean, 3), "GBps": round(nb / med / 1e3, 1)})
+                            log("read %s wg %d x %d %s if %d nt %d: %.2f us (%.0f GB/s)"
+                                % (name, wg, nt, "block" if pat else "stride", inf, ntp, med, nb / med / 1e3))
+        del bufs
+    big = torch.ones((4 << 30) // 4, dtype=torch.float32, device="cuda:0")
+    cfg = sf.ProbeCfg(256, 1024, 0, 8, 1)
+
+    def runb(n):
+        for i in range(n):
+            sf._lib.sffn_read_probe_cfg(big.data_ptr(), 4 << 30, C_byref(cfg), out.data_ptr(), s)
+    runb(2)
+    med, _ = free_kernel_us(runb, 8)
+    stream_gbps = round((4 << 30) / med / 1e3, 1)
+    log("read 4 GiB stream: %.1f us, %.0f GB/s" % (med, stream_gbps))
+    best = {n: min((r for r in rows if r["bytes"] == n), key=lambda r: r["us_median"]) for n, _ in sizes}
+    cfgd = {"workload": "HBM read ceiling of one launch: 4 rotating buffers of 108.2 MB and of 90.2 MB, every "
+                        "probe configuration; kernel-only durations (dispatch-recorded events, median of 64)",
+            "best": best, "stream_4GiB_GBps": stream_gbps, "results": rows}
+    b108 = best["108.2 MB"]
+    out_line = line("HBM read GB/s of one 108.2 MB launch (best probe configuration)", b108["GBps"], "GB/s", 64, 8,
+                    round(b108["us_median"] / 1e3, 6), "u32", cfgd,
+                    {"bound": "hbm", "achieved": b108["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(b108["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_read_probe_cfg", "kernel_us": b108["us_median"], "bytes_per_launch": 108198912},
+                    None)
     print(json.dumps(out_line), flush=True)
+
+
+def C_byref(x):
+    import ctypes
+    return ctypes.byref(x)
+
+
+def bench_merge(args):
+    """Run merging of the int4 W_down^T row gather (denseflux, section 5.5:
+    merge adjacent reads when the gap is below L * B bytes, L and B measured on
+    the device).  L: isolated 1 KB row reads at random offsets of a 1 GiB
+    buffer (one wave, each read finished before the next); B: the best one-launch
+    read rate of the gather's size and the long-stream rate.  Then the config-3
+    top-k layer (int4, 2048 x 11008, keep 17 %, batch 1) timed with merge gaps of
+    0 (off) up to every row of a share."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gated_gate_amd as sf
+    import synth
+
+    s = torch.cuda.current_stream().cuda_stream
+    # --- L: latency of isolated 1 KB row reads ---
+    nbuf = 1 << 30
+    buf = torch.ones(nbuf // 4, dtype=torch.float32, device="cuda:0")
+    rng = np.random.default_rng(7)
+    n = 512
+    offs = torch.from_numpy((rng.integers(0, nbuf // 1024, n) * 1024).astype(np.uint64).view(np.int64)).to("cuda:0")
+    lat = torch.empty(n + 2, dtype=torch.int64, device="cuda:0")
+    for _ in range(2):
+        if sf._lib.sffn_read_latency_probe(buf.data_ptr(), nbuf, 1024, offs.data_ptr(), n, lat.data_ptr(), s) != 0:
+            raise RuntimeError("sffn_read_latency_probe failed")
+    torch.cuda.synchronize()
+    lv = lat.cpu().numpy()
+    ghz = lv[n] / (lv[n + 1] * 10.0)
+    cyc = np.sort(lv[:n])
+    L_ns = float(np.median(cyc)) / ghz
+    log("isolated 1 KB row read: median %.0f cycles = %.0f ns at %.2f GHz (p10 %.0f, p90 %.0f ns)"
+        % (np.median(cyc), L_ns, ghz, np.percentile(cyc, 10) / ghz, np.percentile(cyc, 90) / ghz))
+    del buf
+    # --- B: one-launch read of the gather's bytes (1871 rows of 1 KB) and the long stream ---
+    out = torch.empty(65536, dtype=torch.int32, device="cuda:0")
+    rates = {}
+    for name, nb in (("gather 1.9 MB", 1871 * 1024), ("stream 4 GiB", 4 << 30)):
+        bufs = [torch.ones(nb // 4, dtype=torch.float32, device="cuda:0") for _ in range(1 if nb > (1 << 30) else 16)]
+        cfg = sf.ProbeCfg(256, 1024, 0, 8, 1)
+
+        def run(k, bufs=bufs, nb=nb, cfg=cfg):
+            for i in range(k):
+                sf._lib.sffn_read_probe_cfg(bufs[i % len(bufs)].data_ptr(), nb, C_byref(cfg), out.data_ptr(), s)
+        run(4)
+        med, _ = free_kernel_us(run, 32 if nb > (1 << 30) else 256)
+        rates[name] = nb / med / 1e3
+        log("B (%s): %.2f us, %.0f GB/s" % (name, med, rates[name]))
+        del bufs
+    LB = {k: L_ns * 1e-9 * v * 1e9 for k, v in rates.items()}   # bytes
+    # --- the gather with merge gaps ---
+    d, f = 2048, 11008
+    w = synth.cfg3_weights(d, f)
+    X = synth.cfg3_tokens(args.tokens, d)
+    wt = weights_dev(w)
+    copies = 16
+    layers = [sf.Layer(d, f, 1, sf.W_INT4_G128, sf.ACT_SILU, wt) for _ in range(copies)]
+    del wt
+    Xd = dev_tensor(X)
+    Yd = torch.empty_like(Xd)
+    T = args.tokens
+    k = synth.topk_count(f, 17)
+    steps = min(args.steps, 512)
+    res = []
+    yref = None
+    for gap in (0, 1, 2, 4, 8, 16, 64):
+        pol = sf.make_policy("topk", topk_k=k, merge_gap=gap)
+
+        def runl(s0, nn, pol=pol):
+            for st in range(s0, s0 + nn):
+                layers[st % copies].forward(pol, Xd[st % T:st % T + 1], Yd[st % T:st % T + 1])
+        runl(0, args.warmup)
+        torch.cuda.synchronize()
+        y = Yd[:64].clone()
+        if yref is None:
+            yref = y
+        same = bool(torch.equal(y, yref))
+        us = graph_time_us(runl, steps, 32)
+        # rows read per token with this gap, from the selected sets (shares of R = ceil(f / 256) neurons)
+        idx = torch.empty(f, dtype=torch.int32, device="cuda:0")
+        cnt = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        rows_read = []
+        R = (f + 255) // 256
+        for t in range(16):
+            layers[0].forward(sf.make_policy("topk", topk_k=k), Xd[t:t + 1], Yd[t:t + 1], idx_out=idx, count_out=cnt)
+            torch.cuda.synchronize()
+            sel = np.zeros(f, bool)
+            sel[idx[:int(cnt.item())].cpu().numpy()] = True
+            tot = 0
+            for q in range(0, f, R):
+                sh = np.flatnonzero(sel[q:q + R])
+                tot += sh.size
+                if gap > 0 and sh.size > 1:
+                    g = np.diff(sh) - 1
+                    tot += int(g[g <= gap].sum())
+            rows_read.append(tot)
+        rr = float(np.mean(rows_read))
+        res.append({"merge_gap_rows": gap, "us_per_step": round(us, 3), "rows_read": round(rr, 1),
+                    "extra_rows_pct": round(100.0 * (rr / k - 1.0), 1), "same_output": same})
+        log("merge gap %d rows: %.2f us/step, %.0f rows read (%.1f%% more), same output %s"
+            % (gap, us, rr, 100.0 * (rr / k - 1.0), same))
+        Yd.zero_()
+    base = res[0]["us_per_step"]
+    bestm = min(res, key=lambda r: r["us_per_step"])
+    cfg = {"workload": "run merging of the int4 W_down^T gather, config-3 top-k layer (2048 x 11008, keep 17 %, "
+                       "batch 1, 16 rotating copies)",
+           "L_ns_median": round(L_ns, 1), "clock_GHz": round(float(ghz), 3),
+           "B_GBps": {k2: round(v, 1) for k2, v in rates.items()},
+           "LxB_bytes": {k2: int(v) for k2, v in LB.items()},
+           "LxB_rows_of_1KB": {k2: round(v / 1024, 1) for k2, v in LB.items()},
+           "results": res, "best_gap_rows": bestm["merge_gap_rows"],
+           "rule_gap_rows": int(LB["gather 1.9 MB"] // 1024)}
+    out_line = line("µs/step of the top-k layer vs merge gap (run merging, denseflux §5.5)", base, "us", steps,
+                    args.warmup, round(base / 1e3, 6), "int4", cfg, None, None, higher=False)
+    print(json.dumps(out_line), flush=True)
+    for L in layers:
+        L.close()
 
 
 def bench_copy(args):
@@ -1061,7 +1243,7 @@ def main():
     torch.cuda.set_device(0)
     {"decode": bench_decode, "topk": bench_topk, "schedule": bench_schedule,
      "prefill": bench_prefill, "experts": bench_experts, "breakeven": bench_breakeven,
-     "copy": bench_copy, "reorder": bench_reorder, "read": bench_read}[args.workload](args)
+     "copy": bench_copy, "reorder": bench_reorder, "read": bench_read, "merge": bench_merge}[args.workload](args)
 
 
 if __name__ == "__main__":

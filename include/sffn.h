@@ -152,6 +152,13 @@ typedef struct sffn_layer_desc {
  *               W_up and W_down^T rows) at the measured breakeven; 1 forces
  *               the tiles, 2 the gather (both give the same results within
  *               the bf16 / fp32 tolerance).  Other calls ignore it.
+ *  merge_gap    TOPK forward: run merging of the W_down^T row gather (denseflux,
+ *               section 5.5: adjacent reads are merged when reading the gap costs
+ *               less than a new request, gap < L * B bytes).  A neuron lying
+ *               between two selected neurons of a gather share, with at most
+ *               merge_gap unselected neurons between them, is read as well
+ *               (with h = 0, so the result is unchanged); 0 = off (the default,
+ *               the measured best on MI355X), 0..64.
  */
 typedef struct sffn_policy {
     int32_t mode;
@@ -162,6 +169,8 @@ typedef struct sffn_policy {
     int32_t recent_n;
     int32_t min_keep;
     int32_t batch_path;
+    int32_t merge_gap;
+    int32_t reserved;
     double mass_thresh;
 } sffn_policy;
 

@@ -213,3 +213,28 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_policy_layout_matches_the_header():
+    import ctypes as C
+
+    import activation_sparse_gated_gate_amd as sf
+    assert C.sizeof(sf.Policy) == 48
+    assert sf.Policy.merge_gap.offset == 32 and sf.Policy.mass_thresh.offset == 40
+    assert C.sizeof(sf.ProbeCfg) == 20
+
+
+def test_probe_cfg_and_latency_probe_validation():
+    import ctypes as C
+
+    import activation_sparse_gated_gate_amd as sf
+    lib = sf._lib
+    ok = sf.ProbeCfg(256, 1024, 0, 8, 1)
+    assert lib.sffn_read_probe_cfg(None, 1024, C.byref(ok), 16, None) == sf.SFFN_ERR_INVALID_ARG
+    for bad in (sf.ProbeCfg(0, 1024, 0, 8, 1), sf.ProbeCfg(256, 300, 0, 8, 1), sf.ProbeCfg(256, 1024, 2, 8, 1),
+                sf.ProbeCfg(256, 1024, 0, 5, 1), sf.ProbeCfg(256, 1024, 0, 8, 2)):
+        assert lib.sffn_read_probe_cfg(256, 1024, C.byref(bad), 16, None) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_read_latency_probe(None, 4096, 1024, 16, 4, 16, None) == sf.SFFN_ERR_INVALID_ARG
+    assert lib.sffn_read_latency_probe(256, 4096, 1000, 16, 4, 16, None) == sf.SFFN_ERR_INVALID_ARG   # row size
+    assert lib.sffn_read_latency_probe(256, 512, 1024, 16, 4, 16, None) == sf.SFFN_ERR_INVALID_ARG    # buffer < row
+    assert lib.sffn_read_latency_probe(256, 4096, 1024, 16, 0, 16, None) == sf.SFFN_ERR_INVALID_ARG   # n

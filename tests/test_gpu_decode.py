@@ -403,6 +403,22 @@ def test_int4_batch1_topk_edge_cases(cfg3):
         assert np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("B", [1, 8])
+def test_topk_run_merging_reads_gaps_without_changing_the_result(cfg3, B):
+    """merge_gap > 0 also reads the unselected rows of short gaps with h = 0:
+    the selected set and y are the same values as without merging."""
+    sf = _sf()
+    w, x, layer = cfg3
+    k = synth.topk_count(w.d_ff, 17)
+    base = run_decode(layer, sf.make_policy("topk", topk_k=k, use_union=B > 1), x[:B])
+    for gap in (1, 4, 64):
+        y, idx, n = run_decode(layer, sf.make_policy("topk", topk_k=k, use_union=B > 1, merge_gap=gap), x[:B])
+        assert n == base[2] and np.array_equal(idx, base[1])
+        assert np.array_equal(y, base[0]), gap
+    with pytest.raises(sf.SffnError):
+        run_decode(layer, sf.make_policy("topk", topk_k=k, merge_gap=65), x[:1])
+
+
 def test_topk_ties_lower_index_first():
     # duplicated neurons give bit-identical scores; k cuts through the tie
     w = synth._make_weights(synth.WT_BF16, 512, 256, synth.ACT_SILU, (991, 992, 993))
