@@ -180,27 +180,4 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int *total)
     return res;
 }
 
-// In-place bitonic sort of n (a power of two) 64-bit keys in shared memory,
-// descending.  Each thread handles compare-exchange pairs q = tid, tid + NT, ...
-// of every pass (pair q joins elements i = 2q - (q mod j) and i + j).
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t *key, int n)
-{
-    const int NT = blockDim.x;
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int q = threadIdx.x; q < (n >> 1); q += NT) {
-                const int i = 2 * q - (q & (j - 1));
-                const int p = i + j;
-                const uint64_t x = key[i], y = key[p];
-                const bool desc = (i & k) == 0;
-                if (desc ? (x < y) : (x > y)) {
-                    key[i] = y;
-                    key[p] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 }  // namespace sffn

@@ -89,14 +89,42 @@ __device__ __forceinline__ uint64_t rank_key(float s, int i)
 // global rank of a key is its place in its chunk plus, for every other chunk,
 // the number of larger keys there (a binary search); the key is written to that
 // rank.  The result is the full descending order.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of the chunk's 1024 keys, descending, one key per thread: in
+// the stage that compares positions i and i ^ j inside runs of k, the lower
+// position keeps the larger key when its run descends ((i & k) == 0), the
+// smaller otherwise.  Partners less than 64 apart are in the same wave and are
+// exchanged by lane shuffles without a barrier; the 10 stages with j >= 64 go
+// through LDS, double-buffered, one barrier each.
 __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks)
 {
-    __shared__ uint64_t key[1024];
-    const int i = blockIdx.x * 1024 + threadIdx.x;
-    key[threadIdx.x] = i < L ? rank_key(s[i], i) : 0ull;
-    __syncthreads();
-    bitonic_sort_desc(key, 1024);
-    chunks[(size_t)blockIdx.x * 1024 + threadIdx.x] = key[threadIdx.x];
+    __shared__ uint64_t buf[2][1024];
+    const int tid = threadIdx.x;
+    const int i = blockIdx.x * 1024 + tid;
+    uint64_t v = i < L ? rank_key(s[i], i) : 0ull;
+    int nb = 0;
+    for (int k = 2; k <= 1024; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t o;
+            if (j >= 64) {
+                buf[nb][tid] = v;
+                __syncthreads();
+                o = buf[nb][tid ^ j];
+                nb ^= 1;
+            } else {
+                o = shfl_xor64(v, j);
+            }
+            const bool lower = (tid & j) == 0, desc = (tid & k) == 0;
+            v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+        }
+    }
+    chunks[(size_t)blockIdx.x * 1024 + tid] = v;
 }
 
 __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict__ chunks, int G,
@@ -116,31 +144,57 @@ __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict
     const int c = blockIdx.x, p = threadIdx.x;
     const uint64_t key = all[c * 1024 + p];
     if (key == 0) return;   // padding
+    // in every other chunk, the number of keys above this key (a chunk is sorted
+    // descending): branch-free binary searches of all chunks advanced together,
+    // one LDS read per chunk per step, so the reads of a step are in flight at once
+    constexpr int GMAX = kMaxPrefillRows / 1024;
+    int lo[GMAX];
+#pragma unroll
+    for (int c2 = 0; c2 < GMAX; ++c2) lo[c2] = 0;
+#pragma unroll
+    for (int step = 512; step >= 1; step >>= 1) {
+        uint64_t q[GMAX];
+#pragma unroll
+        for (int c2 = 0; c2 < GMAX; ++c2) q[c2] = all[min(c2, G - 1) * 1024 + lo[c2] + step - 1];   // unconditional reads
+#pragma unroll
+        for (int c2 = 0; c2 < GMAX; ++c2)
+            if (c2 < G && c2 != c && q[c2] > key) lo[c2] += step;
+    }
     int rank = p;
-    for (int c2 = 0; c2 < G; ++c2) {
-        if (c2 == c) continue;
-        const uint64_t *q = all + c2 * 1024;
-        int lo = 0, hi = 1024;   // first position whose key is below this key
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (q[mid] > key) lo = mid + 1; else hi = mid;
-        }
-        rank += lo;
+#pragma unroll
+    for (int c2 = 0; c2 < GMAX; ++c2) {
+        if (c2 < G && c2 != c) rank += lo[c2] + (lo[c2] == 1023 && all[c2 * 1024 + 1023] > key ? 1 : 0);
     }
     sorted[rank] = key;
 }
 
+// The selection proper, one workgroup.  The sorted order is held in LDS as
+// the fp32 scores, block by block of kMassBlock entries with one word of
+// padding per block (so the 64 threads that each walk one block read
+// different banks), and the 16-bit token index of every rank.  The fp64 block
+// sums are taken by wave 0 (lane b adds block b in order, keeping the running
+// sum after every 32 entries), the block bases by a sequential chain over the
+// lanes' totals; the threshold block's scan restarts from its last checkpoint
+// below the threshold.  The keep list is built in rounds of 1024 consecutive
+// tokens (ballot + mbcnt, wave offsets through LDS), so every load and store
+// of the list and the flags is coalesced.
+constexpr int kMassPad = kMassBlock + 1;
+
+__device__ __forceinline__ int mass_slot(int r) { return (r / kMassBlock) * kMassPad + (r % kMassBlock); }
+
 __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const int L = a.L, tid = threadIdx.x, NT = 1024;
-    int N = 1;
-    while (N < L) N <<= 1;
-    uint64_t *key = (uint64_t *)lds_raw;                      // [N]
-    unsigned char *in = lds_raw + (size_t)N * 8;              // [L] membership
-    __shared__ double blk_total[kMaxPrefillRows / kMassBlock + 1];
-    __shared__ double blk_base[kMaxPrefillRows / kMassBlock + 1];
-    __shared__ int s_m, s_all, s_cnt;
+    constexpr int NBMAX = kMaxPrefillRows / kMassBlock;
+    constexpr int NCP = kMassBlock / 32;
+    const int L = a.L, tid = threadIdx.x, NT = 1024, lane = tid & 63, wave = tid >> 6;
+    const int nb = (L + kMassBlock - 1) / kMassBlock;
+    float *sc = (float *)lds_raw;                                        // [nb][kMassPad]
+    uint16_t *tok = (uint16_t *)(sc + (size_t)nb * kMassPad);             // [L]
+    unsigned char *in = (unsigned char *)(tok + ((L + 7) & ~7));          // [L] membership
+    __shared__ double blk_base[NBMAX + 1];
+    __shared__ double cpt[NBMAX][NCP];
+    __shared__ int s_m, s_all;
     __shared__ int tmp[17];
 
     {
@@ -150,58 +204,61 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
 #pragma unroll
         for (int q = 0; q < PER; ++q) kv[q] = tid + q * NT < L ? a.sorted[tid + q * NT] : 0ull;
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-            if (tid + q * NT < L) key[tid + q * NT] = kv[q];
+        for (int q = 0; q < PER; ++q) {
+            const int r = tid + q * NT;
+            if (r < L) {
+                sc[mass_slot(r)] = __uint_as_float((uint32_t)(kv[q] >> 32));
+                tok[r] = (uint16_t)(0xFFFFFFFFu - (uint32_t)kv[q]);
+            }
+        }
     }
     for (int i = tid; i < L; i += NT) in[i] = 0;
     if (tid == 0) s_m = -1;   // no prefix unless a block finds the threshold
     __syncthreads();
-    // fp64 cumulative mass in blocks of kMassBlock sorted entries: thread b adds
-    // block b in order (its values loaded 32 at a time ahead of the adds) and
-    // keeps the running sum after every 32 entries, so that the threshold scan
-    // can start from the last checkpoint below the threshold
-    const int nb = (L + kMassBlock - 1) / kMassBlock;
-    constexpr int NCP = kMassBlock / 32;
-    __shared__ double cpt[kMaxPrefillRows / kMassBlock][NCP];
-    auto score_at = [&](int k) { return __uint_as_float((uint32_t)(key[k] >> 32)); };
-    if (tid < nb) {
+    // fp64 cumulative mass in blocks of kMassBlock sorted entries: lane b of
+    // wave 0 adds block b in order (32 values read ahead of the dependent adds)
+    // and keeps the running sum after every 32 entries; then the block bases
+    // are the sequential sums of the block totals
+    if (wave == 0) {
         double run = 0.0;
-        const int b0 = tid * kMassBlock, b1 = min(L, b0 + kMassBlock);
-        for (int k0 = b0; k0 < b1; k0 += 32) {
-            float v[32];
+        if (lane < nb) {
+            const int b0 = lane * kMassBlock, b1 = min(L, b0 + kMassBlock);
+            const float *sb = sc + (size_t)lane * kMassPad;
+            for (int k0 = 0; k0 < b1 - b0; k0 += 32) {
+                // the 32 reads are unconditional (a short last block reads padding
+                // slots inside the array, masked below), so they are all in flight
+                // before the dependent adds
+                float v[32];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) v[u] = k0 + u < b1 ? score_at(k0 + u) : 0.0f;
-            __builtin_amdgcn_sched_barrier(0);   // keep the 32 reads ahead of the dependent adds
-            if (k0 + 32 <= b1) {
+                for (int u = 0; u < 32; ++u) v[u] = sb[k0 + u];
 #pragma unroll
-                for (int u = 0; u < 32; ++u) run = run + (double)v[u];
-            } else {
+                for (int u = 0; u < 32; ++u) v[u] = b0 + k0 + u < b1 ? v[u] : 0.0f;
+                if (b0 + k0 + 32 <= b1) {
 #pragma unroll
-                for (int u = 0; u < 32; ++u)
-                    if (k0 + u < b1) run = run + (double)v[u];
+                    for (int u = 0; u < 32; ++u) run = run + (double)v[u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 32; ++u)
+                        if (b0 + k0 + u < b1) run = run + (double)v[u];
+                }
+                cpt[lane][k0 >> 5] = run;   // the sum of the block's entries up to k0 + 31
             }
-            cpt[tid][(k0 - b0) >> 5] = run;   // the sum of the block's entries up to k0 + 31
         }
-        blk_total[tid] = run;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        constexpr int NBMAX = kMaxPrefillRows / kMassBlock;
-        double tv[NBMAX];
-#pragma unroll
-        for (int b = 0; b < NBMAX; ++b) tv[b] = b < nb ? blk_total[b] : 0.0;
+        // block b's base = total of blocks 0 .. b-1, added in order
         double base = 0.0;
-#pragma unroll
-        for (int b = 0; b < NBMAX; ++b) {
-            if (b < nb) {
-                blk_base[b] = base;
-                base = base + tv[b];
-            }
+        for (int b = 0; b < nb; ++b) {
+            if (lane == 0) blk_base[b] = base;
+            const double tb = __longlong_as_double(
+                ((long long)__builtin_amdgcn_readlane((int)(__double_as_longlong(run) >> 32), b) << 32) |
+                (long long)(uint32_t)__builtin_amdgcn_readlane((int)__double_as_longlong(run), b));
+            base = base + tb;
         }
-        const double total = base;  // equals the last cumulative value
-        // a non-finite total (a NaN or infinite score) keeps every token, like an all-zero row
-        s_all = (a.mass >= 1.0 || total == 0.0 || !isfinite(total)) ? 1 : 0;
-        blk_base[nb] = total;
+        const double total = base;   // equals the last cumulative value
+        if (lane == 0) {
+            blk_base[nb] = total;
+            // a non-finite total (a NaN or infinite score) keeps every token, like an all-zero row
+            s_all = (a.mass >= 1.0 || total == 0.0 || !isfinite(total)) ? 1 : 0;
+        }
     }
     __syncthreads();
     const bool all = s_all != 0;
@@ -212,27 +269,30 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
         if (tid < nb && blk_base[tid + 1] >= thr && (tid == 0 || blk_base[tid] < thr)) {
             const double base = blk_base[tid];
             const int b0 = tid * kMassBlock, b1 = min(L, b0 + kMassBlock);
+            const float *sb = sc + (size_t)tid * kMassPad;
             // the 32-entry span where the cumulative mass first reaches thr
             int j = 0;
             while (b0 + 32 * (j + 1) < b1 && base + cpt[tid][j] < thr) ++j;
             double run = j > 0 ? cpt[tid][j - 1] : 0.0;
-            const int k0 = b0 + 32 * j;
+            const int k0 = 32 * j;
             float v[32];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) v[u] = k0 + u < b1 ? score_at(k0 + u) : 0.0f;
+            for (int u = 0; u < 32; ++u) v[u] = sb[k0 + u];   // unconditional, masked below
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v[u] = b0 + k0 + u < b1 ? v[u] : 0.0f;
             int hit = -1;
 #pragma unroll
             for (int u = 0; u < 32; ++u) {
-                if (hit < 0 && k0 + u < b1) {
+                if (hit < 0 && b0 + k0 + u < b1) {
                     run = run + (double)v[u];
-                    if (base + run >= thr) hit = k0 + u;
+                    if (base + run >= thr) hit = b0 + k0 + u;
                 }
             }
             s_m = hit;
         }
         __syncthreads();
         // the shortest prefix: ranks 0..m
-        for (int r = tid; r <= s_m; r += NT) in[0xFFFFFFFFu - (uint32_t)key[r]] = 1;
+        for (int r = tid; r <= s_m; r += NT) in[tok[r]] = 1;
     }
     __syncthreads();
     if (all) {
@@ -254,11 +314,11 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
             const int per = (L + NT - 1) / NT;
             const int r0 = min(L, tid * per), r1 = min(L, r0 + per);
             int free = 0;
-            for (int r = r0; r < r1; ++r) free += in[0xFFFFFFFFu - (uint32_t)key[r]] ? 0 : 1;
+            for (int r = r0; r < r1; ++r) free += in[tok[r]] ? 0 : 1;
             int ftot;
             int before = block_exclusive_scan(free, tmp, &ftot);
             for (int r = r0; r < r1 && before < need; ++r) {
-                const int i = (int)(0xFFFFFFFFu - (uint32_t)key[r]);
+                const int i = tok[r];
                 if (!in[i]) {
                     in[i] = 1;
                     ++before;
@@ -267,25 +327,56 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
         }
     }
     __syncthreads();
-    // ascending keep list: contiguous token runs per thread, block scan of counts
-    const int per = (L + NT - 1) / NT;
-    const int i0 = min(L, tid * per), i1 = min(L, i0 + per);
-    int c = 0;
-    for (int i = i0; i < i1; ++i) c += in[i] ? 1 : 0;
-    int tot;
-    int pos = block_exclusive_scan(c, tmp, &tot);
-    for (int i = i0; i < i1; ++i) {
-        const int on = in[i] ? 1 : 0;
-        a.flags[i] = on;
+    // ascending keep list: thread tid holds tokens q NT + tid; the kept count of
+    // every (round q, wave) goes to LDS, one thread per round turns them into
+    // offsets, then every thread writes its kept tokens (two barriers in all,
+    // none between global stores and LDS traffic)
+    constexpr int PER = kMaxPrefillRows / 1024;
+    __shared__ int wcnt[PER][16];
+    __shared__ int qbase[PER + 1];
+    uint32_t onb = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int i = q * NT + tid;
+        const bool on = i < L && in[i];
+        onb |= on ? (1u << q) : 0u;
+        const uint64_t m = __ballot(on);
+        if (lane == 0) wcnt[q][wave] = __popcll(m);
+    }
+    __syncthreads();
+    if (tid < PER) {
+        int run = 0;
+        for (int w2 = 0; w2 < 16; ++w2) {
+            const int c2 = wcnt[tid][w2];
+            wcnt[tid][w2] = run;
+            run += c2;
+        }
+        qbase[tid] = run;   // the round's total for now
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int q = 0; q < PER; ++q) {
+            const int t = qbase[q];
+            qbase[q] = run;
+            run += t;
+        }
+        qbase[PER] = run;
+        *a.count = run;
+        *a.count_copy = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int i = q * NT + tid;
+        const bool on = (onb >> q) & 1u;
+        const uint64_t m = __ballot(on);
+        if (i < L) a.flags[i] = on ? 1 : 0;
         if (on) {
+            const int pos = qbase[q] + wcnt[q][wave] + mbcnt64(m);
             a.keep[pos] = i;
             a.keep_copy[pos] = i;
-            ++pos;
         }
-    }
-    if (tid == 0) {
-        *a.count = tot;
-        *a.count_copy = tot;
     }
 }
 
@@ -681,9 +772,9 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, c.stream, c.A, rows, d, sc_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int N = 1;
-    while (N < rows) N <<= 1;
-    const size_t lds = (size_t)N * 8 + (size_t)rows;
+    // scores (padded blocks), 16-bit token indices, membership bytes
+    const size_t lds = (size_t)((rows + kMassBlock - 1) / kMassBlock) * kMassPad * 4 + (size_t)((rows + 7) & ~7) * 2 +
+                       (size_t)rows;
     const int G = (rows + 1023) / 1024;   // <= kMaxPrefillRows / 1024 = 16
     static std::once_flag once_sel, once_merge;
     static hipError_t err_sel = hipSuccess, err_merge = hipSuccess;
