@@ -1028,44 +1028,77 @@ struct UpTiledArgs {
     int want;
 };
 
-template <int U>
-__device__ __forceinline__ f32x4_t mfma_stream(const uint16_t *__restrict__ w, const uint16_t *__restrict__ xh,
-                                               const uint16_t *__restrict__ xl, int k0, int k1, f32x4_t acc)
+// One MFMA k-step group: U k-steps of the activation operand (bf16 hi / lo,
+// lane order) loaded once and applied to NB weight tiles (NB x 16 rows), two
+// MFMAs per tile and step.  w[b], xh, xl are already offset by lane * 8; step
+// k is 512 elements further.  live[b] false skips tile b (uniform per wave).
+template <int U, int NB>
+__device__ __forceinline__ void mfma_group(const uint16_t *const (&w)[NB], const bool (&live)[NB],
+                                           const uint16_t *__restrict__ xh, const uint16_t *__restrict__ xl, int k,
+                                           int k1, f32x4_t (&acc)[NB])
 {
-    // w, xh, xl already offset by lane * 8; step k is 512 elements further
-    for (int k = k0; k < k1; k += U) {
-        bf16x8_t av[U], bh[U], bl[U];
+    bf16x8_t bh[U], bl[U], av[U][NB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool ok = k + u < k1;
-            const size_t o = (size_t)(k + u) * 512;
-            uint4 wa = ok ? ld16_nt(w + o) : make_uint4(0, 0, 0, 0);
-            uint4 xa = ok ? *(const uint4 *)(xh + o) : make_uint4(0, 0, 0, 0);
-            uint4 xb = ok ? *(const uint4 *)(xl + o) : make_uint4(0, 0, 0, 0);
-            __builtin_memcpy(&av[u], &wa, 16);
-            __builtin_memcpy(&bh[u], &xa, 16);
-            __builtin_memcpy(&bl[u], &xb, 16);
-        }
+    for (int u = 0; u < U; ++u) {
+        const bool ok = k + u < k1;
+        const size_t o = (size_t)(k + u) * 512;
+        const uint4 xa = ok ? *(const uint4 *)(xh + o) : make_uint4(0, 0, 0, 0);
+        const uint4 xb = ok ? *(const uint4 *)(xl + o) : make_uint4(0, 0, 0, 0);
+        __builtin_memcpy(&bh[u], &xa, 16);
+        __builtin_memcpy(&bl[u], &xb, 16);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bh[u], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[u], acc, 0, 0, 0);
+        for (int b = 0; b < NB; ++b) {
+            const uint4 wa = (ok && live[b]) ? ld16_nt(w[b] + o) : make_uint4(0, 0, 0, 0);
+            __builtin_memcpy(&av[u][b], &wa, 16);
         }
     }
-    return acc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (live[b]) {
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][b], bh[u], acc[b], 0, 0, 0);
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][b], bl[u], acc[b], 0, 0, 0);
+            }
+        }
+    }
 }
 
-__global__ __launch_bounds__(64) void k_up_tiled(const UpTiledArgs a)
+// Up on the W_up tiles: a workgroup owns kUpBlocks consecutive blocks of 16
+// neurons; its four waves split the k range in quarters and each streams the
+// activation steps once for all of the workgroup's tiles (the activation
+// operand is as large as a weight tile per step, so sharing it halves the
+// bytes moved); the four partial tiles are added in LDS in wave order, then
+// wave b forms h for block b.  Blocks with no selected neuron skip their weights.
+constexpr int kUpBlocks = 2;
+
+__global__ __launch_bounds__(256) void k_up_tiled(const UpTiledArgs a)
 {
     if (a.path && *a.path != a.want) return;
-    const int t = blockIdx.x, lane = threadIdx.x;
+    __shared__ f32x4_t part[4][kUpBlocks][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * kUpBlocks;
+    const int KS = a.d / 32;
+    const int k0 = (KS * w) / 4, k1 = (KS * (w + 1)) / 4;
+    bool live[kUpBlocks];
+    const uint16_t *wp[kUpBlocks];
+    f32x4_t acc[kUpBlocks];
+#pragma unroll
+    for (int b = 0; b < kUpBlocks; ++b) {
+        live[b] = a.list_cnt[t0 + b] > 0;
+        wp[b] = a.wut + (size_t)(t0 + b) * KS * 512 + lane * 8;
+        acc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int k = k0; k < k1; k += 4) mfma_group<4, kUpBlocks>(wp, live, a.xh + lane * 8, a.xl + lane * 8, k, k1, acc);
+#pragma unroll
+    for (int b = 0; b < kUpBlocks; ++b) part[w][b][lane] = acc[b];
+    __syncthreads();
+    const int t = t0 + w;   // wave w finishes block w
+    if (w >= kUpBlocks) return;
+    const f32x4_t s4 = ((part[0][w][lane] + part[1][w][lane]) + part[2][w][lane]) + part[3][w][lane];
     const int cnt = a.list_cnt[t];
     uint32_t m = 0;
     for (int s2 = 0; s2 < cnt; ++s2) m |= 1u << (a.list_idx[t * 16 + s2] - t * 16);
-    const int KS = a.d / 32;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (cnt > 0)
-        acc = mfma_stream<8>(a.wut + (size_t)t * KS * 512 + lane * 8, a.xh + lane * 8, a.xl + lane * 8, 0, KS, acc);
     // C[neuron 4q + e][token n]
     const int n = lane & 15, q = lane >> 4;
     uint16_t hb[4], lb[4];
@@ -1075,7 +1108,7 @@ __global__ __launch_bounds__(64) void k_up_tiled(const UpTiledArgs a)
         float h = 0.0f;
         if (n < a.B && ((m >> r) & 1u)) {
             const float gp = a.G[(size_t)n * a.f + j];
-            if (a.use_union || gate_pred(a.mode, gp, a.theta)) h = act_f32(a.act, gp) * acc[e];
+            if (a.use_union || gate_pred(a.mode, gp, a.theta)) h = act_f32(a.act, gp) * s4[e];
         }
         hb[e] = bf16_rne_bits(h);
         lb[e] = bf16_rne_bits(h - bf16_lo(hb[e]));
@@ -1099,17 +1132,33 @@ struct DownTiledArgs {
     int want;
 };
 
+// Down on the W_down tiles: one wave per (kDownCols blocks of 16 output
+// columns, d_ff split); each k-step's h operand (hi / lo) is loaded once for
+// the wave's kDownCols weight tiles.
+constexpr int kDownCols = 4;
+
 __global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
 {
     if (a.path && *a.path != a.want) return;
-    const int t = blockIdx.x, p = blockIdx.y, lane = threadIdx.x;
+    const int tc = blockIdx.x * kDownCols, p = blockIdx.y, lane = threadIdx.x;
     const int KS = a.f / 32;
     const int k0 = min(KS, p * a.per), k1 = min(KS, k0 + a.per);
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mfma_stream<8>(a.wdtl + (size_t)t * KS * 512 + lane * 8, a.hh + lane * 8, a.hl + lane * 8, k0, k1, acc);
-    // C[output column 16t + 4q + e][token n]
+    bool live[kDownCols];
+    const uint16_t *wp[kDownCols];
+    f32x4_t acc[kDownCols];
+#pragma unroll
+    for (int b = 0; b < kDownCols; ++b) {
+        live[b] = true;
+        wp[b] = a.wdtl + (size_t)(tc + b) * KS * 512 + lane * 8;
+        acc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int k = k0; k < k1; k += 4) mfma_group<4, kDownCols>(wp, live, a.hh + lane * 8, a.hl + lane * 8, k, k1, acc);
+    // C[output column 16 (tc + b) + 4q + e][token n]
     const int n = lane & 15, q = lane >> 4;
-    *(float4 *)(a.partial + ((size_t)p * 16 + n) * a.d + t * 16 + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+    for (int b = 0; b < kDownCols; ++b)
+        *(float4 *)(a.partial + ((size_t)p * 16 + n) * a.d + (tc + b) * 16 + 4 * q) =
+            make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
 }
 
 __device__ __forceinline__ void down_sum_elem(const float *__restrict__ partial, int ns, int d, int i,
@@ -1181,18 +1230,26 @@ __device__ __forceinline__ void lds_copy16(const void *g, void *lds_wave_base)
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la) : "memory");
 }
 
+// LDS of one class-split gate workgroup: W stages [stage][wave][row in wave][i]
+// (16 bytes each), then x stages [stage][token][half][i][4] (conflict-free reads)
+typedef uint4 GateWsm[kGateStages][4][4 * kGateClsRPW][16];
+typedef float GateXs[kGateStages][16][2][16][4];
+constexpr int kGateSmem = (int)(sizeof(GateWsm) + sizeof(GateXs));
+
+// one class-split gate workgroup: rows tile * kGateClsRows .. + kGateClsRows,
+// accumulator class m, partial sums to a.part
 template <int BT>
-__global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const float *__restrict__ x)
+__device__ __forceinline__ void gate_pipe_tile(const GateClsArgs &a, const float *__restrict__ x, int tile, int m,
+                                               uint8_t *smem)
 {
     constexpr int RPW = kGateClsRPW, S = kGateStages;
-    __shared__ __align__(16) uint4 wsm[S][4][4 * RPW][16];   // [stage][wave][row in wave][i]
-    __shared__ __align__(16) float xs[S][16][2][16][4];      // [stage][token][half][i][4]: conflict-free reads
+    GateWsm &wsm = *reinterpret_cast<GateWsm *>(smem);
+    GateXs &xs = *reinterpret_cast<GateXs *>(smem + sizeof(GateWsm));
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, r = lane >> 4;
-    const int m = blockIdx.y;
     const int nch = a.d / 8, K = (nch + 63) / 64, B = a.B, f = a.f;
-    const int jw = blockIdx.x * kGateClsRows + w * 4 * RPW;   // first row of this wave
+    const int jw = tile * kGateClsRows + w * 4 * RPW;   // first row of this wave
     const size_t kstride = (size_t)f * 128;
     const uint16_t *wsrc = a.wgc + ((size_t)m * K * f + jw) * 128 + lane * 8;
 
@@ -1266,6 +1323,143 @@ __global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const fl
     }
 }
 
+template <int BT>
+__global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const float *__restrict__ x)
+{
+    __shared__ __align__(16) uint8_t smem[kGateSmem];
+    gate_pipe_tile<BT>(a, x, blockIdx.x, blockIdx.y, smem);
+}
+
+// ---------------------------------------------------------------------------
+// 9..16 tokens on the tile path: the class-split gate and the MFMA up
+// projection in one launch.  Up does not need the gate (h = act(g') u is
+// formed afterwards), so the two run side by side: the grid interleaves two
+// gate workgroups (VALU- and LDS-bound) with one up workgroup (bound by the
+// W_up stream), so every CU holds both kinds and the gate's arithmetic hides
+// under the up projection's weight traffic.  Both roles fit one resource
+// budget (the gate's LDS, the larger register count).  u is written in fp32;
+// k_combine_h adds the gate classes and forms the selection, the lists and h.
+// ---------------------------------------------------------------------------
+struct UpUArgs {
+    const uint16_t *wut;             // W_up tiles [f/16][d/32][64][8]
+    const uint16_t *xh, *xl;         // x_hat bf16 hi / lo, lane order [d/32][64][8]
+    int d, f, B;
+    float *U;                        // [B][f]
+};
+
+// u for the blocks 2 ui, 2 ui + 1 of 16 neurons: the four waves split d_model in
+// quarters, each streams its activation steps once for both tiles, and the
+// partial tiles are added in LDS in wave order
+__device__ __forceinline__ void up_u_tiles(const UpUArgs &a, int ui, uint8_t *smem)
+{
+    constexpr int NB = 2;
+    f32x4_t(&part)[4][NB][64] = *reinterpret_cast<f32x4_t(*)[4][NB][64]>(smem);
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int t0 = ui * NB, KS = a.d / 32;
+    const int k0 = (KS * w) / 4, k1 = (KS * (w + 1)) / 4;
+    const bool live[NB] = {true, true};
+    const uint16_t *wp[NB];
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        wp[b] = a.wut + (size_t)(t0 + b) * KS * 512 + lane * 8;
+        acc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int k = k0; k < k1; k += 4) mfma_group<4, NB>(wp, live, a.xh + lane * 8, a.xl + lane * 8, k, k1, acc);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part[w][b][lane] = acc[b];
+    __syncthreads();
+    if (w >= NB) return;
+    const f32x4_t s4 = ((part[0][w][lane] + part[1][w][lane]) + part[2][w][lane]) + part[3][w][lane];
+    // C[neuron 4q + e][token n]
+    const int n = lane & 15, q = lane >> 4;
+    if (n < a.B)
+        *(float4 *)(a.U + (size_t)n * a.f + (t0 + w) * 16 + 4 * q) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+}
+
+constexpr int kDualPeriod = 3;   // per period: two gate workgroups, then one up workgroup
+
+template <int BT>
+__global__ __launch_bounds__(256) void k_gate_up_dual(const GateClsArgs ga, const float *__restrict__ x,
+                                                      const UpUArgs ua)
+{
+    __shared__ __align__(16) uint8_t smem[kGateSmem];
+    const int per = blockIdx.x / kDualPeriod, ph = blockIdx.x % kDualPeriod;
+    if (ph < 2) {
+        const int gi = 2 * per + ph;   // gate workgroups: f / 16 = 4 classes x f / 64 tiles
+        gate_pipe_tile<BT>(ga, x, gi >> 2, gi & 3, smem);
+    } else {
+        up_u_tiles(ua, per, smem);     // f / 32 up workgroups
+    }
+}
+
+// g' = ((class 0 + class 2) + (class 1 + class 3)) + b, the selection, the
+// lists per block of 16 neurons and h = act(g') u on the selected (token,
+// neuron) pairs (0 elsewhere) as bf16 hi / lo in lane order over d_ff.  One
+// wave per 32 neurons; lane (g, n) takes neurons 8 g .. 8 g + 7 of token n
+// (one 16-byte piece of the lane order: step j0 / 32, k-group g, slot n).
+__global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part, const float *__restrict__ U, int B,
+                                                  int f, float bias, int mode, float theta, int act, int use_union,
+                                                  float *__restrict__ G, int *__restrict__ list_cnt,
+                                                  int *__restrict__ list_idx, uint16_t *__restrict__ hh,
+                                                  uint16_t *__restrict__ hl)
+{
+    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15, s = blockIdx.x;
+    const int j = s * 32 + 8 * g;   // first of the lane's 8 neurons
+    float gp[8];
+    uint32_t on = 0;
+    if (n < B) {
+        const size_t cs = (size_t)B * f, o = (size_t)n * f + j;
+        float p[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 v0 = *(const float4 *)(part + c * cs + o), v1 = *(const float4 *)(part + c * cs + o + 4);
+            p[c][0] = v0.x; p[c][1] = v0.y; p[c][2] = v0.z; p[c][3] = v0.w;
+            p[c][4] = v1.x; p[c][5] = v1.y; p[c][6] = v1.z; p[c][7] = v1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            gp[e] = ((p[0][e] + p[2][e]) + (p[1][e] + p[3][e])) + bias;
+            on |= gate_pred(mode, gp[e], theta) ? (1u << e) : 0u;
+        }
+        *(float4 *)(G + o) = make_float4(gp[0], gp[1], gp[2], gp[3]);
+        *(float4 *)(G + o + 4) = make_float4(gp[4], gp[5], gp[6], gp[7]);
+    }
+    // union over the tokens: neuron 8 g + e is selected if any lane of group g has bit e
+    uint32_t mask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint64_t bal = __ballot((on >> e) & 1u);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) mask |= ((bal >> (16 * gg)) & 0xFFFFull) ? (1u << (8 * gg + e)) : 0u;
+    }
+    if (lane < 32 && ((mask >> lane) & 1u)) {
+        const int b = lane >> 4;
+        const uint32_t mb = (mask >> (16 * b)) & 0xFFFFu;
+        list_idx[(size_t)(2 * s + b) * 16 + __popc(mb & ((1u << (lane & 15)) - 1u))] = s * 32 + lane;
+    }
+    if (lane < 2) list_cnt[2 * s + lane] = __popc((mask >> (16 * lane)) & 0xFFFFu);
+    uint16_t hb[8], lb[8];
+    float u[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (n < B) {
+        const float4 u0 = *(const float4 *)(U + (size_t)n * f + j), u1 = *(const float4 *)(U + (size_t)n * f + j + 4);
+        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float h = 0.0f;
+        if (n < B && ((mask >> (8 * g + e)) & 1u) && (use_union || ((on >> e) & 1u))) h = act_f32(act, gp[e]) * u[e];
+        hb[e] = bf16_rne_bits(h);
+        lb[e] = bf16_rne_bits(h - bf16_lo(hb[e]));
+    }
+    const size_t o = ((size_t)s * 64 + (g << 4) + n) * 8;
+    uint4 ph, pl;
+    __builtin_memcpy(&ph, hb, 16);
+    __builtin_memcpy(&pl, lb, 16);
+    *(uint4 *)(hh + o) = ph;
+    *(uint4 *)(hl + o) = pl;
+}
+
 // g' = ((class 0 + class 2) + (class 1 + class 3)) + b; selection flags; ascending
 // lists per block of 16 rows (ballot + mbcnt), the format of the gate kernels
 __global__ __launch_bounds__(64) void k_gate_combine(const float *__restrict__ part, int B, int f, float bias,
@@ -1286,6 +1480,68 @@ __global__ __launch_bounds__(64) void k_gate_combine(const float *__restrict__ p
     const uint64_t below = m & ((1ull << lane) - 1ull) & (0xFFFFull << (16 * sb));
     if (on) list_idx[(size_t)(j >> 4) * 16 + __popcll(below)] = j;
     if ((lane & 15) == 0) list_cnt[j >> 4] = __popcll(m & (0xFFFFull << (16 * sb)));
+}
+
+// RMSNorm prologue with the MFMA operand split: one wave per token slot (16
+// slots); x_hat as k_rmsnorm computes it (same order, same scale), plus x_hat
+// as bf16 hi / lo in lane order.  Slots >= B write zero operands only.
+__global__ __launch_bounds__(64) void k_rmsnorm_split(const float *__restrict__ x, float *__restrict__ xhat,
+                                                      int B, int d, float eps, uint16_t *__restrict__ xh,
+                                                      uint16_t *__restrict__ xl)
+{
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float r = 0.0f;
+    const float *xt = x + (size_t)min(t, B - 1) * d;
+    if (t < B) {
+        const int nch = d / 4;
+        float acc = 0.0f;
+        for (int k0 = 0; k0 * 64 < nch; k0 += 16) {
+            float4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int c = (k0 + u) * 64 + lane;
+                v[u] = c < nch ? *(const float4 *)(xt + 4 * c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if ((k0 + u) * 64 + lane < nch) {
+                    acc = __builtin_fmaf(v[u].x, v[u].x, acc);
+                    acc = __builtin_fmaf(v[u].y, v[u].y, acc);
+                    acc = __builtin_fmaf(v[u].z, v[u].z, acc);
+                    acc = __builtin_fmaf(v[u].w, v[u].w, acc);
+                }
+            }
+        }
+        const float ss = wave_tree_sum(acc);
+        r = 1.0f / sqrtf(ss / (float)d + eps);
+    }
+    // pieces of 8 values: step s, k-group g -> lane slot (g << 4) | t
+    for (int pc = lane; pc < d / 8; pc += 64) {
+        const int s = pc >> 2, g = pc & 3;
+        uint16_t h[8], lo[8];
+        float v[8];
+        if (t < B) {
+            const float4 v0 = *(const float4 *)(xt + 8 * pc), v1 = *(const float4 *)(xt + 8 * pc + 4);
+            v[0] = v0.x * r; v[1] = v0.y * r; v[2] = v0.z * r; v[3] = v0.w * r;
+            v[4] = v1.x * r; v[5] = v1.y * r; v[6] = v1.z * r; v[7] = v1.w * r;
+            *(float4 *)(xhat + (size_t)t * d + 8 * pc) = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4 *)(xhat + (size_t)t * d + 8 * pc + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = bf16_rne_bits(v[e]);
+            lo[e] = bf16_rne_bits(v[e] - bf16_lo(h[e]));
+        }
+        const size_t o = ((size_t)s * 64 + (g << 4) + t) * 8;
+        uint4 ph, pl;
+        __builtin_memcpy(&ph, h, 16);
+        __builtin_memcpy(&pl, lo, 16);
+        *(uint4 *)(xh + o) = ph;
+        *(uint4 *)(xl + o) = pl;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1766,12 +2022,27 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     hipStream_t st = c.stream;
     hipError_t e;
 
+    // 9..16 tokens on the tile path: gate and up in one kernel (k_gu_tiles),
+    // with the MFMA operand split done by the RMSNorm prologue
+    bool gu_fused = false;
+    if constexpr (WT == SFFN_W_BF16 && BT == 16)
+        gu_fused = forward && c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && L.wut &&
+                   (c.batch_path ? c.batch_path == kPathTiled : gather_below_permille(B) == 0);
+    uint16_t *const xsh = (uint16_t *)(sc + S.xsplit), *const xsl = xsh + (size_t)16 * d;
+
     const float *xin = c.x;
     if (D.rmsnorm) {
         float *xh = (float *)(sc + S.xhat);
-        hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(64), 0, st, c.x, xh, d, D.eps);
+        if (gu_fused)
+            hipLaunchKernelGGL(k_rmsnorm_split, dim3(16), dim3(64), 0, st, c.x, xh, B, d, D.eps, xsh, xsl);
+        else
+            hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(64), 0, st, c.x, xh, d, D.eps);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         xin = xh;
+    } else if (gu_fused) {
+        hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xsh, xsl,
+                           (const int *)nullptr, 0, f, 0, (int *)nullptr);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     float *G = (float *)(sc + S.G);
     float *U = (float *)(sc + S.U);
@@ -1833,17 +2104,30 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
 
     if constexpr (WT == SFFN_W_BF16 && BT >= 8) {
         if (c.mode != SFFN_MODE_TOPK && c.mode != SFFN_MODE_DENSE && L.wut) {
-            // fixed-order gate with per-block lists, then MFMA up and down
-            // class-split gate in the fixed order, lists per block of 16 rows
-            GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
+            const int R = 16;
+            uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
             hipEvent_t evb = nullptr, eve = nullptr;
             if (forward) L.timer->take(&evb, &eve);
-            SFFN_LAUNCH((k_gate_pipe<BT>), dim3(f / kGateClsRows, 4), dim3(256), 0, st, evb, eve, ga, (const float *)xin);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_gate_combine, dim3(f / 64), dim3(64), 0, st, (const float *)ga.part, B, f, c.bias,
-                               c.mode, c.theta, G, lcnt, lidx);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            const int R = 16;
+            if (gu_fused) {
+                // class-split gate and MFMA u side by side, then g', selection, lists and h
+                GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
+                UpUArgs ua{L.wut, xsh, xsl, d, f, B, U};
+                SFFN_LAUNCH((k_gate_up_dual<BT>), dim3(kDualPeriod * (f / 32)), dim3(256), 0, st, evb, eve, ga,
+                            (const float *)xin, ua);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                hipLaunchKernelGGL(k_combine_h, dim3(f / 32), dim3(64), 0, st, (const float *)ga.part, (const float *)U,
+                                   B, f, c.bias, c.mode, c.theta, D.act, c.use_union, G, lcnt, lidx, hh, hl);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            } else {
+                // class-split gate in the fixed order, lists per block of 16 rows
+                GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
+                SFFN_LAUNCH((k_gate_pipe<BT>), dim3(f / kGateClsRows, 4), dim3(256), 0, st, evb, eve, ga,
+                            (const float *)xin);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                hipLaunchKernelGGL(k_gate_combine, dim3(f / 64), dim3(64), 0, st, (const float *)ga.part, B, f, c.bias,
+                                   c.mode, c.theta, G, lcnt, lidx);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
             const int nblk = (f + R - 1) / R;
             if (c.idx_out || c.count_out) {
                 const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
@@ -1863,22 +2147,22 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
             int *path = fixed ? nullptr : (int *)(sc + S.path);
             float *partial = (float *)(sc + S.partial);
             const float *resid = D.residual ? c.x : nullptr;
-            const int KS = f / 32, T = d / 16;
-            // about 1800 waves in flight for the down tiles: split d_ff so that (d/16) x splits fills the chip
-            const int ns0 = std::max(1, std::min(std::min(KS / 4, kMaxDownSplits), (1792 + T - 1) / T));
+            const int KS = f / 32, T = d / (16 * kDownCols);
+            // about 800 waves for the down tiles: split d_ff so that (d / 64) x splits fills the chip
+            const int ns0 = std::max(1, std::min(std::min(KS / 4, kMaxDownSplits), (800 + T - 1) / T));
             const int per = ((KS + ns0 - 1) / ns0 + 3) / 4 * 4;
             const int ns = (KS + per - 1) / per;
             if (fixed != kPathGather) {
                 // (1) MFMA tiles: up on every W_up block with a selected neuron, down on all of W_down
-                uint16_t *xh = (uint16_t *)(sc + S.xsplit), *xl = xh + (size_t)16 * d;
-                uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
-                hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xh, xl,
-                                   (const int *)lcnt, nblk, f, thr, path);
-                if ((e = hipGetLastError()) != hipSuccess) return e;
-                UpTiledArgs ua{L.wut, xh, xl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh, hl,
-                               path, kPathTiled};
-                hipLaunchKernelGGL(k_up_tiled, dim3(f / 16), dim3(64), 0, st, ua);
-                if ((e = hipGetLastError()) != hipSuccess) return e;
+                if (!gu_fused) {
+                    hipLaunchKernelGGL(k_split_x, dim3((2 * d + 255) / 256), dim3(256), 0, st, xin, B, d, xsh, xsl,
+                                       (const int *)lcnt, nblk, f, thr, path);
+                    if ((e = hipGetLastError()) != hipSuccess) return e;
+                    UpTiledArgs ua{L.wut, xsh, xsl, G, lcnt, lidx, d, f, B, c.mode, D.act, c.use_union, c.theta, hh,
+                                   hl, path, kPathTiled};
+                    hipLaunchKernelGGL(k_up_tiled, dim3(f / (16 * kUpBlocks)), dim3(256), 0, st, ua);
+                    if ((e = hipGetLastError()) != hipSuccess) return e;
+                }
                 DownTiledArgs da{L.wdtl, hh, hl, d, f, per, partial, path, kPathTiled};
                 hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
