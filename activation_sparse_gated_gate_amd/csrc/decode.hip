@@ -1208,6 +1208,7 @@ struct GateClsArgs {
 // (8 KB, shared) into stage k % 2, one slice ahead of the FMAs, without holding
 // registers for them.
 constexpr int kGateStages = 2;
+constexpr int kGateXAhead = 2;   // tokens of x read ahead of the FMAs
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left at their no-wait maxima)
@@ -1291,13 +1292,28 @@ __device__ __forceinline__ void gate_pipe_tile(const GateClsArgs &a, const float
             uint4 wv[RPW];
 #pragma unroll
             for (int q = 0; q < RPW; ++q) wv[q] = wsm[st][w][4 * q + r][i];
+            // x of token t + kGateXAhead is read while token t computes (a rotating
+            // register set per token in flight; the scheduling barriers keep the
+            // compiler from pulling the reads back next to their use)
+            constexpr int XA = kGateXAhead;
+            f32x4_t xq[XA + 1][2];
+#pragma unroll
+            for (int t = 0; t < XA; ++t) {
+                xq[t][0] = *(const f32x4_t *)&xs[st][t][0][i][0];
+                xq[t][1] = *(const f32x4_t *)&xs[st][t][1][i][0];
+            }
 #pragma unroll
             for (int t = 0; t < BT; ++t) {
-                const float4 x0 = *(const float4 *)&xs[st][t][0][i][0];
-                const float4 x1 = *(const float4 *)&xs[st][t][1][i][0];
-                const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                if (t + XA < BT) {
+                    xq[(t + XA) % (XA + 1)][0] = *(const f32x4_t *)&xs[st][t + XA][0][i][0];
+                    xq[(t + XA) % (XA + 1)][1] = *(const f32x4_t *)&xs[st][t + XA][1][i][0];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const f32x4_t x0 = xq[t % (XA + 1)][0], x1 = xq[t % (XA + 1)][1];
+                const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
                 for (int q = 0; q < RPW; ++q) acc[q][t] = chunk_dot<SFFN_W_BF16>(wv[q], 0.0f, xv, acc[q][t]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __builtin_amdgcn_s_barrier();   // stage st is refilled by the next iteration's issue
@@ -1347,37 +1363,45 @@ struct UpUArgs {
     float *U;                        // [B][f]
 };
 
-// u for the blocks 2 ui, 2 ui + 1 of 16 neurons: the four waves split d_model in
-// quarters, each streams its activation steps once for both tiles, and the
-// partial tiles are added in LDS in wave order
+// u for the blocks NB ui .. NB ui + NB - 1 of 16 neurons: the four waves split
+// d_model in quarters, each streams its activation steps once for all NB tiles
+// (U steps in flight), and the partial tiles are added in LDS in wave order
+template <int NB, int U>
 __device__ __forceinline__ void up_u_tiles(const UpUArgs &a, int ui, uint8_t *smem)
 {
-    constexpr int NB = 2;
     f32x4_t(&part)[4][NB][64] = *reinterpret_cast<f32x4_t(*)[4][NB][64]>(smem);
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int t0 = ui * NB, KS = a.d / 32;
     const int k0 = (KS * w) / 4, k1 = (KS * (w + 1)) / 4;
-    const bool live[NB] = {true, true};
+    bool live[NB];
     const uint16_t *wp[NB];
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+        live[b] = true;
         wp[b] = a.wut + (size_t)(t0 + b) * KS * 512 + lane * 8;
         acc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (int k = k0; k < k1; k += 4) mfma_group<4, NB>(wp, live, a.xh + lane * 8, a.xl + lane * 8, k, k1, acc);
+    for (int k = k0; k < k1; k += U) mfma_group<U, NB>(wp, live, a.xh + lane * 8, a.xl + lane * 8, k, k1, acc);
 #pragma unroll
     for (int b = 0; b < NB; ++b) part[w][b][lane] = acc[b];
     __syncthreads();
-    if (w >= NB) return;
-    const f32x4_t s4 = ((part[0][w][lane] + part[1][w][lane]) + part[2][w][lane]) + part[3][w][lane];
     // C[neuron 4q + e][token n]
     const int n = lane & 15, q = lane >> 4;
-    if (n < a.B)
-        *(float4 *)(a.U + (size_t)n * a.f + (t0 + w) * 16 + 4 * q) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+    for (int b = w; b < NB; b += 4) {
+        const f32x4_t s4 = ((part[0][b][lane] + part[1][b][lane]) + part[2][b][lane]) + part[3][b][lane];
+        if (n < a.B)
+            *(float4 *)(a.U + (size_t)n * a.f + (t0 + b) * 16 + 4 * q) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+    }
 }
 
-constexpr int kDualPeriod = 3;   // per period: two gate workgroups, then one up workgroup
+// up blocks of 16 neurons per up workgroup and MFMA k-steps in flight per wave;
+// a period of the grid is kDualNB gate workgroups then one up workgroup (there
+// are f / 16 of the first and f / (16 kDualNB) of the second)
+constexpr int kDualNB = 2, kDualU = 4;
+constexpr int kDualPeriod = kDualNB + 1;
+
+static_assert(4 * kDualNB * 64 * 16 <= kGateSmem, "the up role's partial tiles fit the gate's LDS");
 
 template <int BT>
 __global__ __launch_bounds__(256) void k_gate_up_dual(const GateClsArgs ga, const float *__restrict__ x,
@@ -1385,11 +1409,11 @@ __global__ __launch_bounds__(256) void k_gate_up_dual(const GateClsArgs ga, cons
 {
     __shared__ __align__(16) uint8_t smem[kGateSmem];
     const int per = blockIdx.x / kDualPeriod, ph = blockIdx.x % kDualPeriod;
-    if (ph < 2) {
-        const int gi = 2 * per + ph;   // gate workgroups: f / 16 = 4 classes x f / 64 tiles
+    if (ph < kDualNB) {
+        const int gi = kDualNB * per + ph;   // gate workgroups: 4 classes x f / 64 tiles
         gate_pipe_tile<BT>(ga, x, gi >> 2, gi & 3, smem);
     } else {
-        up_u_tiles(ua, per, smem);     // f / 32 up workgroups
+        up_u_tiles<kDualNB, kDualU>(ua, per, smem);
     }
 }
 
@@ -2112,7 +2136,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 // class-split gate and MFMA u side by side, then g', selection, lists and h
                 GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
                 UpUArgs ua{L.wut, xsh, xsl, d, f, B, U};
-                SFFN_LAUNCH((k_gate_up_dual<BT>), dim3(kDualPeriod * (f / 32)), dim3(256), 0, st, evb, eve, ga,
+                SFFN_LAUNCH((k_gate_up_dual<BT>), dim3(kDualPeriod * (f / (16 * kDualNB))), dim3(256), 0, st, evb, eve, ga,
                             (const float *)xin, ua);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 hipLaunchKernelGGL(k_combine_h, dim3(f / 32), dim3(64), 0, st, (const float *)ga.part, (const float *)U,
