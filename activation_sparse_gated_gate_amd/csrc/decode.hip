@@ -1161,20 +1161,38 @@ __global__ __launch_bounds__(64) void k_down_tiled(const DownTiledArgs a)
             make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
 }
 
-__device__ __forceinline__ void down_sum_elem(const float *__restrict__ partial, int ns, int d, int i,
-                                              const float *__restrict__ resid, float *__restrict__ out)
+// four consecutive outputs (i4 = index of the group): the split partials added
+// in split order, then the residual.  All loads of a batch of 16 splits are
+// issued before the adds (a split past ns reloads the last one, unused).
+__device__ __forceinline__ void down_sum4(const float *__restrict__ partial, int ns, int d, int i4,
+                                          const float *__restrict__ resid, float *__restrict__ out)
 {
-    const int n = i / d, c = i - n * d;
-    float y = 0.0f;
-    for (int p = 0; p < ns; ++p) y += partial[((size_t)p * 16 + n) * d + c];
-    out[i] = resid ? y + resid[i] : y;
+    const size_t stride = (size_t)16 * d;
+    const float *src = partial + 4 * (size_t)i4;
+    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < ns; p0 += 16) {
+        f32x4_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = *(const f32x4_t *)(src + (size_t)min(p0 + u, ns - 1) * stride);
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (p0 + u < ns)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] += v[u][e];
+    }
+    if (resid) {
+        const float4 r = *(const float4 *)(resid + 4 * (size_t)i4);
+        y[0] += r.x; y[1] += r.y; y[2] += r.z; y[3] += r.w;
+    }
+    *(float4 *)(out + 4 * (size_t)i4) = make_float4(y[0], y[1], y[2], y[3]);
 }
 
+// partial is [splits][16][d] (16 token slots); out [B][d]
 __global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ partial, int ns, int B, int d,
                                                   const float *__restrict__ resid, float *__restrict__ out)
 {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < B * d) down_sum_elem(partial, ns, d, i, resid, out);
+    const int i4 = blockIdx.x * 256 + threadIdx.x;
+    if (i4 < B * d / 4) down_sum4(partial, ns, d, i4, resid, out);
 }
 
 
@@ -1432,6 +1450,14 @@ __global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part
     const int j = s * 32 + 8 * g;   // first of the lane's 8 neurons
     float gp[8];
     uint32_t on = 0;
+    // u first, so that its loads share the partials' round trip (token slots >= B
+    // read token B - 1's, unused)
+    float u[8];
+    {
+        const size_t ou = (size_t)min(n, B - 1) * f + j;
+        const float4 u0 = *(const float4 *)(U + ou), u1 = *(const float4 *)(U + ou + 4);
+        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+    }
     if (n < B) {
         const size_t cs = (size_t)B * f, o = (size_t)n * f + j;
         float p[4][8];
@@ -1464,11 +1490,6 @@ __global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part
     }
     if (lane < 2) list_cnt[2 * s + lane] = __popc((mask >> (16 * lane)) & 0xFFFFu);
     uint16_t hb[8], lb[8];
-    float u[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    if (n < B) {
-        const float4 u0 = *(const float4 *)(U + (size_t)n * f + j), u1 = *(const float4 *)(U + (size_t)n * f + j + 4);
-        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float h = 0.0f;
@@ -1539,32 +1560,38 @@ __global__ __launch_bounds__(64) void k_rmsnorm_split(const float *__restrict__ 
         const float ss = wave_tree_sum(acc);
         r = 1.0f / sqrtf(ss / (float)d + eps);
     }
-    // pieces of 8 values: step s, k-group g -> lane slot (g << 4) | t
-    for (int pc = lane; pc < d / 8; pc += 64) {
-        const int s = pc >> 2, g = pc & 3;
-        uint16_t h[8], lo[8];
-        float v[8];
-        if (t < B) {
-            const float4 v0 = *(const float4 *)(xt + 8 * pc), v1 = *(const float4 *)(xt + 8 * pc + 4);
-            v[0] = v0.x * r; v[1] = v0.y * r; v[2] = v0.z * r; v[3] = v0.w * r;
-            v[4] = v1.x * r; v[5] = v1.y * r; v[6] = v1.z * r; v[7] = v1.w * r;
-            *(float4 *)(xhat + (size_t)t * d + 8 * pc) = make_float4(v[0], v[1], v[2], v[3]);
-            *(float4 *)(xhat + (size_t)t * d + 8 * pc + 4) = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
+    // x_hat and its split, 16 float4 chunks per lane in flight: chunk c holds
+    // values 4c .. 4c + 3, half (c & 1) of the 8-value piece c / 2 = 4 s + g,
+    // which sits in lane slot (g << 4) | t of step s
+    const int nch = d / 4;
+    for (int k0 = 0; k0 * 64 < nch; k0 += 16) {
+        f32x4_t v[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        for (int u = 0; u < 16; ++u) {
+            const int c = min((k0 + u) * 64 + lane, nch - 1);
+            v[u] = t < B ? *(const f32x4_t *)(xt + 4 * c) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            h[e] = bf16_rne_bits(v[e]);
-            lo[e] = bf16_rne_bits(v[e] - bf16_lo(h[e]));
+        for (int u = 0; u < 16; ++u) {
+            const int c = (k0 + u) * 64 + lane;
+            if (c < nch) {
+                const f32x4_t y = v[u] * r;
+                if (t < B) *(f32x4_t *)(xhat + (size_t)t * d + 4 * c) = y;
+                const int pc = c >> 1, sstep = pc >> 2, g = pc & 3;
+                uint16_t h[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = bf16_rne_bits(y[e]);
+                    lo[e] = bf16_rne_bits(y[e] - bf16_lo(h[e]));
+                }
+                const size_t o = ((size_t)sstep * 64 + (g << 4) + t) * 8 + 4 * (c & 1);
+                uint2 ph, pl;
+                __builtin_memcpy(&ph, h, 8);
+                __builtin_memcpy(&pl, lo, 8);
+                *(uint2 *)(xh + o) = ph;
+                *(uint2 *)(xl + o) = pl;
+            }
         }
-        const size_t o = ((size_t)s * 64 + (g << 4) + t) * 8;
-        uint4 ph, pl;
-        __builtin_memcpy(&ph, h, 16);
-        __builtin_memcpy(&pl, lo, 16);
-        *(uint4 *)(xh + o) = ph;
-        *(uint4 *)(xl + o) = pl;
     }
 }
 
@@ -1933,8 +1960,8 @@ __global__ __launch_bounds__(1024) void k_batched_out(const float *__restrict__ 
                                                       const int *__restrict__ path)
 {
     if (*path == kPathTiled) {
-        const int i = blockIdx.x * 16 + (int)threadIdx.x;
-        if (threadIdx.x < 16 && i < B * d) down_sum_elem(partial, ns, d, i, resid, out);
+        const int i4 = blockIdx.x * 4 + (int)threadIdx.x;
+        if (threadIdx.x < 4 && i4 < B * d / 4) down_sum4(partial, ns, d, i4, resid, out);
         return;
     }
     reduce16_block(partial, P, B * d, resid, out);
@@ -2191,7 +2218,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 hipLaunchKernelGGL(k_down_tiled, dim3(T, ns), dim3(64), 0, st, da);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 if (fixed == kPathTiled) {
-                    hipLaunchKernelGGL(k_down_sum, dim3((B * d + 255) / 256), dim3(256), 0, st,
+                    hipLaunchKernelGGL(k_down_sum, dim3((B * d / 4 + 255) / 256), dim3(256), 0, st,
                                        (const float *)partial, ns, B, d, resid, c.out);
                     return hipGetLastError();
                 }
