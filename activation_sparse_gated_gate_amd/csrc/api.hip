@@ -73,7 +73,8 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
     if (D.layouts & SFFN_LAYOUT_DECODE) {
         S.xhat = take(B * d * 4);
         S.G = take(B * f * 4);
-        S.U = take(B * f * 4);
+        // u; the batched tile path keeps one partial per half of d_model
+        S.U = take((D.layouts & SFFN_LAYOUT_BATCH ? 2 : 1) * B * f * 4);
         S.keys = take(B * f * 8);
         S.bits = take(B * (f / 32) * 4);
         S.list_cnt = take((size_t)f * 4);

@@ -1372,7 +1372,8 @@ __global__ __launch_bounds__(256) void k_gate_pipe(const GateClsArgs a, const fl
 // W_up stream), so every CU holds both kinds and the gate's arithmetic hides
 // under the up projection's weight traffic.  Both roles fit one resource
 // budget (the gate's LDS, the larger register count).  u is written in fp32;
-// k_combine_h adds the gate classes and forms the selection, the lists and h.
+// k_combine_h adds the gate classes and the two halves of u and forms the
+// selection, the lists and h.
 // ---------------------------------------------------------------------------
 struct UpUArgs {
     const uint16_t *wut;             // W_up tiles [f/16][d/32][64][8]
@@ -1381,16 +1382,18 @@ struct UpUArgs {
     float *U;                        // [B][f]
 };
 
-// u for the blocks NB ui .. NB ui + NB - 1 of 16 neurons: the four waves split
-// d_model in quarters, each streams its activation steps once for all NB tiles
-// (U steps in flight), and the partial tiles are added in LDS in wave order
+// u over one half of d_model (hf = 0, 1) for the blocks NB ui .. NB ui + NB - 1
+// of 16 neurons: the four waves split the half in quarters, each streams its
+// activation steps once for all NB tiles (U steps in flight), and the partial
+// tiles are added in LDS in wave order into U + hf B f
 template <int NB, int U>
-__device__ __forceinline__ void up_u_tiles(const UpUArgs &a, int ui, uint8_t *smem)
+__device__ __forceinline__ void up_u_tiles(const UpUArgs &a, int ui, int hf, uint8_t *smem)
 {
     f32x4_t(&part)[4][NB][64] = *reinterpret_cast<f32x4_t(*)[4][NB][64]>(smem);
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int t0 = ui * NB, KS = a.d / 32;
-    const int k0 = (KS * w) / 4, k1 = (KS * (w + 1)) / 4;
+    const int h0 = (KS * hf) / 2, h1 = (KS * (hf + 1)) / 2;
+    const int k0 = h0 + ((h1 - h0) * w) / 4, k1 = h0 + ((h1 - h0) * (w + 1)) / 4;
     bool live[NB];
     const uint16_t *wp[NB];
     f32x4_t acc[NB];
@@ -1406,32 +1409,39 @@ __device__ __forceinline__ void up_u_tiles(const UpUArgs &a, int ui, uint8_t *sm
     __syncthreads();
     // C[neuron 4q + e][token n]
     const int n = lane & 15, q = lane >> 4;
+    float *Uh = a.U + (size_t)hf * a.B * a.f;
     for (int b = w; b < NB; b += 4) {
         const f32x4_t s4 = ((part[0][b][lane] + part[1][b][lane]) + part[2][b][lane]) + part[3][b][lane];
         if (n < a.B)
-            *(float4 *)(a.U + (size_t)n * a.f + (t0 + b) * 16 + 4 * q) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+            *(float4 *)(Uh + (size_t)n * a.f + (t0 + b) * 16 + 4 * q) = make_float4(s4[0], s4[1], s4[2], s4[3]);
     }
 }
 
-// up blocks of 16 neurons per up workgroup and MFMA k-steps in flight per wave;
-// a period of the grid is kDualNB gate workgroups then one up workgroup (there
-// are f / 16 of the first and f / (16 kDualNB) of the second)
+// up blocks of 16 neurons per up item and MFMA k-steps in flight per wave.
+// Work items: f / 16 gate workgroups (4 classes x f / 64 tiles) and f / 16 up
+// items (f / (16 kDualNB) block groups x 2 halves of d_model).  The grid
+// interleaves two gate items with one first-half up item, then runs the
+// second-half up items: the shorter up items come last, so the launch drains
+// quickly once the gate items are done.
 constexpr int kDualNB = 2, kDualU = 4;
-constexpr int kDualPeriod = kDualNB + 1;
-
-static_assert(4 * kDualNB * 64 * 16 <= kGateSmem, "the up role's partial tiles fit the gate's LDS");
 
 template <int BT>
 __global__ __launch_bounds__(256) void k_gate_up_dual(const GateClsArgs ga, const float *__restrict__ x,
                                                       const UpUArgs ua)
 {
     __shared__ __align__(16) uint8_t smem[kGateSmem];
-    const int per = blockIdx.x / kDualPeriod, ph = blockIdx.x % kDualPeriod;
-    if (ph < kDualNB) {
-        const int gi = kDualNB * per + ph;   // gate workgroups: 4 classes x f / 64 tiles
-        gate_pipe_tile<BT>(ga, x, gi >> 2, gi & 3, smem);
+    const int ngu = ua.f / (16 * kDualNB);   // up block groups
+    const int b = blockIdx.x;
+    if (b < 3 * ngu) {
+        const int per = b / 3, ph = b % 3;
+        if (ph < 2) {
+            const int gi = 2 * per + ph;
+            gate_pipe_tile<BT>(ga, x, gi >> 2, gi & 3, smem);
+        } else {
+            up_u_tiles<kDualNB, kDualU>(ua, per, 0, smem);
+        }
     } else {
-        up_u_tiles<kDualNB, kDualU>(ua, per, smem);
+        up_u_tiles<kDualNB, kDualU>(ua, b - 3 * ngu, 1, smem);
     }
 }
 
@@ -1454,9 +1464,15 @@ __global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part
     // read token B - 1's, unused)
     float u[8];
     {
-        const size_t ou = (size_t)min(n, B - 1) * f + j;
-        const float4 u0 = *(const float4 *)(U + ou), u1 = *(const float4 *)(U + ou + 4);
-        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+        // u = (first half of d_model) + (second half)
+        const size_t ou = (size_t)min(n, B - 1) * f + j, hs = (size_t)B * f;
+        const f32x4_t a0 = *(const f32x4_t *)(U + ou), a1 = *(const f32x4_t *)(U + ou + 4);
+        const f32x4_t b0 = *(const f32x4_t *)(U + hs + ou), b1 = *(const f32x4_t *)(U + hs + ou + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] = a0[e] + b0[e];
+            u[4 + e] = a1[e] + b1[e];
+        }
     }
     if (n < B) {
         const size_t cs = (size_t)B * f, o = (size_t)n * f + j;
@@ -2163,7 +2179,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                 // class-split gate and MFMA u side by side, then g', selection, lists and h
                 GateClsArgs ga{L.wgt, d, f, B, (float *)(sc + S.gpart)};
                 UpUArgs ua{L.wut, xsh, xsl, d, f, B, U};
-                SFFN_LAUNCH((k_gate_up_dual<BT>), dim3(kDualPeriod * (f / (16 * kDualNB))), dim3(256), 0, st, evb, eve, ga,
+                SFFN_LAUNCH((k_gate_up_dual<BT>), dim3(2 * (f / 16)), dim3(256), 0, st, evb, eve, ga,
                             (const float *)xin, ua);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 hipLaunchKernelGGL(k_combine_h, dim3(f / 32), dim3(64), 0, st, (const float *)ga.part, (const float *)U,
