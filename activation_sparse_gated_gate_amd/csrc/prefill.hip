@@ -565,6 +565,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
 // that one MFMA operand read touches over all banks.
 // ---------------------------------------------------------------------------
 constexpr int BBM = 256, BBN = 256, BBK = 32, BSTAGES = 4;
+constexpr int kGemmWaves = 8;   // waves per 256 x 256 workgroup
 
 __device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base)
 {
@@ -580,9 +581,16 @@ __device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base
 
 constexpr int gemm_waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
+// NW waves per workgroup: 4 (2 x 2 waves of 128 x 128) or 8 (2 x 4 waves of
+// 128 x 64, two waves per SIMD so that one wave's products run while the other
+// waits at a barrier or an LDS read)
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    constexpr int WNN = NW / 2;            // waves along n
+    constexpr int JB = 8 / WNN;            // 32-column blocks per wave (4 or 2)
+    constexpr int QA = BBM / NW / 16;      // 16-row copies per wave and operand (4 or 2)
     __shared__ __align__(1024) uint16_t As[BSTAGES][BBM * BBK];
     __shared__ __align__(1024) uint16_t Bs[BSTAGES][BBN * BBK];
     __shared__ int rowsrc[BBM];
@@ -593,10 +601,10 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
     const int nt = a.N / BBN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WNN, wn = w % WNN;
     const int KT = a.K / BBK;
-    // per wave and stage: 4 copies of A rows and 4 of B rows
-    constexpr int CPS = 8;
+    // per wave and stage: QA copies of A rows and QA of B rows
+    constexpr int CPS = 2 * QA;
 
     // Workgroups are dealt to the 8 XCDs round-robin; renumbering them so that
     // each XCD walks a contiguous run of tiles (M-tiles fastest) keeps the
@@ -607,37 +615,38 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
         const int tm = tile % mt, tn = tile / mt;
         const int m0 = tm * BBM, n0 = tn * BBN;
         __syncthreads();
-        {
+        if (tid < BBM) {
             // rows past M read a valid row; their results are not written
             const int m = min(m0 + tid, M - 1);
             rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
         }
         __syncthreads();
-        // this wave copies rows 64 w + 16 q + (lane >> 2), q = 0..3, of both
+        // this wave copies rows 16 QA w + 16 q + (lane >> 2), q < QA, of both
         // operands; lane position p = lane & 3 holds logical chunk p ^ ((r >> 2) & 3)
-        uint32_t aoff[4];   // element offsets of the gathered A rows (< 2^31 for every supported shape)
+        constexpr int RW = 16 * QA;   // rows copied per wave
+        uint32_t aoff[QA];   // element offsets of the gathered A rows (< 2^31 for every supported shape)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = 64 * w + 16 * q + (lane >> 2);
+        for (int q = 0; q < QA; ++q) {
+            const int r = RW * w + 16 * q + (lane >> 2);
             aoff[q] = (uint32_t)rowsrc[r] * (uint32_t)a.K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
         }
         // (r >> 2) & 3 does not depend on q (16 q only changes higher bits)
-        const int rb0 = 64 * w + (lane >> 2);
+        const int rb0 = RW * w + (lane >> 2);
         const uint16_t *bsrc = a.B + (size_t)(n0 + rb0) * a.K + (((lane & 3) ^ ((rb0 >> 2) & 3)) * 8);
         auto issue = [&](int kt) {
             const int st = kt % BSTAGES;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(64 * w + 16 * q) * BBK]);
-                lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(64 * w + 16 * q) * BBK]);
+            for (int q = 0; q < QA; ++q) {
+                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(RW * w + 16 * q) * BBK]);
+                lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(RW * w + 16 * q) * BBK]);
             }
         };
 
-        f32x16 acc[4][4];
+        f32x16 acc[4][JB];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JB; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -656,7 +665,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
             // every operand fragment of the slice is read from LDS before the first
             // product, so only the first two reads' latency is exposed; the refill of
             // the stage finished two slices ago goes out behind them
-            bf16x8 fa[BBK / 16][4], fb[BBK / 16][4];
+            bf16x8 fa[BBK / 16][4], fb[BBK / 16][JB];
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks) {
                 const int kc = 2 * ks + (lane >> 5);
@@ -664,8 +673,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 128 + i * 32 + (lane & 31);
                     fa[ks][i] = *(const bf16x8 *)&as[r * BBK + ((kc ^ ((r >> 2) & 3)) * 8)];
-                    const int c = wn * 128 + i * 32 + (lane & 31);
-                    fb[ks][i] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
+                }
+#pragma unroll
+                for (int j = 0; j < JB; ++j) {
+                    const int c = wn * 32 * JB + j * 32 + (lane & 31);
+                    fb[ks][j] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
                 }
             }
             if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
@@ -675,7 +687,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < JB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
         }
         __builtin_amdgcn_s_barrier();   // the next tile's first copies reuse the stages
@@ -683,8 +695,8 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
         // epilogue: lane holds col = lane & 31 and rows 8 g + 4 (lane >> 5) + e of a 32 x 32 block
         const int ccol = lane & 31;
         if constexpr (EPI == EPI_GATE_UP) {
-            // wave columns: [gate | up] of neurons nb .. nb + 31, then of nb + 32 .. nb + 63
-            const int nb = (n0 + wn * 128) / 2;
+            // wave columns: [gate | up] of neurons nb .. nb + 31 (then of nb + 32 .. nb + 63)
+            const int nb = (n0 + wn * 32 * JB) / 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -695,7 +707,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
                         const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
                         if (m < M) {
 #pragma unroll
-                            for (int hb = 0; hb < 2; ++hb) {
+                            for (int hb = 0; hb < JB / 2; ++hb) {
                                 const float gv = acc[i][2 * hb][4 * g + e], uv = acc[i][2 * hb + 1][4 * g + e];
                                 const float h = gv / (1.0f + expf(-gv)) * uv;
                                 a.H[(size_t)m * a.ldo + nb + 32 * hb + ccol] = f32_to_bf16_rne(h);
@@ -715,8 +727,8 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs a)
                         if (m < M) {
                             const int tok = kept_row(a, m);
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int n = n0 + wn * 128 + j * 32 + ccol;
+                            for (int j = 0; j < JB; ++j) {
+                                const int n = n0 + wn * 32 * JB + j * 32 + ccol;
                                 const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
                                 a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
                             }
@@ -837,7 +849,8 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     L.timer->take(&evb, &eve);
     // one workgroup per compute unit (128 KB of LDS each), looping over tiles
     const int G = gemm_grid(c.stream);
-    SFFN_LAUNCH(k_gemm_big<EPI_GATE_UP>, dim3(std::min(tiles1, G)), dim3(256), 0, c.stream, evb, eve, g);
+    SFFN_LAUNCH((k_gemm_big<EPI_GATE_UP, kGemmWaves>), dim3(std::min(tiles1, G)), dim3(kGemmWaves * 64), 0, c.stream,
+                evb, eve, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmArgs g2{};
     g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
@@ -848,7 +861,8 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     const int tiles2 = mt_big * (d / BBN);
     g2.gate = G / 2;   // measured: 220 big tiles on 256 units beat 880 small ones; 100 do not
     g2.gate_big = 1;
-    hipLaunchKernelGGL(k_gemm_big<EPI_DOWN>, dim3(std::min(tiles2, G)), dim3(256), 0, c.stream, g2);
+    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves>), dim3(std::min(tiles2, G)), dim3(kGemmWaves * 64), 0,
+                       c.stream, g2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     g2.gate_big = 0;
     const int tiles2s = mt_max * (d / GBN);
