@@ -549,54 +549,82 @@ struct GatherArgs {
     int share_bits;  // top-k: 1 = equal shares of the union's ascending list (from the bit words),
                      // 2 = workgroup q owns the neurons [q R, q R + R), R = ceil(f / P) <= 64
     int merge_gap;   // share 2: also read the unselected neurons of gaps of at most this many rows
+    int P;           // workgroups (partitions of the share, partial sums); 0: kGatherWGs
 };
 
 // Top-k share by neuron range: wave 0 of workgroup q takes the neurons
-// [q R, q R + R) (R <= 64, one per lane), loads each one's bit words, g' and u
-// for every token in one round trip, forms h = act(g') u for the tokens whose
-// set holds the neuron (all tokens with the union rule) and compacts the
-// neurons of the union into jl / hs in ascending order (ballot + mbcnt).
-// Returns the number of neurons (all threads).
+// [q R, q R + R) in chunks of 64 (one per lane), loads each one's bit words, g'
+// and u for every token (the loads of all chunks are issued before the first
+// use), forms h = act(g') u for the tokens whose set holds the neuron (all
+// tokens with the union rule) and compacts the neurons of the union into
+// jl / hs in ascending order (ballot + mbcnt).  Returns the number of neurons
+// (all threads).
 template <int BT>
 __device__ int share_of_range(const GatherArgs &a, int R, int *jl, float *hs, int *s_ns)
 {
+    constexpr int MAXC = BT == 1 ? 8 : 1;   // chunks of 64 neurons: R <= 512 at batch 1, else <= 64
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
-        const int j = blockIdx.x * R + lane;
-        const bool in = lane < R && j < a.f;
-        uint32_t tb = 0;       // bit t: neuron j is in token t's set
-        float h[BT];
+        uint32_t wb[MAXC][BT];
+        float gv[MAXC][BT], uv[MAXC][BT];
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            h[t] = 0.0f;
-            if (in && t < a.B) {
-                const uint32_t w = a.bits[(size_t)t * a.nw32 + (j >> 5)];
-                const float gp = a.G[(size_t)t * a.f + j], u = a.U[(size_t)t * a.f + j];
-                if ((w >> (j & 31)) & 1u) tb |= 1u << t;
-                h[t] = act_f32(a.act, gp) * u;
+        for (int c = 0; c < MAXC; ++c) {
+            const int j = blockIdx.x * R + 64 * c + lane;
+            const bool in = 64 * c + lane < R && j < a.f;
+            const int jc = in ? j : 0;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                const int tc = min(t, a.B - 1);
+                wb[c][t] = 0u;
+                gv[c][t] = 0.0f;
+                uv[c][t] = 0.0f;
+                if (64 * c < R) {
+                    wb[c][t] = a.bits[(size_t)tc * a.nw32 + (jc >> 5)];
+                    gv[c][t] = a.G[(size_t)tc * a.f + jc];
+                    uv[c][t] = a.U[(size_t)tc * a.f + jc];
+                }
             }
         }
-        const bool on = tb != 0;
-        const uint64_t sel = __ballot(on);
-        // run merging: an unselected neuron whose gap between the selected
-        // neighbours on either side is at most merge_gap rows is read as well
-        bool rd = on;
-        if (a.merge_gap > 0 && !on && in) {
-            const uint64_t below = sel & ((1ull << lane) - 1ull), above = lane < 63 ? sel >> (lane + 1) : 0ull;
-            if (below && above) {
-                const int prev = 63 - __builtin_clzll(below), next = lane + 1 + __builtin_ctzll(above);
-                rd = next - prev - 1 <= a.merge_gap;
-            }
-        }
-        const uint64_t m = __ballot(rd);
-        if (rd) {
-            const int pos = mbcnt64(m);
-            jl[pos] = j;
+        int base = 0;
 #pragma unroll
-            for (int t = 0; t < BT; ++t)
-                if (t < a.B) hs[pos * BT + t] = (on && (a.use_union || ((tb >> t) & 1u))) ? h[t] : 0.0f;
+        for (int c = 0; c < MAXC; ++c) {
+            if (64 * c >= R) break;
+            const int j = blockIdx.x * R + 64 * c + lane;
+            const bool in = 64 * c + lane < R && j < a.f;
+            uint32_t tb = 0;       // bit t: neuron j is in token t's set
+            float h[BT];
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                h[t] = 0.0f;
+                if (in && t < a.B) {
+                    if ((wb[c][t] >> (j & 31)) & 1u) tb |= 1u << t;
+                    h[t] = act_f32(a.act, gv[c][t]) * uv[c][t];
+                }
+            }
+            const bool on = tb != 0;
+            const uint64_t sel = __ballot(on);
+            // run merging: an unselected neuron whose gap between the selected
+            // neighbours on either side (within its chunk) is at most merge_gap
+            // rows is read as well
+            bool rd = on;
+            if (a.merge_gap > 0 && !on && in) {
+                const uint64_t below = sel & ((1ull << lane) - 1ull), above = lane < 63 ? sel >> (lane + 1) : 0ull;
+                if (below && above) {
+                    const int prev = 63 - __builtin_clzll(below), next = lane + 1 + __builtin_ctzll(above);
+                    rd = next - prev - 1 <= a.merge_gap;
+                }
+            }
+            const uint64_t m = __ballot(rd);
+            if (rd) {
+                const int pos = base + mbcnt64(m);
+                jl[pos] = j;
+#pragma unroll
+                for (int t = 0; t < BT; ++t)
+                    if (t < a.B) hs[pos * BT + t] = (on && (a.use_union || ((tb >> t) & 1u))) ? h[t] : 0.0f;
+            }
+            base += __popcll(m);
         }
-        if (lane == 0) *s_ns = __popcll(m);
+        if (lane == 0) *s_ns = base;
     }
     __syncthreads();
     return *s_ns;
@@ -2055,12 +2083,23 @@ static int gate_rows_per_block()
     return Cfg<WT, BT>::NW * Cfg<WT, BT>::RPW;
 }
 
+// Workgroups of the top-k gather (each owns a range of ceil(f / P) neurons,
+// at most 512 at batch 1 and 64 above).  Every one writes a partial y of B d
+// floats that the reduce reads back, but fewer partitions were measured slower
+// at batch 1 (2048 / 11008 int4, keep 17-50 %: 37.9-43.0 us per step at 128,
+// 39.7-54.7 at 64, 48.0-78.6 at 32, against about 36 at 256): a workgroup's
+// rows come in batches, one round trip each, so the partition count stays.
+static int topk_gather_wgs(int B, int f)
+{
+    return B <= 1 ? std::max(kGatherWGs, (f + 511) / 512) : std::max(kGatherWGs, (f + 63) / 64);
+}
+
 template <int WT, int BT>
 static hipError_t run_gather(const GatherArgs &a0, hipStream_t st)
 {
     using C = Cfg<WT, BT>;
     GatherArgs a = a0;
-    const int P = kGatherWGs;
+    const int P = a.P > 0 ? a.P : kGatherWGs;
     a.maxs = (a.f + P - 1) / P + 1;
     a.stage_x = a.mode != SFFN_MODE_TOPK;
     const size_t lds = (a.stage_x ? (size_t)BT * C::KMAX * 64 * C::E * 4 : 0) + (size_t)a.maxs * BT * 4 +
@@ -2325,7 +2364,8 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         // for, comes from the bit words in a launch of its own
         g.share_bits = 2;
         g.merge_gap = c.merge_gap;
-        g.R = (f + kGatherWGs - 1) / kGatherWGs;
+        g.P = topk_gather_wgs(B, f);
+        g.R = (f + g.P - 1) / g.P;
         g.idx_out = nullptr;
         g.count_out = nullptr;
         if (c.idx_out || c.count_out) {
@@ -2339,8 +2379,8 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     if ((e = run_gather<WT, BT>(g, st)) != hipSuccess) return e;
 
     const int BD = B * d;
-    hipLaunchKernelGGL(k_reduce16, dim3((BD + 15) / 16), dim3(1024), 0, st, (const float *)partial, kGatherWGs, BD,
-                       D.residual ? c.x : nullptr, c.out);
+    hipLaunchKernelGGL(k_reduce16, dim3((BD + 15) / 16), dim3(1024), 0, st, (const float *)partial,
+                       g.P > 0 ? g.P : kGatherWGs, BD, D.residual ? c.x : nullptr, c.out);
     return hipGetLastError();
 }
 
