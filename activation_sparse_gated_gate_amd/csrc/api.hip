@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <new>
 #include <stdio.h>
 #include <string.h>
@@ -133,6 +134,20 @@ static bool desc_ok(const sffn_layer_desc *D, sffn_status *why)
         }
     }
     return true;
+}
+
+// compute units of the current device, cached per device (256 when the query fails)
+int compute_units()
+{
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 hipError_t allow_full_dynamic_lds(const void *kernel, std::once_flag &once, hipError_t &err, int &limit)

@@ -808,18 +808,11 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     return hipGetLastError();
 }
 
-// compute units of the current device (cached per device), a multiple of 8 when possible
+// compute units of the current device, a multiple of 8 when possible
 static int gemm_grid(hipStream_t)
 {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n >= 8 ? n / 8 * 8 : n;
-    }
-    return cus[dev];
+    const int n = compute_units();
+    return n >= 8 ? n / 8 * 8 : n;
 }
 
 hipError_t launch_prefill_forward(const PrefillForwardCall &c)

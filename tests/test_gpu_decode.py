@@ -220,6 +220,25 @@ def test_batched_mfma_sparse_blocks(B):
     layer.close()
 
 
+@pytest.mark.parametrize("B", [9, 16])
+def test_batched_gate_up_launch_with_a_half_slice(B):
+    # d_model 1280 = 2.5 gate slices of 512: the last slice of the class-split gate
+    # is half empty (its x pieces and lanes past the row are skipped), with and
+    # without the RMSNorm prologue (which writes the class-major x), and every
+    # selection mode of the tile path (9..16 tokens)
+    sf = _sf()
+    d, f = 1280, 1024
+    w = synth._make_weights(synth.WT_BF16, d, f, synth.ACT_SILU, (1931, 1932, 1933))
+    x = synth.round_to_bf16(synth.normal_f32(1934 + B, (B, d)))
+    for rms in (False, True):
+        layer = make_layer(w, 16, rmsnorm=rms, residual=rms, layouts=sf.LAYOUT_DECODE | sf.LAYOUT_BATCH)
+        _check(layer, w, x, "all", 2e-3, union=True)
+        _check(layer, w, x, "thresh", 2e-3, theta=synth.gate_threshold_for_active_fraction(0.3), union=True)
+        _check(layer, w, x, "thresh", 2e-3, theta=synth.gate_threshold_for_active_fraction(0.3), union=False)
+        _check(layer, w, x, "exact", 2e-3, bias=synth.gate_offset_for_active_fraction(0.05), union=False)
+        layer.close()
+
+
 @pytest.mark.parametrize("B", [5, 8, 16])
 def test_batched_tile_and_gather_paths_match_the_oracle(B):
     # the device picks the tile or the gather path from the union size; both forced
