@@ -1226,6 +1226,147 @@ __global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ part
 
 
 // ---------------------------------------------------------------------------
+// int4 top-k at 5..16 tokens: the down projection on MFMA over all of W_down.
+// The tokens' union is most of d_ff at these batch sizes (about 3/4 of the
+// neurons at 8 tokens, keep 17 %), so the whole int4 W_down [d][f] is read once,
+// densely, with h = 0 outside each token's set, instead of gathering rows:
+//   k_form_h_i4     h = act(g') u on the selected (token, neuron) pairs (the
+//                   union rule as in the gather), as bf16 hi + lo in MFMA lane
+//                   order (16 token slots)
+//   k_down_i4_mfma  one wave per (4 blocks of 16 output columns, d_ff split):
+//                   per group of 128 neurons (one fp16 scale per output
+//                   column) the 4-bit weights, exact in bf16, times h hi and lo
+//                   on v_mfma_f32_16x16x32_bf16, then the group's sum times the
+//                   scale into the fp32 total; partial y per split
+//   k_down_sum      the splits in order, plus the residual
+// Inside a group the MFMA k order is permuted (k-step ks, lane k-group kg,
+// element e <-> neuron 32 kg + 8 ks + e) so that each lane's four k-steps of
+// W are one 16-byte load; h is stored in the same order.
+// ---------------------------------------------------------------------------
+struct FormHArgs {
+    const uint32_t *bits;   // [B][f/32] top-k sets
+    const float *G, *U;     // [B][f]
+    int B, f, nw32, act, use_union;
+    uint16_t *hh, *hl;      // [f/128][4 k-steps][64 lanes][8]
+};
+
+// one thread per (group, k-step, lane): 8 neurons 128 g + 32 kg + 8 ks .. + 8 of token t
+__global__ __launch_bounds__(256) void k_form_h_i4(const FormHArgs a)
+{
+    const int g = blockIdx.x, ks = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kg = lane >> 4, t = lane & 15;
+    const int j0 = 128 * g + 32 * kg + 8 * ks;
+    uint32_t uni = 0, own = 0;   // bits of the 8 neurons: union over the tokens, this token's
+    for (int t2 = 0; t2 < a.B; ++t2) {
+        const uint32_t w = (a.bits[(size_t)t2 * a.nw32 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
+        uni |= w;
+        if (t2 == t) own = w;
+    }
+    const int tc = min(t, a.B - 1);
+    const f32x4_t g0 = *(const f32x4_t *)(a.G + (size_t)tc * a.f + j0), g1 = *(const f32x4_t *)(a.G + (size_t)tc * a.f + j0 + 4);
+    const f32x4_t u0 = *(const f32x4_t *)(a.U + (size_t)tc * a.f + j0), u1 = *(const f32x4_t *)(a.U + (size_t)tc * a.f + j0 + 4);
+    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    const float uv[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+    uint16_t hb[8], lb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool on = t < a.B && ((uni >> e) & 1u) && (a.use_union || ((own >> e) & 1u));
+        const float h = on ? act_f32(a.act, gv[e]) * uv[e] : 0.0f;
+        hb[e] = bf16_rne_bits(h);
+        lb[e] = bf16_rne_bits(h - bf16_lo(hb[e]));
+    }
+    const size_t o = (((size_t)g * 4 + ks) * 64 + lane) * 8;
+    uint4 ph, pl;
+    __builtin_memcpy(&ph, hb, 16);
+    __builtin_memcpy(&pl, lb, 16);
+    *(uint4 *)(a.hh + o) = ph;
+    *(uint4 *)(a.hl + o) = pl;
+}
+
+struct DownI4Args {
+    const uint8_t *wd;        // W_down int4 [d][f] (element j of a row: nibble j % 2 of byte j / 2)
+    const uint16_t *sdt;      // fp16 scales [f/128][d]
+    const uint16_t *hh, *hl;  // h, as k_form_h_i4 writes it
+    int d, f, per;            // per: groups of 128 neurons per split
+    float *partial;           // [splits][16][d]
+};
+
+constexpr int kDownI4Cols = 4;     // blocks of 16 output columns per wave
+constexpr int kDownI4Waves = 1024;  // waves of the launch: d_ff splits so that (d / 64) x splits reach it
+constexpr int kDownI4Groups = 4;    // most groups of 128 neurons per split (all loaded at once)
+
+// the 4-bit values of one dword as 8 bf16 (exact: small integers)
+__device__ __forceinline__ bf16x8_t i4x8_to_bf16(uint32_t w)
+{
+    uint16_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (uint16_t)(__float_as_uint((float)nib(w, e)) >> 16);
+    bf16x8_t r;
+    __builtin_memcpy(&r, b, 16);
+    return r;
+}
+
+__global__ __launch_bounds__(64) void k_down_i4_mfma(const DownI4Args a)
+{
+    const int lane = threadIdx.x, n = lane & 15, q = lane >> 4;
+    const int col0 = blockIdx.x * 16 * kDownI4Cols, p = blockIdx.y;
+    const int ng = a.f / 128;
+    const int g0 = min(ng, p * a.per), cnt = min(ng, g0 + a.per) - g0;   // cnt <= kDownI4Groups
+    const size_t rowb = (size_t)a.f / 2;
+    // every load of the split first (one round trip): per group h (4 k-steps,
+    // hi and lo), W (one 16-byte piece per column block) and the scales of the
+    // lane's 4 output columns; groups past the split reload its last one (unused)
+    uint4 hv[kDownI4Groups][4][2], wv[kDownI4Groups][kDownI4Cols];
+    uint2 sv[kDownI4Groups][kDownI4Cols];
+#pragma unroll
+    for (int i = 0; i < kDownI4Groups; ++i) {
+        const int g = g0 + min(i, max(cnt - 1, 0));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const size_t o = (((size_t)g * 4 + ks) * 64 + lane) * 8;
+            hv[i][ks][0] = *(const uint4 *)(a.hh + o);
+            hv[i][ks][1] = *(const uint4 *)(a.hl + o);
+        }
+#pragma unroll
+        for (int c = 0; c < kDownI4Cols; ++c) {
+            const int col = col0 + 16 * c + n;   // A row of this lane
+            wv[i][c] = ld16_nt(a.wd + (size_t)col * rowb + 64 * (size_t)g + 16 * q);
+            sv[i][c] = *(const uint2 *)(a.sdt + (size_t)g * a.d + col0 + 16 * c + 4 * q);
+        }
+    }
+    f32x4_t acc[kDownI4Cols];
+#pragma unroll
+    for (int c = 0; c < kDownI4Cols; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kDownI4Groups; ++i) {
+        if (i >= cnt) break;
+#pragma unroll
+        for (int c = 0; c < kDownI4Cols; ++c) {
+            const uint32_t wd4[4] = {wv[i][c].x, wv[i][c].y, wv[i][c].z, wv[i][c].w};
+            f32x4_t s4 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8_t wf = i4x8_to_bf16(wd4[ks]);
+                bf16x8_t hf, lf;
+                __builtin_memcpy(&hf, &hv[i][ks][0], 16);
+                __builtin_memcpy(&lf, &hv[i][ks][1], 16);
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, hf, s4, 0, 0, 0);
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, lf, s4, 0, 0, 0);
+            }
+            // C[output column 4q + e][token n]: the group's sum times the column's scale
+            const float sc[4] = {half_bits_to_float((uint16_t)sv[i][c].x), half_bits_to_float((uint16_t)(sv[i][c].x >> 16)),
+                                 half_bits_to_float((uint16_t)sv[i][c].y), half_bits_to_float((uint16_t)(sv[i][c].y >> 16))};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[c][e] = __builtin_fmaf(sc[e], s4[e], acc[c][e]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kDownI4Cols; ++c)
+        *(float4 *)(a.partial + ((size_t)p * 16 + n) * a.d + col0 + 16 * c + 4 * q) =
+            make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+}
+
+// ---------------------------------------------------------------------------
 // batched gate GEMV in the fixed order (5..16 tokens, bf16, BATCH layout).
 // The fixed order splits a row into 64 lane accumulators (accumulator c sums
 // chunks c, c + 64, ... with an fma chain per chunk) and adds them in a halving
@@ -2347,6 +2488,35 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                            (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs,
                            topk ? (const uint32_t *)bits : nullptr, B);
         return hipGetLastError();
+    }
+
+    if constexpr (WT == SFFN_W_INT4_G128 && BT >= 8) {
+        // (f <= kMaxTopkNeurons keeps the splits within kMaxDownSplits)
+        if (topk && f / 128 <= kMaxDownSplits * kDownI4Groups) {
+            // 5..16 tokens: the union is most of d_ff, so the down projection reads
+            // all of W_down on MFMA instead of gathering rows
+            if (c.idx_out || c.count_out) {
+                const int maxs = (f + kGatherWGs - 1) / kGatherWGs + 1;
+                hipLaunchKernelGGL(k_emit_list, dim3(kGatherWGs), dim3(256), (size_t)(maxs + nL + 1) * 4, st,
+                                   (const int *)lcnt, (const int *)lidx, nL, R, c.idx_out, c.count_out, maxs,
+                                   (const uint32_t *)bits, B);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
+            uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
+            FormHArgs fh{bits, G, U, B, f, nw32, D.act, c.use_union, hh, hl};
+            hipLaunchKernelGGL(k_form_h_i4, dim3(f / 128), dim3(256), 0, st, fh);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const int ng = f / 128, T = d / (16 * kDownI4Cols);
+            const int ns0 = std::max(1, std::min(std::min(ng, kMaxDownSplits), (kDownI4Waves + T - 1) / T));
+            const int per = std::min((ng + ns0 - 1) / ns0, kDownI4Groups), ns = (ng + per - 1) / per;
+            float *partial = (float *)(sc + S.partial);
+            DownI4Args da{L.wd, L.sdt, hh, hl, d, f, per, partial};
+            hipLaunchKernelGGL(k_down_i4_mfma, dim3(T, ns), dim3(64), 0, st, da);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_down_sum, dim3((B * d / 4 + 255) / 256), dim3(256), 0, st, (const float *)partial, ns,
+                               B, d, D.residual ? c.x : nullptr, c.out);
+            return hipGetLastError();
+        }
     }
 
     GatherArgs g{};
