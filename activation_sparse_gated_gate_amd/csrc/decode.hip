@@ -1244,7 +1244,7 @@ __global__ __launch_bounds__(256) void k_down_sum(const float *__restrict__ part
 // W are one 16-byte load; h is stored in the same order.
 // ---------------------------------------------------------------------------
 struct FormHArgs {
-    const uint32_t *bits;   // [B][f/32] top-k sets
+    const uint32_t *bits;   // [B][f/32] top-k sets, or nullptr: G already holds h for every neuron (dense)
     const float *G, *U;     // [B][f]
     int B, f, nw32, act, use_union;
     uint16_t *hh, *hl;      // [f/128][4 k-steps][64 lanes][8]
@@ -1256,22 +1256,27 @@ __global__ __launch_bounds__(256) void k_form_h_i4(const FormHArgs a)
     const int g = blockIdx.x, ks = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int kg = lane >> 4, t = lane & 15;
     const int j0 = 128 * g + 32 * kg + 8 * ks;
-    uint32_t uni = 0, own = 0;   // bits of the 8 neurons: union over the tokens, this token's
-    for (int t2 = 0; t2 < a.B; ++t2) {
-        const uint32_t w = (a.bits[(size_t)t2 * a.nw32 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
-        uni |= w;
-        if (t2 == t) own = w;
+    uint32_t uni = 0xFFu, own = 0xFFu;   // bits of the 8 neurons: union over the tokens, this token's
+    if (a.bits) {
+        uni = 0;
+        own = 0;
+        for (int t2 = 0; t2 < a.B; ++t2) {
+            const uint32_t w = (a.bits[(size_t)t2 * a.nw32 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
+            uni |= w;
+            if (t2 == t) own = w;
+        }
     }
     const int tc = min(t, a.B - 1);
     const f32x4_t g0 = *(const f32x4_t *)(a.G + (size_t)tc * a.f + j0), g1 = *(const f32x4_t *)(a.G + (size_t)tc * a.f + j0 + 4);
-    const f32x4_t u0 = *(const f32x4_t *)(a.U + (size_t)tc * a.f + j0), u1 = *(const f32x4_t *)(a.U + (size_t)tc * a.f + j0 + 4);
+    const float *Ut = a.bits ? a.U : a.G;   // dense: h is read from G (u unused)
+    const f32x4_t u0 = *(const f32x4_t *)(Ut + (size_t)tc * a.f + j0), u1 = *(const f32x4_t *)(Ut + (size_t)tc * a.f + j0 + 4);
     const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
     const float uv[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
     uint16_t hb[8], lb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const bool on = t < a.B && ((uni >> e) & 1u) && (a.use_union || ((own >> e) & 1u));
-        const float h = on ? act_f32(a.act, gv[e]) * uv[e] : 0.0f;
+        const float h = !on ? 0.0f : a.bits ? act_f32(a.act, gv[e]) * uv[e] : gv[e];
         hb[e] = bf16_rne_bits(h);
         lb[e] = bf16_rne_bits(h - bf16_lo(hb[e]));
     }
@@ -2258,6 +2263,32 @@ static hipError_t run_gather(const GatherArgs &a0, hipStream_t st)
     return hipGetLastError();
 }
 
+// int4, 5..16 tokens: h in MFMA lane order (from the top-k sets, or bits ==
+// nullptr: G already holds h), the down projection over all of W_down on MFMA,
+// and the sum of the d_ff splits plus the residual
+static hipError_t down_i4_mfma(const Layer &L, uint8_t *sc, const ScratchLayout &S, const uint32_t *bits,
+                               const float *G, const float *U, int B, int act, int use_union, const float *x,
+                               float *out, hipStream_t st)
+{
+    const sffn_layer_desc &D = L.desc;
+    const int d = D.d_model, f = D.d_ff;
+    hipError_t e;
+    uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
+    FormHArgs fh{bits, G, U, B, f, f / 32, act, use_union, hh, hl};
+    hipLaunchKernelGGL(k_form_h_i4, dim3(f / 128), dim3(256), 0, st, fh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ng = f / 128, T = d / (16 * kDownI4Cols);
+    const int ns0 = std::max(1, std::min(std::min(ng, kMaxDownSplits), (kDownI4Waves + T - 1) / T));
+    const int per = std::min((ng + ns0 - 1) / ns0, kDownI4Groups), ns = (ng + per - 1) / per;
+    float *partial = (float *)(sc + S.partial);
+    DownI4Args da{L.wd, L.sdt, hh, hl, d, f, per, partial};
+    hipLaunchKernelGGL(k_down_i4_mfma, dim3(T, ns), dim3(64), 0, st, da);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_down_sum, dim3((B * d / 4 + 255) / 256), dim3(256), 0, st, (const float *)partial, ns, B, d,
+                       D.residual ? x : nullptr, out);
+    return hipGetLastError();
+}
+
 template <int WT, int BT>
 static hipError_t decode_typed(const DecodeCall &c, bool forward)
 {
@@ -2343,6 +2374,11 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
         r.w0 = L.wg; r.s0 = L.sg; r.w1 = L.wu; r.s1 = L.su;
         r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
         if ((e = run_rowdot<WT, BT, OUT_DENSE_GU>(r, st)) != hipSuccess) return e;
+        if constexpr (WT == SFFN_W_INT4_G128 && BT >= 8) {
+            // int4, 5..16 tokens: the dense down projection on MFMA, as the top-k path's
+            if (f / 128 <= kMaxDownSplits * kDownI4Groups)
+                return down_i4_mfma(L, sc, S, nullptr, G, nullptr, B, D.act, 1, c.x, c.out, st);
+        }
         RowDotArgs q{};
         q.w0 = L.wd; q.s0 = L.sd; q.rows = d; q.cols = f; q.B = B; q.x = G; q.o0 = c.out;
         q.resid = D.residual ? c.x : nullptr;
@@ -2502,20 +2538,7 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
                                    (const uint32_t *)bits, B);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
             }
-            uint16_t *hh = (uint16_t *)(sc + S.hsplit), *hl = hh + (size_t)16 * f;
-            FormHArgs fh{bits, G, U, B, f, nw32, D.act, c.use_union, hh, hl};
-            hipLaunchKernelGGL(k_form_h_i4, dim3(f / 128), dim3(256), 0, st, fh);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            const int ng = f / 128, T = d / (16 * kDownI4Cols);
-            const int ns0 = std::max(1, std::min(std::min(ng, kMaxDownSplits), (kDownI4Waves + T - 1) / T));
-            const int per = std::min((ng + ns0 - 1) / ns0, kDownI4Groups), ns = (ng + per - 1) / per;
-            float *partial = (float *)(sc + S.partial);
-            DownI4Args da{L.wd, L.sdt, hh, hl, d, f, per, partial};
-            hipLaunchKernelGGL(k_down_i4_mfma, dim3(T, ns), dim3(64), 0, st, da);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_down_sum, dim3((B * d / 4 + 255) / 256), dim3(256), 0, st, (const float *)partial, ns,
-                               B, d, D.residual ? c.x : nullptr, c.out);
-            return hipGetLastError();
+            return down_i4_mfma(L, sc, S, bits, G, U, B, D.act, c.use_union, c.x, c.out, st);
         }
     }
 

@@ -356,7 +356,8 @@ def test_cfg3_int4_dense_mode_matches_all(cfg3, B):
     assert rel_l2(y, ref["y"]) <= 5e-3
 
 
-@pytest.mark.parametrize("wt,B", [(synth.WT_F32, 4), (synth.WT_BF16, 8), (synth.WT_BF16, 16)])
+@pytest.mark.parametrize("wt,B", [(synth.WT_F32, 4), (synth.WT_BF16, 8), (synth.WT_BF16, 16), (synth.WT_I4, 5),
+                                  (synth.WT_I4, 8)])
 def test_dense_mode_batches(wt, B):
     sf = _sf()
     w = synth._make_weights(wt, 1024, 2816, synth.ACT_SILU, (1931, 1932, 1933))
