@@ -47,13 +47,26 @@ METRIC = "µs/layer & effective HBM GB/s (% of peak) vs active fraction a; break
 # files); after any change the figure is reported as null until the counters are taken again.
 COUNTER_TRAFFIC = {
     "k_decode_b1": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
-                    "sha256_16": "6cae23c4f2f93fb8",
+                    "sha256_16": "af97e1b2d8ed3b62",
                     "workload": "a = 0.1, bf16 4096 x 11008, batch 1",
-                    "fetch_kib": 52941.38, "write_kib": 4166.70, "fetch_factor": 1.9998, "write_factor": 1.0000},
+                    "fetch_kib": 52955.26, "write_kib": 4170.64, "fetch_factor": 1.9998, "write_factor": 1.0000},
+    "k_gu_i4_b1": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
+                   "sha256_16": "af97e1b2d8ed3b62",
+                   "workload": "int4-g128 2048 x 11008, batch 1, top-k",
+                   "fetch_kib": 11517.50, "write_kib": 192.42, "fetch_factor": 1.9998, "write_factor": 1.0000},
+    "k_gate_up_dual": {"sources": ("decode.hip", "dev_common.h", "sffn_internal.h"),
+                       "sha256_16": "af97e1b2d8ed3b62",
+                       "workload": "bf16 3584 x 18944, 16 tokens, 28-layer schedule",
+                       "fetch_kib": 134504.73, "write_kib": 7104.45, "fetch_factor": 1.9998, "write_factor": 1.0000},
+    "k_gemm_big_gate_up": {"sources": ("prefill.hip", "dev_common.h", "sffn_internal.h"),
+                           "sha256_16": "e1782b7ad9150d88",
+                           "workload": "bf16 5120 x 25600, L 16384, mass 0.5 (2674 kept rows)",
+                           "fetch_kib": 1265454.08, "write_kib": 133700.00, "fetch_factor": 1.9998,
+                           "write_factor": 1.0000},
     "k_expert_select": {"sources": ("experts.hip", "dev_common.h", "sffn_internal.h"),
-                        "sha256_16": "ed04238792f59b9f",
+                        "sha256_16": "21e6c3996a640c44",
                         "workload": "16384 tokens x 384 experts, tau 0.5, buckets 3..6",
-                        "fetch_kib": 12313.18, "write_kib": 896.00, "fetch_factor": 1.9998, "write_factor": 1.0000},
+                        "fetch_kib": 12313.15, "write_kib": 896.00, "fetch_factor": 1.9998, "write_factor": 1.0000},
 }
 
 
@@ -615,9 +628,10 @@ def bench_schedule(args):
             layers[8].forward(pols[8], xs[8], xs[9])
     kus = main_kernel_us([layers[8]], gl, 64)
     flops_gate = 2.0 * B * f * d
-    # the gate kernel reads W_gate once (2 d f bytes), x_hat (B d fp32) and writes four class partials
-    bytes_gate = 2.0 * d * f + 4.0 * B * d + 4.0 * 4 * B * f
-    achieved = bytes_gate / kus / 1e3
+    # the combined gate + up launch reads W_gate and W_up once each (4 d f bytes) and x_hat
+    # (B d fp32), and writes the four gate class partials and the two halves of u (fp32)
+    bytes_gu = 4.0 * d * f + 4.0 * B * d + 4.0 * 4 * B * f + 4.0 * 2 * B * f
+    achieved = bytes_gu / kus / 1e3
     alu_frac = flops_gate / kus / 1e6 / VALU_FP32_PEAK_TFLOPS
     cpu = None
     if args.cpu_tokens > 0:
@@ -636,9 +650,10 @@ def bench_schedule(args):
            "us_per_layer_by_segment": seg, "union_density": [round(v, 4) for v in dens],
            "bytes_per_step": int(bytes_step)}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_gate_pipe<16> (fixed-order gate GEMV, 16 tokens, fp32 FMA, class-split, LDS-staged)",
-            "kernel_us": round(kus, 3), "bytes_per_launch": int(bytes_gate), "flops_per_launch": flops_gate,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("k_gate_up_dual"),
+            "kernel": "k_gate_up_dual<16> (fixed-order class-split gate GEMV on fp32 FMA and MFMA up, one launch, "
+                      "16 tokens)",
+            "kernel_us": round(kus, 3), "bytes_per_launch": int(bytes_gu), "flops_per_launch": flops_gate,
             "alu_frac": round(alu_frac, 4)}
     out = line("µs per 28-layer step & effective HBM GB/s", round(gbps, 1), "GB/s", steps, 2,
                round(us_step / 1e3, 4), "bf16", cfg, roof, cpu)
@@ -771,8 +786,8 @@ def bench_prefill(args):
                        "top-P mass with recent_n 128, min_keep 1; value at mass 0.5", "results": rows,
            "block_selection": brows}
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "k_gemm_big<gate_up> (gathered rows x interleaved W_gate/W_up, SwiGLU epilogue)",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic("k_gemm_big_gate_up"),
+            "kernel": "k_gemm_big<gate_up, 8 waves> (gathered rows x interleaved W_gate/W_up, SwiGLU epilogue)",
             "kernel_us": round(kus, 3), "flops_per_launch": fl}
     out = line("ms per prefill FFN layer & TFLOP/s vs mass", mid["tflops"], "TFLOP/s", reps, 1, mid["ffn_ms"],
                "bf16", cfg, roof, cpu)
