@@ -340,61 +340,149 @@ struct TopkArgs {
 };
 
 // The exact top k of one token's f fp64 score keys (key = the bits of the
-// non-negative score, so the integer order is the value order), ties to the
-// lower index, decided by the 1024 threads of a workgroup: thread tid holds
-// keys j = tid + 1024 q.  Radix select from the top in 12-bit digits (key bits
-// 63..52, 51..40, 39..28, 27..16, 15..4, then 3..0): each pass counts in an LDS
-// histogram the keys that share the digits chosen so far, and a block scan in
-// descending digit order finds the digit of the k-th key; keys in higher digits
-// are kept.  It stops as soon as
-//   - the chosen bin is kept whole (every key at or above it is kept), or
-//   - the bin holds at most kTopkCand keys: these candidates are ranked exactly
-//     by pairwise comparison of (key desc, index asc) and the best ones kept.
-// Only a bin of more than kTopkCand identical keys is resolved by an
-// index-order scan (the lowest indices of the equal keys).  With scores spread
-// over many octaves two passes leave a handful of candidates.  The two
-// histograms alternate between passes and each bin is cleared as it is read.
+// non-negative score with bit 63 cleared, so the integer order is the value
+// order), ties to the lower index, decided by the 1024 threads of a workgroup:
+// thread tid holds keys j = tid + 1024 q.  Radix select from the top:
+//   pass 0   the 11 exponent bits (key bits 62..52).  Scores spread over few
+//            octaves, so lanes of one wave often share a digit; the histogram
+//            is kept in kTopkSlots copies indexed by lane, which keeps such
+//            lanes off one LDS word (their atomic adds would serialise)
+//   pass 1   key bits 51..40 of the keys in the chosen exponent (high words)
+//   then     12-bit digits 39..28, 27..16, 15..4 and bits 3..0.
+// Each pass counts the keys that share the digits chosen so far, and a block
+// scan in descending digit order finds the digit of the k-th key; keys in
+// higher digits are kept.  It stops as soon as the chosen bin is kept whole,
+// or holds at most kTopkCand keys: those are ranked exactly by (key desc,
+// index asc), sixteen threads per candidate, and the k-th names the threshold
+// (key, index) that every thread compares its keys with.  Only a bin of more
+// than kTopkCand equal keys is resolved by an index-order scan.
 // Returns the thread's decisions: bit q set = key q kept.
-constexpr int kTopkCand = 256;
+constexpr int kTopkCand = 64;    // at most this many keys left in the chosen bin: rank them exactly
+constexpr int kTopkSlots = 4;    // copies of the first pass's histogram, one per lane & (kTopkSlots - 1)
 
 struct TopkLds {
-    uint32_t hist[2][4096];
+    uint32_t h0[2048 * kTopkSlots];   // pass 0: (key bits 62..52) * kTopkSlots + lane slot
+    uint32_t hist[2][4096];           // later passes (12-bit digits), alternating
     int wsum[16];
-    int s_digit, s_above, s_cnt, s_ncand;
+    int s_digit, s_above, s_cnt, s_ncand, s_tidx;
+    uint64_t s_tkey;
     uint64_t ckey[kTopkCand];
     int cidx[kTopkCand];
-    uint32_t kept_bm[kMaxTopkNeurons / 32];
 };
 
 constexpr int kTopkPer = kMaxTopkNeurons / 1024;   // keys per thread
+
+// block scan of per-thread bin counts given in descending digit order (c[0] the
+// highest digit of the thread, digits hi0 - e): finds the digit holding the
+// kk-th key, the keys above it and its count, in L.s_digit / s_above / s_cnt
+template <int E>
+__device__ __forceinline__ void topk_scan_pick(const int (&c)[E], int hi0, int kk, TopkLds &L)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int cs = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs += c[e];
+    int incl = wave_incl_scan(cs);
+    if (lane == 63) L.wsum[wave] = incl;
+    __syncthreads();
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) incl += w2 < wave ? L.wsum[w2] : 0;
+    int above = incl - cs;
+    if (above < kk && kk <= incl) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (above < kk && kk <= above + c[e]) {
+                L.s_digit = hi0 - e;
+                L.s_above = above;
+                L.s_cnt = c[e];
+            }
+            above += c[e];
+        }
+    }
+    __syncthreads();
+}
 
 __device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, TopkLds &L)
 {
     constexpr int PER = kTopkPer, NT = 1024;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 2 * 4096; i += NT) (&L.hist[0][0])[i] = 0;
-    for (int i = tid; i < kMaxTopkNeurons / 32; i += NT) L.kept_bm[i] = 0;
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < (int)sizeof(L.h0) / 16; i += NT) ((uint4 *)L.h0)[i] = zero;
+    __syncthreads();
+    // pass 0, and meanwhile the later passes' counters are cleared
+    const int slot = lane & (kTopkSlots - 1);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (q * NT >= f) break;   // uniform
+        const int j = tid + NT * q;
+        if (j < f) atomicAdd(&L.h0[(int)(kv[q] >> 52) * kTopkSlots + slot], 1u);
+    }
+    for (int i = tid; i < (int)sizeof(L.hist) / 16; i += NT) ((uint4 *)L.hist)[i] = zero;
     if (tid == 0) L.s_ncand = 0;
     __syncthreads();
-    uint64_t prefix = 0, pmask = 0;
     int kk = k;
+    {
+        // thread tid: digits 2047 - 2 tid and 2046 - 2 tid, 2 kTopkSlots consecutive words
+        const uint4 *r = (const uint4 *)&L.h0[(2046 - 2 * tid) * kTopkSlots];
+        int c2[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < kTopkSlots / 4; ++i) {
+            const uint4 lo = r[i], hi = r[kTopkSlots / 4 + i];
+            c2[1] += (int)(lo.x + lo.y + lo.z + lo.w);
+            c2[0] += (int)(hi.x + hi.y + hi.z + hi.w);
+        }
+        topk_scan_pick<2>(c2, 2047 - 2 * tid, kk, L);
+    }
+    kk -= L.s_above;
+    const uint32_t d0 = (uint32_t)L.s_digit;
+    uint64_t prefix = (uint64_t)d0 << 52, pmask = 0xFFFull << 52;
     int mode = 3;   // 1: keep the chosen bin whole, 2: rank the candidates, 3: equal keys by index
-    for (int pass = 0; pass < 6; ++pass) {
+    int cnt = L.s_cnt;
+    if (cnt == kk) mode = 1;
+    else if (cnt <= kTopkCand) mode = 2;
+    if (mode == 3) {
+        // pass 1 on the high words: exponent d0, digit = key bits 51..40
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q * NT >= f) break;
+            const int j = tid + NT * q;
+            const uint32_t hw = (uint32_t)(kv[q] >> 32);
+            if (j < f && (hw >> 20) == d0) atomicAdd(&L.hist[1][(hw >> 8) & 0xFFFu], 1u);
+        }
+        __syncthreads();
+        {
+            int c4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dg = 4095 - (4 * tid + e);
+                c4[e] = (int)L.hist[1][dg];
+                L.hist[1][dg] = 0;   // clear for pass 3
+            }
+            topk_scan_pick<4>(c4, 4095 - 4 * tid, kk, L);
+        }
+        kk -= L.s_above;
+        prefix |= (uint64_t)L.s_digit << 40;
+        pmask |= 0xFFFull << 40;
+        cnt = L.s_cnt;
+        if (cnt == kk) mode = 1;
+        else if (cnt <= kTopkCand) mode = 2;
+    }
+    for (int pass = 2; pass < 6 && mode == 3; ++pass) {
+        // rare: more than kTopkCand keys share the top 24 bits
         const int width = pass < 5 ? 12 : 4;
         const int shift = pass < 5 ? 52 - 12 * pass : 0;
         const int nb = 1 << width;
         uint32_t *h = L.hist[pass & 1];
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            if (q * NT >= f) break;   // uniform
+            if (q * NT >= f) break;
             const int j = tid + NT * q;
             if (j < f && (kv[q] & pmask) == prefix) atomicAdd(&h[(int)(kv[q] >> shift) & (nb - 1)], 1u);
         }
         __syncthreads();
         // thread tid owns digits nb-1-4tid .. nb-4-4tid (descending) and clears
-        // them for the pass after next; a block scan in thread order gives the
-        // keys above each digit
-        int c4[4], cs = 0;
+        // them for the pass after next
+        int c4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int dg = nb - 1 - (4 * tid + e);
@@ -403,35 +491,19 @@ __device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, To
                 c4[e] = (int)h[dg];
                 h[dg] = 0;
             }
-            cs += c4[e];
         }
-        int incl = wave_incl_scan(cs);
-        if (lane == 63) L.wsum[wave] = incl;
-        __syncthreads();
-#pragma unroll
-        for (int w2 = 0; w2 < 16; ++w2) incl += w2 < wave ? L.wsum[w2] : 0;
-        int above = incl - cs;
-        if (above < kk && kk <= incl) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (above < kk && kk <= above + c4[e]) {
-                    L.s_digit = nb - 1 - (4 * tid + e);
-                    L.s_above = above;
-                    L.s_cnt = c4[e];
-                }
-                above += c4[e];
-            }
-        }
-        __syncthreads();
+        topk_scan_pick<4>(c4, nb - 1 - 4 * tid, kk, L);
         kk -= L.s_above;   // still to keep from the chosen bin
         prefix |= (uint64_t)L.s_digit << shift;
         pmask |= (uint64_t)(nb - 1) << shift;
-        const int cnt = L.s_cnt;
-        if (cnt == kk) { mode = 1; break; }       // uniform
-        if (cnt <= kTopkCand) { mode = 2; break; }
+        cnt = L.s_cnt;
+        if (cnt == kk) mode = 1;            // uniform
+        else if (cnt <= kTopkCand) mode = 2;
     }
+    uint32_t dm = 0;
     if (mode == 2) {
-        // the candidates (keys of the chosen bin) into LDS, then each one's rank
+        // the candidates (keys of the chosen bin, at most kTopkCand) into LDS,
+        // ranked by (key desc, index asc); the kk-th is the threshold (tkey, tidx)
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             if (q * NT >= f) break;
@@ -449,20 +521,53 @@ __device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, To
             }
         }
         __syncthreads();
-        const int nc = L.s_ncand;
-        if (tid < nc) {
-            const uint64_t my = L.ckey[tid];
-            const int mi = L.cidx[tid];
-            int r = 0;
-            for (int i = 0; i < nc; ++i) {
-                const uint64_t o = L.ckey[i];
-                r += (o > my || (o == my && L.cidx[i] < mi)) ? 1 : 0;
+        {
+            // sixteen threads per candidate, each a sixteenth of the comparisons
+            const int nc = L.s_ncand;
+            const int ci = tid >> 4, part = tid & 15;
+            uint64_t my = 0;
+            int mi = 0, r = 0;
+            if (ci < nc) {
+                my = L.ckey[ci];
+                mi = L.cidx[ci];
+                for (int i = part; i < nc; i += 16) {
+                    const uint64_t o = L.ckey[i];
+                    r += (o > my || (o == my && L.cidx[i] < mi)) ? 1 : 0;
+                }
             }
-            if (r < kk) atomicOr(&L.kept_bm[mi >> 5], 1u << (mi & 31));
+            r += __shfl_xor(r, 1, 64);
+            r += __shfl_xor(r, 2, 64);
+            r += __shfl_xor(r, 4, 64);
+            r += __shfl_xor(r, 8, 64);
+            if (part == 0 && ci < nc && r == kk - 1) {
+                L.s_tkey = my;
+                L.s_tidx = mi;
+            }
         }
         __syncthreads();
+        const uint64_t tk = L.s_tkey;
+        const int ti = L.s_tidx;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q * NT >= f) break;   // uniform
+            const int j = tid + NT * q;
+            const bool on = j < f && (kv[q] > tk || (kv[q] == tk && j <= ti));
+            dm |= on ? (1u << q) : 0u;
+        }
+        return dm;
     }
-    uint32_t dm = 0;
+    if (mode == 1 && (uint32_t)pmask == 0u) {
+        // the kept bin is a prefix of the high words
+        const uint32_t ph = (uint32_t)(prefix >> 32), mh = (uint32_t)(pmask >> 32);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (q * NT >= f) break;   // uniform
+            const int j = tid + NT * q;
+            const bool on = j < f && ((uint32_t)(kv[q] >> 32) & mh) >= ph;
+            dm |= on ? (1u << q) : 0u;
+        }
+        return dm;
+    }
     int base_rank = 0;   // equal keys before this round (index order), mode 3 only
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -472,8 +577,6 @@ __device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, To
         bool on;
         if (mode == 1) {
             on = j < f && v >= prefix;
-        } else if (mode == 2) {
-            on = j < f && (v > prefix || ((L.kept_bm[j >> 5] >> (j & 31)) & 1u));
         } else {
             // more than kTopkCand keys equal to the threshold: the lowest indices
             const bool tie = j < f && v == prefix;
@@ -496,13 +599,15 @@ __device__ uint32_t topk_decide(const uint64_t (&kv)[kTopkPer], int f, int k, To
     return dm;
 }
 
+// Every load is issued before any is used (the index is clamped instead of the
+// load made conditional, which would make each load wait for the previous
+// one); keys past f are never counted.  Bit 63 is cleared afterwards.
 __device__ __forceinline__ void load_token_keys(uint64_t (&kv)[kTopkPer], const uint64_t *keys, int f)
 {
 #pragma unroll
-    for (int q = 0; q < kTopkPer; ++q) {
-        const int j = threadIdx.x + 1024 * q;
-        kv[q] = j < f ? keys[j] : 0;
-    }
+    for (int q = 0; q < kTopkPer; ++q) kv[q] = keys[min((int)threadIdx.x + 1024 * q, f - 1)];
+#pragma unroll
+    for (int q = 0; q < kTopkPer; ++q) kv[q] &= 0x7FFFFFFFFFFFFFFFull;
 }
 
 // One workgroup per token: the token's selection as bit words (key j in bit
