@@ -2125,9 +2125,10 @@ struct GuI4Args {
     const float *x;              // [d]
     const double *wdn;           // ||W_down[:, j]||_2
     float *G, *U;                // [f]
-    uint64_t *keys;              // [f]
+    uint64_t *keys;              // [f], or null: no score keys
     int f, RB;
     float bias;
+    int act = 0, write_h = 0;    // write_h: G receives h = act(g') u instead of g' (U unused; the dense layer)
 };
 
 template <int KC, int NW>
@@ -2174,8 +2175,12 @@ __global__ __launch_bounds__(NW * 64) void k_gu_i4_b1(const GuI4Args a)
         const float g = wave_tree_sum_dpp(ag), u = wave_tree_sum_dpp(au);
         if (lane == 0) {
             const float gp = g + a.bias;
-            a.G[r0 + i] = gp;
-            a.U[r0 + i] = u;
+            if (a.write_h) {
+                a.G[r0 + i] = act_f32(a.act, gp) * u;
+            } else {
+                a.G[r0 + i] = gp;
+                a.U[r0 + i] = u;
+            }
             gsm[i] = gp;
             usm[i] = u;
         }
@@ -2196,8 +2201,88 @@ __global__ __launch_bounds__(NW * 64) void k_gu_i4_b1(const GuI4Args a)
         }
     }
     __syncthreads();
-    if ((int)threadIdx.x < nr)
+    if (a.keys && (int)threadIdx.x < nr)   // keys = nullptr: g' and u only (the dense layer)
         a.keys[r0 + threadIdx.x] = topk_key(gsm[threadIdx.x], usm[threadIdx.x], a.wdn[r0 + threadIdx.x]);
+}
+
+// int4 dense layer for one token, down projection: y_i = sum_j W_down[i][j] h_j
+// (+ x_i) with h from the gate + up kernel.  The down projection decides
+// nothing, so its order is free.  Each workgroup stages h once in LDS (every
+// load issued before the first store; a pad of 4 values after every 32, so
+// that the 64 lanes of a wave, each on its own 32-neuron run, spread over the
+// banks) and owns kDenseDownRows rows of the natural W_down [d][f]: a wave
+// takes one row at a time and requests every 16-byte chunk of it (32 weights
+// of one scale group) at once.
+constexpr int kDenseDownRows = 8;        // rows per workgroup, two per wave
+constexpr int kDenseDownChunks = 8;      // chunks per lane and row: f <= 64 * 8 * 32 = 16384
+struct DenseDownArgs {
+    const uint8_t *wd;      // W_down int4 [d][f / 2] (element j of a row: nibble j % 2 of byte j / 2)
+    const uint16_t *sd;     // fp16 scales [d][f / 128]
+    const float *H;         // h [f]
+    int d, f;
+    const float *resid;     // x [d] or null
+    float *out;             // y [d]
+};
+
+__device__ __forceinline__ int dense_h_pos(int j) { return j + (j >> 5) * 4; }
+
+__global__ __launch_bounds__(256) void k_dense_down_i4_b1(const DenseDownArgs a)
+{
+    extern __shared__ float hs[];   // f + f / 8 values
+    constexpr int RW = kDenseDownRows / 4;   // rows per wave
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nch = a.f / 32, ng = a.f / 128;
+    const size_t rowb = (size_t)a.f / 2;
+    // the wave's weights first (they do not wait for h), then h: one round trip
+    uint4 wv[RW][kDenseDownChunks];
+    uint16_t sv[RW][kDenseDownChunks];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int row = min((int)blockIdx.x * kDenseDownRows + 4 * r + wave, a.d - 1);
+#pragma unroll
+        for (int i = 0; i < kDenseDownChunks; ++i) {
+            const int c = min(lane + 64 * i, nch - 1);   // unconditional: every load in flight at once
+            wv[r][i] = ld16_nt(a.wd + (size_t)row * rowb + 16 * (size_t)c);
+            sv[r][i] = a.sd[(size_t)row * ng + (c >> 2)];
+        }
+    }
+    {
+        f32x4_t hv[kDenseDownChunks * 2];   // f <= 1024 * 2 kDenseDownChunks
+#pragma unroll
+        for (int i = 0; i < kDenseDownChunks * 2; ++i)
+            hv[i] = *(const f32x4_t *)(a.H + min(4 * (int)threadIdx.x + 1024 * i, a.f - 4));
+#pragma unroll
+        for (int i = 0; i < kDenseDownChunks * 2; ++i) {
+            const int j = 4 * (int)threadIdx.x + 1024 * i;
+            if (j < a.f) *(f32x4_t *)(hs + dense_h_pos(j)) = hv[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int row = (int)blockIdx.x * kDenseDownRows + 4 * r + wave;
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kDenseDownChunks; ++i) {
+            const int c = lane + 64 * i;
+            if (c >= nch) break;
+            const uint32_t w4[4] = {wv[r][i].x, wv[r][i].y, wv[r][i].z, wv[r][i].w};
+            const float *hc = hs + dense_h_pos(32 * c);
+            float t = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f32x4_t h0 = *(const f32x4_t *)(hc + 8 * k), h1 = *(const f32x4_t *)(hc + 8 * k + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = __builtin_fmaf((float)nib(w4[k], e), h0[e], t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t = __builtin_fmaf((float)nib(w4[k], 4 + e), h1[e], t);
+            }
+            acc = __builtin_fmaf(half_bits_to_float(sv[r][i]), t, acc);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (lane == 0 && row < a.d) a.out[row] = a.resid ? acc + a.resid[row] : acc;
+    }
 }
 
 // y = sum over the partials in a fixed order (+ residual): 16 columns per
@@ -2476,6 +2561,30 @@ static hipError_t decode_typed(const DecodeCall &c, bool forward)
     }
 
     if (c.mode == SFFN_MODE_DENSE) {
+        if constexpr (WT == SFFN_W_INT4_G128 && BT == 1) {
+            // one token: the streaming gate + up kernel (g' and u), then the row-streaming down GEMV
+            if (d % 2048 == 0 && d <= 4096 && f <= 64 * kDenseDownChunks * 32) {
+                static std::once_flag once;
+                static hipError_t err = hipSuccess;
+                static int lim = 0;
+                if ((e = allow_full_dynamic_lds((const void *)k_dense_down_i4_b1, once, err, lim)) != hipSuccess) return e;
+                const size_t lds = (size_t)(f + f / 8) * 4;
+                if (lds <= (size_t)lim) {
+                    GuI4Args ga{L.wg, L.wu, L.sg, L.su, xin, L.wdn, G, U, nullptr, f, fused_rows_per_wg(f), c.bias,
+                                D.act, 1};
+                    const int P = (f + ga.RB - 1) / ga.RB;
+                    if (d == 2048)
+                        hipLaunchKernelGGL((k_gu_i4_b1<1, kGuI4Waves>), dim3(P), dim3(kGuI4Waves * 64), 0, st, ga);
+                    else
+                        hipLaunchKernelGGL((k_gu_i4_b1<2, kGuI4Waves>), dim3(P), dim3(kGuI4Waves * 64), 0, st, ga);
+                    if ((e = hipGetLastError()) != hipSuccess) return e;
+                    DenseDownArgs dd{L.wd, L.sd, G, d, f, D.residual ? c.x : nullptr, c.out};
+                    hipLaunchKernelGGL(k_dense_down_i4_b1, dim3((d + kDenseDownRows - 1) / kDenseDownRows), dim3(256),
+                                       lds, st, dd);
+                    return hipGetLastError();
+                }
+            }
+        }
         r.w0 = L.wg; r.s0 = L.sg; r.w1 = L.wu; r.s1 = L.su;
         r.rows = f; r.cols = d; r.x = xin; r.o0 = G;
         if ((e = run_rowdot<WT, BT, OUT_DENSE_GU>(r, st)) != hipSuccess) return e;
