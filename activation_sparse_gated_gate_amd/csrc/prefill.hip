@@ -74,7 +74,6 @@ struct SelectArgs {
     double mass;
     int32_t *keep, *count;
     int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
-    int32_t *flags;  // [L] 1 = kept
 };
 
 __device__ __forceinline__ uint64_t rank_key(float s, int i)
@@ -89,19 +88,77 @@ __device__ __forceinline__ uint64_t rank_key(float s, int i)
 // global rank of a key is its place in its chunk plus, for every other chunk,
 // the number of larger keys there (a binary search); the key is written to that
 // rank.  The result is the full descending order.
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m)
+// the key of lane lane ^ J (J < 64): lane swaps for 32 and 16, a rotation by
+// 8 inside a row of 16 for 8, rotations by 4 and 12 for 4 (lane i ^ 4 is
+// i - 4 or i + 4), quad permutations for 2 and 1; each half of the key moves
+// separately.  Every lane of the wave must be active.
+template <int J>
+__device__ __forceinline__ uint32_t xchg32(uint32_t v)
 {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-    return ((uint64_t)hi << 32) | lo;
+    const int lane = threadIdx.x & 63;
+    if constexpr (J == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return lane < 32 ? p[1] : p[0];
+    } else if constexpr (J == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else if constexpr (J == 8) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);   // row_ror:8
+    } else if constexpr (J == 4) {
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false);   // row_ror:4, lane i - 4
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x12C, 0xf, 0xf, false);   // row_ror:12, lane i + 4
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 2) {
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);    // quad [2,3,0,1]
+    } else {
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);    // quad [1,0,3,2]
+    }
 }
 
-// Bitonic sort of the chunk's 1024 keys, descending, one key per thread: in
-// the stage that compares positions i and i ^ j inside runs of k, the lower
-// position keeps the larger key when its run descends ((i & k) == 0), the
-// smaller otherwise.  Partners less than 64 apart are in the same wave and are
-// exchanged by lane shuffles without a barrier; the 10 stages with j >= 64 go
+template <int J>
+__device__ __forceinline__ uint64_t xchg64(uint64_t v)
+{
+    return ((uint64_t)xchg32<J>((uint32_t)(v >> 32)) << 32) | xchg32<J>((uint32_t)v);
+}
+
+// one compare-exchange stage of the bitonic network: positions tid and
+// tid ^ J inside runs of K; the lower position keeps the larger key when its
+// run descends ((tid & K) == 0), the smaller otherwise
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t v, uint64_t o, int tid)
+{
+    const bool lower = (tid & J) == 0, desc = (tid & K) == 0;
+    return (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_in_wave(uint64_t &v, int tid)
+{
+    if constexpr (J >= 1) {
+        v = bitonic_step<K, J>(v, xchg64<J>(v), tid);
+        bitonic_in_wave<K, J / 2>(v, tid);
+    }
+}
+
+// Bitonic sort of the chunk's 1024 keys, descending, one key per thread.
+// Partners less than 64 apart are in the same wave and are exchanged without
+// LDS (lane swaps and DPP); the 10 stages with partners 64 or more apart go
 // through LDS, double-buffered, one barrier each.
+template <int K>
+__device__ __forceinline__ void bitonic_merge_k(uint64_t &v, int tid, uint64_t (&buf)[2][1024], int &nb)
+{
+#pragma unroll
+    for (int j = K >> 1; j >= 64; j >>= 1) {
+        buf[nb][tid] = v;
+        __syncthreads();
+        const uint64_t o = buf[nb][tid ^ j];
+        nb ^= 1;
+        const bool lower = (tid & j) == 0, desc = (tid & K) == 0;
+        v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+    bitonic_in_wave<K, (K >> 1) < 32 ? (K >> 1) : 32>(v, tid);
+}
+
 __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks)
 {
     __shared__ uint64_t buf[2][1024];
@@ -109,61 +166,88 @@ __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ 
     const int i = blockIdx.x * 1024 + tid;
     uint64_t v = i < L ? rank_key(s[i], i) : 0ull;
     int nb = 0;
-    for (int k = 2; k <= 1024; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t o;
-            if (j >= 64) {
-                buf[nb][tid] = v;
-                __syncthreads();
-                o = buf[nb][tid ^ j];
-                nb ^= 1;
-            } else {
-                o = shfl_xor64(v, j);
-            }
-            const bool lower = (tid & j) == 0, desc = (tid & k) == 0;
-            v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
-        }
-    }
+    bitonic_merge_k<2>(v, tid, buf, nb);
+    bitonic_merge_k<4>(v, tid, buf, nb);
+    bitonic_merge_k<8>(v, tid, buf, nb);
+    bitonic_merge_k<16>(v, tid, buf, nb);
+    bitonic_merge_k<32>(v, tid, buf, nb);
+    bitonic_merge_k<64>(v, tid, buf, nb);
+    bitonic_merge_k<128>(v, tid, buf, nb);
+    bitonic_merge_k<256>(v, tid, buf, nb);
+    bitonic_merge_k<512>(v, tid, buf, nb);
+    bitonic_merge_k<1024>(v, tid, buf, nb);
     chunks[(size_t)blockIdx.x * 1024 + tid] = v;
 }
 
+// The rank search runs on two levels: every chunk's 32 splitters (the last,
+// smallest key of each run of 32) say how many whole runs lie above the key,
+// then a search inside the one run that straddles it.  The splitter tables
+// are small, so the first five steps hit few LDS words; only the last five
+// read the full chunks at scattered addresses.
 __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict__ chunks, int G,
                                                       uint64_t *__restrict__ sorted)
 {
     extern __shared__ __align__(16) uint64_t all[];   // [G][1024]
+    constexpr int GMAX = kMaxPrefillRows / 1024;
+    __shared__ uint64_t spl[GMAX][32];
     {
-        constexpr int GMAX = kMaxPrefillRows / 1024;
         uint64_t kv[GMAX];
 #pragma unroll
         for (int q = 0; q < GMAX; ++q) kv[q] = q < G ? chunks[q * 1024 + threadIdx.x] : 0ull;
 #pragma unroll
-        for (int q = 0; q < GMAX; ++q)
-            if (q < G) all[q * 1024 + threadIdx.x] = kv[q];
+        for (int q = 0; q < GMAX; ++q) {
+            if (q < G) {
+                all[q * 1024 + threadIdx.x] = kv[q];
+                if ((threadIdx.x & 31) == 31) spl[q][threadIdx.x >> 5] = kv[q];
+            }
+        }
     }
     __syncthreads();
     const int c = blockIdx.x, p = threadIdx.x;
     const uint64_t key = all[c * 1024 + p];
     if (key == 0) return;   // padding
     // in every other chunk, the number of keys above this key (a chunk is sorted
-    // descending): branch-free binary searches of all chunks advanced together,
-    // one LDS read per chunk per step, so the reads of a step are in flight at once
-    constexpr int GMAX = kMaxPrefillRows / 1024;
+    // descending): branch-free binary searches of all chunks advanced together
+    // (unconditional reads, so the reads of a step are in flight at once).
+    // Level 1: runs whose smallest key is above the key, s in 0..32
+    int run[GMAX];
+#pragma unroll
+    for (int c2 = 0; c2 < GMAX; ++c2) run[c2] = 0;
+#pragma unroll
+    for (int step = 16; step >= 1; step >>= 1) {
+        uint64_t q[GMAX];
+#pragma unroll
+        for (int c2 = 0; c2 < GMAX; ++c2) q[c2] = spl[min(c2, G - 1)][run[c2] + step - 1];
+#pragma unroll
+        for (int c2 = 0; c2 < GMAX; ++c2)
+            if (q[c2] > key) run[c2] += step;
+    }
+    // run[c2] is 0..31 here; 31 with the last splitter above too means all 32 runs
+#pragma unroll
+    for (int c2 = 0; c2 < GMAX; ++c2) run[c2] += (run[c2] == 31 && spl[min(c2, G - 1)][31] > key) ? 1 : 0;
+    // Level 2: inside run r (when r < 32), the keys above the key
     int lo[GMAX];
 #pragma unroll
     for (int c2 = 0; c2 < GMAX; ++c2) lo[c2] = 0;
 #pragma unroll
-    for (int step = 512; step >= 1; step >>= 1) {
+    for (int step = 16; step >= 1; step >>= 1) {
         uint64_t q[GMAX];
 #pragma unroll
-        for (int c2 = 0; c2 < GMAX; ++c2) q[c2] = all[min(c2, G - 1) * 1024 + lo[c2] + step - 1];   // unconditional reads
+        for (int c2 = 0; c2 < GMAX; ++c2)
+            q[c2] = all[min(c2, G - 1) * 1024 + min(run[c2], 31) * 32 + lo[c2] + step - 1];
 #pragma unroll
         for (int c2 = 0; c2 < GMAX; ++c2)
-            if (c2 < G && c2 != c && q[c2] > key) lo[c2] += step;
+            if (q[c2] > key) lo[c2] += step;
     }
     int rank = p;
 #pragma unroll
     for (int c2 = 0; c2 < GMAX; ++c2) {
-        if (c2 < G && c2 != c) rank += lo[c2] + (lo[c2] == 1023 && all[c2 * 1024 + 1023] > key ? 1 : 0);
+        if (c2 < G && c2 != c) {
+            // the whole table is above when run = 32; else 32 run + the keys of the run above
+            // (lo = 31 with its last key above too means 32, impossible: that key is the
+            // run's splitter, which is not above)
+            rank += run[c2] == 32 ? 1024 : 32 * run[c2] + lo[c2];
+        }
     }
     sorted[rank] = key;
 }
@@ -303,8 +387,9 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     __syncthreads();
     // min_keep: add the highest-ranked tokens not yet kept.  Threads own
     // contiguous runs of ranks; a scan of their not-yet-kept counts tells each
-    // thread how many of its tokens are among the first `need` ones.
-    {
+    // thread how many of its tokens are among the first `need` ones.  Nothing
+    // to do when the prefix (ranks 0..s_m) already holds min_keep tokens.
+    if (a.min_keep > (all ? L : s_m + 1)) {
         int c = 0;
         for (int i = tid; i < L; i += NT) c += in[i];
         int tot;
@@ -371,7 +456,6 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
         const int i = q * NT + tid;
         const bool on = (onb >> q) & 1u;
         const uint64_t m = __ballot(on);
-        if (i < L) a.flags[i] = on ? 1 : 0;
         if (on) {
             const int pos = qbase[q] + wcnt[q][wave] + mbcnt64(m);
             a.keep[pos] = i;
@@ -435,6 +519,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
     __shared__ __align__(16) uint16_t As[GBM * GLDA];
     __shared__ __align__(16) uint16_t Bs[GBN * GLDA];
     __shared__ int rowsrc[GBM];
+    __shared__ int rowtok[GBM];   // DOWN: the kept token of each tile row (the epilogue's scatter)
 
     const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
@@ -449,8 +534,11 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
         const int m0 = tm * GBM, n0 = tn * GBN;
         __syncthreads();
         if (tid < GBM) {
-            const int m = m0 + tid;
-            rowsrc[tid] = m < M ? (EPI == EPI_GATE_UP ? kept_row(a, m) : m) : -1;
+            // rows past M read a valid row (every load unconditional, so all are
+            // in flight at once); their results are not written
+            const int m = min(m0 + tid, M - 1);
+            rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
+            if constexpr (EPI == EPI_DOWN) rowtok[tid] = kept_row(a, m);
         }
         __syncthreads();
 
@@ -461,8 +549,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
             for (int q = 0; q < 4; ++q) {
                 const int c = tid + q * 256;        // 0..1023
                 const int r = c >> 3, kc = c & 7;   // row, 8-element chunk
-                const int src = rowsrc[r];
-                ra[q] = src >= 0 ? ld16(a.A + (size_t)src * a.K + (size_t)kt * GBK + kc * 8) : make_uint4(0, 0, 0, 0);
+                ra[q] = ld16(a.A + (size_t)rowsrc[r] * a.K + (size_t)kt * GBK + kc * 8);
                 rb[q] = ld16(a.B + (size_t)(n0 + r) * a.K + (size_t)kt * GBK + kc * 8);
             }
         };
@@ -533,23 +620,26 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
                         }
                     }
         } else {
+            // the residual rows of every output first (rows past M read their
+            // clamped row), then the guarded stores
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j) {
+                    const int n = n0 + wn * 64 + j * 32 + ccol;
+                    float y[16];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
+                    for (int ge = 0; ge < 16; ++ge) {
+                        const int rl = wm * 64 + i * 32 + 8 * (ge >> 2) + 4 * (lane >> 5) + (ge & 3);
+                        y[ge] = bf16_lo(a.Y[(size_t)rowtok[rl] * a.ldo + n]);
+                    }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int rl = wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
-                            const int m = m0 + rl;
-                            if (m < M) {
-                                const int tok = kept_row(a, m);
-                                const int n = n0 + wn * 64 + j * 32 + ccol;
-                                const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
-                                a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
-                            }
-                        }
+                    for (int ge = 0; ge < 16; ++ge) {
+                        const int rl = wm * 64 + i * 32 + 8 * (ge >> 2) + 4 * (lane >> 5) + (ge & 3);
+                        if (m0 + rl < M)
+                            a.X[(size_t)rowtok[rl] * a.ldo + n] = f32_to_bf16_rne(y[ge] + acc[i][j][ge]);
+                    }
+                }
         }
     }
 }
@@ -594,6 +684,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
     __shared__ __align__(1024) uint16_t As[BSTAGES][BBM * BBK];
     __shared__ __align__(1024) uint16_t Bs[BSTAGES][BBN * BBK];
     __shared__ int rowsrc[BBM];
+    __shared__ int rowtok[BBM];   // DOWN: the kept token of each tile row (the epilogue's scatter)
 
     const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
@@ -619,6 +710,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
             // rows past M read a valid row; their results are not written
             const int m = min(m0 + tid, M - 1);
             rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
+            if constexpr (EPI == EPI_DOWN) rowtok[tid] = kept_row(a, m);
         }
         __syncthreads();
         // this wave copies rows 16 QA w + 16 q + (lane >> 2), q < QA, of both
@@ -716,22 +808,27 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
                     }
                 }
         } else {
+            // per group of 4 rows: the residual values first (rows past M read
+            // their clamped row), then the guarded stores
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     __builtin_amdgcn_sched_barrier(0);
+                    const int rl0 = wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+                    float y[4][JB];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < JB; ++j)
+                            y[e][j] = bf16_lo(a.Y[(size_t)rowtok[rl0 + e] * a.ldo + n0 + wn * 32 * JB + j * 32 + ccol]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
-                        if (m < M) {
-                            const int tok = kept_row(a, m);
+                        if (m0 + rl0 + e < M) {
 #pragma unroll
-                            for (int j = 0; j < JB; ++j) {
-                                const int n = n0 + wn * 32 * JB + j * 32 + ccol;
-                                const float y = bf16_lo(a.Y[(size_t)tok * a.ldo + n]);
-                                a.X[(size_t)tok * a.ldo + n] = f32_to_bf16_rne(y + acc[i][j][4 * g + e]);
-                            }
+                            for (int j = 0; j < JB; ++j)
+                                a.X[(size_t)rowtok[rl0 + e] * a.ldo + n0 + wn * 32 * JB + j * 32 + ccol] =
+                                    f32_to_bf16_rne(y[e][j] + acc[i][j][4 * g + e]);
                         }
                     }
                 }
@@ -780,7 +877,6 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     const int d = L.desc.d_model, rows = c.rows;
     const ScratchLayout S = scratch_layout(L.desc);
     float *sc_s = (float *)(c.scratch + S.tscore);
-    int32_t *flags = (int32_t *)(c.scratch + S.tflag);
     hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, c.stream, c.A, rows, d, sc_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -803,7 +899,7 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
                        sorted);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
-                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), flags};
+                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt)};
     hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
     return hipGetLastError();
 }

@@ -371,6 +371,22 @@ def test_dense_mode_batches(wt, B):
     layer.close()
 
 
+@pytest.mark.parametrize("d,f,rms", [(4096, 1408, True), (2048, 896, False), (1024, 1408, False)])
+def test_int4_dense_one_token(d, f, rms):
+    """The int4 dense layer at one token: d_model a multiple of 2048 runs the
+    streaming gate + up kernel (writing h) and the row-streaming down GEMV
+    (4096: two chunks per lane; RMSNorm and residual), other widths the plain
+    fixed-order GEMVs; both against the oracle's every-neuron FFN."""
+    sf = _sf()
+    w = synth._make_weights(synth.WT_I4, d, f, synth.ACT_SILU, (1941 + d, 1942, 1943))
+    x = synth.normal_f32(1944, (1, d))
+    layer = make_layer(w, 1, rmsnorm=rms, residual=rms)
+    y, _, _ = run_decode(layer, sf.make_policy("dense", gate_bias=0.125), x, want_list=False)
+    ref = oracle.decode(w, x, mode="all", bias=0.125, rmsnorm=rms, residual=rms)
+    assert rel_l2(y, ref["y"]) <= TOL[synth.WT_I4]
+    layer.close()
+
+
 def test_thresh_theta_must_express_a_threshold_on_the_activation():
     """THRESH is |act(g')| > tau taken as g' > theta: for SiLU that needs theta
     above 0.45511541... (SiLU(theta) beyond SiLU's minimum depth), for ReLU
