@@ -1753,8 +1753,9 @@ __global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part
             u[4 + e] = a1[e] + b1[e];
         }
     }
-    if (n < B) {
-        const size_t cs = (size_t)B * f, o = (size_t)n * f + j;
+    {
+        // the class partials (unconditional loads: slots past B read token B - 1's, unused)
+        const size_t cs = (size_t)B * f, o = (size_t)min(n, B - 1) * f + j;
         float p[4][8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1765,10 +1766,12 @@ __global__ __launch_bounds__(64) void k_combine_h(const float *__restrict__ part
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             gp[e] = ((p[0][e] + p[2][e]) + (p[1][e] + p[3][e])) + bias;
-            on |= gate_pred(mode, gp[e], theta) ? (1u << e) : 0u;
+            on |= (n < B && gate_pred(mode, gp[e], theta)) ? (1u << e) : 0u;
         }
-        *(float4 *)(G + o) = make_float4(gp[0], gp[1], gp[2], gp[3]);
-        *(float4 *)(G + o + 4) = make_float4(gp[4], gp[5], gp[6], gp[7]);
+        if (n < B) {
+            *(float4 *)(G + o) = make_float4(gp[0], gp[1], gp[2], gp[3]);
+            *(float4 *)(G + o + 4) = make_float4(gp[4], gp[5], gp[6], gp[7]);
+        }
     }
     // union over the tokens: neuron 8 g + e is selected if any lane of group g has bit e
     uint32_t mask = 0;
@@ -1832,6 +1835,47 @@ __global__ __launch_bounds__(64) void k_rmsnorm_split(const float *__restrict__ 
     const int t = blockIdx.x, lane = threadIdx.x;
     float r = 0.0f;
     const float *xt = x + (size_t)min(t, B - 1) * d;
+    if (d <= 4096) {
+        // every chunk of the row in registers (at most 16 per lane), loaded once,
+        // unconditionally; slots past B load token B - 1's and write zeros
+        const int nch = d / 4;
+        f32x4_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = *(const f32x4_t *)(xt + 4 * min(u * 64 + lane, nch - 1));
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (u * 64 + lane < nch) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(v[u][e], v[u][e], acc);
+            }
+        }
+        const float ss = wave_tree_sum_dpp(acc);
+        r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int c = u * 64 + lane;
+            if (c < nch) {
+                f32x4_t y = v[u] * r;
+                if (t < B) *(f32x4_t *)(xhat + (size_t)t * d + 4 * c) = y;
+                else y = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                const int pc = c >> 1, sstep = pc >> 2, g = pc & 3;
+                uint16_t h[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = bf16_rne_bits(y[e]);
+                    lo[e] = bf16_rne_bits(y[e] - bf16_lo(h[e]));
+                }
+                const size_t o = ((size_t)sstep * 64 + (g << 4) + t) * 8 + 4 * (c & 1);
+                uint2 ph, pl;
+                __builtin_memcpy(&ph, h, 8);
+                __builtin_memcpy(&pl, lo, 8);
+                *(uint2 *)(xh + o) = ph;
+                *(uint2 *)(xl + o) = pl;
+            }
+        }
+        return;
+    }
     if (t < B) {
         const int nch = d / 4;
         float acc = 0.0f;
