@@ -28,21 +28,53 @@ namespace sffn {
 // Sequence q's token range with the offsets clamped to [0, rows] and made
 // non-decreasing (running maximum), so the ranges are disjoint, ascending and
 // inside the batch whatever the offsets hold.  Called by every thread.
+// integer reductions and scans over the 256 threads of a workgroup: inside
+// each wave through lane exchanges, then the four wave results through LDS
+// (red, at least 4 words); integer arithmetic, so the order does not matter
+__device__ __forceinline__ int block256_max(int v, int *red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = max(max(red[0], red[1]), max(red[2], red[3]));
+    __syncthreads();   // red may be reused
+    return v;
+}
+
+__device__ __forceinline__ int block256_sum(int v, int *red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return v;
+}
+
+// exclusive prefix sum in thread order
+__device__ __forceinline__ int block256_exclusive(int v, int *red)
+{
+    const int w = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if ((threadIdx.x & 63) == 63) red[w] = incl;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 3; ++w2) base += w2 < w ? red[w2] : 0;
+    __syncthreads();
+    return base + incl - v;
+}
+
 __device__ __forceinline__ void seq_range(const int32_t *__restrict__ cu, int q, int rows, int *o0, int *o1,
                                           int *red)
 {
     int m = 0;
     for (int p = threadIdx.x; p <= q; p += blockDim.x) m = max(m, min(max(cu[p], 0), rows));
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + off]);
-        __syncthreads();
-    }
-    const int a = red[0];
+    const int a = block256_max(m, red);
     *o0 = a;
     *o1 = max(a, min(max(cu[q + 1], 0), rows));
-    __syncthreads();
 }
 
 struct BlkArgs {
@@ -64,7 +96,7 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
     __shared__ double cum[kMaxBlocksPerSeq];
     __shared__ int ord[kMaxBlocksPerSeq];
     __shared__ uint8_t kept[kMaxBlocksPerSeq];
-    __shared__ int red[256];
+    __shared__ int red[4];
     const int q = blockIdx.x, tid = threadIdx.x, B = a.block;
     __shared__ int s_bad;   // a non-finite block mass (from a NaN or infinite score)
     int o0, o1;
@@ -151,14 +183,9 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
     int part = 0;
     for (int b = tid; b < nb; b += 256)
         if (kept[b]) part += min(B, Lq - b * B);
-    red[tid] = part;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off) red[tid] += red[tid + off];
-        __syncthreads();
-    }
+    const int kept_tokens = block256_sum(part, red);
     if (tid == 0) {
-        int cnt = red[0];
+        int cnt = kept_tokens;
         if (!dense) {
             const int need = min(a.min_keep, Lq);
             for (int k = 0; k < nb && cnt < need; ++k) {
@@ -179,8 +206,7 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
 __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
 {
     __shared__ int pos[kMaxBlocksPerSeq + 1];
-    __shared__ int part[256];
-    __shared__ int red[256];
+    __shared__ int red[4];
     const int q = blockIdx.x, tid = threadIdx.x, B = a.block;
     int o0, o1;
     seq_range(a.cu, q, a.rows, &o0, &o1, red);
@@ -189,13 +215,7 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
     // offset of this sequence in the list: the earlier sequences' counts
     int acc = 0;
     for (int p = tid; p < q; p += 256) acc += a.counts[p];
-    red[tid] = acc;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off) red[tid] += red[tid + off];
-        __syncthreads();
-    }
-    const int base_out = red[0];
+    const int base_out = block256_sum(acc, red);
     if (q == a.nseq - 1 && tid == 0) {
         *a.count_out = base_out + a.counts[q];
         *a.count_copy = base_out + a.counts[q];
@@ -209,16 +229,8 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
         v[i] = (b < nb && fl[b]) ? min(B, Lq - b * B) : 0;
         sum += v[i];
     }
-    part[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int x = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += x;
-        __syncthreads();
-    }
     // pos[b] = kept tokens of the blocks before b, for b = 0..nb
-    int run = part[tid] - sum;
+    int run = block256_exclusive(sum, red);
     if (tid == 0) pos[0] = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
