@@ -32,13 +32,13 @@ inline size_t row_bytes(int wtype, int cols)
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// compute units of the current device (cached per device)
+int compute_units();
+
 // Raises a kernel's dynamic-LDS limit, once per process (thread-safe), to all
 // the LDS a workgroup may hold on the current device minus the kernel's static
 // LDS.  *limit receives that number of bytes; a launch asking for more must be
 // refused by the caller.
-// compute units of the current device (cached per device)
-int compute_units();
-
 hipError_t allow_full_dynamic_lds(const void *kernel, std::once_flag &once, hipError_t &err, int &limit);
 
 // ---------------------------------------------------------------------------
