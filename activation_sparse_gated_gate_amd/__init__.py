@@ -31,7 +31,8 @@ EXPORTS = ("sffn_workspace_size", "sffn_create", "sffn_select", "sffn_forward", 
            "sffn_status_string", "sffn_last_hip_error", "sffn_set_kernel_timer", "sffn_expert_select",
            "sffn_select_blocks", "sffn_schedule_mass", "sffn_neuron_counts", "sffn_frequency_order",
            "sffn_decode_block_rows", "sffn_create_permuted", "sffn_read_probe", "sffn_forward_noalloc",
-           "sffn_noalloc_scratch_bytes", "sffn_read_probe_cfg", "sffn_read_latency_probe")
+           "sffn_noalloc_scratch_bytes", "sffn_read_probe_cfg", "sffn_read_latency_probe",
+           "sffn_token_select_path")
 
 
 class LayerDesc(C.Structure):
@@ -117,6 +118,8 @@ def _load():
     lib.sffn_read_probe_cfg.argtypes = [P, Z, C.POINTER(ProbeCfg), P, P]
     lib.sffn_read_latency_probe.restype = I
     lib.sffn_read_latency_probe.argtypes = [P, Z, I, P, I, P, P]
+    lib.sffn_token_select_path.restype = I
+    lib.sffn_token_select_path.argtypes = [P, P, Z, P, P]
     lib.sffn_create_permuted.restype = I
     lib.sffn_create_permuted.argtypes = [C.POINTER(LayerDesc), P, P, P, P, P, Z, P, C.POINTER(P)]
     return lib
@@ -312,6 +315,17 @@ class Layer:
                          self._stream(stream))
         if st != SFFN_OK:
             raise SffnError(st, "sffn_select")
+
+    def token_select_path(self, stream=None) -> int:
+        """Which path made the last token selection on this layer's scratch:
+        1 the exact-mass radix select, 0 the sort (sffn_token_select_path)."""
+        import torch
+        out = torch.full((1,), -1, dtype=torch.int32, device=self.scratch.device)
+        st = _lib.sffn_token_select_path(self.handle, self.scratch.data_ptr(), self.scratch_bytes,
+                                         out.data_ptr(), self._stream(stream))
+        if st != SFFN_OK:
+            raise SffnError(st, "sffn_token_select_path")
+        return int(out.item())
 
     def select_blocks(self, policy: BlockPolicy, A, cu_seqlens, idx_out, count_out, stream=None):
         st = sffn_select_blocks(self.handle, policy, A.data_ptr(), A.shape[0], cu_seqlens.data_ptr(),

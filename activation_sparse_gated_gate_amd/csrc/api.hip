@@ -90,7 +90,9 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         S.path = (D.layouts & SFFN_LAYOUT_BATCH) ? take(256) : 0;   // the chosen forward path
     }
     if (D.layouts & SFFN_LAYOUT_PREFILL) {
-        S.tscore = take(B * 4 * 2);   // scores and their sorted copy
+        // scores and their sorted copy; at least round_up(B, 16) floats, which the
+        // exact-mass selection reads 16 at a time
+        S.tscore = take(std::max(B * 4 * 2, (B + 15) / 16 * 16 * 4));
         S.tflag = take(B * 4);
         S.pH = take(B * f * 2);       // H (bf16) for up to L gathered rows
         // token sort keys: the sorted chunks of 1024 (the last one padded), then the full order
@@ -100,6 +102,7 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         // (sffn_forward in TOKENS mode reads them when it is given no list)
         S.tkeep = take(B * 4);
         S.tkcnt = take(4);
+        S.tdone = take(4);   // 1 when the exact-mass path made the last token selection
     }
     S.total = o;
     return S;
@@ -365,6 +368,18 @@ sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void 
     t.n = n;
     t.next = 0;
     return SFFN_OK;
+}
+
+sffn_status sffn_token_select_path(sffn_t layer, const void *scratch, size_t scratch_bytes, int32_t *path,
+                                   void *stream)
+{
+    if (!layer || !scratch || !path) return SFFN_ERR_INVALID_ARG;
+    const sffn_layer_desc &D = layer->L.desc;
+    if (!(D.layouts & SFFN_LAYOUT_PREFILL)) return SFFN_ERR_INVALID_ARG;
+    const ScratchLayout S = scratch_layout(D);
+    if (scratch_bytes < S.total) return SFFN_ERR_WORKSPACE;
+    return hip_status(hipMemcpyAsync(path, (const uint8_t *)scratch + S.tdone, 4, hipMemcpyDeviceToDevice,
+                                     (hipStream_t)stream));
 }
 
 static bool decode_mode(int m)

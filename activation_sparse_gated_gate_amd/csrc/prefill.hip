@@ -74,6 +74,7 @@ struct SelectArgs {
     double mass;
     int32_t *keep, *count;
     int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
+    const int32_t *skip;               // nonzero: the exact-mass path made the selection
 };
 
 __device__ __forceinline__ uint64_t rank_key(float s, int i)
@@ -159,8 +160,10 @@ __device__ __forceinline__ void bitonic_merge_k(uint64_t &v, int tid, uint64_t (
     bitonic_in_wave<K, (K >> 1) < 32 ? (K >> 1) : 32>(v, tid);
 }
 
-__global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks)
+__global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks,
+                                                      const int32_t *__restrict__ skip)
 {
+    if (*skip) return;
     __shared__ uint64_t buf[2][1024];
     const int tid = threadIdx.x;
     const int i = blockIdx.x * 1024 + tid;
@@ -185,8 +188,9 @@ __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ 
 // are small, so the first five steps hit few LDS words; only the last five
 // read the full chunks at scattered addresses.
 __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict__ chunks, int G,
-                                                      uint64_t *__restrict__ sorted)
+                                                      uint64_t *__restrict__ sorted, const int32_t *__restrict__ skip)
 {
+    if (*skip) return;
     extern __shared__ __align__(16) uint64_t all[];   // [G][1024]
     constexpr int GMAX = kMaxPrefillRows / 1024;
     __shared__ uint64_t spl[GMAX][32];
@@ -252,6 +256,72 @@ __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict
     sorted[rank] = key;
 }
 
+// Positions in ascending token order of flagged tokens, 1024 threads: bit q of
+// a thread's flags is token q * 1024 + tid.  The flagged count of every (round
+// q, wave) goes to LDS, one thread per round turns its row into wave offsets,
+// then one thread turns the round totals into round offsets (three barriers,
+// none between global stores and LDS traffic).  A flagged token of round q then
+// sits at qbase[q] + wbase[q][wave] + its rank among the flagged lanes of its
+// wave; qbase[16] is the number of flagged tokens.
+static_assert(kMaxPrefillRows == 16 * 1024, "16 rounds of 1024 tokens");
+struct OrderScan {
+    int wbase[16][16];
+    int qbase[17];
+};
+
+__device__ __forceinline__ void order_scan(uint32_t fb, OrderScan &os)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const uint64_t m = __ballot((fb >> q) & 1u);
+        if (lane == 0) os.wbase[q][wave] = __popcll(m);
+    }
+    __syncthreads();
+    if (tid < 16) {
+        int run = 0;
+        for (int w2 = 0; w2 < 16; ++w2) {
+            const int c2 = os.wbase[tid][w2];
+            os.wbase[tid][w2] = run;
+            run += c2;
+        }
+        os.qbase[tid] = run;   // the round's total for now
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int q = 0; q < 16; ++q) {
+            const int t = os.qbase[q];
+            os.qbase[q] = run;
+            run += t;
+        }
+        os.qbase[16] = run;
+    }
+    __syncthreads();
+}
+
+// the position of round q's token of this thread (meaningful when it is flagged);
+// every lane of the wave must call it
+__device__ __forceinline__ int order_pos(uint32_t fb, int q, const OrderScan &os)
+{
+    const uint64_t m = __ballot((fb >> q) & 1u);
+    return os.qbase[q] + os.wbase[q][threadIdx.x >> 6] + mbcnt64(m);
+}
+
+// the ascending keep list of the tokens flagged in onb, into both copies
+__device__ __forceinline__ void write_keep(uint32_t onb, const OrderScan &os, int32_t *keep, int32_t *keep_copy)
+{
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int pos = order_pos(onb, q, os);
+        if ((onb >> q) & 1u) {
+            const int i = q * 1024 + (int)threadIdx.x;
+            keep[pos] = i;
+            keep_copy[pos] = i;
+        }
+    }
+}
+
 // The selection proper, one workgroup.  The sorted order is held in LDS as
 // the fp32 scores, block by block of kMassBlock entries with one word of
 // padding per block (so the 64 threads that each walk one block read
@@ -268,6 +338,7 @@ __device__ __forceinline__ int mass_slot(int r) { return (r / kMassBlock) * kMas
 
 __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
 {
+    if (*a.skip) return;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     constexpr int NBMAX = kMaxPrefillRows / kMassBlock;
     constexpr int NCP = kMassBlock / 32;
@@ -412,54 +483,328 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
         }
     }
     __syncthreads();
-    // ascending keep list: thread tid holds tokens q NT + tid; the kept count of
-    // every (round q, wave) goes to LDS, one thread per round turns them into
-    // offsets, then every thread writes its kept tokens (two barriers in all,
-    // none between global stores and LDS traffic)
-    constexpr int PER = kMaxPrefillRows / 1024;
-    __shared__ int wcnt[PER][16];
-    __shared__ int qbase[PER + 1];
     uint32_t onb = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
+    for (int q = 0; q < kMaxPrefillRows / 1024; ++q) {
         const int i = q * NT + tid;
-        const bool on = i < L && in[i];
-        onb |= on ? (1u << q) : 0u;
-        const uint64_t m = __ballot(on);
-        if (lane == 0) wcnt[q][wave] = __popcll(m);
+        onb |= (i < L && in[i]) ? (1u << q) : 0u;
     }
-    __syncthreads();
-    if (tid < PER) {
-        int run = 0;
-        for (int w2 = 0; w2 < 16; ++w2) {
-            const int c2 = wcnt[tid][w2];
-            wcnt[tid][w2] = run;
-            run += c2;
-        }
-        qbase[tid] = run;   // the round's total for now
-    }
-    __syncthreads();
+    __shared__ OrderScan os;
+    order_scan(onb, os);
     if (tid == 0) {
-        int run = 0;
-        for (int q = 0; q < PER; ++q) {
-            const int t = qbase[q];
-            qbase[q] = run;
-            run += t;
+        *a.count = os.qbase[16];
+        *a.count_copy = os.qbase[16];
+    }
+    write_keep(onb, os, a.keep, a.keep_copy);
+}
+
+// ---------------------------------------------------------------------------
+// t2, exact-mass path (one workgroup of 1024 threads).
+// The scores are >= 0.  Let u be the ulp of the smallest nonzero score: every
+// score is an integer multiple of u, and so is every partial sum of scores.
+// When the total is at most 2^53 u, every partial sum the blocked fp64 prefix
+// forms (inside a block, of the block totals, and a block base plus a partial
+// block) is a multiple of u no larger than 2^53 u, so it is an fp64 number:
+// each addition is exact, and the prefix at rank m is the exact sum of the
+// m + 1 largest scores, whatever the order of the additions.  The shortest
+// prefix is then fixed by the threshold score alone, found by a radix select
+// on the score bits with the mass of every digit summed as an integer in units
+// of u (integer sums do not depend on the order of the atomics).  The ties at
+// the threshold score are taken in ascending index order, as the sorted order
+// does.  Scores outside the condition (negative, infinite or NaN, more than
+// 2^26 between the largest and the smallest nonzero score -- which also keeps
+// every integer sum below 2^64 -- or a total above 2^53 u), a threshold that
+// underflows to zero, or a min_keep that the prefix and the recent window do
+// not reach leave *done = 0: the sorted path then makes the selection.
+// Thread t holds the 16 consecutive tokens 16 t .. 16 t + 15.
+struct MassSelectArgs {
+    const float *s;   // L scores; the array spans at least round_up(L, 16) floats
+    int L, recent_n, min_keep;
+    double mass;
+    int32_t *keep, *count;
+    int32_t *keep_copy, *count_copy;
+    int32_t *done;   // 1: the selection is made; 0: the sorted path makes it
+};
+
+// maximum over the wave, in every lane: lane swaps for xor 32 and 16, row
+// rotations by 8 and 4 (after the first, lanes i and i ^ 8 agree, so the
+// rotation by 4 reads the value of lane i ^ 4), quad permutations for 2 and 1.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
+{
+    const int lane = threadIdx.x & 63;
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = max(v, (uint32_t)(lane < 32 ? p[1] : p[0]));
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max(v, (uint32_t)((lane & 16) ? p[0] : p[1]));
+    }
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));   // row_ror:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));   // row_ror:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));    // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));    // quad [1,0,3,2]
+    return v;
+}
+
+// one step of a DPP prefix over 64-bit values (both halves moved, 0 where the
+// source lane lies outside the pattern)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+    return v + (((uint64_t)hi << 32) | lo);
+}
+
+// inclusive prefix over the 64 lanes (the steps of wave_incl_scan on 64 bits)
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
+{
+    v = dpp_add_u64<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add_u64<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add_u64<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add_u64<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add_u64<0x142, 0xa>(v);   // row_bcast:15
+    v = dpp_add_u64<0x143, 0xc>(v);   // row_bcast:31
+    return v;
+}
+
+// exclusive prefix of one int per thread over the 1024 threads (one barrier;
+// wcnt[16] must not be reused before another barrier)
+__device__ __forceinline__ int block1024_exclusive(int v, int *wcnt, int *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wcnt[wave] = incl;
+    __syncthreads();
+    int below = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+        const int t = wcnt[w2];
+        tot += t;
+        below += w2 < wave ? t : 0;
+    }
+    *total = tot;
+    return below + incl - v;
+}
+
+// a nonzero score of bits b (at most 0x7F7FFFFF, exponent field at least emin)
+// in units of u = 2^(emin - 150): its significand shifted left by the exponent
+// difference (below 2^50 when that difference is at most 26)
+__device__ __forceinline__ uint64_t score_units(uint32_t b, int emin)
+{
+    const uint32_t e = max(b >> 23, 1u);
+    const uint64_t sig = (b & 0x7FFFFFu) | (b >= 0x800000u ? 0x800000u : 0u);
+    return sig << (e - (uint32_t)emin);
+}
+
+// One radix pass over the score bits.  Candidates are the tokens whose bits
+// above the digit (b >> SHIFT) & (NB - 1) equal `prefix`; hm[d] receives the
+// integer mass of digit d.  The cumulative mass counted from the largest digit
+// down, starting at `above` (the mass of the tokens above every candidate),
+// first reaches thr inside exactly one digit: the return value.  `above`
+// becomes the mass above that digit, `bin` the digit's own mass.  The first
+// pass (every token a candidate) also takes the total T from its sums, returns
+// -1 when T exceeds 2^53 or mass * T underflows to zero, and sets thr.  hm[0, NB)
+// is zero on entry and on return.
+template <int NB, int SHIFT, bool FIRST>
+__device__ __forceinline__ int mass_radix_pass(const uint32_t (&b)[16], int emin, uint32_t valid, uint32_t prefix,
+                                               double mass, double u, double &thr, uint64_t &above, uint64_t &bin,
+                                               uint64_t *hm, uint64_t *wtot, int *s_dig, uint64_t *s_res)
+{
+    constexpr int W = NB == 4096 ? 12 : NB == 1024 ? 10 : 9;
+    static_assert((1 << W) == NB, "digit width");
+    constexpr int BPT = NB >= 1024 ? NB / 1024 : 1;   // digits per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (((valid >> k) & 1u) && b[k] != 0u && (FIRST || (b[k] >> (SHIFT + W)) == prefix))
+            atomicAdd((unsigned long long *)&hm[(b[k] >> SHIFT) & (NB - 1)],
+                      (unsigned long long)score_units(b[k], emin));
+    __syncthreads();
+    const bool owns = tid * BPT < NB;
+    uint64_t loc[BPT];
+    uint64_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        loc[k] = owns ? hm[tid * BPT + k] : 0ull;
+        sum += loc[k];
+    }
+#pragma unroll
+    for (int k = 0; k < BPT; ++k)
+        if (owns) hm[tid * BPT + k] = 0ull;   // for the next pass (after the barriers below)
+    const uint64_t incl = wave_incl_scan_u64(sum);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    uint64_t total = 0, below = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+        const uint64_t t = wtot[w2];
+        total += t;
+        below += w2 < wave ? t : 0ull;
+    }
+    if (FIRST) {
+        if (total > (1ull << 53)) return -1;
+        thr = mass * ((double)total * u);   // mass * total, the total exact
+        if (!(thr > 0.0)) return -1;
+    }
+    // mass of the candidates above this thread's digits, then down its digits;
+    // the integers are at most 2^53 and u is a power of two, so every product is
+    // the exact mass and the comparison is the blocked prefix's own
+    uint64_t cum = above + (total - (incl + below));
+#pragma unroll
+    for (int k = BPT - 1; k >= 0; --k) {
+        const uint64_t nxt = cum + loc[k];
+        if (owns && (double)nxt * u >= thr && (double)cum * u < thr) {
+            *s_dig = tid * BPT + k;
+            s_res[0] = cum;
+            s_res[1] = loc[k];
         }
-        qbase[PER] = run;
-        *a.count = run;
-        *a.count_copy = run;
+        cum = nxt;
     }
     __syncthreads();
+    above = s_res[0];
+    bin = s_res[1];
+    return *s_dig;
+}
+
+__global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs a)
+{
+    __shared__ uint64_t hm[4096];
+    __shared__ uint64_t wtot[16];
+    __shared__ uint32_t wred[2][16];
+    __shared__ int wcnt[2][16];
+    __shared__ int s_dig, s_j;
+    __shared__ uint64_t s_res[2];
+    const int L = a.L, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // four 16-byte loads per thread, unconditional: threads past the end read
+    // the last 16 floats of the padded array (masked below)
+    uint32_t b[16];
+    {
+        const int base = min(16 * tid, ((L + 15) & ~15) - 16);
+        const uint4 *p = (const uint4 *)(a.s + base);
+        uint4 v[4];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int i = q * NT + tid;
-        const bool on = (onb >> q) & 1u;
-        const uint64_t m = __ballot(on);
-        if (on) {
-            const int pos = qbase[q] + wcnt[q][wave] + mbcnt64(m);
-            a.keep[pos] = i;
-            a.keep_copy[pos] = i;
+        for (int m = 0; m < 4; ++m) v[m] = p[m];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            b[4 * m] = v[m].x;
+            b[4 * m + 1] = v[m].y;
+            b[4 * m + 2] = v[m].z;
+            b[4 * m + 3] = v[m].w;
+        }
+    }
+    const int nv = min(max(L - 16 * tid, 0), 16);
+    const uint32_t valid = nv >= 16 ? 0xFFFFu : (1u << nv) - 1u;
+    for (int i = tid; i < 4096; i += 1024) hm[i] = 0ull;
+    // the largest score bits (above 0x7F7FFFFF: negative, infinite or NaN) and
+    // the smallest exponent field of a nonzero score, 1 for subnormals (they
+    // share exponent 1's ulp)
+    uint32_t bmax = 0, emn = 255;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if ((valid >> k) & 1u) {
+            bmax = max(bmax, b[k]);
+            if (b[k] - 1u < 0x7F7FFFFFu) emn = min(emn, max(b[k] >> 23, 1u));
+        }
+    }
+    bmax = wave_max_dpp(bmax);
+    const uint32_t nemn = wave_max_dpp(255u - emn);
+    if (lane == 0) {
+        wred[0][wave] = bmax;
+        wred[1][wave] = nemn;
+    }
+    __syncthreads();
+    uint32_t gmax = 0, gne = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+        gmax = max(gmax, wred[0][w2]);
+        gne = max(gne, wred[1][w2]);
+    }
+    const int emin = 255 - (int)gne;   // 255 when every score is zero
+    const int emax = max((int)(gmax >> 23), 1);
+    // mass >= 1 keeps every token whatever the scores; so does a zero total
+    const bool all = a.mass >= 1.0 || gmax == 0u;
+    if (!all && (gmax > 0x7F7FFFFFu || emax - emin > 26)) {
+        if (tid == 0) *a.done = 0;
+        return;
+    }
+    bool prefix = false;
+    uint32_t sb = 0;
+    int j = 0, c_eq = 0;
+    if (!all && a.mass > 0.0) {
+        const double u = __longlong_as_double((long long)(emin - 150 + 1023) << 52);   // 2^(emin - 150), normal in fp64
+        double thr = 0.0;
+        uint64_t above = 0, bin = 0;
+        const int d1 = mass_radix_pass<4096, 19, true>(b, emin, valid, 0u, a.mass, u, thr, above, bin, hm, wtot,
+                                                       &s_dig, s_res);
+        if (d1 < 0) {
+            if (tid == 0) *a.done = 0;
+            return;
+        }
+        const int d2 = mass_radix_pass<1024, 9, false>(b, emin, valid, (uint32_t)d1, a.mass, u, thr, above, bin, hm,
+                                                       wtot, &s_dig, s_res);
+        const int d3 = mass_radix_pass<512, 0, false>(b, emin, valid, ((uint32_t)d1 << 10) | (uint32_t)d2, a.mass, u,
+                                                      thr, above, bin, hm, wtot, &s_dig, s_res);
+        sb = ((uint32_t)d1 << 19) | ((uint32_t)d2 << 9) | (uint32_t)d3;
+        // the digit holds c_eq tokens of score sb (its mass is > 0, so sb > 0);
+        // the prefix takes the fewest j of them with above + j q* reaching thr
+        const uint64_t qs = score_units(sb, emin);
+        c_eq = (int)(bin / qs);
+        if (tid == 0) {
+            const double u_inv = __longlong_as_double((long long)(150 - emin + 1023) << 52);
+            long long jj = (long long)ceil((thr * u_inv - (double)above) / (double)qs);
+            jj = jj < 1 ? 1 : jj > c_eq ? c_eq : jj;
+            while (jj > 1 && (double)(above + (uint64_t)(jj - 1) * qs) * u >= thr) --jj;
+            while (jj < c_eq && (double)(above + (uint64_t)jj * qs) * u < thr) ++jj;
+            s_j = (int)jj;
+        }
+        __syncthreads();
+        j = s_j;
+        prefix = true;
+    }
+    const int r0 = L - min(a.recent_n, L);
+    uint32_t onb = 0, tie = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const bool hi = prefix && b[k] > sb;
+        const bool eq = prefix && b[k] == sb;
+        onb |= (all || hi || 16 * tid + k >= r0) ? (1u << k) : 0u;
+        tie |= eq ? (1u << k) : 0u;
+    }
+    onb &= valid;
+    tie &= valid;
+    if (j == c_eq) {
+        onb |= tie;
+    } else {
+        // the j lowest-indexed tokens of score sb
+        int nt;
+        int r = block1024_exclusive(__popc(tie), wcnt[0], &nt);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if ((tie >> k) & 1u) {
+                onb |= r < j ? (1u << k) : 0u;
+                ++r;
+            }
+        }
+    }
+    int n;
+    int pos = block1024_exclusive(__popc(onb), wcnt[1], &n);
+    if (!all && n < a.min_keep) {
+        if (tid == 0) *a.done = 0;
+        return;
+    }
+    if (tid == 0) {
+        *a.count = n;
+        *a.count_copy = n;
+        *a.done = 1;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if ((onb >> k) & 1u) {
+            a.keep[pos] = 16 * tid + k;
+            a.keep_copy[pos] = 16 * tid + k;
+            ++pos;
         }
     }
 }
@@ -893,13 +1238,20 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     if (lds > (size_t)lim_sel || (size_t)G * 1024 * 8 > (size_t)lim_merge) return hipErrorInvalidConfiguration;
     uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);     // ceil(rows / 1024) * 1024 keys
     uint64_t *sorted = (uint64_t *)(c.scratch + S.tsorted);   // rows keys
-    hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks);
+    int32_t *done = (int32_t *)(c.scratch + S.tdone);
+    // the exact-mass path first; the sorted path's kernels return at once when it made the selection
+    MassSelectArgs ma{sc_s, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
+                      (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), done};
+    hipLaunchKernelGGL(k_token_mass_select, dim3(1), dim3(1024), 0, c.stream, ma);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks,
+                       (const int32_t *)done);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_tsort_merge, dim3(G), dim3(1024), (size_t)G * 1024 * 8, c.stream, (const uint64_t *)chunks, G,
-                       sorted);
+                       sorted, (const int32_t *)done);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
-                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt)};
+                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), (const int32_t *)done};
     hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
     return hipGetLastError();
 }

@@ -107,7 +107,7 @@ PersistentLayout persistent_layout(const sffn_layer_desc &d);
 struct ScratchLayout {
     size_t xhat, G, U, keys, bits, list_cnt, list_idx, partial, H;       // decode
     size_t xsplit, hsplit, gpart, path;                                  // decode, batches (BATCH layout)
-    size_t tscore, tflag, pH, tkeys, tsorted, tkeep, tkcnt;              // prefill
+    size_t tscore, tflag, pH, tkeys, tsorted, tkeep, tkcnt, tdone;       // prefill
     size_t total;
     int n_lists_gate, rows_per_list_gate;
 };

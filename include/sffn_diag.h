@@ -76,6 +76,18 @@ sffn_status sffn_read_latency_probe(const void *buf, size_t bytes, int32_t row_b
 sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void *const *end_events,
                                   int32_t n);
 
+/*
+ * Which of the two paths of the token selection (sffn_select with a TOKENS
+ * policy) made the last selection on this scratch: copies 1 (the exact-mass
+ * radix select, taken when every partial sum of the scores is exact in fp64)
+ * or 0 (the sort of all scores) into *path (device, one int32), asynchronously
+ * on `stream`.  Meaningful only after such a selection.  SFFN_ERR_INVALID_ARG
+ * for a null pointer or a layer without the PREFILL layout,
+ * SFFN_ERR_WORKSPACE for a scratch smaller than the layer's.
+ */
+sffn_status sffn_token_select_path(sffn_t layer, const void *scratch, size_t scratch_bytes, int32_t *path,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,6 +115,51 @@ def test_selection_edge_cases(small):
     assert check_select(layer, T, 0.5, 0, 1)[2].size == L // 2
 
 
+def _rows_with_scores(v, d=256):
+    """Attention rows whose norm is exactly |v_i| (bf16): one nonzero element
+    per row (its square and square root are exact in fp32)."""
+    A = np.zeros((v.size, d), np.uint16)
+    A[:, 3] = synth.f32_to_bf16_bits(v.astype(np.float32))
+    return A
+
+
+@pytest.fixture(scope="module")
+def mid():
+    w = synth._make_weights(synth.WT_BF16, 256, 512, synth.ACT_SILU, (721, 722, 723))
+    layer = make_prefill_layer(w, 3000)
+    yield layer
+    layer.close()
+
+
+@pytest.mark.parametrize("kind", ["lognormal", "small_ints", "equal", "wide"])
+def test_exact_mass_and_sorted_paths(mid, kind):
+    """Both paths of the selection against the oracle, keep lists bit-exact.
+    Scores whose partial sums are all exact in fp64 (range at most 2^29 and
+    total at most 2^53 ulps of the smallest nonzero score, with at most 2^26
+    between the largest and the smallest nonzero score) take the exact-mass
+    radix select, ties at the threshold included; a wider range takes the sort.
+    3000 tokens: three rounds of 1024 and a ragged tail."""
+    rng = np.random.default_rng({"lognormal": 1, "small_ints": 2, "equal": 3, "wide": 4}[kind])
+    L = 3000
+    v = {"lognormal": lambda: 71.6 * np.exp(rng.standard_normal(L)),
+         "small_ints": lambda: rng.integers(0, 5, L).astype(np.float64),
+         "equal": lambda: np.full(L, 3.25),
+         "wide": lambda: np.exp(6.0 * rng.standard_normal(L))}[kind]()
+    A = _rows_with_scores(v)
+    for mass, recent, mk in ((0.3, 0, 1), (0.5, 16, 1), (0.77, 5, 3), (0.999, 0, 1), (1.0, 0, 1),
+                             (0.0, 0, 1), (0.05, 0, 200)):
+        keep = check_select(mid, A, mass, recent, mk)[2]
+        path = mid.token_select_path()
+        if mass >= 1.0:
+            assert path == 1, (kind, mass)              # every token, whatever the scores
+        elif kind == "wide":
+            assert path == 0, (kind, mass)              # the range alone rules the exact path out
+        elif mass == 0.0:
+            assert path == 0, (kind, mass)              # empty prefix, min_keep from the sorted order
+        elif mk <= 3:
+            assert path == 1, (kind, mass, recent, mk)  # mk = 200 may exceed the prefix: either path
+
+
 @pytest.mark.parametrize("L", [1, 7, 129, 300])
 def test_ragged_lengths(L):
     w = synth._make_weights(synth.WT_BF16, 256, 512, synth.ACT_SILU, (711, 712, 713))
@@ -166,6 +211,8 @@ def test_cfg5_selection_and_every_tile(cfg5, mass):
     compared with the oracle; un-kept rows bitwise equal to Y."""
     w, Y, A, layer = cfg5
     keep_t, cnt_t, keep = check_select(layer, A, mass, synth.CFG5_RECENT, synth.CFG5_MIN_KEEP)
+    # the workload's scores keep every partial sum exact: no sort
+    assert layer.token_select_path() == 1
     X = gpu_forward(layer, Y, keep_t, cnt_t)
     Xk = synth.bf16_bits_to_f32(X[keep])
     assert np.isfinite(Xk).all(), "kept rows not written (NaN fill left) or non-finite"
