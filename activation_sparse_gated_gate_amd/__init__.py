@@ -318,7 +318,7 @@ class Layer:
 
     def token_select_path(self, stream=None) -> int:
         """Which path made the last token selection on this layer's scratch:
-        1 the exact-mass radix select, 0 the sort (sffn_token_select_path)."""
+        1 the exact-mass radix select, 2 the sort (sffn_token_select_path)."""
         import torch
         out = torch.full((1,), -1, dtype=torch.int32, device=self.scratch.device)
         st = _lib.sffn_token_select_path(self.handle, self.scratch.data_ptr(), self.scratch_bytes,

@@ -102,7 +102,9 @@ ScratchLayout scratch_layout(const sffn_layer_desc &D)
         // (sffn_forward in TOKENS mode reads them when it is given no list)
         S.tkeep = take(B * 4);
         S.tkcnt = take(4);
-        S.tdone = take(4);   // 1 when the exact-mass path made the last token selection
+        // the token selection's path and arrival words: [0] 1 when the exact-mass
+        // path made the last selection, 2 when the sorted path did
+        S.tdone = take(3 * 4);
     }
     S.total = o;
     return S;

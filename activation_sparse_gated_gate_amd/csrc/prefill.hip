@@ -5,15 +5,17 @@
 // only on the important tokens S, Z[~S] = 0 and X_next = Y + Z.
 //   t1 k_token_norms   s_i = ||A_i||_2 (attention output row), sum of squares in
 //                      the fixed fp32 order (64 lane accumulators), IEEE sqrt.
-//   t2 k_tsort_chunk / k_tsort_merge sort the (score, index) keys descending
-//                      (chunks of 1024 in LDS, then exact merge ranks);
-//      k_token_select  (one workgroup) fp64 cumulative mass in blocks of 256 sorted entries,
-//                      shortest prefix reaching mass * total, plus the last
-//                      recent_n tokens, plus top-ranked tokens up to min_keep;
-//                      mass >= 1, total == 0 or a non-finite total keeps every
-//                      token.  Writes the
-//                      ascending keep list, its length and per-token flags, all
-//                      on the device (no host synchronisation).
+//   t2 k_token_select  fp64 cumulative mass of the scores in descending order, in
+//                      blocks of 256, shortest prefix reaching mass * total, plus
+//                      the last recent_n tokens, plus top-ranked tokens up to
+//                      min_keep; mass >= 1, total == 0 or a non-finite total
+//                      keeps every token.  When every partial sum is exact in
+//                      fp64, a radix select on the score bits finds the prefix
+//                      with no sort (one workgroup); otherwise the (score, index)
+//                      keys are sorted (chunks of 1024 in LDS, then exact merge
+//                      ranks) and the blocked prefix is taken in order.  Writes
+//                      the ascending keep list and its length, all on the device
+//                      (no host synchronisation).
 //   t3 k_gemm_big<GATE_UP> H = SiLU(Y_S W_gate^T) (.) (Y_S W_up^T), bf16 MFMA with
 //                      the A rows gathered through the keep list and the gate /
 //                      up columns of the same neurons in one tile (the weights
@@ -25,6 +27,8 @@
 // is sized for the largest count without a host round trip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "dev_common.h"
 
 namespace sffn {
@@ -32,11 +36,13 @@ namespace sffn {
 // ---------------------------------------------------------------------------
 // t1: token norms
 // ---------------------------------------------------------------------------
+// zero3 (or null): three words the selection kernel that follows finds zero
 __global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict__ A, int L, int d,
-                                                     float *__restrict__ s)
+                                                     float *__restrict__ s, int32_t *__restrict__ zero3)
 {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (zero3 && blockIdx.x == 0 && threadIdx.x < 3) zero3[threadIdx.x] = 0;
     if (row >= L) return;
     const int nch = d / 8;
     const uint8_t *rp = (const uint8_t *)(A + (size_t)row * d);
@@ -68,13 +74,16 @@ __global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict_
 // t2: token selection (one workgroup of 1024 threads)
 // ---------------------------------------------------------------------------
 struct SelectArgs {
-    const float *s;
-    const uint64_t *sorted;   // the L keys in descending order
+    const float *s;           // L scores; the array spans at least round_up(L, 16) floats
     int L, recent_n, min_keep;
     double mass;
     int32_t *keep, *count;
     int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
-    const int32_t *skip;               // nonzero: the exact-mass path made the selection
+    uint64_t *chunks;         // ceil(L / 1024) chunks of 1024 keys, each sorted descending
+    uint64_t *sorted;         // the L keys in descending order
+    // [0] the path taken (0 undecided, 1 exact mass, 2 sorted), [1] chunks
+    // sorted, [2] chunks merged; zero when the selection starts
+    int32_t *sync;
 };
 
 __device__ __forceinline__ uint64_t rank_key(float s, int i)
@@ -83,9 +92,9 @@ __device__ __forceinline__ uint64_t rank_key(float s, int i)
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
-// t2, sort in two steps.  k_tsort_chunk: every workgroup sorts 1024 keys
-// descending in LDS (padding keys are 0, below every token's key).
-// k_tsort_merge: the keys are unique (the index is part of the key), so the
+// t2, sorted path, sort in two steps.  tsort_chunk: every workgroup sorts 1024
+// keys descending in LDS (padding keys are 0, below every token's key).
+// tsort_merge: the keys are unique (the index is part of the key), so the
 // global rank of a key is its place in its chunk plus, for every other chunk,
 // the number of larger keys there (a binary search); the key is written to that
 // rank.  The result is the full descending order.
@@ -160,14 +169,11 @@ __device__ __forceinline__ void bitonic_merge_k(uint64_t &v, int tid, uint64_t (
     bitonic_in_wave<K, (K >> 1) < 32 ? (K >> 1) : 32>(v, tid);
 }
 
-__global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ s, int L, uint64_t *__restrict__ chunks,
-                                                      const int32_t *__restrict__ skip)
+__device__ __forceinline__ void tsort_chunk(const SelectArgs &a, int c, uint64_t (&buf)[2][1024])
 {
-    if (*skip) return;
-    __shared__ uint64_t buf[2][1024];
     const int tid = threadIdx.x;
-    const int i = blockIdx.x * 1024 + tid;
-    uint64_t v = i < L ? rank_key(s[i], i) : 0ull;
+    const int i = c * 1024 + tid;
+    uint64_t v = i < a.L ? rank_key(a.s[i], i) : 0ull;
     int nb = 0;
     bitonic_merge_k<2>(v, tid, buf, nb);
     bitonic_merge_k<4>(v, tid, buf, nb);
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ 
     bitonic_merge_k<256>(v, tid, buf, nb);
     bitonic_merge_k<512>(v, tid, buf, nb);
     bitonic_merge_k<1024>(v, tid, buf, nb);
-    chunks[(size_t)blockIdx.x * 1024 + tid] = v;
+    a.chunks[(size_t)c * 1024 + tid] = v;
 }
 
 // The rank search runs on two levels: every chunk's 32 splitters (the last,
@@ -187,11 +193,9 @@ __global__ __launch_bounds__(1024) void k_tsort_chunk(const float *__restrict__ 
 // then a search inside the one run that straddles it.  The splitter tables
 // are small, so the first five steps hit few LDS words; only the last five
 // read the full chunks at scattered addresses.
-__global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict__ chunks, int G,
-                                                      uint64_t *__restrict__ sorted, const int32_t *__restrict__ skip)
+__device__ __forceinline__ void tsort_merge(const SelectArgs &a, int G, int c, uint64_t *all /* [G][1024] */)
 {
-    if (*skip) return;
-    extern __shared__ __align__(16) uint64_t all[];   // [G][1024]
+    const uint64_t *chunks = a.chunks;
     constexpr int GMAX = kMaxPrefillRows / 1024;
     __shared__ uint64_t spl[GMAX][32];
     {
@@ -207,9 +211,8 @@ __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict
         }
     }
     __syncthreads();
-    const int c = blockIdx.x, p = threadIdx.x;
-    const uint64_t key = all[c * 1024 + p];
-    if (key == 0) return;   // padding
+    const int p = threadIdx.x;
+    const uint64_t key = all[c * 1024 + p];   // 0: padding, not written
     // in every other chunk, the number of keys above this key (a chunk is sorted
     // descending): branch-free binary searches of all chunks advanced together
     // (unconditional reads, so the reads of a step are in flight at once).
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(1024) void k_tsort_merge(const uint64_t *__restrict
             rank += run[c2] == 32 ? 1024 : 32 * run[c2] + lo[c2];
         }
     }
-    sorted[rank] = key;
+    if (key != 0) a.sorted[rank] = key;
 }
 
 // Positions in ascending token order of flagged tokens, 1024 threads: bit q of
@@ -336,10 +339,8 @@ constexpr int kMassPad = kMassBlock + 1;
 
 __device__ __forceinline__ int mass_slot(int r) { return (r / kMassBlock) * kMassPad + (r % kMassBlock); }
 
-__global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
+__device__ __forceinline__ void select_sorted(const SelectArgs &a, unsigned char *lds_raw)
 {
-    if (*a.skip) return;
-    extern __shared__ __align__(16) unsigned char lds_raw[];
     constexpr int NBMAX = kMaxPrefillRows / kMassBlock;
     constexpr int NCP = kMassBlock / 32;
     const int L = a.L, tid = threadIdx.x, NT = 1024, lane = tid & 63, wave = tid >> 6;
@@ -515,16 +516,8 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
 // 2^26 between the largest and the smallest nonzero score -- which also keeps
 // every integer sum below 2^64 -- or a total above 2^53 u), a threshold that
 // underflows to zero, or a min_keep that the prefix and the recent window do
-// not reach leave *done = 0: the sorted path then makes the selection.
-// Thread t holds the 16 consecutive tokens 16 t .. 16 t + 15.
-struct MassSelectArgs {
-    const float *s;   // L scores; the array spans at least round_up(L, 16) floats
-    int L, recent_n, min_keep;
-    double mass;
-    int32_t *keep, *count;
-    int32_t *keep_copy, *count_copy;
-    int32_t *done;   // 1: the selection is made; 0: the sorted path makes it
-};
+// not reach return 2 without writing anything: the sorted path then makes the
+// selection.  Thread t holds the 16 consecutive tokens 16 t .. 16 t + 15.
 
 // maximum over the wave, in every lane: lane swaps for xor 32 and 16, row
 // rotations by 8 and 4 (after the first, lanes i and i ^ 8 agree, so the
@@ -588,51 +581,52 @@ __device__ __forceinline__ int block1024_exclusive(int v, int *wcnt, int *total)
     return below + incl - v;
 }
 
-// a nonzero score of bits b (at most 0x7F7FFFFF, exponent field at least emin)
-// in units of u = 2^(emin - 150): its significand shifted left by the exponent
-// difference (below 2^50 when that difference is at most 26)
-__device__ __forceinline__ uint64_t score_units(uint32_t b, int emin)
-{
-    const uint32_t e = max(b >> 23, 1u);
-    const uint64_t sig = (b & 0x7FFFFFu) | (b >= 0x800000u ? 0x800000u : 0u);
-    return sig << (e - (uint32_t)emin);
-}
+// A finite score >= 0 of bits b is sig(b) * 2^(uexp(b) - 150): the significand
+// (with the implicit bit of normal numbers) and the exponent that sets its ulp
+// (the exponent field, 1 for subnormals).  In units of u = 2^(emin - 150) it
+// is the integer sig(b) << (uexp(b) - emin).  Every digit of the passes below
+// lies inside one exponent (the first digit holds the 8 exponent bits), so a
+// digit sums the bare significands and its mass in units of u is that sum
+// shifted by the digit's exponent: below 2^38 << 26 = 2^64.
+__device__ __forceinline__ uint32_t score_sig(uint32_t b) { return (b & 0x7FFFFFu) | (b >= 0x800000u ? 0x800000u : 0u); }
+__device__ __forceinline__ int score_uexp(uint32_t b) { return max((int)(b >> 23), 1); }
 
-// One radix pass over the score bits.  Candidates are the tokens whose bits
-// above the digit (b >> SHIFT) & (NB - 1) equal `prefix`; hm[d] receives the
-// integer mass of digit d.  The cumulative mass counted from the largest digit
-// down, starting at `above` (the mass of the tokens above every candidate),
-// first reaches thr inside exactly one digit: the return value.  `above`
-// becomes the mass above that digit, `bin` the digit's own mass.  The first
-// pass (every token a candidate) also takes the total T from its sums, returns
-// -1 when T exceeds 2^53 or mass * T underflows to zero, and sets thr.  hm[0, NB)
-// is zero on entry and on return.
+// The digit (b >> SHIFT) & (NB - 1) of the candidates, the tokens whose bits
+// above it equal `prefix` (the first pass: every finite nonzero score): their
+// significands summed into hm (zero before).
 template <int NB, int SHIFT, bool FIRST>
-__device__ __forceinline__ int mass_radix_pass(const uint32_t (&b)[16], int emin, uint32_t valid, uint32_t prefix,
-                                               double mass, double u, double &thr, uint64_t &above, uint64_t &bin,
-                                               uint64_t *hm, uint64_t *wtot, int *s_dig, uint64_t *s_res)
+__device__ __forceinline__ void digit_sums(const uint32_t (&b)[16], uint32_t valid, uint32_t prefix, uint64_t *hm)
 {
     constexpr int W = NB == 4096 ? 12 : NB == 1024 ? 10 : 9;
     static_assert((1 << W) == NB, "digit width");
-    constexpr int BPT = NB >= 1024 ? NB / 1024 : 1;   // digits per thread
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-        if (((valid >> k) & 1u) && b[k] != 0u && (FIRST || (b[k] >> (SHIFT + W)) == prefix))
-            atomicAdd((unsigned long long *)&hm[(b[k] >> SHIFT) & (NB - 1)],
-                      (unsigned long long)score_units(b[k], emin));
-    __syncthreads();
-    const bool owns = tid * BPT < NB;
-    uint64_t loc[BPT];
+    for (int k = 0; k < 16; ++k) {
+        const bool cand = FIRST ? (b[k] - 1u < 0x7F7FFFFFu) : ((b[k] >> (SHIFT + W)) == prefix);
+        if (((valid >> k) & 1u) && cand)
+            atomicAdd((unsigned long long *)&hm[(b[k] >> SHIFT) & (NB - 1)], (unsigned long long)score_sig(b[k]));
+    }
+}
+
+// The digits' masses in units of u, this thread's BPT consecutive digits in
+// loc, scanned from the largest digit down starting at `above` (the mass of
+// the tokens above every candidate): the one digit where the cumulative mass
+// first reaches the threshold.  The threshold is held as the integer need, the
+// fewest units of u whose mass reaches thr = mass * T * u in fp64: every
+// cumulative mass is an integer m <= 2^53 and m * u is exact, so m * u >= thr
+// exactly when m >= need.  FIRST: the total T comes from the same sums; returns
+// -1 when T exceeds 2^53 or thr underflows to zero, and sets need.  Returns
+// the digit (every thread); `above` becomes the mass above it and `bin` its
+// own mass.
+template <int BPT, bool FIRST>
+__device__ __forceinline__ int digit_find(const uint64_t (&loc)[BPT], int nb, double mass, double u, int emin,
+                                          uint64_t &need, uint64_t &above, uint64_t &bin, uint64_t *wtot, int *s_dig,
+                                          uint64_t *s_res)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool owns = tid * BPT < nb;
     uint64_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-        loc[k] = owns ? hm[tid * BPT + k] : 0ull;
-        sum += loc[k];
-    }
-#pragma unroll
-    for (int k = 0; k < BPT; ++k)
-        if (owns) hm[tid * BPT + k] = 0ull;   // for the next pass (after the barriers below)
+    for (int k = 0; k < BPT; ++k) sum += loc[k];
     const uint64_t incl = wave_incl_scan_u64(sum);
     if (lane == 63) wtot[wave] = incl;
     __syncthreads();
@@ -645,17 +639,18 @@ __device__ __forceinline__ int mass_radix_pass(const uint32_t (&b)[16], int emin
     }
     if (FIRST) {
         if (total > (1ull << 53)) return -1;
-        thr = mass * ((double)total * u);   // mass * total, the total exact
+        const double thr = mass * ((double)total * u);   // mass * total, the total exact
         if (!(thr > 0.0)) return -1;
+        // thr / u scales by a power of two: exact unless it underflows, and then
+        // (or when it is below 1) the fewest units is 1
+        const double q = thr * __longlong_as_double((long long)(150 - emin + 1023) << 52);
+        need = q <= 1.0 ? 1ull : (uint64_t)ceil(q);
     }
-    // mass of the candidates above this thread's digits, then down its digits;
-    // the integers are at most 2^53 and u is a power of two, so every product is
-    // the exact mass and the comparison is the blocked prefix's own
     uint64_t cum = above + (total - (incl + below));
 #pragma unroll
     for (int k = BPT - 1; k >= 0; --k) {
         const uint64_t nxt = cum + loc[k];
-        if (owns && (double)nxt * u >= thr && (double)cum * u < thr) {
+        if (owns && nxt >= need && cum < need) {
             *s_dig = tid * BPT + k;
             s_res[0] = cum;
             s_res[1] = loc[k];
@@ -668,13 +663,15 @@ __device__ __forceinline__ int mass_radix_pass(const uint32_t (&b)[16], int emin
     return *s_dig;
 }
 
-__global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs a)
+// returns 1 when it made the selection (keep lists and counts written), 2 when
+// the sorted path must.  lds: at least max(4096 words, L ints).
+__device__ __forceinline__ int mass_select(const SelectArgs &a, unsigned char *lds)
 {
-    __shared__ uint64_t hm[4096];
+    uint64_t *hm = (uint64_t *)lds;
     __shared__ uint64_t wtot[16];
     __shared__ uint32_t wred[2][16];
     __shared__ int wcnt[2][16];
-    __shared__ int s_dig, s_j;
+    __shared__ int s_dig;
     __shared__ uint64_t s_res[2];
     const int L = a.L, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // four 16-byte loads per thread, unconditional: threads past the end read
@@ -697,15 +694,17 @@ __global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs
     const int nv = min(max(L - 16 * tid, 0), 16);
     const uint32_t valid = nv >= 16 ? 0xFFFFu : (1u << nv) - 1u;
     for (int i = tid; i < 4096; i += 1024) hm[i] = 0ull;
-    // the largest score bits (above 0x7F7FFFFF: negative, infinite or NaN) and
-    // the smallest exponent field of a nonzero score, 1 for subnormals (they
-    // share exponent 1's ulp)
+    __syncthreads();   // while the loads are in flight
+    // the first digit's sums, and beside them the largest score bits (above
+    // 0x7F7FFFFF: negative, infinite or NaN) and the smallest exponent of a
+    // nonzero score
+    digit_sums<4096, 19, true>(b, valid, 0u, hm);
     uint32_t bmax = 0, emn = 255;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         if ((valid >> k) & 1u) {
             bmax = max(bmax, b[k]);
-            if (b[k] - 1u < 0x7F7FFFFFu) emn = min(emn, max(b[k] >> 23, 1u));
+            if (b[k] - 1u < 0x7F7FFFFFu) emn = min(emn, (uint32_t)score_uexp(b[k]));
         }
     }
     bmax = wave_max_dpp(bmax);
@@ -724,43 +723,64 @@ __global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs
     const int emin = 255 - (int)gne;   // 255 when every score is zero
     const int emax = max((int)(gmax >> 23), 1);
     // mass >= 1 keeps every token whatever the scores; so does a zero total
-    const bool all = a.mass >= 1.0 || gmax == 0u;
-    if (!all && (gmax > 0x7F7FFFFFu || emax - emin > 26)) {
-        if (tid == 0) *a.done = 0;
-        return;
+    if (a.mass >= 1.0 || gmax == 0u) {
+        for (int i = tid; i < L; i += 1024) {
+            a.keep[i] = i;
+            a.keep_copy[i] = i;
+        }
+        if (tid == 0) {
+            *a.count = L;
+            *a.count_copy = L;
+        }
+        return 1;
     }
+    if (gmax > 0x7F7FFFFFu || emax - emin > 26) return 2;
     bool prefix = false;
     uint32_t sb = 0;
     int j = 0, c_eq = 0;
-    if (!all && a.mass > 0.0) {
+    if (a.mass > 0.0) {
         const double u = __longlong_as_double((long long)(emin - 150 + 1023) << 52);   // 2^(emin - 150), normal in fp64
-        double thr = 0.0;
-        uint64_t above = 0, bin = 0;
-        const int d1 = mass_radix_pass<4096, 19, true>(b, emin, valid, 0u, a.mass, u, thr, above, bin, hm, wtot,
-                                                       &s_dig, s_res);
-        if (d1 < 0) {
-            if (tid == 0) *a.done = 0;
-            return;
+        uint64_t need = 0, above = 0, bin = 0;
+        int d1;
+        {
+            // digit d holds exponent max(d >> 4, 1); a nonzero sum has it >= emin
+            uint64_t loc[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int d = tid * 4 + k;
+                const uint64_t r = hm[d];
+                loc[k] = r == 0ull ? 0ull : r << (max(d >> 4, 1) - emin);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) hm[tid * 4 + k] = 0ull;   // for the next pass (after the barriers)
+            d1 = digit_find<4, true>(loc, 4096, a.mass, u, emin, need, above, bin, wtot, &s_dig, s_res);
         }
-        const int d2 = mass_radix_pass<1024, 9, false>(b, emin, valid, (uint32_t)d1, a.mass, u, thr, above, bin, hm,
-                                                       wtot, &s_dig, s_res);
-        const int d3 = mass_radix_pass<512, 0, false>(b, emin, valid, ((uint32_t)d1 << 10) | (uint32_t)d2, a.mass, u,
-                                                      thr, above, bin, hm, wtot, &s_dig, s_res);
+        if (d1 < 0) return 2;
+        const int sh = max(d1 >> 4, 1) - emin;   // the exponent of every later candidate
+        digit_sums<1024, 9, false>(b, valid, (uint32_t)d1, hm);
+        __syncthreads();
+        int d2;
+        {
+            uint64_t loc[1];
+            loc[0] = hm[tid] << sh;
+            hm[tid] = 0ull;
+            d2 = digit_find<1, false>(loc, 1024, a.mass, u, emin, need, above, bin, wtot, &s_dig, s_res);
+        }
+        digit_sums<512, 0, false>(b, valid, ((uint32_t)d1 << 10) | (uint32_t)d2, hm);
+        __syncthreads();
+        int d3;
+        {
+            uint64_t loc[1];
+            loc[0] = tid < 512 ? hm[tid] << sh : 0ull;
+            d3 = digit_find<1, false>(loc, 512, a.mass, u, emin, need, above, bin, wtot, &s_dig, s_res);
+        }
         sb = ((uint32_t)d1 << 19) | ((uint32_t)d2 << 9) | (uint32_t)d3;
         // the digit holds c_eq tokens of score sb (its mass is > 0, so sb > 0);
-        // the prefix takes the fewest j of them with above + j q* reaching thr
-        const uint64_t qs = score_units(sb, emin);
+        // the prefix takes the fewest j of them with above + j q* >= need:
+        // 1 <= j <= c_eq since above < need <= above + bin
+        const uint64_t qs = (uint64_t)score_sig(sb) << (score_uexp(sb) - emin);
         c_eq = (int)(bin / qs);
-        if (tid == 0) {
-            const double u_inv = __longlong_as_double((long long)(150 - emin + 1023) << 52);
-            long long jj = (long long)ceil((thr * u_inv - (double)above) / (double)qs);
-            jj = jj < 1 ? 1 : jj > c_eq ? c_eq : jj;
-            while (jj > 1 && (double)(above + (uint64_t)(jj - 1) * qs) * u >= thr) --jj;
-            while (jj < c_eq && (double)(above + (uint64_t)jj * qs) * u < thr) ++jj;
-            s_j = (int)jj;
-        }
-        __syncthreads();
-        j = s_j;
+        j = (int)((need - above + qs - 1) / qs);
         prefix = true;
     }
     const int r0 = L - min(a.recent_n, L);
@@ -769,7 +789,7 @@ __global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs
     for (int k = 0; k < 16; ++k) {
         const bool hi = prefix && b[k] > sb;
         const bool eq = prefix && b[k] == sb;
-        onb |= (all || hi || 16 * tid + k >= r0) ? (1u << k) : 0u;
+        onb |= (hi || 16 * tid + k >= r0) ? (1u << k) : 0u;
         tie |= eq ? (1u << k) : 0u;
     }
     onb &= valid;
@@ -790,23 +810,100 @@ __global__ __launch_bounds__(1024) void k_token_mass_select(const MassSelectArgs
     }
     int n;
     int pos = block1024_exclusive(__popc(onb), wcnt[1], &n);
-    if (!all && n < a.min_keep) {
-        if (tid == 0) *a.done = 0;
-        return;
+    if (n < a.min_keep) return 2;
+    // the list staged in LDS (the digit sums are done with), then stored coalesced
+    int32_t *klist = (int32_t *)lds;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if ((onb >> k) & 1u) klist[pos++] = 16 * tid + k;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) {
+        const int32_t v = klist[i];
+        a.keep[i] = v;
+        a.keep_copy[i] = v;
     }
     if (tid == 0) {
         *a.count = n;
         *a.count_copy = n;
-        *a.done = 1;
     }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if ((onb >> k) & 1u) {
-            a.keep[pos] = 16 * tid + k;
-            a.keep_copy[pos] = 16 * tid + k;
-            ++pos;
+    return 1;
+}
+
+// ---------------------------------------------------------------------------
+// t2, the selection kernel: ceil(L / 1024) workgroups of 1024 threads.
+// Workgroup 0 tries the exact-mass path and publishes the path taken in
+// sync[0]; the others wait for it and end when it made the selection.  On the
+// sorted path every workgroup sorts its chunk of 1024 keys, all wait until
+// every chunk is sorted (sync[1]), each merges its chunk into the full order,
+// and workgroup 0 waits for every merge (sync[2]) and makes the selection from
+// the sorted order.  At most 16 workgroups, each waiting only for workgroups
+// of the same launch, so all of them run at once; every wait is bounded
+// (kSpinPolls polls), so every workgroup ends even if one never started, and
+// then workgroup 0 writes an empty selection.
+// ---------------------------------------------------------------------------
+constexpr int kSpinPolls = 1 << 20;   // a few tens of ms
+
+// the value at p once it reaches v (acquire at device scope), or what it holds
+// after kSpinPolls polls; one thread
+__device__ __forceinline__ int spin_until(int32_t *p, int v)
+{
+    int x = 0;
+    for (int it = 0; it < kSpinPolls; ++it) {
+        x = __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        if (x >= v) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return x;
+}
+
+// every thread's global stores made visible at device scope, then one arrival
+// at *p; when wait_for > 0, the workgroup waits until *p reaches it and returns
+// whether it did (every thread), with device-scope acquire
+__device__ __forceinline__ bool arrive_and_wait(int32_t *p, int wait_for, int *s_flag)
+{
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = wait_for > 0 ? (spin_until(p, wait_for) >= wait_for ? 1 : 0) : 1;
+    }
+    __syncthreads();
+    __threadfence();
+    return *s_flag != 0;
+}
+
+__global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ int s_flag;
+    const int c = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+    if (c == 0) {
+        const int path = mass_select(a, lds);
+        if (tid == 0) __hip_atomic_store(&a.sync[0], path, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (path == 1) return;
+    } else {
+        if (tid == 0) s_flag = spin_until(&a.sync[0], 1);
+        __syncthreads();
+        if (s_flag != 2) return;
+    }
+    __syncthreads();   // the LDS is reused
+    tsort_chunk(a, c, *reinterpret_cast<uint64_t(*)[2][1024]>(lds));
+    bool ok = arrive_and_wait(&a.sync[1], G, &s_flag);
+    if (ok) tsort_merge(a, G, c, (uint64_t *)lds);
+    if (c != 0) {
+        arrive_and_wait(&a.sync[2], 0, &s_flag);
+        return;
+    }
+    ok = ok && arrive_and_wait(&a.sync[2], G, &s_flag);
+    if (!ok) {
+        if (tid == 0) {
+            *a.count = 0;
+            *a.count_copy = 0;
         }
+        return;
     }
+    select_sorted(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1212,7 +1309,7 @@ __global__ __launch_bounds__(256) void k_copy_unkept(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 hipError_t launch_token_norms(const uint16_t *A, int rows, int d, float *s, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, st, A, rows, d, s);
+    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, st, A, rows, d, s, (int32_t *)nullptr);
     return hipGetLastError();
 }
 
@@ -1222,37 +1319,26 @@ hipError_t launch_prefill_select(const PrefillSelectCall &c)
     const int d = L.desc.d_model, rows = c.rows;
     const ScratchLayout S = scratch_layout(L.desc);
     float *sc_s = (float *)(c.scratch + S.tscore);
-    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, c.stream, c.A, rows, d, sc_s);
+    int32_t *sync = (int32_t *)(c.scratch + S.tdone);
+    hipLaunchKernelGGL(k_token_norms, dim3((rows + 3) / 4), dim3(256), 0, c.stream, c.A, rows, d, sc_s, sync);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // scores (padded blocks), 16-bit token indices, membership bytes
-    const size_t lds = (size_t)((rows + kMassBlock - 1) / kMassBlock) * kMassPad * 4 + (size_t)((rows + 7) & ~7) * 2 +
-                       (size_t)rows;
+    // dynamic LDS, the largest of: the exact-mass digits (4096 words), a chunk
+    // sort (2 x 1024 keys), the merge (every chunk), the sorted selection (scores
+    // in padded blocks, 16-bit token indices, membership bytes)
     const int G = (rows + 1023) / 1024;   // <= kMaxPrefillRows / 1024 = 16
-    static std::once_flag once_sel, once_merge;
-    static hipError_t err_sel = hipSuccess, err_merge = hipSuccess;
-    static int lim_sel = 0, lim_merge = 0;
+    const size_t lds_sel = (size_t)((rows + kMassBlock - 1) / kMassBlock) * kMassPad * 4 +
+                           (size_t)((rows + 7) & ~7) * 2 + (size_t)rows;
+    const size_t lds = std::max(std::max((size_t)4096 * 8, (size_t)G * 1024 * 8), lds_sel);
+    static std::once_flag once_sel;
+    static hipError_t err_sel = hipSuccess;
+    static int lim_sel = 0;
     if ((e = allow_full_dynamic_lds((const void *)k_token_select, once_sel, err_sel, lim_sel)) != hipSuccess) return e;
-    if ((e = allow_full_dynamic_lds((const void *)k_tsort_merge, once_merge, err_merge, lim_merge)) != hipSuccess)
-        return e;
-    if (lds > (size_t)lim_sel || (size_t)G * 1024 * 8 > (size_t)lim_merge) return hipErrorInvalidConfiguration;
-    uint64_t *chunks = (uint64_t *)(c.scratch + S.tkeys);     // ceil(rows / 1024) * 1024 keys
-    uint64_t *sorted = (uint64_t *)(c.scratch + S.tsorted);   // rows keys
-    int32_t *done = (int32_t *)(c.scratch + S.tdone);
-    // the exact-mass path first; the sorted path's kernels return at once when it made the selection
-    MassSelectArgs ma{sc_s, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
-                      (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), done};
-    hipLaunchKernelGGL(k_token_mass_select, dim3(1), dim3(1024), 0, c.stream, ma);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_tsort_chunk, dim3(G), dim3(1024), 0, c.stream, (const float *)sc_s, rows, chunks,
-                       (const int32_t *)done);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_tsort_merge, dim3(G), dim3(1024), (size_t)G * 1024 * 8, c.stream, (const uint64_t *)chunks, G,
-                       sorted, (const int32_t *)done);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    SelectArgs a{sc_s, sorted, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
-                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt), (const int32_t *)done};
-    hipLaunchKernelGGL(k_token_select, dim3(1), dim3(1024), lds, c.stream, a);
+    if (lds > (size_t)lim_sel) return hipErrorInvalidConfiguration;
+    SelectArgs a{sc_s, rows, c.recent_n, c.min_keep, c.mass, c.idx_out, c.count_out,
+                 (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt),
+                 (uint64_t *)(c.scratch + S.tkeys), (uint64_t *)(c.scratch + S.tsorted), sync};
+    hipLaunchKernelGGL(k_token_select, dim3(G), dim3(1024), lds, c.stream, a);
     return hipGetLastError();
 }
 

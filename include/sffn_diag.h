@@ -80,7 +80,7 @@ sffn_status sffn_set_kernel_timer(sffn_t layer, void *const *begin_events, void 
  * Which of the two paths of the token selection (sffn_select with a TOKENS
  * policy) made the last selection on this scratch: copies 1 (the exact-mass
  * radix select, taken when every partial sum of the scores is exact in fp64)
- * or 0 (the sort of all scores) into *path (device, one int32), asynchronously
+ * or 2 (the sort of all scores) into *path (device, one int32), asynchronously
  * on `stream`.  Meaningful only after such a selection.  SFFN_ERR_INVALID_ARG
  * for a null pointer or a layer without the PREFILL layout,
  * SFFN_ERR_WORKSPACE for a scratch smaller than the layer's.

@@ -153,9 +153,9 @@ def test_exact_mass_and_sorted_paths(mid, kind):
         if mass >= 1.0:
             assert path == 1, (kind, mass)              # every token, whatever the scores
         elif kind == "wide":
-            assert path == 0, (kind, mass)              # the range alone rules the exact path out
+            assert path == 2, (kind, mass)              # the range alone rules the exact path out
         elif mass == 0.0:
-            assert path == 0, (kind, mass)              # empty prefix, min_keep from the sorted order
+            assert path == 2, (kind, mass)              # empty prefix, min_keep from the sorted order
         elif mk <= 3:
             assert path == 1, (kind, mass, recent, mk)  # mk = 200 may exceed the prefix: either path
 
