@@ -90,13 +90,199 @@ struct BlkArgs {
     int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
 };
 
+// Exact block masses.  Let u be the ulp of the sequence's smallest nonzero
+// score: every score, block mass and sum of block masses is an integer
+// multiple of u.  When the sequence's total is below 2^53 u, every partial sum
+// of scores is an fp64 number, so every fp64 addition of them is exact and its
+// result does not depend on the order: the block masses are then summed with
+// all tokens at once and the rank-order sums by a scan.  Otherwise (a
+// negative, infinite or NaN score, more than 2^26 between the largest and the
+// smallest nonzero score, or a total of 2^52 u or more as summed here -- an
+// fp64 sum in any order, within a factor 1 + 2^-38 of the true one) the block
+// masses are added in token order and their rank-order sums in rank order.
+constexpr int kBlkPer = kMaxPrefillRows / 256;   // tokens per thread
+
+// a sum over the wave (a bound check only: any grouping will do)
+__device__ __forceinline__ double wave_tree_sum_f64(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// inclusive prefix of doubles over the 64 lanes (exact sums: any grouping)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_add_f64(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, false);
+    return v + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The sequence's block masses into S[0, nb), summed with all tokens at once;
+// false (S not usable) when the scores break the condition.  The mass of a run
+// of a thread's consecutive tokens inside one block goes in with one atomic.
+__device__ bool blk_masses_exact(const BlkArgs &a, int o0, int Lq, int nb, double *S, int *red, double *wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, B = a.block;
+    if (Lq == 0) return false;
+    // the sequence's scores through LDS: coalesced loads (all in flight,
+    // clamped), then thread t takes tokens 64 t .. 64 t + 63; one pad word per
+    // 64 puts a wave's 64 reads of one step in 64 different banks
+    __shared__ uint32_t stage[kMaxPrefillRows + kMaxPrefillRows / 64];
+    uint32_t b[kBlkPer];
+#pragma unroll
+    for (int k = 0; k < kBlkPer; ++k) b[k] = __float_as_uint(a.s[o0 + min(k * 256 + tid, Lq - 1)]);
+#pragma unroll
+    for (int k = 0; k < kBlkPer; ++k) {
+        const int i = k * 256 + tid;
+        stage[i + (i >> 6)] = b[k];
+    }
+    for (int bb = tid; bb < nb; bb += 256) S[bb] = 0.0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kBlkPer; ++k) {
+        const int i = kBlkPer * tid + k;
+        b[k] = stage[i + (i >> 6)];
+    }
+    const int nv = min(max(Lq - kBlkPer * tid, 0), kBlkPer);
+    uint32_t bmax = 0, emn = 255;
+#pragma unroll
+    for (int k = 0; k < kBlkPer; ++k) {
+        if (k < nv) {
+            bmax = max(bmax, b[k]);
+            if (b[k] - 1u < 0x7F7FFFFFu) emn = min(emn, (uint32_t)max((int)(b[k] >> 23), 1));
+        }
+    }
+    // block masses: this thread's tokens fall in a few consecutive blocks.  In
+    // chunks of 16 tokens, which hold at most one block start (B >= 16): the
+    // masked sums before and from that start, without branches per token
+    double tsum = 0.0;
+    if (nv > 0) {
+        double run = 0.0;
+        int cur = (kBlkPer * tid) / B;
+        int next = (cur + 1) * B;   // the first token of the next block
+#pragma unroll
+        for (int c = 0; c < kBlkPer / 16; ++c) {
+            const int p = next - (kBlkPer * tid + 16 * c);   // >= 0; < 16: a block starts here
+            double lo = 0.0, hi = 0.0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const double v = 16 * c + k < nv ? (double)__uint_as_float(b[16 * c + k]) : 0.0;
+                lo += k < p ? v : 0.0;
+                hi += k < p ? 0.0 : v;
+            }
+            run += lo;
+            if (p < 16) {
+                // cur may pass nb only after the sequence's last token, with run = 0
+                if (cur < nb) atomicAdd(&S[cur], run);
+                tsum += run;
+                run = hi;
+                ++cur;
+                next += B;
+            }
+        }
+        // the last block's run (a start past the sequence's end opens no block)
+        if (cur < nb) atomicAdd(&S[cur], run);
+        tsum += run;
+    }
+    bmax = wave_max_dpp(bmax);
+    const uint32_t nemn = wave_max_dpp(255u - emn);
+    tsum = wave_tree_sum_f64(tsum);
+    if (lane == 0) {
+        red[wave] = (int)bmax;
+        red[4 + wave] = (int)nemn;
+        wsum[wave] = tsum;
+    }
+    __syncthreads();
+    uint32_t gmax = 0, gne = 0;
+    double total = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        gmax = max(gmax, (uint32_t)red[w2]);
+        gne = max(gne, (uint32_t)red[4 + w2]);
+        total += wsum[w2];
+    }
+    const int emin = 255 - (int)gne, emax = max((int)(gmax >> 23), 1);
+    if (gmax > 0x7F7FFFFFu || (gmax != 0u && emax - emin > 26)) return false;
+    // total < 2^52 u, u = 2^(emin - 150)
+    if (gmax != 0u && !(total < __longlong_as_double((long long)(emin - 98 + 1023) << 52))) return false;
+    return true;
+}
+
+// rank-order sums of the masses in cum[0, nb) (in rank order), in place, by a
+// scan: 4 consecutive ranks per thread (nb <= 1024); exact sums only
+__device__ void blk_rank_sums_exact(double *cum, int nb, double *wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double v[4], sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = tid * 4 + k;
+        v[k] = r < nb ? cum[r] : 0.0;
+        sum += v[k];
+    }
+    double incl = sum;
+    incl = dpp_add_f64<0x111, 0xf>(incl);   // row_shr:1
+    incl = dpp_add_f64<0x112, 0xf>(incl);   // row_shr:2
+    incl = dpp_add_f64<0x114, 0xf>(incl);   // row_shr:4
+    incl = dpp_add_f64<0x118, 0xf>(incl);   // row_shr:8
+    incl = dpp_add_f64<0x142, 0xa>(incl);   // row_bcast:15
+    incl = dpp_add_f64<0x143, 0xc>(incl);   // row_bcast:31
+    __syncthreads();   // wsum is free again
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    double c = incl - sum;
+#pragma unroll
+    for (int w2 = 0; w2 < 3; ++w2) c += w2 < wave ? wsum[w2] : 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int r = tid * 4 + k;
+        c += v[k];
+        if (r < nb) cum[r] = c;
+    }
+}
+
+// The kept blocks' token count, further blocks in rank order until
+// min(min_keep, Lq) tokens are kept (not for a dense sequence), the count and
+// the flags out.
+__device__ void blk_finish(const BlkArgs &a, int q, int o0, int Lq, int nb, bool dense, const int *ord,
+                           uint8_t *kept, int *red)
+{
+    const int tid = threadIdx.x, B = a.block;
+    __syncthreads();
+    int part = 0;
+    for (int b = tid; b < nb; b += 256)
+        if (kept[b]) part += min(B, Lq - b * B);
+    const int kept_tokens = block256_sum(part, red);
+    if (tid == 0) {
+        int cnt = kept_tokens;
+        if (!dense) {
+            const int need = min(a.min_keep, Lq);
+            for (int k = 0; k < nb && cnt < need; ++k) {
+                const int b = ord[k];
+                if (!kept[b]) {
+                    kept[b] = 1;
+                    cnt += min(B, Lq - b * B);
+                }
+            }
+        }
+        a.counts[q] = cnt;
+    }
+    __syncthreads();
+    uint8_t *fl = a.flags + (size_t)(o0 / B + q);
+    for (int b = tid; b < nb; b += 256) fl[b] = kept[b];
+}
+
 __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
 {
     __shared__ double S[kMaxBlocksPerSeq];
     __shared__ double cum[kMaxBlocksPerSeq];
     __shared__ int ord[kMaxBlocksPerSeq];
     __shared__ uint8_t kept[kMaxBlocksPerSeq];
-    __shared__ int red[4];
+    __shared__ int red[8];
+    __shared__ double wsum[4];
     const int q = blockIdx.x, tid = threadIdx.x, B = a.block;
     __shared__ int s_bad;   // a non-finite block mass (from a NaN or infinite score)
     int o0, o1;
@@ -104,36 +290,66 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
     seq_range(a.cu, q, a.rows, &o0, &o1, red);
     const int Lq = o1 - o0;
     const int nb = (Lq + B - 1) / B;   // <= kMaxBlocksPerSeq (block >= 16, rows <= 16384)
-    for (int b = tid; b < nb; b += 256) {
-        const int t1 = min((b + 1) * B, Lq);
-        double m = 0.0;
-        // 32 scores loaded at a time, then added in token order
-        for (int t0 = b * B; t0 < t1; t0 += 32) {
-            float v[32];
+    for (int bb = tid; bb < nb; bb += 256) kept[bb] = 0;
+    const bool exact = blk_masses_exact(a, o0, Lq, nb, S, red, wsum);
+    if (!exact) {
+        __syncthreads();
+        for (int b = tid; b < nb; b += 256) {
+            const int t1 = min((b + 1) * B, Lq);
+            double m = 0.0;
+            // 32 scores loaded at a time, then added in token order
+            for (int t0 = b * B; t0 < t1; t0 += 32) {
+                float v[32];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) v[i] = a.s[o0 + min(t0 + i, t1 - 1)];
+                for (int i = 0; i < 32; ++i) v[i] = a.s[o0 + min(t0 + i, t1 - 1)];
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                if (t0 + i < t1) m = m + (double)v[i];
+                for (int i = 0; i < 32; ++i)
+                    if (t0 + i < t1) m = m + (double)v[i];
+            }
+            S[b] = m;
+            if (!isfinite(m)) s_bad = 1;
         }
-        S[b] = m;
-        kept[b] = 0;
-        if (!isfinite(m)) s_bad = 1;
     }
     __syncthreads();
-    // rank of each block by counting; the masses are also stored in rank order
-    for (int b = tid; b < nb; b += 256) {
-        const double m = S[b];
-        int r = 0;
-        for (int b2 = 0; b2 < nb; ++b2) {
-            const double m2 = S[b2];
-            r += (m2 > m) || (m2 == m && b2 < b);
+    // rank of each block by counting (mass desc, index asc): with nb < 256 the
+    // comparisons of a block are split over P = 256 / nb threads, whose counts
+    // are added in LDS; the masses then go in rank order
+    {
+        const int P = nb >= 256 ? 1 : 256 / max(nb, 1);
+        for (int bb = tid; bb < nb; bb += 256) ord[bb] = 0;   // the counts, for now
+        __syncthreads();
+        for (int w = tid; w < nb * P; w += 256) {
+            const int bb = w % nb, part = w / nb;
+            const int c0 = part * nb / P, c1 = (part + 1) * nb / P;
+            const double m = S[bb];
+            int r = 0;
+            for (int b0 = c0; b0 < c1; b0 += 8) {
+                double m2[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m2[i] = S[min(b0 + i, c1 - 1)];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) r += (b0 + i < c1) && ((m2[i] > m) || (m2[i] == m && b0 + i < bb));
+            }
+            if (r) atomicAdd(&ord[bb], r);
         }
-        ord[r] = b;
-        cum[r] = m;
+        __syncthreads();
+        int rk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rk[k] = tid + 256 * k < nb ? ord[tid + 256 * k] : 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int bb = tid + 256 * k;
+            if (bb < nb) {
+                ord[rk[k]] = bb;
+                cum[rk[k]] = S[bb];
+            }
+        }
     }
     __syncthreads();
-    if (tid == 0) {
+    if (exact) {
+        blk_rank_sums_exact(cum, nb, wsum);
+    } else if (tid == 0) {
         // cumulative mass in rank order, in place; 16 masses read at a time
         double c = 0.0;
         for (int k0 = 0; k0 < nb; k0 += 16) {
@@ -179,28 +395,7 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
             for (int b = first + tid; b < nb; b += 256) kept[b] = 1;
         }
     }
-    __syncthreads();
-    int part = 0;
-    for (int b = tid; b < nb; b += 256)
-        if (kept[b]) part += min(B, Lq - b * B);
-    const int kept_tokens = block256_sum(part, red);
-    if (tid == 0) {
-        int cnt = kept_tokens;
-        if (!dense) {
-            const int need = min(a.min_keep, Lq);
-            for (int k = 0; k < nb && cnt < need; ++k) {
-                const int b = ord[k];
-                if (!kept[b]) {
-                    kept[b] = 1;
-                    cnt += min(B, Lq - b * B);
-                }
-            }
-        }
-        a.counts[q] = cnt;
-    }
-    __syncthreads();
-    uint8_t *fl = a.flags + (size_t)(o0 / B + q);
-    for (int b = tid; b < nb; b += 256) fl[b] = kept[b];
+    blk_finish(a, q, o0, Lq, nb, dense, ord, kept, red);
 }
 
 __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
@@ -239,11 +434,13 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
         if (b < nb) pos[b + 1] = run;
     }
     __syncthreads();
-    for (int t = tid; t < Lq; t += 256) {
-        const int b = t / B;
-        if (pos[b + 1] != pos[b]) {
-            a.idx_out[base_out + pos[b] + (t - b * B)] = o0 + t;
-            a.keep_copy[base_out + pos[b] + (t - b * B)] = o0 + t;
+    // every wave writes whole kept blocks, its lanes over the block's tokens
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int b = wave; b < nb; b += 4) {
+        const int p0 = pos[b], len = pos[b + 1] - p0;   // 0: not kept
+        for (int j = lane; j < len; j += 64) {
+            a.idx_out[base_out + p0 + j] = o0 + b * B + j;
+            a.keep_copy[base_out + p0 + j] = o0 + b * B + j;
         }
     }
 }

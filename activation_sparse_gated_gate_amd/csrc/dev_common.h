@@ -133,6 +133,49 @@ __device__ __forceinline__ int wave_incl_scan(int v)
     return v;
 }
 
+// maximum over the wave, in every lane: lane swaps for xor 32 and 16, row
+// rotations by 8 and 4 (after the first, lanes i and i ^ 8 agree, so the
+// rotation by 4 reads the value of lane i ^ 4), quad permutations for 2 and 1.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
+{
+    const int lane = threadIdx.x & 63;
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = max(v, (uint32_t)(lane < 32 ? p[1] : p[0]));
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max(v, (uint32_t)((lane & 16) ? p[0] : p[1]));
+    }
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));   // row_ror:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));   // row_ror:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));    // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));    // quad [1,0,3,2]
+    return v;
+}
+
+// one step of a DPP prefix over 64-bit values (both halves moved, 0 where the
+// source lane lies outside the pattern)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+    return v + (((uint64_t)hi << 32) | lo);
+}
+
+// inclusive prefix over the 64 lanes (the steps of wave_incl_scan on 64 bits)
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
+{
+    v = dpp_add_u64<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add_u64<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add_u64<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add_u64<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add_u64<0x142, 0xa>(v);   // row_bcast:15
+    v = dpp_add_u64<0x143, 0xc>(v);   // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ int mbcnt64(uint64_t m)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));

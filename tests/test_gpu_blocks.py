@@ -124,6 +124,25 @@ def test_degenerate_rows_ties_and_one_token_sequences(mid):
     check(layer, A[:300], cu_of([1] * 300), 0.5)                             # nseq = rows
 
 
+@pytest.mark.parametrize("kind", ["wide", "small_ints"])
+def test_exact_and_ordered_block_masses(mid, kind):
+    """Scores whose sums are all exact in fp64 take the integer block masses;
+    a range wider than 2^26 between the largest and the smallest nonzero score
+    takes the fp64 sums in token and rank order.  Both against the oracle, on
+    a varlen batch with a ragged last block per sequence and block sizes of
+    16 and 48 (blocks straddling the 64-token runs of a thread)."""
+    w, Y, A, layer = mid
+    L = A.shape[0]
+    rng = np.random.default_rng({"wide": 31, "small_ints": 32}[kind])
+    v = np.exp(6.0 * rng.standard_normal(L)) if kind == "wide" else rng.integers(0, 4, L).astype(np.float64)
+    B = np.zeros_like(A)
+    B[:, 7] = synth.f32_to_bf16_bits(v.astype(np.float32))   # one element per row: score = |v| exactly
+    cu = cu_of([2500, 1700, 1, 1799])
+    for mass in (0.0, 0.3, 0.7, 1.0):
+        for block in (16, 48, 128):
+            check(layer, B, cu, mass, block=block, recent_n=5)
+
+
 def test_bad_offsets_stay_in_bounds(mid):
     # offsets that are not a valid partition are clamped and made ascending:
     # no fault, an ascending list of in-range tokens, the count at most rows
