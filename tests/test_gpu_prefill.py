@@ -231,6 +231,20 @@ def test_cfg5_selection_and_every_tile(cfg5, mass):
                                                                      max(errs)))
 
 
+@pytest.mark.parametrize("mass", [0.3, 0.7])
+def test_cfg5_sorted_path_full_length(cfg5, mass):
+    """Full length through the sorted path: 100 attention rows scaled by 2^-40
+    (exact in bf16) put more than 2^26 between the largest and the smallest
+    score, so the exact-mass select gives way to the sort, whose 16 workgroups
+    meet at two device-scope arrival counters.  Keep list bit-exact."""
+    w, Y, A, layer = cfg5
+    A2 = A.copy()
+    rows = np.arange(0, A.shape[0], A.shape[0] // 100)[:100]
+    A2[rows] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(A[rows]) * np.float32(2.0 ** -40))
+    check_select(layer, A2, mass, synth.CFG5_RECENT, synth.CFG5_MIN_KEEP)
+    assert layer.token_select_path() == 2
+
+
 @pytest.mark.parametrize("M", [2048, 1800, 1000])
 def test_large_tile_down_projection_every_row(M):
     """d_model 5120 (20 column tiles of 256): 2048 and 1800 kept rows give 8 row
