@@ -801,13 +801,15 @@ __device__ __forceinline__ int mass_select(const SelectArgs &a, unsigned char *l
 // ---------------------------------------------------------------------------
 constexpr int kSpinPolls = 1 << 20;   // a few tens of ms
 
-// the value at p once it reaches v (acquire at device scope), or what it holds
-// after kSpinPolls polls; one thread
+// the value at p once it reaches v, or what it holds after kSpinPolls polls;
+// one thread.  The polls are relaxed device-scope loads: an acquire on every
+// poll would invalidate the XCD's L2 each time; a caller that then reads data
+// published before the word fences once after the wait.
 __device__ __forceinline__ int spin_until(int32_t *p, int v)
 {
     int x = 0;
     for (int it = 0; it < kSpinPolls; ++it) {
-        x = __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        x = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (x >= v) break;
         __builtin_amdgcn_s_sleep(2);
     }
@@ -837,7 +839,10 @@ __global__ __launch_bounds__(1024) void k_token_select(const SelectArgs a)
     const int c = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
     if (c == 0) {
         const int path = mass_select(a, lds);
-        if (tid == 0) __hip_atomic_store(&a.sync[0], path, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        // relaxed: the other workgroups use only the word's value (the sorted path
+        // reads the scores, written by the previous launch); a release here would
+        // write back the XCD's L2
+        if (tid == 0) __hip_atomic_store(&a.sync[0], path, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (path == 1) return;
     } else {
         if (tid == 0) s_flag = spin_until(&a.sync[0], 1);
