@@ -328,7 +328,8 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) m2[i] = S[min(b0 + i, c1 - 1)];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) r += (b0 + i < c1) && ((m2[i] > m) || (m2[i] == m && b0 + i < bb));
+                for (int i = 0; i < 8; ++i)   // bitwise, not short-circuit: no branch per comparison
+                r += (int)((b0 + i < c1) & ((m2[i] > m) | ((m2[i] == m) & (b0 + i < bb))));
             }
             if (r) atomicAdd(&ord[bb], r);
         }
