@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_token_norms(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// t2: token selection (one workgroup of 1024 threads)
+// t2: token selection (one launch of ceil(L / 1024) workgroups of 1024 threads)
 // ---------------------------------------------------------------------------
 struct SelectArgs {
     const float *s;           // L scores; the array spans at least round_up(L, 16) floats
@@ -325,7 +325,7 @@ __device__ __forceinline__ void write_keep(uint32_t onb, const OrderScan &os, in
     }
 }
 
-// The selection proper, one workgroup.  The sorted order is held in LDS as
+// The sorted path's selection, by workgroup 0.  The sorted order is held in LDS as
 // the fp32 scores, block by block of kMassBlock entries with one word of
 // padding per block (so the 64 threads that each walk one block read
 // different banks), and the 16-bit token index of every rank.  The fp64 block
@@ -333,8 +333,8 @@ __device__ __forceinline__ void write_keep(uint32_t onb, const OrderScan &os, in
 // sum after every 32 entries), the block bases by a sequential chain over the
 // lanes' totals; the threshold block's scan restarts from its last checkpoint
 // below the threshold.  The keep list is built in rounds of 1024 consecutive
-// tokens (ballot + mbcnt, wave offsets through LDS), so every load and store
-// of the list and the flags is coalesced.
+// tokens (ballot + mbcnt, wave offsets through LDS), so every store of the list
+// is coalesced.
 constexpr int kMassPad = kMassBlock + 1;
 
 __device__ __forceinline__ int mass_slot(int r) { return (r / kMassBlock) * kMassPad + (r % kMassBlock); }

@@ -454,6 +454,41 @@ def test_token_select_minimal_prefix_on_random_scores():
         assert math.fsum(top[:m - 1]) < mass * total * (1 + 1e-12)
 
 
+def _ulp_units(s):
+    """Each fp32 score >= 0 as an exact integer in units of the ulp of the
+    smallest nonzero score (Python ints), and that ulp's exponent."""
+    b = [int(x) for x in s.view(np.uint32)]
+    nz = [max(x >> 23, 1) for x in b if x]
+    emin = min(nz)
+    q = [(((x & 0x7FFFFF) | (0x800000 if x >= 0x800000 else 0)) << (max(x >> 23, 1) - emin)) if x else 0 for x in b]
+    return q, emin - 150
+
+
+def test_exact_mass_condition_makes_the_blocked_prefix_order_free():
+    """The shortcut the kernels take (an exactness theorem, not a reading of the
+    pages): when the total is at most 2^53 ulps of the smallest nonzero score,
+    every partial sum is an fp64 number, so the oracle's blocked fp64 prefix
+    equals the exact prefix at every rank, whatever the order of the additions.
+    Outside the condition the blocked prefix rounds, which is why the kernels
+    then sort and add in order."""
+    for seed, L in ((31, 1000), (32, 5000), (33, 16384)):
+        s = (71.6 * np.exp(synth.normal_f32(seed, (L,)).astype(np.float64))).astype(np.float32)
+        q, e = _ulp_units(s)
+        assert sum(q) <= 2 ** 53
+        _, order, cum = oracle.token_select(s, 0.5, 0, 1)
+        run = 0
+        for r, i in enumerate(order):
+            run += q[i]
+            assert cum[r] == math.ldexp(float(run), e), (seed, r)   # float(run) exact: run <= 2^53
+    # 2^60 and then ones: past 2^53 ulps the blocked prefix rounds, the exact one does not
+    s = np.array([2.0 ** 60] + [1.0] * 300, np.float32)
+    q, e = _ulp_units(s)
+    assert sum(q) > 2 ** 53
+    _, order, cum = oracle.token_select(s, 0.5, 0, 1)
+    assert Fraction(float(cum[-1])) != Fraction(2 ** 60 + 300)   # the blocked prefix rounds
+    assert 300.0 + 2.0 ** 60 != cum[-1]                            # another order, other bits
+
+
 def test_token_select_guards_and_degenerate_rows():
     s = np.exp(synth.normal_f32(10, (300,))).astype(np.float32)
     L = s.size
