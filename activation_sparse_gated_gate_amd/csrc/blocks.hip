@@ -88,6 +88,7 @@ struct BlkArgs {
     int32_t *counts;         // kept tokens per sequence [nseq]
     int32_t *idx_out, *count_out;
     int32_t *keep_copy, *count_copy;   // the same list and count in the scratch (for forward without a list)
+    int emit_here;           // one sequence: k_blk_select writes the list itself (offset 0), no k_blk_emit
 };
 
 // Exact block masses.  Let u be the ulp of the sequence's smallest nonzero
@@ -275,6 +276,9 @@ __device__ void blk_finish(const BlkArgs &a, int q, int o0, int Lq, int nb, bool
     for (int b = tid; b < nb; b += 256) fl[b] = kept[b];
 }
 
+__device__ int emit_blocks(const BlkArgs &a, int o0, int Lq, int nb, const uint8_t *kept, int base_out, int *pos,
+                           int *red);
+
 __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
 {
     __shared__ double S[kMaxBlocksPerSeq];
@@ -397,6 +401,52 @@ __global__ __launch_bounds__(256) void k_blk_select(const BlkArgs a)
         }
     }
     blk_finish(a, q, o0, Lq, nb, dense, ord, kept, red);
+    if (a.emit_here) {
+        // one sequence: the list starts at 0 and its length is the kept total
+        __shared__ int pos[kMaxBlocksPerSeq + 1];
+        const int n = emit_blocks(a, o0, Lq, nb, kept, 0, pos, red);
+        if (tid == 0) {
+            *a.count_out = n;
+            *a.count_copy = n;
+        }
+    }
+}
+
+// The sequence's kept token indices at base_out in the batch-wide list: an
+// exclusive prefix of the kept block sizes (4 blocks per thread, then the 256
+// partials) in pos, then every wave writes whole kept blocks, its lanes over
+// the block's tokens.  kept: one byte per block (LDS or global).  Returns the
+// sequence's kept tokens (every thread).
+__device__ int emit_blocks(const BlkArgs &a, int o0, int Lq, int nb, const uint8_t *kept, int base_out, int *pos,
+                           int *red)
+{
+    const int tid = threadIdx.x, B = a.block;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = tid * 4 + i;
+        v[i] = (b < nb && kept[b]) ? min(B, Lq - b * B) : 0;
+        sum += v[i];
+    }
+    // pos[b] = kept tokens of the blocks before b, for b = 0..nb
+    int run = block256_exclusive(sum, red);
+    if (tid == 0) pos[0] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = tid * 4 + i;
+        run += v[i];
+        if (b < nb) pos[b + 1] = run;
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int b = wave; b < nb; b += 4) {
+        const int p0 = pos[b], len = pos[b + 1] - p0;   // 0: not kept
+        for (int j = lane; j < len; j += 64) {
+            a.idx_out[base_out + p0 + j] = o0 + b * B + j;
+            a.keep_copy[base_out + p0 + j] = o0 + b * B + j;
+        }
+    }
+    return pos[nb];
 }
 
 __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
@@ -416,34 +466,7 @@ __global__ __launch_bounds__(256) void k_blk_emit(const BlkArgs a)
         *a.count_out = base_out + a.counts[q];
         *a.count_copy = base_out + a.counts[q];
     }
-    // exclusive prefix of kept block sizes: 4 blocks per thread, then the 256 partials
-    const uint8_t *fl = a.flags + (size_t)(o0 / B + q);
-    int v[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = tid * 4 + i;
-        v[i] = (b < nb && fl[b]) ? min(B, Lq - b * B) : 0;
-        sum += v[i];
-    }
-    // pos[b] = kept tokens of the blocks before b, for b = 0..nb
-    int run = block256_exclusive(sum, red);
-    if (tid == 0) pos[0] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = tid * 4 + i;
-        run += v[i];
-        if (b < nb) pos[b + 1] = run;
-    }
-    __syncthreads();
-    // every wave writes whole kept blocks, its lanes over the block's tokens
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int b = wave; b < nb; b += 4) {
-        const int p0 = pos[b], len = pos[b + 1] - p0;   // 0: not kept
-        for (int j = lane; j < len; j += 64) {
-            a.idx_out[base_out + p0 + j] = o0 + b * B + j;
-            a.keep_copy[base_out + p0 + j] = o0 + b * B + j;
-        }
-    }
+    emit_blocks(a, o0, Lq, nb, a.flags + (size_t)(o0 / B + q), base_out, pos, red);
 }
 
 hipError_t launch_block_select(const BlockSelectCall &c)
@@ -456,8 +479,9 @@ hipError_t launch_block_select(const BlockSelectCall &c)
     BlkArgs a{sc, c.cu, c.rows, c.nseq, c.block, c.mass, c.min_full, c.max_full, c.recent_n, c.min_keep,
               c.scratch + S.tkeys, (int32_t *)(c.scratch + S.tflag), c.idx_out, c.count_out,
               (int32_t *)(c.scratch + S.tkeep), (int32_t *)(c.scratch + S.tkcnt)};
+    a.emit_here = c.nseq == 1 ? 1 : 0;
     hipLaunchKernelGGL(k_blk_select, dim3(c.nseq), dim3(256), 0, c.stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess || a.emit_here) return e;
     hipLaunchKernelGGL(k_blk_emit, dim3(c.nseq), dim3(256), 0, c.stream, a);
     return hipGetLastError();
 }
