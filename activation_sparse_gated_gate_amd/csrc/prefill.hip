@@ -1076,8 +1076,9 @@ __device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base
 constexpr int gemm_waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // NW waves per workgroup: 4 (2 x 2 waves of 128 x 128) or 8 (2 x 4 waves of
-// 128 x 64, two waves per SIMD so that one wave's products run while the other
-// waits at a barrier or an LDS read)
+// 128 x 64, two waves per SIMD; waves w and w + 4 share a SIMD, and the two
+// groups of four alternate between reading a slice's fragments and issuing its
+// products, so each SIMD's matrix unit is fed while the other wave reads)
 template <int EPI, int NW>
 __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 {
@@ -1146,22 +1147,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-        for (int p = 0; p < BSTAGES - 1; ++p)
-            if (p < KT) issue(p);
-        for (int kt = 0; kt < KT; ++kt) {
-            // slice kt has landed once only the later slices' copies are outstanding
-            const int later = min(KT - 1 - kt, BSTAGES - 2);
-            if (later >= 2) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(2 * CPS));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(CPS));
-            else __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(0));
-            // every wave's copies of slice kt are in LDS, and every wave has finished
-            // slice kt - 1, whose stage the next copies refill
-            __builtin_amdgcn_s_barrier();
+        // the slice's operand fragments of this wave, from LDS into registers
+        bf16x8 fa[BBK / 16][4], fb[BBK / 16][JB];
+        auto read_frags = [&](int kt) {
             const uint16_t *as = As[kt % BSTAGES], *bs = Bs[kt % BSTAGES];
-            // every operand fragment of the slice is read from LDS before the first
-            // product, so only the first two reads' latency is exposed; the refill of
-            // the stage finished two slices ago goes out behind them
-            bf16x8 fa[BBK / 16][4], fb[BBK / 16][JB];
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks) {
                 const int kc = 2 * ks + (lane >> 5);
@@ -1176,8 +1165,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
                     fb[ks][j] = *(const bf16x8 *)&bs[c * BBK + ((kc ^ ((c >> 2) & 3)) * 8)];
                 }
             }
-            if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto products = [&]() {
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks)
 #pragma unroll
@@ -1185,6 +1174,72 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 #pragma unroll
                     for (int j = 0; j < JB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+        };
+        // wait until this wave's copies of slice kt have landed, given the
+        // slices issued after it (lgkm0: and every LDS read of this wave)
+        auto wait_slice = [&](int kt, bool lgkm0) {
+            const int later = min(min(KT - 1, kt + BSTAGES - 2) - kt, BSTAGES - 2);
+            const int n = later >= 2 ? 2 * CPS : later == 1 ? CPS : 0;
+            if (lgkm0) {
+                if (n == 2 * CPS) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(2 * CPS) & ~(0xF << 8));
+                else if (n == CPS) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(CPS) & ~(0xF << 8));
+                else __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(0) & ~(0xF << 8));
+            } else {
+                if (n == 2 * CPS) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(2 * CPS));
+                else if (n == CPS) __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(CPS));
+                else __builtin_amdgcn_s_waitcnt(gemm_waitcnt_vm(0));
+            }
+        };
+
+        for (int p = 0; p < BSTAGES - 1; ++p)
+            if (p < KT) issue(p);
+        if constexpr (NW == 8) {
+            // Two groups of four waves, one wave of each per SIMD, one phase
+            // apart: while the waves of one group issue a slice's products, the
+            // other group's waves read their fragments of the slice and issue
+            // their copies, so every SIMD has products to run across the
+            // barriers.  Phases are separated by workgroup barriers; the lead
+            // group (waves 0-3) reads slice kt in phase 2 kt - 1 and multiplies
+            // in phase 2 kt, the other one phase later.  The stage of slice kt
+            // is refilled (slice kt + 4) from phase 2 kt + 1 on, after the
+            // second group's reads of it have completed; every wave's copies of
+            // slice kt + 1 have landed by the barrier that opens phase 2 kt + 1.
+            // Both groups take the same number of barriers: the second one more
+            // at the start, the lead one more at the end.
+            const bool lead = w < NW / 2;
+            wait_slice(0, false);
+            __builtin_amdgcn_s_barrier();
+            if (!lead) __builtin_amdgcn_s_barrier();
+            for (int kt = 0; kt < KT; ++kt) {
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(kt);
+                if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
+                // the second group's reads must be complete before the stage can
+                // be refilled; its copies of slice kt + 1 must have landed
+                if (!lead) wait_slice(kt + 1, true);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                products();
+                __builtin_amdgcn_sched_barrier(0);
+                if (lead) wait_slice(kt + 1, false);
+                __builtin_amdgcn_s_barrier();
+            }
+            if (lead) __builtin_amdgcn_s_barrier();
+        } else {
+            for (int kt = 0; kt < KT; ++kt) {
+                // every wave's copies of slice kt are in LDS, and every wave has
+                // finished slice kt - 1, whose stage the next copies refill
+                wait_slice(kt, false);
+                __builtin_amdgcn_s_barrier();
+                // every operand fragment of the slice is read from LDS before the
+                // first product, so only the first two reads' latency is exposed;
+                // the refill of the stage finished two slices ago goes out behind them
+                read_frags(kt);
+                if (kt + BSTAGES - 1 < KT) issue(kt + BSTAGES - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                products();
+            }
         }
         __builtin_amdgcn_s_barrier();   // the next tile's first copies reuse the stages
 
