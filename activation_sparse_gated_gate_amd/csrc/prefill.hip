@@ -20,7 +20,7 @@
 //                      the A rows gathered through the keep list and the gate /
 //                      up columns of the same neurons in one tile (the weights
 //                      are interleaved in blocks of 32 rows at creation).
-//   t4 k_gemm_big<DOWN> / k_gemm<DOWN> Z = H W_down^T; epilogue X_next[S_m] = bf16(Y[S_m] + Z_m),
+//   t4 k_gemm_big<DOWN> Z = H W_down^T; epilogue X_next[S_m] = bf16(Y[S_m] + Z_m),
 //                      a scatter through the keep list.
 //   k_copy_unkept      X_next[i] = Y[i] for i not kept (skipped when X_next == Y).
 // Tiles whose rows start past the device-side count exit at once, so the grid
@@ -876,9 +876,6 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 enum { EPI_GATE_UP = 0, EPI_DOWN = 1 };
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int GLDA = GBK + 8;  // LDS row pitch in bf16 (16-byte pad)
-
 struct GemmArgs {
     const uint16_t *A;      // GATE_UP: Y [L][K] gathered through keep; DOWN: H [Mmax][K]
     const uint16_t *B;      // [N][K]
@@ -901,8 +898,8 @@ __device__ __forceinline__ int gemm_rows(const GemmArgs &a) { return min(max(*a.
 __device__ __forceinline__ int kept_row(const GemmArgs &a, int m) { return min(max(a.keep[m], 0), a.rows - 1); }
 
 // The device-side row count decides between the two tile sizes without a host
-// round trip: with too few 256 x 256 tiles for the compute units, 128 x 128
-// tiles keep every unit busy.
+// round trip: with too few 256 x 256 tiles for the compute units, 128 x 256
+// tiles keep more units busy.
 __device__ __forceinline__ bool gemm_gate_open(const GemmArgs &a, int M)
 {
     if (a.gate == 0) return true;
@@ -917,140 +914,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
     return (uint16_t)(u >> 16);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs a)
-{
-    __shared__ __align__(16) uint16_t As[GBM * GLDA];
-    __shared__ __align__(16) uint16_t Bs[GBN * GLDA];
-    __shared__ int rowsrc[GBM];
-    __shared__ int rowtok[GBM];   // DOWN: the kept token of each tile row (the epilogue's scatter)
-
-    const int M = gemm_rows(a);
-    if (!gemm_gate_open(a, M)) return;
-    const int mt = (M + GBM - 1) / GBM;
-    const int nt = a.N / GBN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, 64 x 64 each
-    const int KT = a.K / GBK;
-
-    for (int tile = blockIdx.x; tile < mt * nt; tile += gridDim.x) {
-        const int tm = tile % mt, tn = tile / mt;
-        const int m0 = tm * GBM, n0 = tn * GBN;
-        __syncthreads();
-        if (tid < GBM) {
-            // rows past M read a valid row (every load unconditional, so all are
-            // in flight at once); their results are not written
-            const int m = min(m0 + tid, M - 1);
-            rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
-            if constexpr (EPI == EPI_DOWN) rowtok[tid] = kept_row(a, m);
-        }
-        __syncthreads();
-
-        // each thread moves 4 A chunks and 4 B chunks of 16 bytes per k-tile
-        uint4 ra[4], rb[4];
-        auto gload = [&](int kt) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + q * 256;        // 0..1023
-                const int r = c >> 3, kc = c & 7;   // row, 8-element chunk
-                ra[q] = ld16(a.A + (size_t)rowsrc[r] * a.K + (size_t)kt * GBK + kc * 8);
-                rb[q] = ld16(a.B + (size_t)(n0 + r) * a.K + (size_t)kt * GBK + kc * 8);
-            }
-        };
-        auto sstore = [&]() {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + q * 256;
-                const int r = c >> 3, kc = c & 7;
-                *(uint4 *)&As[r * GLDA + kc * 8] = ra[q];
-                *(uint4 *)&Bs[r * GLDA + kc * 8] = rb[q];
-            }
-        };
-
-        f32x16 acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-        gload(0);
-        sstore();
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-            for (int ks = 0; ks < GBK / 16; ++ks) {
-                bf16x8 fa[2], fb[2];
-                const int kk = ks * 16 + (lane >> 5) * 8;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    fa[i] = *(const bf16x8 *)&As[(wm * 64 + i * 32 + (lane & 31)) * GLDA + kk];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    fb[j] = *(const bf16x8 *)&Bs[(wn * 64 + j * 32 + (lane & 31)) * GLDA + kk];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
-            __syncthreads();
-            if (kt + 1 < KT) {
-                sstore();
-                __syncthreads();
-            }
-        }
-
-        // epilogue.  Output element (row, col) of a 32x32 tile: lane holds
-        // col = lane & 31 and rows 8*g + 4*(lane >> 5) + e for acc index 4*g + e.
-        const int ccol = lane & 31;
-        if constexpr (EPI == EPI_GATE_UP) {
-            // wave columns: [gate of neurons j0..j0+31 | up of the same neurons]
-            const int j = (n0 + wn * 64) / 2 + ccol;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rl = wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
-                        const int m = m0 + rl;
-                        if (m < M) {
-                            const float gv = acc[i][0][4 * g + e], uv = acc[i][1][4 * g + e];
-                            const float h = gv / (1.0f + expf(-gv)) * uv;
-                            a.H[(size_t)m * a.ldo + j] = f32_to_bf16_rne(h);
-                        }
-                    }
-        } else {
-            // the residual rows of every output first (rows past M read their
-            // clamped row), then the guarded stores
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int n = n0 + wn * 64 + j * 32 + ccol;
-                    float y[16];
-#pragma unroll
-                    for (int ge = 0; ge < 16; ++ge) {
-                        const int rl = wm * 64 + i * 32 + 8 * (ge >> 2) + 4 * (lane >> 5) + (ge & 3);
-                        y[ge] = bf16_lo(a.Y[(size_t)rowtok[rl] * a.ldo + n]);
-                    }
-#pragma unroll
-                    for (int ge = 0; ge < 16; ++ge) {
-                        const int rl = wm * 64 + i * 32 + 8 * (ge >> 2) + 4 * (lane >> 5) + (ge & 3);
-                        if (m0 + rl < M)
-                            a.X[(size_t)rowtok[rl] * a.ldo + n] = f32_to_bf16_rne(y[ge] + acc[i][j][ge]);
-                    }
-                }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Large-tile variant: 256 x 256 tiles, four waves of 128 x 128 (4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16, 16 MFMAs per 8 KB of LDS operand reads), both
+// TM x 256 tiles (TM = 256, or 128 when too few 256-row tiles fill the compute
+// units), eight waves of TM / 2 x 64 (blocks of v_mfma_f32_32x32x16_bf16), both
 // operands copied global -> LDS asynchronously (global_load_lds_dwordx4) in
 // slices of 32 along k, four stages deep (three slices in flight while one is
 // consumed).  A copy writes one contiguous kilobyte (sixteen 64-byte rows of 32
@@ -1075,32 +941,36 @@ __device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base
 
 constexpr int gemm_waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// NW waves per workgroup: 4 (2 x 2 waves of 128 x 128) or 8 (2 x 4 waves of
-// 128 x 64, two waves per SIMD; waves w and w + 4 share a SIMD, and the two
-// groups of four alternate between reading a slice's fragments and issuing its
-// products, so each SIMD's matrix unit is fed while the other wave reads)
-template <int EPI, int NW>
+// TM x 256 tiles (TM = 256 or 128 rows).  NW waves per workgroup: 4 (2 x 2
+// waves of 128 x 128, TM = 256) or 8 (2 x 4 waves of TM / 2 x 64, two waves per
+// SIMD; waves w and w + 4 share a SIMD, and the two groups of four alternate
+// between reading a slice's fragments and issuing its products, so each SIMD's
+// matrix unit is fed while the other wave reads)
+template <int EPI, int NW, int TM>
 __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 {
-    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert((NW == 4 && TM == 256) || (NW == 8 && (TM == 256 || TM == 128)), "tile shape");
     constexpr int WNN = NW / 2;            // waves along n
     constexpr int JB = 8 / WNN;            // 32-column blocks per wave (4 or 2)
-    constexpr int QA = BBM / NW / 16;      // 16-row copies per wave and operand (4 or 2)
-    __shared__ __align__(1024) uint16_t As[BSTAGES][BBM * BBK];
+    constexpr int WM = TM / 2;             // rows per wave (128 or 64)
+    constexpr int IB = WM / 32;            // 32-row blocks per wave (4 or 2)
+    constexpr int QAA = TM / NW / 16;      // 16-row copies of A per wave and stage (4, 2 or 1)
+    constexpr int QAB = BBN / NW / 16;     // 16-row copies of B per wave and stage (4 or 2)
+    __shared__ __align__(1024) uint16_t As[BSTAGES][TM * BBK];
     __shared__ __align__(1024) uint16_t Bs[BSTAGES][BBN * BBK];
-    __shared__ int rowsrc[BBM];
-    __shared__ int rowtok[BBM];   // DOWN: the kept token of each tile row (the epilogue's scatter)
+    __shared__ int rowsrc[TM];
+    __shared__ int rowtok[TM];   // DOWN: the kept token of each tile row (the epilogue's scatter)
 
     const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
-    const int mt = (M + BBM - 1) / BBM;
+    const int mt = (M + TM - 1) / TM;
     const int nt = a.N / BBN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w / WNN, wn = w % WNN;
     const int KT = a.K / BBK;
-    // per wave and stage: QA copies of A rows and QA of B rows
-    constexpr int CPS = 2 * QA;
+    // per wave and stage: QAA copies of A rows and QAB of B rows
+    constexpr int CPS = QAA + QAB;
 
     // Workgroups are dealt to the 8 XCDs round-robin; renumbering them so that
     // each XCD walks a contiguous run of tiles (M-tiles fastest) keeps the
@@ -1109,54 +979,56 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
     const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     for (int tile = v; tile < mt * nt; tile += G) {
         const int tm = tile % mt, tn = tile / mt;
-        const int m0 = tm * BBM, n0 = tn * BBN;
+        const int m0 = tm * TM, n0 = tn * BBN;
         __syncthreads();
-        if (tid < BBM) {
+        if (tid < TM) {
             // rows past M read a valid row; their results are not written
             const int m = min(m0 + tid, M - 1);
             rowsrc[tid] = EPI == EPI_GATE_UP ? kept_row(a, m) : m;
             if constexpr (EPI == EPI_DOWN) rowtok[tid] = kept_row(a, m);
         }
         __syncthreads();
-        // this wave copies rows 16 QA w + 16 q + (lane >> 2), q < QA, of both
-        // operands; lane position p = lane & 3 holds logical chunk p ^ ((r >> 2) & 3)
-        constexpr int RW = 16 * QA;   // rows copied per wave
-        uint32_t aoff[QA];   // element offsets of the gathered A rows (< 2^31 for every supported shape)
+        // this wave copies rows 16 Q w + 16 q + (lane >> 2), q < Q, of each operand
+        // (Q = QAA for A, QAB for B); lane position p = lane & 3 holds logical
+        // chunk p ^ ((r >> 2) & 3)
+        constexpr int RWA = 16 * QAA, RWB = 16 * QAB;   // rows copied per wave
+        uint32_t aoff[QAA];   // element offsets of the gathered A rows (< 2^31 for every supported shape)
 #pragma unroll
-        for (int q = 0; q < QA; ++q) {
-            const int r = RW * w + 16 * q + (lane >> 2);
+        for (int q = 0; q < QAA; ++q) {
+            const int r = RWA * w + 16 * q + (lane >> 2);
             aoff[q] = (uint32_t)rowsrc[r] * (uint32_t)a.K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 8);
         }
         // (r >> 2) & 3 does not depend on q (16 q only changes higher bits)
-        const int rb0 = RW * w + (lane >> 2);
+        const int rb0 = RWB * w + (lane >> 2);
         const uint16_t *bsrc = a.B + (size_t)(n0 + rb0) * a.K + (((lane & 3) ^ ((rb0 >> 2) & 3)) * 8);
         auto issue = [&](int kt) {
             const int st = kt % BSTAGES;
 #pragma unroll
-            for (int q = 0; q < QA; ++q) {
-                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(RW * w + 16 * q) * BBK]);
-                lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(RW * w + 16 * q) * BBK]);
-            }
+            for (int q = 0; q < QAA; ++q)
+                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(RWA * w + 16 * q) * BBK]);
+#pragma unroll
+            for (int q = 0; q < QAB; ++q)
+                lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(RWB * w + 16 * q) * BBK]);
         };
 
-        f32x16 acc[4][JB];
+        f32x16 acc[IB][JB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IB; ++i)
 #pragma unroll
             for (int j = 0; j < JB; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
         // the slice's operand fragments of this wave, from LDS into registers
-        bf16x8 fa[BBK / 16][4], fb[BBK / 16][JB];
+        bf16x8 fa[BBK / 16][IB], fb[BBK / 16][JB];
         auto read_frags = [&](int kt) {
             const uint16_t *as = As[kt % BSTAGES], *bs = Bs[kt % BSTAGES];
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks) {
                 const int kc = 2 * ks + (lane >> 5);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = wm * 128 + i * 32 + (lane & 31);
+                for (int i = 0; i < IB; ++i) {
+                    const int r = wm * WM + i * 32 + (lane & 31);
                     fa[ks][i] = *(const bf16x8 *)&as[r * BBK + ((kc ^ ((r >> 2) & 3)) * 8)];
                 }
 #pragma unroll
@@ -1170,7 +1042,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 #pragma unroll
             for (int ks = 0; ks < BBK / 16; ++ks)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < IB; ++i)
 #pragma unroll
                     for (int j = 0; j < JB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
@@ -1249,13 +1121,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
             // wave columns: [gate | up] of neurons nb .. nb + 31 (then of nb + 32 .. nb + 63)
             const int nb = (n0 + wn * 32 * JB) / 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < IB; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     __builtin_amdgcn_sched_barrier(0);   // bound the live values of the epilogue
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int m = m0 + wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                        const int m = m0 + wm * WM + i * 32 + 8 * g + 4 * (lane >> 5) + e;
                         if (m < M) {
 #pragma unroll
                             for (int hb = 0; hb < JB / 2; ++hb) {
@@ -1270,11 +1142,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
             // per group of 4 rows: the residual values first (rows past M read
             // their clamped row), then the guarded stores
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < IB; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     __builtin_amdgcn_sched_barrier(0);
-                    const int rl0 = wm * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+                    const int rl0 = wm * WM + i * 32 + 8 * g + 4 * (lane >> 5);
                     float y[4][JB];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -1383,7 +1255,6 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
         hipLaunchKernelGGL(k_copy_unkept, dim3(rows), dim3(256), 0, c.stream, c.Y, c.X, (const int32_t *)flags, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int mt_max = (rows + GBM - 1) / GBM;
     GemmArgs g{};
     g.A = c.Y; g.B = L.wgu; g.K = d; g.N = 2 * f; g.keep = c.keep; g.count = c.count; g.H = H; g.ldo = f;
     g.rows = rows;
@@ -1393,7 +1264,7 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     L.timer->take(&evb, &eve);
     // one workgroup per compute unit (128 KB of LDS each), looping over tiles
     const int G = gemm_grid(c.stream);
-    SFFN_LAUNCH((k_gemm_big<EPI_GATE_UP, kGemmWaves>), dim3(std::min(tiles1, G)), dim3(kGemmWaves * 64), 0, c.stream,
+    SFFN_LAUNCH((k_gemm_big<EPI_GATE_UP, kGemmWaves, 256>), dim3(std::min(tiles1, G)), dim3(kGemmWaves * 64), 0, c.stream,
                 evb, eve, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmArgs g2{};
@@ -1401,16 +1272,19 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     g2.ldo = d;
     g2.rows = rows;
     // down projection: 256 x 256 tiles when they fill at least half of the compute
-    // units, else 128 x 128 tiles (both launched; the device-side count opens one)
+    // units, else 128 x 256 tiles (both launched; the device-side count opens one)
     const int tiles2 = mt_big * (d / BBN);
-    g2.gate = G / 2;   // measured: 220 big tiles on 256 units beat 880 small ones; 100 do not
+    // measured: 220 tiles of 256 rows on 256 units beat 420 of 128 rows (2.15 against
+    // 2.44 ms per FFN at 2674 rows); with 100 (1143 rows) the 128-row tiles win
+    g2.gate = G / 2;
     g2.gate_big = 1;
-    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves>), dim3(std::min(tiles2, G)), dim3(kGemmWaves * 64), 0,
+    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves, 256>), dim3(std::min(tiles2, G)), dim3(kGemmWaves * 64), 0,
                        c.stream, g2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     g2.gate_big = 0;
-    const int tiles2s = mt_max * (d / GBN);
-    hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(std::min(tiles2s, 2048)), dim3(256), 0, c.stream, g2);
+    const int tiles2s = ((rows + 127) / 128) * (d / BBN);
+    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves, 128>), dim3(std::min(tiles2s, G)), dim3(kGemmWaves * 64), 0,
+                       c.stream, g2);
     return hipGetLastError();
 }
 
