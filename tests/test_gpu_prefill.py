@@ -249,8 +249,8 @@ def test_cfg5_sorted_path_full_length(cfg5, mass):
 def test_large_tile_down_projection_every_row(M):
     """d_model 5120 (20 column tiles of 256): 2048 and 1800 kept rows give 8 row
     tiles of 256, 160 large tiles, at least half of the compute units, which
-    opens the 256 x 256 down-projection kernel; 1000 rows (80 large tiles) run
-    the 128 x 128 one.  Every row is compared with the oracle (the keep list
+    opens the 256 x 256 down-projection tiles; 1000 rows (80 large tiles) run
+    the 128 x 256 ones.  Every row is compared with the oracle (the keep list
     is given by the caller, a seeded random subset with a ragged last tile)."""
     import torch
     w = synth._make_weights(synth.WT_BF16, 5120, 512, synth.ACT_SILU, (741, 742, 743))
