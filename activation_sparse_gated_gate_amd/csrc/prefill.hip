@@ -875,6 +875,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 enum { EPI_GATE_UP = 0, EPI_DOWN = 1 };
+// which of the down projection's launches a GemmArgs opens
+enum { ROLE_SMALL = 0, ROLE_BIG = 1, ROLE_SPLIT = 2 };
 
 struct GemmArgs {
     const uint16_t *A;      // GATE_UP: Y [L][K] gathered through keep; DOWN: H [Mmax][K]
@@ -882,12 +884,14 @@ struct GemmArgs {
     int K, N;
     const int32_t *keep;    // kept token indices
     const int32_t *count;   // device count M
-    uint16_t *H;            // GATE_UP output [Mmax][N/2]
+    uint16_t *H;            // GATE_UP output [Mmax][N/2]; split DOWN: the partial sums go past its row M
     const uint16_t *Y;      // DOWN: residual rows
     uint16_t *X;            // DOWN: output rows (scatter)
     int ldo;                // row length of H (GATE_UP) or X/Y (DOWN)
-    int gate;               // 0: always run; else run only if (256 x 256 tiles >= gate) == (gate_big != 0)
-    int gate_big;
+    int gate;               // 0: always run; else the role decides from the number of 256 x 256 tiles
+    int role;               // ROLE_BIG: tiles >= gate, or a k split; ROLE_SMALL: neither; ROLE_SPLIT: the split's sum
+    int units;              // compute units (one workgroup each)
+    int hrows;              // DOWN: rows H holds
     int rows;               // tokens of the call: the count and the kept indices are clamped to it
 };
 
@@ -896,16 +900,6 @@ struct GemmArgs {
 // an access outside Y, X or H.
 __device__ __forceinline__ int gemm_rows(const GemmArgs &a) { return min(max(*a.count, 0), a.rows); }
 __device__ __forceinline__ int kept_row(const GemmArgs &a, int m) { return min(max(a.keep[m], 0), a.rows - 1); }
-
-// The device-side row count decides between the two tile sizes without a host
-// round trip: with too few 256 x 256 tiles for the compute units, 128 x 256
-// tiles keep more units busy.
-__device__ __forceinline__ bool gemm_gate_open(const GemmArgs &a, int M)
-{
-    if (a.gate == 0) return true;
-    const int big = ((M + 255) / 256) * (a.N / 256);
-    return (big >= a.gate) == (a.gate_big != 0);
-}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 {
@@ -926,6 +920,40 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 // ---------------------------------------------------------------------------
 constexpr int BBM = 256, BBN = 256, BBK = 32, BSTAGES = 4;
 constexpr int kGemmWaves = 8;   // waves per 256 x 256 workgroup
+
+// The down projection's k ranges when too few 256 x 256 tiles fill the compute
+// units (1: no split): among S = 2..8 with K a multiple of 32 S and the S
+// partial sums ([S][M][N] fp32) fitting in H's rows past M, the S with the
+// fewest tile rounds per unit of work (rounds / S), the smallest on ties.
+__device__ __forceinline__ int down_split(const GemmArgs &a, int M)
+{
+    const int tiles = ((M + BBM - 1) / BBM) * (a.N / BBN);
+    int best = 1, br = 0, bs = 0;   // the best cost so far is br / bs (bs = 0: none)
+    for (int S = 2; S <= 8; ++S) {
+        if (a.K % (S * BBK) != 0) continue;
+        if ((size_t)S * M * a.N * 4 > (size_t)(a.hrows - M) * a.K * 2) continue;
+        const int r = (tiles * S + a.units - 1) / a.units;
+        if (bs == 0 || r * bs < br * S) {
+            best = S;
+            br = r;
+            bs = S;
+        }
+    }
+    return best;
+}
+
+// The device-side row count decides between the tile sizes without a host
+// round trip: with too few 256 x 256 tiles for the compute units, the k range
+// is split over more 256 x 256 workgroups when the partial sums fit, else
+// 128 x 256 tiles keep more units busy.
+__device__ __forceinline__ bool gemm_gate_open(const GemmArgs &a, int M)
+{
+    if (a.gate == 0) return true;
+    const int big = ((M + BBM - 1) / BBM) * (a.N / BBN);
+    if (big >= a.gate) return a.role == ROLE_BIG;
+    // the 256 x 256 kernel also runs the split, whose sums ROLE_SPLIT adds
+    return (down_split(a, M) > 1) == (a.role != ROLE_SMALL);
+}
 
 __device__ __forceinline__ void lds_copy16_pf(const void *g, void *lds_wave_base)
 {
@@ -963,12 +991,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
 
     const int M = gemm_rows(a);
     if (!gemm_gate_open(a, M)) return;
+    // the down projection in 256 x 256 tiles with too few of them: S k ranges of
+    // K / S each, S work items per tile, fp32 partial sums instead of the epilogue
+    int S = 1;
+    if constexpr (EPI == EPI_DOWN && TM == 256)
+        if (a.gate != 0 && ((M + BBM - 1) / BBM) * (a.N / BBN) < a.gate) S = down_split(a, M);
     const int mt = (M + TM - 1) / TM;
     const int nt = a.N / BBN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w / WNN, wn = w % WNN;
-    const int KT = a.K / BBK;
+    const int KT = a.K / BBK / S;
     // per wave and stage: QAA copies of A rows and QAB of B rows
     constexpr int CPS = QAA + QAB;
 
@@ -977,9 +1010,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
     // workgroups that share a weight tile on the same L2.
     const int G = gridDim.x;
     const int v = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    for (int tile = v; tile < mt * nt; tile += G) {
-        const int tm = tile % mt, tn = tile / mt;
+    for (int tile = v; tile < mt * nt * S; tile += G) {
+        const int tm = tile % mt, ts = (tile / mt) % S, tn = tile / (mt * S);
         const int m0 = tm * TM, n0 = tn * BBN;
+        const int k0 = ts * (a.K / S);   // first k of the item's range
         __syncthreads();
         if (tid < TM) {
             // rows past M read a valid row; their results are not written
@@ -1000,12 +1034,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
         }
         // (r >> 2) & 3 does not depend on q (16 q only changes higher bits)
         const int rb0 = RWB * w + (lane >> 2);
-        const uint16_t *bsrc = a.B + (size_t)(n0 + rb0) * a.K + (((lane & 3) ^ ((rb0 >> 2) & 3)) * 8);
+        const uint16_t *bsrc = a.B + (size_t)(n0 + rb0) * a.K + k0 + (((lane & 3) ^ ((rb0 >> 2) & 3)) * 8);
         auto issue = [&](int kt) {
             const int st = kt % BSTAGES;
 #pragma unroll
             for (int q = 0; q < QAA; ++q)
-                lds_copy16_pf(a.A + aoff[q] + (size_t)kt * BBK, &As[st][(RWA * w + 16 * q) * BBK]);
+                lds_copy16_pf(a.A + aoff[q] + (size_t)(k0 + kt * BBK), &As[st][(RWA * w + 16 * q) * BBK]);
 #pragma unroll
             for (int q = 0; q < QAB; ++q)
                 lds_copy16_pf(bsrc + (size_t)q * 16 * a.K + (size_t)kt * BBK, &Bs[st][(RWB * w + 16 * q) * BBK]);
@@ -1138,6 +1172,24 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
                         }
                     }
                 }
+        } else if (S > 1) {
+            // the item's fp32 partial sums of rows m < M: [S][M][N] past H's row M
+            float *part = (float *)(a.H + (size_t)M * a.K) + (size_t)ts * M * a.N;
+#pragma unroll
+            for (int i = 0; i < IB; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + wm * WM + i * 32 + 8 * g + 4 * (lane >> 5) + e;
+                        if (m < M) {
+#pragma unroll
+                            for (int j = 0; j < JB; ++j)
+                                part[(size_t)m * a.N + n0 + wn * 32 * JB + j * 32 + ccol] = acc[i][j][4 * g + e];
+                        }
+                    }
+                }
         } else {
             // per group of 4 rows: the residual values first (rows past M read
             // their clamped row), then the guarded stores
@@ -1164,6 +1216,36 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_big(const GemmArgs a)
                     }
                 }
         }
+    }
+}
+
+// The split down projection's partial sums added in k-range order, then the
+// residual and the scatter: X[keep[m]][n] = bf16(Y[keep[m]][n] + sum_s part[s][m][n]),
+// four columns per thread.
+__global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs a)
+{
+    const int M = gemm_rows(a);
+    if (!gemm_gate_open(a, M)) return;
+    const int S = down_split(a, M);
+    const float *part = (const float *)(a.H + (size_t)M * a.K);
+    const int q4 = a.N / 4;
+    const size_t total = (size_t)M * q4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const int m = (int)(i / q4), n = (int)(i % q4) * 4;
+        float4 z = *(const float4 *)(part + (size_t)m * a.N + n);
+        for (int t = 1; t < S; ++t) {
+            const float4 p = *(const float4 *)(part + ((size_t)t * M + m) * a.N + n);
+            z.x += p.x;
+            z.y += p.y;
+            z.z += p.z;
+            z.w += p.w;
+        }
+        const size_t o = (size_t)kept_row(a, m) * a.ldo + n;
+        const float y0 = bf16_lo(a.Y[o]), y1 = bf16_lo(a.Y[o + 1]), y2 = bf16_lo(a.Y[o + 2]), y3 = bf16_lo(a.Y[o + 3]);
+        a.X[o] = f32_to_bf16_rne(y0 + z.x);
+        a.X[o + 1] = f32_to_bf16_rne(y1 + z.y);
+        a.X[o + 2] = f32_to_bf16_rne(y2 + z.z);
+        a.X[o + 3] = f32_to_bf16_rne(y3 + z.w);
     }
 }
 
@@ -1271,17 +1353,25 @@ hipError_t launch_prefill_forward(const PrefillForwardCall &c)
     g2.A = H; g2.B = L.wdp; g2.K = f; g2.N = d; g2.keep = c.keep; g2.count = c.count; g2.Y = c.Y; g2.X = c.X;
     g2.ldo = d;
     g2.rows = rows;
+    g2.H = H;
+    g2.hrows = L.desc.max_rows;
+    g2.units = G;
     // down projection: 256 x 256 tiles when they fill at least half of the compute
-    // units, else 128 x 256 tiles (both launched; the device-side count opens one)
+    // units; else the k range split over more 256 x 256 workgroups with a
+    // fixed-order sum of the partial sums when they fit in H's free rows, else
+    // 128 x 256 tiles (all launched; the device-side count opens one path)
     const int tiles2 = mt_big * (d / BBN);
     // measured: 220 tiles of 256 rows on 256 units beat 420 of 128 rows (2.15 against
-    // 2.44 ms per FFN at 2674 rows); with 100 (1143 rows) the 128-row tiles win
+    // 2.44 ms per FFN at 2674 rows)
     g2.gate = G / 2;
-    g2.gate_big = 1;
-    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves, 256>), dim3(std::min(tiles2, G)), dim3(kGemmWaves * 64), 0,
-                       c.stream, g2);
+    g2.role = ROLE_BIG;
+    hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves, 256>), dim3(std::max(1, std::min(tiles2 * 8, G))),
+                       dim3(kGemmWaves * 64), 0, c.stream, g2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    g2.gate_big = 0;
+    g2.role = ROLE_SPLIT;
+    hipLaunchKernelGGL(k_split_reduce, dim3(4 * G), dim3(256), 0, c.stream, g2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    g2.role = ROLE_SMALL;
     const int tiles2s = ((rows + 127) / 128) * (d / BBN);
     hipLaunchKernelGGL((k_gemm_big<EPI_DOWN, kGemmWaves, 128>), dim3(std::min(tiles2s, G)), dim3(kGemmWaves * 64), 0,
                        c.stream, g2);

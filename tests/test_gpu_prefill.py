@@ -273,6 +273,52 @@ def test_large_tile_down_projection_every_row(M):
     layer.close()
 
 
+def _down_split(M, d, f, hrows, units):
+    """The k ranges the down projection splits into for M kept rows: 0 for
+    256 x 256 tiles, 1 for 128 x 256 tiles, else S (the kernel's rule restated
+    so that a test can assert which path it covers)."""
+    tiles = -(-M // 256) * (d // 256)
+    if tiles >= units // 2:
+        return 0
+    best, br, bs = 1, 0, 0
+    for S in range(2, 9):
+        if f % (32 * S) or S * M * d * 4 > (hrows - M) * f * 2:
+            continue
+        r = -(-tiles * S // units)
+        if bs == 0 or r * bs < br * S:
+            best, br, bs = S, r, S
+    return best
+
+
+@pytest.mark.parametrize("d,f,L,M", [(256, 4096, 512, 200), (512, 4096, 600, 300), (1024, 2048, 1500, 257)])
+def test_split_k_down_projection_every_row(d, f, L, M):
+    """Few kept rows with room for the partial sums past them in H: the down
+    projection splits its k range over several 256 x 256 workgroups and adds
+    the partial sums in a fixed order (a ragged last row tile).  Every row is
+    compared with the oracle, and a second run gives the same bits."""
+    import torch
+    units = torch.cuda.get_device_properties(0).multi_processor_count
+    assert _down_split(M, d, f, L, units) >= 2
+    w = synth._make_weights(synth.WT_BF16, d, f, synth.ACT_SILU, (761, 762, 763))
+    Y, _ = synth.cfg5_activations(L=L, d=d)
+    rng = np.random.default_rng(764 + M)
+    keep = np.sort(rng.choice(L, size=M, replace=False)).astype(np.int32)
+    layer = make_prefill_layer(w, L)
+    kt = torch.from_numpy(keep).to("cuda:0")
+    ct = torch.tensor([M], dtype=torch.int32, device="cuda:0")
+    X = gpu_forward(layer, Y, kt, ct)
+    assert np.array_equal(gpu_forward(layer, Y, kt, ct), X)
+    ref = oracle.prefill(w, Y, keep)
+    Xf, Rf = synth.bf16_bits_to_f32(X), synth.bf16_bits_to_f32(ref)
+    assert np.isfinite(Xf[keep]).all()
+    errs = np.array([rel_l2(Xf[i], Rf[i]) for i in keep])
+    assert rel_l2(Xf[keep], Rf[keep]) <= 2e-3, rel_l2(Xf[keep], Rf[keep])
+    assert errs.max() <= ROW_SANITY, (errs.max(), int(keep[int(np.argmax(errs))]))
+    rest = np.setdiff1d(np.arange(L), keep)
+    assert np.array_equal(X[rest], Y[rest])
+    layer.close()
+
+
 def test_forward_without_a_list_uses_the_last_selection(small):
     """sffn_forward(TOKENS) with no keep list runs on the selection the last
     sffn_select or sffn_select_blocks call left in the same scratch."""
